@@ -1,0 +1,57 @@
+"""Top-k sparse multi-query attention oracle (float64).  Test infrastructure only.
+
+Source: the decoder's sparse attention takes Q, the KV cache and an index; the
+KV rows it attends to are fetched through a page table ([V32] section
+实验方法和结果).  Every query head of a row shares the same latent KV rows
+(multi-query).  The result depends on the index *set* only; the order of the
+indices is a rounding effect of the blockwise merge, not part of the
+definition ([V32] sections 实验方法和结果, 结论 and 进一步探索 eq. (1)(2)).
+
+For row r, head h, over the multiset J_r = {idx[r, t] : idx[r, t] >= 0}:
+
+    s_j = scale * q[r,h,:] . kv[j, :]            (all d_qk columns)
+    o   = sum_{j in J_r} softmax(s)_j * kv[j, :d_v]  (V = first d_v columns)
+    lse = max_j s_j + ln sum_j exp(s_j - max)
+
+Negative entries are padding and are skipped; a repeated index counts with its
+multiplicity; an empty set gives o = 0, lse = -inf.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["sparse_mqa"]
+
+
+def sparse_mqa(q, kv_latent, topk_idx, d_v: int, scale: float, rows=None):
+    """q [R, H, d_qk], kv_latent [n_kv, d_qk], topk_idx int [R, k].
+
+    rows: optional subset of query rows to evaluate (others NaN).
+    Returns out [R, H, d_v] float64 and lse [H, R] float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    kv = np.asarray(kv_latent, dtype=np.float64)
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    n_rows, heads, d_qk = q.shape
+    if kv.shape[1] != d_qk or not (0 < d_v <= d_qk):
+        raise ValueError("bad latent dims")
+    if idx.size and idx.max() >= kv.shape[0]:
+        raise ValueError("index out of range")
+    row_list = range(n_rows) if rows is None else sorted(set(int(r) for r in rows))
+    fill = 0.0 if rows is None else np.nan
+    out = np.full((n_rows, heads, d_v), fill)
+    lse = np.full((heads, n_rows), fill)
+    for r in row_list:
+        sel = idx[r][idx[r] >= 0]
+        if sel.size == 0:
+            out[r] = 0.0
+            lse[:, r] = -np.inf
+            continue
+        kr = kv[sel]                                  # gathered rows [n, d_qk]
+        logits = float(scale) * (q[r] @ kr.T)         # [H, n]
+        m = logits.max(axis=1)
+        e = np.exp(logits - m[:, None])
+        l_sum = e.sum(axis=1)
+        out[r] = (e @ kr[:, :d_v]) / l_sum[:, None]
+        lse[:, r] = m + np.log(l_sum)
+    return out, lse

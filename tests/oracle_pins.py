@@ -1,0 +1,486 @@
+"""Pins that tie the float64 oracle to facts other than itself.
+
+Each pin is a function taking the oracle module (or a mutated stand-in) and
+raising AssertionError when the oracle disagrees with:
+
+* a closed form (zero query -> mean of visible V rows; one-hot logits select
+  one V row; RoPE of position 0 is the identity; pair norms are kept),
+* brute force with pure-Python loops and ``math.fsum`` on tiny inputs,
+* an independent library implementation (torch CPU float64
+  ``scaled_dot_product_attention``, scipy ``logsumexp``, complex128 rotation),
+* an algebraic identity (the blockwise online-softmax merge of
+  「推理引擎的“蝴蝶效应” -- 从V32 模型的输出不一致说起」 section 进一步探索, eq. (1)(2)),
+* invariants (permutation of a sparse index row, packing of sequences,
+  grouped-query = repeated heads, relative-position property of RoPE).
+
+``tests/test_oracle_pins.py`` runs every pin on the oracle;
+``tests/test_oracle_mutants.py`` plants plausible mistakes in the oracle and
+checks that some pin fails for each.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from vision_encoder_attention_amd import workloads as W
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _cu(lengths):
+    return np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+
+
+def _visible(i, lq, lk, causal):
+    """Keys row i (local) may see — restated here from the causal reading
+    (bottom-right alignment), independently of the oracle's helper."""
+    if not causal:
+        return lk
+    return max(0, min(lk, i + lk - lq + 1))
+
+
+# =========================================================== dense attention
+
+def pin_zero_query_mean(orc):
+    """q = 0: every visible key has the same logit, so o_i is the mean of the
+    visible V rows and lse_i = ln(#visible); scale = 0 gives the same."""
+    rng = _rng(101)
+    lq, lk = [5, 1, 9, 4], [5, 3, 12, 0]
+    hq, hkv, d = 4, 2, 8
+    tq, tk = sum(lq), sum(lk)
+    k = rng.standard_normal((tk, hkv, d))
+    v = rng.standard_normal((tk, hkv, d))
+    for causal in (False, True):
+        for q, scale in ((np.zeros((tq, hq, d)), 0.7), (rng.standard_normal((tq, hq, d)), 0.0)):
+            out, lse = orc.attention(q, k, v, _cu(lq), _cu(lk), causal, scale)
+            cq, ck = _cu(lq), _cu(lk)
+            for b in range(len(lq)):
+                for i in range(lq[b]):
+                    n = _visible(i, lq[b], lk[b], causal)
+                    for h in range(hq):
+                        g = h // (hq // hkv)
+                        row = cq[b] + i
+                        if n == 0:
+                            assert np.all(out[row, h] == 0) and lse[h, row] == -np.inf
+                        else:
+                            want = v[ck[b]:ck[b] + n, g].mean(axis=0)
+                            assert np.allclose(out[row, h], want, rtol=0, atol=1e-14)
+                            assert abs(lse[h, row] - math.log(n)) < 1e-14
+
+
+def pin_one_hot_select(orc):
+    """k_j = e_j and q_i = c e_{pi_g(i)} with c*scale = 100: s_ij is 100 at
+    j = pi_g(i) and 0 elsewhere, so o_i = v_{pi_g(i)} up to (n-1) e^-100 and
+    lse_i = 100 + ln(1 + (n-1) e^-100).  A different permutation per key/value
+    head pins the head mapping, the q-vs-k roles and the V row index."""
+    rng = _rng(102)
+    lq, lk = [6, 7], [6, 7]
+    hq, hkv, d = 4, 2, 8
+    cq, ck = _cu(lq), _cu(lk)
+    scale = 0.25
+    c = 100.0 / scale
+    q = np.zeros((sum(lq), hq, d))
+    k = np.zeros((sum(lk), hkv, d))
+    v = rng.standard_normal((sum(lk), hkv, d))
+    perms = {}
+    for b in range(2):
+        for j in range(lk[b]):
+            k[ck[b] + j, :, j] = 1.0
+        for h in range(hq):
+            g = h // (hq // hkv)
+            p = perms.setdefault((b, g), rng.permutation(lk[b]))
+            for i in range(lq[b]):
+                q[cq[b] + i, h, p[i]] = c
+    out, lse = orc.attention(q, k, v, cq, ck, False, scale)
+    for b in range(2):
+        n = lk[b]
+        for h in range(hq):
+            g = h // (hq // hkv)
+            for i in range(lq[b]):
+                row = cq[b] + i
+                want = v[ck[b] + perms[(b, g)][i], g]
+                assert np.allclose(out[row, h], want, rtol=0, atol=1e-35 + 1e-40)
+                assert abs(lse[h, row] - (100.0 + math.log1p((n - 1) * math.exp(-100.0)))) < 1e-12
+
+
+def _brute(q, k, v, lq, lk, causal, scale):
+    """Pure-Python loops, math.exp and math.fsum; no numpy arithmetic."""
+    cq, ck = _cu(lq), _cu(lk)
+    hq, hkv = q.shape[1], k.shape[1]
+    d, dv = q.shape[2], v.shape[2]
+    out = [[[0.0] * dv for _ in range(hq)] for _ in range(sum(lq))]
+    lse = [[0.0] * sum(lq) for _ in range(hq)]
+    for b in range(len(lq)):
+        for h in range(hq):
+            g = h // (hq // hkv)
+            for i in range(lq[b]):
+                row = int(cq[b]) + i
+                n = _visible(i, lq[b], lk[b], causal)
+                if n == 0:
+                    lse[h][row] = -math.inf
+                    continue
+                s = [scale * math.fsum(float(q[row, h, c]) * float(k[ck[b] + j, g, c]) for c in range(d))
+                     for j in range(n)]
+                m = max(s)
+                e = [math.exp(x - m) for x in s]
+                tot = math.fsum(e)
+                for c in range(dv):
+                    out[row][h][c] = math.fsum(e[j] * float(v[ck[b] + j, g, c]) for j in range(n)) / tot
+                lse[h][row] = m + math.log(tot)
+    return np.array(out), np.array(lse)
+
+
+def pin_brute_force(orc):
+    """Tiny packed batches (L_q != L_k, empty sequences, GQA, both masks)
+    against pure-Python loops."""
+    for seed, (lq, lk, hq, hkv) in enumerate([([3, 0, 5], [4, 2, 5], 4, 2), ([1, 6], [7, 3], 2, 1),
+                                              ([4], [4], 3, 3)]):
+        rng = _rng(200 + seed)
+        d, dv = 4, 3
+        q = rng.standard_normal((sum(lq), hq, d))
+        k = rng.standard_normal((sum(lk), hkv, d))
+        v = rng.standard_normal((sum(lk), hkv, dv))
+        for causal in (False, True):
+            o1, l1 = orc.attention(q, k, v, _cu(lq), _cu(lk), causal, 0.6)
+            o2, l2 = _brute(q, k, v, lq, lk, causal, 0.6)
+            assert np.allclose(o1, o2, rtol=0, atol=1e-14)
+            fin = np.isfinite(l2)
+            assert np.array_equal(fin, np.isfinite(l1))
+            assert np.allclose(l1[fin], l2[fin], rtol=0, atol=1e-14)
+
+
+def pin_torch_sdpa(orc):
+    """torch CPU float64 scaled_dot_product_attention with an explicit boolean
+    mask (an independent implementation of the same definition), GQA via
+    repeated heads, rows that all see at least one key."""
+    import torch
+    rng = _rng(103)
+    lq, lk = [37, 64, 5], [37, 80, 9]
+    hq, hkv, d = 6, 2, 16
+    q = rng.standard_normal((sum(lq), hq, d))
+    k = rng.standard_normal((sum(lk), hkv, d))
+    v = rng.standard_normal((sum(lk), hkv, d))
+    cq, ck = _cu(lq), _cu(lk)
+    for causal in (False, True):
+        out, lse = orc.attention(q, k, v, cq, ck, causal, 0.3)
+        for b in range(3):
+            qt = torch.from_numpy(q[cq[b]:cq[b + 1]]).permute(1, 0, 2)             # [H, Lq, d]
+            kt = torch.from_numpy(k[ck[b]:ck[b + 1]]).permute(1, 0, 2).repeat_interleave(hq // hkv, 0)
+            vt = torch.from_numpy(v[ck[b]:ck[b + 1]]).permute(1, 0, 2).repeat_interleave(hq // hkv, 0)
+            mask = torch.ones(lq[b], lk[b], dtype=torch.bool)
+            if causal:
+                mask = torch.tril(mask, diagonal=lk[b] - lq[b])
+            ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=0.3)
+            assert np.allclose(out[cq[b]:cq[b + 1]], ref.permute(1, 0, 2).numpy(), rtol=0, atol=1e-13)
+            # lse against scipy's logsumexp of the masked logits
+            from scipy.special import logsumexp
+            s = 0.3 * torch.einsum("hid,hjd->hij", qt, kt).numpy()
+            s = np.where(mask.numpy()[None], s, -np.inf)
+            assert np.allclose(lse[:, cq[b]:cq[b + 1]], logsumexp(s, axis=2), rtol=0, atol=1e-12)
+
+
+def pin_online_merge(orc):
+    """Blockwise online softmax with the merge of eq. (1)(2) (and the matching
+    O merge) over random key blocks equals the oracle's two-pass result."""
+    rng = _rng(104)
+    lq = lk = 50
+    d = 8
+    q = rng.standard_normal((lq, 1, d)) * 3
+    k = rng.standard_normal((lk, 1, d))
+    v = rng.standard_normal((lk, 1, d))
+    out, lse = orc.attention(q, k, v, _cu([lq]), _cu([lk]), False, 0.5)
+    for trial in range(5):
+        cuts = np.sort(rng.choice(np.arange(1, lk), size=rng.integers(1, 8), replace=False))
+        bounds = [0] + list(cuts) + [lk]
+        for i in range(lq):
+            m, s, o = -np.inf, 0.0, np.zeros(d)
+            for a, z in zip(bounds[:-1], bounds[1:]):
+                sb = 0.5 * (k[a:z, 0] @ q[i, 0])
+                mb = sb.max()
+                eb = np.exp(sb - mb)
+                m_new = max(m, mb)                                     # eq. (1)
+                wa, wb = math.exp(m - m_new), math.exp(mb - m_new)
+                s_new = wa * s + wb * eb.sum()                         # eq. (2)
+                o = (wa * s * o + wb * (eb @ v[a:z, 0])) / s_new      # same weights on O
+                m, s = m_new, s_new
+            assert np.allclose(out[i, 0], o, rtol=0, atol=1e-13)
+            assert abs(lse[0, i] - (m + math.log(s))) < 1e-13
+
+
+def pin_single_key_and_causal_edges(orc):
+    """One key: lse = s_00 and o = v_0.  Causal row 0 (L_q = L_k) sees only
+    key 0.  Causal with L_q = L_k = 1 equals non-causal.  A causal row with
+    L_q > L_k near the top sees nothing (o = 0, lse = -inf)."""
+    rng = _rng(105)
+    d = 5
+    q = rng.standard_normal((1, 1, d))
+    k = rng.standard_normal((1, 1, d))
+    v = rng.standard_normal((1, 1, d))
+    for causal in (False, True):
+        out, lse = orc.attention(q, k, v, _cu([1]), _cu([1]), causal, 0.9)
+        assert np.allclose(out[0, 0], v[0, 0], rtol=0, atol=1e-15)
+        assert abs(lse[0, 0] - 0.9 * float(q[0, 0] @ k[0, 0])) < 1e-14
+    q = rng.standard_normal((6, 1, d))
+    k = rng.standard_normal((6, 1, d))
+    v = rng.standard_normal((6, 1, d))
+    out, lse = orc.attention(q, k, v, _cu([6]), _cu([6]), True, 0.9)
+    assert np.allclose(out[0, 0], v[0, 0], rtol=0, atol=1e-15)
+    q = rng.standard_normal((5, 1, d))
+    k = rng.standard_normal((2, 1, d))
+    v = rng.standard_normal((2, 1, d))
+    out, lse = orc.attention(q, k, v, _cu([5]), _cu([2]), True, 0.9)
+    assert np.all(out[:3] == 0) and np.all(lse[0, :3] == -np.inf)
+    assert np.allclose(out[3, 0], v[0, 0], rtol=0, atol=1e-15)
+
+
+def pin_packing_and_gqa(orc):
+    """A packed batch equals separate single-sequence calls (exactly), and
+    grouped-query attention equals multi-head attention with each key/value
+    head repeated for its group (exactly)."""
+    rng = _rng(106)
+    lq, lk = [7, 3, 11], [9, 3, 11]
+    hq, hkv, d = 6, 3, 8
+    q = rng.standard_normal((sum(lq), hq, d))
+    k = rng.standard_normal((sum(lk), hkv, d))
+    v = rng.standard_normal((sum(lk), hkv, d))
+    cq, ck = _cu(lq), _cu(lk)
+    for causal in (False, True):
+        out, lse = orc.attention(q, k, v, cq, ck, causal, 0.4)
+        for b in range(3):
+            o1, l1 = orc.attention(q[cq[b]:cq[b + 1]], k[ck[b]:ck[b + 1]], v[ck[b]:ck[b + 1]],
+                                   _cu([lq[b]]), _cu([lk[b]]), causal, 0.4)
+            assert np.array_equal(o1, out[cq[b]:cq[b + 1]])
+            assert np.array_equal(l1, lse[:, cq[b]:cq[b + 1]])
+        k_rep = np.repeat(k, hq // hkv, axis=1)
+        v_rep = np.repeat(v, hq // hkv, axis=1)
+        o2, l2 = orc.attention(q, k_rep, v_rep, cq, ck, causal, 0.4)
+        assert np.array_equal(o2, out) and np.array_equal(l2, lse)
+
+
+def pin_probs(orc):
+    """Debug probabilities of a piece: every row sums to 1 (to 1e-14), P V of
+    the piece equals the attention output of its rows, and the piece returned
+    starts at its own first row."""
+    rng = _rng(107)
+    lq = lk = 40
+    hq, hkv, d = 2, 1, 8
+    q = rng.standard_normal((lq, hq, d))
+    k = rng.standard_normal((lk, hkv, d))
+    v = rng.standard_normal((lk, hkv, d))
+    for causal in (False, True):
+        out, _ = orc.attention(q, k, v, _cu([lq]), _cu([lk]), causal, 0.5)
+        for q0, rows in ((0, 13), (13, 13), (26, 14)):
+            p = orc.attn_probs(q, k, _cu([lq]), _cu([lk]), causal, 0.5, head=1, seq=0, q0=q0, rows=rows)
+            assert p.shape == (rows, lk)
+            assert np.allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+            assert np.allclose(p @ v[:, 0], out[q0:q0 + rows, 1], rtol=0, atol=1e-14)
+            if causal:
+                beyond = np.arange(lk)[None, :] > (q0 + np.arange(rows))[:, None]
+                assert np.all(p[beyond] == 0) and np.all(p[~beyond] > 0)
+
+
+def pin_row_subset(orc):
+    """Evaluating a subset of rows/heads gives the same values as the full call."""
+    rng = _rng(108)
+    lq, lk = [20, 30], [25, 30]
+    q = rng.standard_normal((50, 4, 8))
+    k = rng.standard_normal((55, 2, 8))
+    v = rng.standard_normal((55, 2, 8))
+    for causal in (False, True):
+        out, lse = orc.attention(q, k, v, _cu(lq), _cu(lk), causal, 0.3)
+        rows = np.array([0, 7, 19, 20, 33, 49])
+        o2, l2 = orc.attention(q, k, v, _cu(lq), _cu(lk), causal, 0.3, rows=rows, heads=[1, 3])
+        assert np.array_equal(o2[rows][:, [1, 3]], out[rows][:, [1, 3]])
+        assert np.array_equal(l2[[1, 3]][:, rows], lse[[1, 3]][:, rows])
+
+
+DENSE_PINS = [pin_zero_query_mean, pin_one_hot_select, pin_brute_force, pin_torch_sdpa, pin_online_merge,
+              pin_single_key_and_causal_edges, pin_packing_and_gqa, pin_probs, pin_row_subset]
+
+
+# ====================================================================== RoPE
+
+def pin_rope_identity_and_norm(orc):
+    """Position 0 is the identity; every rotated pair keeps its length."""
+    rng = _rng(301)
+    x = rng.standard_normal((9, 3, 16))
+    assert np.array_equal(orc.rope_1d(x, np.zeros(9, np.int64), 1e4), x)
+    assert np.array_equal(orc.rope_2d(x, np.zeros((9, 2), np.int64), 1e4), x)
+    pos = rng.integers(0, 5000, 9)
+    y = orc.rope_1d(x, pos, 1e4)
+    assert np.allclose(np.hypot(y[..., 0::2], y[..., 1::2]), np.hypot(x[..., 0::2], x[..., 1::2]),
+                       rtol=1e-14, atol=0)
+
+
+def pin_rope_complex(orc):
+    """Adjacent pairs as complex numbers z = x[2i] + i x[2i+1]: RoPE multiplies
+    z by e^{i phi} with phi = pos * theta^(-2i/d) (complex128), i.e. a
+    counter-clockwise turn by an angle whose per-pair frequency starts at 1
+    and falls geometrically by theta^(-2/d) per pair."""
+    rng = _rng(302)
+    d, theta = 12, 500.0
+    x = rng.standard_normal((7, 2, d))
+    pos = np.array([0, 1, 2, 3, 10, 100, 977])
+    y = orc.rope_1d(x, pos, theta)
+    freq = theta ** (-np.arange(0, d, 2) / d)                 # 1, theta^-2/d, theta^-4/d, ...
+    z = (x[..., 0::2] + 1j * x[..., 1::2]) * np.exp(1j * pos[:, None, None] * freq[None, None, :])
+    assert np.allclose(y[..., 0::2], z.real, rtol=0, atol=1e-12)
+    assert np.allclose(y[..., 1::2], z.imag, rtol=0, atol=1e-12)
+    # recovered angle of a unit vector, pair by pair
+    e = np.zeros((1, 1, d))
+    e[..., 0::2] = 1.0
+    ang = orc.rope_1d(e, np.array([1]), theta)
+    got = np.arctan2(ang[0, 0, 1::2], ang[0, 0, 0::2])
+    assert abs(got[0] - 1.0) < 1e-15
+    assert np.allclose(got[1:] / got[:-1], theta ** (-2.0 / d), rtol=1e-12, atol=0)
+
+
+def pin_rope_relative(orc):
+    """<R(p) q, R(p') k> depends only on p - p'."""
+    rng = _rng(303)
+    d = 16
+    q = rng.standard_normal((1, 1, d))
+    k = rng.standard_normal((1, 1, d))
+    vals = []
+    for p in (5, 40, 1234):
+        rq = orc.rope_1d(q, np.array([p]), 1e4)
+        rk = orc.rope_1d(k, np.array([p - 3]), 1e4)
+        vals.append(float((rq * rk).sum()))
+    assert np.allclose(vals, vals[0], rtol=0, atol=1e-12)
+
+
+def pin_rope_2d_halves(orc):
+    """2D with column 0 leaves the second half untouched and turns the first
+    half like a 1D rotation of width d/2 by the row; with row 0 the mirror
+    holds for the column."""
+    rng = _rng(304)
+    d = 16
+    x = rng.standard_normal((6, 2, d))
+    rows = np.array([0, 1, 5, 9, 76, 33])
+    pos = np.stack([rows, np.zeros(6, np.int64)], 1)
+    y = orc.rope_2d(x, pos, 1e4)
+    assert np.array_equal(y[..., d // 2:], x[..., d // 2:])
+    assert np.allclose(y[..., :d // 2], orc.rope_1d(x[..., :d // 2], rows, 1e4), rtol=0, atol=1e-15)
+    pos = np.stack([np.zeros(6, np.int64), rows], 1)
+    y = orc.rope_2d(x, pos, 1e4)
+    assert np.array_equal(y[..., :d // 2], x[..., :d // 2])
+    assert np.allclose(y[..., d // 2:], orc.rope_1d(x[..., d // 2:], rows, 1e4), rtol=0, atol=1e-15)
+
+
+def pin_qkv_split(orc):
+    """Column layout [Q heads | K heads | V heads]: at position 0 q[t,h,c] is
+    column h*d + c and k[t,g,c] is column (Hq + g)*d + c."""
+    hq, hkv, d, t = 3, 2, 4, 5
+    x = np.tile(np.arange((hq + 2 * hkv) * d, dtype=np.float64), (t, 1)) + 1000 * np.arange(t)[:, None]
+    q, k = orc.qkv_rope(x, np.zeros(t, np.int64), 1e4, hq, hkv, d)
+    for h in range(hq):
+        assert np.array_equal(q[:, h, :], x[:, h * d:(h + 1) * d])
+    for g in range(hkv):
+        assert np.array_equal(k[:, g, :], x[:, (hq + g) * d:(hq + g + 1) * d])
+    # 1D vs 2D chosen by the positions' rank
+    rng = _rng(305)
+    x = rng.standard_normal((t, (hq + 2 * hkv) * d))
+    p1 = np.arange(t)
+    q1, _ = orc.qkv_rope(x, p1, 1e4, hq, hkv, d)
+    assert np.allclose(q1, orc.rope_1d(x[:, :hq * d].reshape(t, hq, d), p1, 1e4), rtol=0, atol=0)
+
+
+ROPE_PINS = [pin_rope_identity_and_norm, pin_rope_complex, pin_rope_relative, pin_rope_2d_halves, pin_qkv_split]
+
+
+# ================================================================ sparse MQA
+
+def _sparse_small(seed, rows=4, heads=5, n_kv=30, d_qk=12, k=9):
+    rng = _rng(seed)
+    q = rng.standard_normal((rows, heads, d_qk))
+    kv = rng.standard_normal((n_kv, d_qk))
+    idx = np.stack([rng.permutation(n_kv)[:k] for _ in range(rows)]).astype(np.int64)
+    return q, kv, idx
+
+
+def pin_sparse_permutation(orc):
+    """Result depends on the index set only: permuting each row changes the
+    output by rounding at most."""
+    q, kv, idx = _sparse_small(401)
+    o1, l1 = orc.sparse_mqa(q, kv, idx, 8, 0.3)
+    o2, l2 = orc.sparse_mqa(q, kv, W.permute_rows(idx.astype(np.int32), 9), 8, 0.3)
+    assert np.allclose(o1, o2, rtol=0, atol=1e-14) and np.allclose(l1, l2, rtol=0, atol=1e-14)
+
+
+def pin_sparse_brute(orc):
+    """Pure-Python loops over the selected rows (V = first d_v columns)."""
+    q, kv, idx = _sparse_small(402, rows=3, heads=2, n_kv=10, d_qk=5, k=4)
+    idx[1, 2] = -1                                  # one padding entry
+    dv = 3
+    out, lse = orc.sparse_mqa(q, kv, idx, dv, 0.7)
+    for r in range(3):
+        sel = [int(j) for j in idx[r] if j >= 0]
+        for h in range(2):
+            s = [0.7 * math.fsum(q[r, h, c] * kv[j, c] for c in range(5)) for j in sel]
+            m = max(s)
+            e = [math.exp(x - m) for x in s]
+            tot = math.fsum(e)
+            for c in range(dv):
+                want = math.fsum(e[t] * kv[sel[t], c] for t in range(len(sel))) / tot
+                assert abs(out[r, h, c] - want) < 1e-14
+            assert abs(lse[h, r] - (m + math.log(tot))) < 1e-14
+
+
+def pin_sparse_reductions(orc):
+    """k = n_kv in order equals dense non-causal attention of each row's heads
+    over the whole latent (torch CPU float64 SDPA); k = 1 gives o = v_idx and
+    lse = s; padding entries are skipped; a repeated index counts twice;
+    an all-padding row gives o = 0, lse = -inf."""
+    import torch
+    rng = _rng(403)
+    rows, heads, n_kv, d_qk, dv = 3, 4, 11, 10, 6
+    q = rng.standard_normal((rows, heads, d_qk))
+    kv = rng.standard_normal((n_kv, d_qk))
+    idx = np.tile(np.arange(n_kv), (rows, 1))
+    out, lse = orc.sparse_mqa(q, kv, idx, dv, 0.4)
+    kt = torch.from_numpy(kv)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(q), kt, kt[..., :dv], scale=0.4)
+    assert np.allclose(out, ref.numpy(), rtol=0, atol=1e-13)
+    one = rng.integers(0, n_kv, (rows, 1))
+    o1, l1 = orc.sparse_mqa(q, kv, one, dv, 0.4)
+    for r in range(rows):
+        assert np.allclose(o1[r], np.broadcast_to(kv[one[r, 0], :dv], (heads, dv)), rtol=0, atol=1e-15)
+        assert np.allclose(l1[:, r], 0.4 * (q[r] @ kv[one[r, 0]]), rtol=0, atol=1e-14)
+    pad = np.array([[3, -1, 5, -7], [-1, -1, -1, -1], [2, 2, 9, -1]])
+    o2, l2 = orc.sparse_mqa(q, kv, pad, dv, 0.4)
+    o3, l3 = orc.sparse_mqa(q[:1], kv, np.array([[3, 5]]), dv, 0.4)
+    assert np.allclose(o2[0], o3[0], rtol=0, atol=1e-15)
+    assert np.all(o2[1] == 0) and np.all(l2[:, 1] == -np.inf)
+    # duplicate: rows {2, 2, 9} = dense attention over keys [kv2, kv2, kv9]
+    k3 = torch.from_numpy(kv[[2, 2, 9]])[None]
+    ref3 = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(q[2:3]), k3, k3[..., :dv], scale=0.4)
+    assert np.allclose(o2[2], ref3.numpy()[0], rtol=0, atol=1e-14)
+
+
+SPARSE_PINS = [pin_sparse_permutation, pin_sparse_brute, pin_sparse_reductions]
+
+
+# =================================================================== pieces
+
+def pin_pieces(orc, figures):
+    """Piece arithmetic against the figures printed for the 8547-token image:
+    any buffer that fits N = 3535 in one piece but not 3536 gives qb = 1462
+    and 6 pieces; the buggy last piece wrote up to N*N floats (7300万, 292 MB)."""
+    f = figures["vision_pieces"]
+    n = f["tokens"]
+    assert f["grid_cols_rows"][0] * f["grid_cols_rows"][1] == n
+    assert (f["image_px"][0] // 14, f["image_px"][1] // 14) == tuple(f["grid_cols_rows"])
+    safe = f["safe_n_max_single_piece"]
+    for cap in (safe * safe, (safe + 1) ** 2 - 1, int(f["buffer_capacity_wan_floats"] * 1e4)):
+        assert orc.piece_rows_for_capacity(cap, safe) == safe
+        assert orc.piece_rows_for_capacity(cap, n) == f["qb"]
+    pieces = orc.piece_ranges(n, f["qb"])
+    assert len(pieces) == f["pieces"]
+    assert pieces[0] == (0, f["qb"]) and pieces[-1][1] == n
+    assert all(b == c for (_, b), (c, _) in zip(pieces[:-1], pieces[1:]))
+    assert round(n * n / 1e4, -2) == f["overrun_end_wan_floats"]
+    assert round(n * n * 4 / 1e6) == f["overrun_end_mb_approx"]
+    assert orc.piece_ranges(n, 0) == [(0, n)] and orc.piece_ranges(0, 5) == []

@@ -1,0 +1,95 @@
+"""Planted mistakes in the oracle must each fail at least one pin (CPU only).
+
+Every mutant is the oracle's own source file with ONE plausible mistake
+substituted in (a dropped term, a wrong sign or index, a swapped operand or
+axis).  The mutated module is executed in isolation and the pins of its family
+are run against it; the test passes when some pin rejects the mutant.  The
+snippet being replaced must exist verbatim, so the list stays in step with the
+oracle.
+"""
+import importlib
+import inspect
+import json
+import os
+import types
+
+import pytest
+
+import oracle
+from tests import oracle_pins as P
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_figures.json")
+
+MUTANTS = [
+    # (oracle module, original snippet, planted mistake, description)
+    ("attention", "return h // (num_heads_q // num_heads_kv)", "return h % num_heads_kv",
+     "query heads interleaved over key/value heads"),
+    ("attention", "np.clip(i_local + (len_k - len_q) + 1, 0, len_k)", "np.clip(i_local + 1, 0, len_k)",
+     "causal mask aligned top-left"),
+    ("attention", "np.clip(i_local + (len_k - len_q) + 1, 0, len_k)",
+     "np.clip(i_local + (len_k - len_q), 0, len_k)", "causal mask excludes the diagonal"),
+    ("attention", "return (e @ vv) / l_sum[:, None], m + np.log(l_sum)",
+     "return (e @ vv) / l_sum[:, None], np.log(l_sum)", "lse drops the row max"),
+    ("attention", "return (e @ vv) / l_sum[:, None], m + np.log(l_sum)",
+     "return (e @ vv), m + np.log(l_sum)", "output not normalised"),
+    ("attention", "logits = scale * (q[r, h, :] @ kk.T)", "logits = scale * scale * (q[r, h, :] @ kk.T)",
+     "scale applied twice"),
+    ("attention", "kk = k[k0:k0 + len_k, g, :]", "kk = k[q0:q0 + len_k, g, :]",
+     "keys addressed with the query prefix offset"),
+    ("attention", "vv = v[k0:k0 + len_k, g, :]", "vv = v[k0:k0 + len_k, h % v.shape[1], :]",
+     "values from the wrong head"),
+    ("attention", "e = np.where(mask, np.exp(lg - m[:, None]), 0.0)",
+     "e = np.exp(np.where(mask, logits, 0.0) - m[:, None])", "masked keys given logit 0 instead of excluded"),
+    ("attention", "m = lg.max(axis=1)                                   # pass 1: row max",
+     "m = lg.max(axis=1) * 0.5", "row max halved"),
+    ("rope", "-2.0 * i / span", "-1.0 * i / span", "frequency exponent -i/d"),
+    ("rope", "out[..., 0::2] = x0 * c - x1 * s", "out[..., 0::2] = x0 * c + x1 * s", "rotation sign flipped"),
+    ("rope", "x0 = x[..., 0::2]\n    x1 = x[..., 1::2]", "x0 = x[..., : d_r // 2]\n    x1 = x[..., d_r // 2:]",
+     "rotate-half pairing"),
+    ("rope", "_rotate_span(x[..., : d // 2], positions[:, 0], theta)",
+     "_rotate_span(x[..., : d // 2], positions[:, 1], theta)", "2D first half turned by the column"),
+    ("rope", "k = x[:, hq * d:(hq + hkv) * d]", "k = x[:, (hq + hkv) * d:(hq + 2 * hkv) * d]",
+     "K read from the V columns"),
+    ("sparse", "sel = idx[r][idx[r] >= 0]", "sel = idx[r]", "padding entries not skipped"),
+    ("sparse", "kr[:, :d_v]", "kr[:, d_qk - d_v:]", "V taken from the last latent columns"),
+    ("sparse", "sel = idx[r][idx[r] >= 0]", "sel = np.unique(idx[r][idx[r] >= 0])", "repeated indices collapsed"),
+    ("sparse", "lse[:, r] = m + np.log(l_sum)", "lse[:, r] = np.log(l_sum)", "lse drops the row max"),
+    ("pieces", "return min(n, cap_floats // n)", "return min(n, -(-cap_floats // n))", "piece rows rounded up"),
+]
+
+FAMILY = {"attention": P.DENSE_PINS, "rope": P.ROPE_PINS, "sparse": P.SPARSE_PINS, "pieces": ["pieces"]}
+
+
+def _mutated_oracle(modname, old, new):
+    mod = importlib.import_module("oracle." + modname)
+    src = inspect.getsource(mod)
+    assert src.count(old) >= 1, "snippet not found in oracle/%s.py: %r" % (modname, old)
+    mut = types.ModuleType("oracle_mutant_" + modname)
+    exec(compile(src.replace(old, new, 1), "<mutant %s>" % modname, "exec"), mut.__dict__)
+    ns = types.SimpleNamespace(**{n: getattr(oracle, n) for n in dir(oracle) if not n.startswith("_")})
+    for name in getattr(mod, "__all__", []):
+        setattr(ns, name, getattr(mut, name))
+    return ns
+
+
+@pytest.mark.parametrize("modname,old,new,desc", MUTANTS, ids=[m[3] for m in MUTANTS])
+def test_mutant_is_caught(modname, old, new, desc):
+    orc = _mutated_oracle(modname, old, new)
+    caught = []
+    for pin in FAMILY[modname]:
+        try:
+            if pin == "pieces":
+                with open(GOLDEN) as f:
+                    P.pin_pieces(orc, json.load(f))
+            else:
+                pin(orc)
+        except Exception as e:  # a failed assertion or a crash both reject the mutant
+            caught.append((getattr(pin, "__name__", pin), type(e).__name__))
+    assert caught, "planted mistake '%s' passed every pin" % desc
+
+
+def test_unmutated_source_passes_through_the_same_harness():
+    orc = _mutated_oracle("attention", "return h // (num_heads_q // num_heads_kv)",
+                          "return h // (num_heads_q // num_heads_kv)")
+    for pin in P.DENSE_PINS:
+        pin(orc)
