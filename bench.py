@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Benchmark of the tiled-attention hot path on one MI355X.
+
+A step is one pass of the dense hot path over the vision-encoder workload:
+qkv_rope (fused QKV split + 2D-grid RoPE, 8547 tokens, 16 heads, d = 64) then
+attn_fwd (non-causal, query pieces of 1462 rows).  Inputs are seeded synthetic
+tensors already resident in device memory.  Prints ONE JSON line on stdout;
+details go to stderr.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
+
+The other workloads (varlen causal GQA prefill, 32K causal prefill, top-k
+sparse MQA) are timed too and reported under "workloads" in the same line.
+Kernel times come from HIP events recorded on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def err(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dense_flops(case) -> float:
+    """2 flops per MAC over Q K^T and P V, allowed (query, key) pairs only."""
+    import numpy as np
+    lq, lk = case.seqlens_q.astype(np.int64), case.seqlens_k.astype(np.int64)
+    if case.causal:
+        pairs = 0
+        for a, b in zip(lq, lk):
+            i = np.arange(a)
+            pairs += int(np.clip(i + (b - a) + 1, 0, b).sum())
+    else:
+        pairs = int((lq * lk).sum())
+    return 4.0 * case.head_dim * case.num_heads_q * pairs
+
+
+def rope_bytes(case) -> float:
+    """Algorithmic HBM bytes of qkv_rope: read Q and K columns, write q and k, read positions."""
+    t = case.total_q
+    qk = (case.num_heads_q + case.num_heads_kv) * case.head_dim * 2
+    return float(t * (2 * qk + case.positions.itemsize * (case.positions.size // t)))
+
+
+def sparse_bytes(case) -> float:
+    """Gathered latent rows counted once per query row (all heads share them),
+    plus Q, O, indices and lse."""
+    r, h, dqk, dv, k = case.num_rows, case.num_heads, case.d_qk, case.d_v, case.k
+    return float(r * k * dqk * 2 + r * h * dqk * 2 + r * h * dv * 2 + r * k * 4 + r * h * 4)
+
+
+def sparse_flops(case) -> float:
+    return 2.0 * case.num_rows * case.num_heads * case.k * (case.d_qk + case.d_v)
+
+
+class Timer:
+    """Per-launch HIP event pairs on torch's current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def run(self, name, fn):
+        e0 = self.torch.cuda.Event(enable_timing=True)
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        self.pairs.setdefault(name, []).append((e0, e1))
+
+    def ms(self, name):
+        v = [a.elapsed_time(b) for a, b in self.pairs[name]]
+        return sum(v) / len(v), min(v)
+
+
+def bench_vision(torch, args):
+    from vision_encoder_attention_amd import runner as R
+    from vision_encoder_attention_amd import workloads as W
+    case = W.vision()
+    st = R.stage_dense(case)
+    for _ in range(args.warmup):
+        R.run_dense(st)
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        tm.run("qkv_rope", lambda: R.run_rope(st))
+        tm.run("attn_fwd", lambda: R.run_attn(st))
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    return case, tm, wall_ms
+
+
+def bench_other(torch, steps):
+    """The remaining workloads: one timed kernel family each."""
+    from vision_encoder_attention_amd import runner as R
+    from vision_encoder_attention_amd import workloads as W
+    res = {}
+    for name in ("varlen_gqa", "long_causal"):
+        case = W.full_case(name)
+        st = R.stage_dense(case)
+        R.run_dense(st)
+        torch.cuda.synchronize()
+        tm = Timer(torch)
+        for _ in range(steps):
+            if case.x_qkv is not None:
+                tm.run("qkv_rope", lambda: R.run_rope(st))
+            tm.run("attn_fwd", lambda: R.run_attn(st))
+        torch.cuda.synchronize()
+        fl = dense_flops(case)
+        a_ms, a_min = tm.ms("attn_fwd")
+        ent = {"attn_fwd_ms": round(a_ms, 4), "attn_fwd_min_ms": round(a_min, 4),
+               "attn_tflops": round(fl / a_ms / 1e9, 2), "attn_frac_bf16_peak": round(fl / a_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+               "flops": fl, "tokens": case.total_q, "causal": case.causal,
+               "heads": [case.num_heads_q, case.num_heads_kv], "head_dim": case.head_dim}
+        if case.x_qkv is not None:
+            r_ms, _ = tm.ms("qkv_rope")
+            rb = rope_bytes(case)
+            ent.update({"qkv_rope_ms": round(r_ms, 4), "qkv_rope_gbs": round(rb / r_ms / 1e6, 1),
+                        "qkv_rope_frac_hbm": round(rb / r_ms / 1e6 / PEAK_HBM_GBS, 4)})
+        res[case.name] = ent
+        del st
+        torch.cuda.empty_cache()
+    # sparse MQA: evict L2 / MALL between timed launches (untimed fill of 1 GiB)
+    case = W.full_case("sparse_mqa")
+    st = R.stage_sparse(case)
+    R.run_sparse(st)
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    tm = Timer(torch)
+    for _ in range(steps):
+        scratch.fill_(1)
+        tm.run("sparse", lambda: R.run_sparse(st))
+    torch.cuda.synchronize()
+    s_ms, s_min = tm.ms("sparse")
+    by, fl = sparse_bytes(case), sparse_flops(case)
+    res[case.name] = {"sparse_mqa_ms": round(s_ms, 4), "sparse_mqa_min_ms": round(s_min, 4),
+                      "gbs": round(by / s_ms / 1e6, 1), "frac_hbm": round(by / s_ms / 1e6 / PEAK_HBM_GBS, 4),
+                      "tflops": round(fl / s_ms / 1e9, 2), "bytes": by, "flops": fl}
+    del scratch, st
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline():
+    """The float64 oracle on a bounded sample of the same workload: RoPE of
+    all 8547 tokens and attention of 8 of the 16 heads (all rows)."""
+    import numpy as np
+    import oracle
+    from vision_encoder_attention_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = 1
+    case = W.vision()
+    heads = list(range(8))
+    t0 = time.perf_counter()
+    q, k = oracle.qkv_rope(W.bf16_bits_to_f64(case.x_qkv), case.positions, case.theta, case.num_heads_q,
+                           case.num_heads_kv, case.head_dim)
+    oracle.attention(q, k, W.bf16_bits_to_f64(case.v_from_x()), case.cu_seqlens_q, case.cu_seqlens_k, False,
+                     float(np.float32(case.scale)), heads=heads)
+    dt = time.perf_counter() - t0
+    fl = dense_flops(case) * len(heads) / case.num_heads_q
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": "float64 oracle: qkv_rope of all 8547 tokens + attention of 8 of 16 heads, all 8547 rows "
+                      "(%.3g attention flops in %.1f s; numpy matmul on %d BLAS threads, elementwise ops on 1)"
+                      % (fl, dt, cores)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        err("bench.py measures one GPU: this library's path runs on a single MI355X "
+            "(every workload here fits one GPU; multi-GPU sharding is described in DESIGN.md, not run). "
+            "Use --gpus 1.")
+        sys.exit(2)
+
+    import torch
+    import vision_encoder_attention_amd as vea
+    if not torch.cuda.is_available():
+        err("no GPU visible")
+        sys.exit(1)
+    vea.load_library()
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    err("device: %s, %d CUs" % (props.name, props.multi_processor_count))
+
+    case, tm, wall_ms = bench_vision(torch, args)
+    fl = dense_flops(case)
+    a_ms, a_min = tm.ms("attn_fwd")
+    r_ms, r_min = tm.ms("qkv_rope")
+    rb = rope_bytes(case)
+    achieved = fl / a_ms / 1e9
+    err("vision: step %.4f ms (wall), attn_fwd %.4f ms avg (%.1f TFLOP/s), qkv_rope %.4f ms (%.0f GB/s)"
+        % (wall_ms, a_ms, achieved, r_ms, rb / r_ms / 1e6))
+
+    line = {
+        "metric": "attention fwd TFLOP/s (qkv_rope + piecewise attn_fwd step), % of bf16 MFMA peak",
+        "value": round(fl / wall_ms / 1e9, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "vision_encoder_8547tok_111x77grid_h16_d64_qb1462_2dRoPE",
+                   "tokens": case.total_q, "heads": case.num_heads_q, "head_dim": case.head_dim,
+                   "piece_rows": case.piece_rows, "causal": False, "flops_per_step": fl},
+        "kernels": {"attn_fwd_ms": round(a_ms, 5), "attn_fwd_min_ms": round(a_min, 5),
+                    "qkv_rope_ms": round(r_ms, 5), "qkv_rope_gbs": round(rb / r_ms / 1e6, 1),
+                    "qkv_rope_frac_hbm": round(rb / r_ms / 1e6 / PEAK_HBM_GBS, 4)},
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_bf16_kernel<64,false>", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+    }
+    if not args.no_extra:
+        line["workloads"] = bench_other(torch, max(5, min(args.steps, 20)))
+        for k, v in line["workloads"].items():
+            err("%s: %s" % (k, v))
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+        err("cpu_baseline: %s" % line["cpu_baseline"])
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,189 @@
+/*
+ * vea.h — C ABI of the MI355X (gfx950) tiled-attention forward library.
+ *
+ * Operations (page titles used in the citations below):
+ *   [3090]   「DeepSeek V4.1 上 4×RTX 3090：视觉链路的两个坑和修复」
+ *   [MI250]  「AMD MI250部署DeepSeek-V4-Flash：先修正确性再谈性能」
+ *   [SGLang] 「从 SGLang Kernel源码到 GPU Trace：DeepSeek V4.1 Flash - Prefill」
+ *   [V32]    「推理引擎的“蝴蝶效应” -- 从V32 模型的输出不一致说起」
+ *
+ * Conventions shared by every call
+ *   - All tensor pointers are DEVICE pointers, row-major, owned by the caller.
+ *     The library allocates nothing and keeps no state between calls.
+ *   - Strides are in ELEMENTS.  Within a token, heads are contiguous and each
+ *     head holds head_dim contiguous elements.
+ *   - 16-byte vector loads are used: every tensor pointer must be 16-byte
+ *     aligned and every token stride a multiple of 16 bytes.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Every
+ *     call is asynchronous on that stream; nothing synchronises the host
+ *     unless the environment variable VEA_CHECK=1 is set.
+ *   - Return value: VEA_OK (0) or a negative vea_status.  Arguments are
+ *     validated before anything is launched; on an error nothing runs.  A
+ *     launch failure is reported as VEA_EHIP and never swallowed.  A fault
+ *     inside a kernel surfaces at the caller's next synchronisation (an
+ *     asynchronous illegal access is reported by the NEXT GPU call, as the
+ *     cuBLAS "status 13" of [3090] section 三 shows); VEA_CHECK=1 synchronises
+ *     after every call and additionally checks device-side index data on the
+ *     host (cu_seqlens monotone and consistent with the totals, top-k indices
+ *     below n_kv), returning VEA_ERANGE on a violation.
+ *   - Results are bitwise identical from run to run: no kernel uses global
+ *     atomics, and every output element has exactly one writer.
+ */
+#ifndef VEA_H
+#define VEA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum vea_status {
+  VEA_OK = 0,
+  VEA_EINVAL = -1,       /* null pointer, non-finite scale/theta, misaligned pointer or stride */
+  VEA_EDTYPE = -2,       /* dtype not supported by this call */
+  VEA_ESHAPE = -3,       /* inconsistent sizes (negative counts, Hq % Hkv != 0, short stride) */
+  VEA_EUNSUPPORTED = -4, /* valid request outside the compiled kernel set (e.g. head_dim) */
+  VEA_ERANGE = -5,       /* VEA_CHECK only: bad cu_seqlens or top-k index found on the host */
+  VEA_EWORKSPACE = -6,   /* reserved for calls that take a caller workspace */
+  VEA_EHIP = -7          /* the HIP runtime reported an error (launch or VEA_CHECK sync) */
+} vea_status;
+
+typedef enum vea_dtype { VEA_F32 = 0, VEA_BF16 = 1 } vea_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* vea_status_str(int status);
+
+/* Library version string, e.g. "vea 0.1.0 gfx950". */
+const char* vea_version(void);
+
+/*
+ * vea_attn_fwd — blockwise scaled-dot-product attention forward over a packed
+ * variable-length batch.
+ *
+ * Computes, for every sequence b, query head h and query row i of b,
+ *     o_i = softmax_j( scale * q_i . k_j  over allowed j ) . V,
+ *     lse_i = ln sum_{allowed j} exp(scale * q_i . k_j)     (natural log)
+ * with the key/value head g = h / (num_heads_q / num_heads_kv).
+ * Sources: query pieces with piece-local S/P addressing [3090] section 三;
+ * fp32 accumulation of Q K^T and P V and fp32 softmax statistics [MI250]
+ * sections 3.1 and 4.1; masked keys excluded (not an additive bias) [MI250]
+ * section 3.3; cu_seqlens varlen entry and per-sequence key bound, the
+ * softmax_lse output [SGLang] sections 2.2 and 3.2; the online-softmax merge
+ * [V32] section 进一步探索 eq. (1)(2).
+ *
+ *   dtype          VEA_BF16 (head_dim 64 or 128) or VEA_F32 (head_dim 64).
+ *   q              [total_q, num_heads_q, head_dim], token stride q_tok_stride.
+ *   k, v           [total_k, num_heads_kv, head_dim], token strides k/v_tok_stride
+ *                  (v may be a strided view into a fused QKV buffer).
+ *   cu_seqlens_q/k device int32 [batch+1], non-decreasing, cu[0] = 0,
+ *                  cu_q[batch] = total_q, cu_k[batch] = total_k.  Values are
+ *                  clamped to [0, total] inside the kernels, so malformed
+ *                  offsets cannot cause out-of-bounds accesses.
+ *   max_seqlen_q   >= every query length (sizes the launch; a shorter value
+ *                  leaves the rows beyond it unwritten).  max_seqlen_k is
+ *                  accepted for symmetry and checked under VEA_CHECK.
+ *   causal         0: every key of the sequence is allowed.  1: bottom-right
+ *                  aligned causal mask: row i (0-based in its sequence) sees
+ *                  keys j <= i + (L_k - L_q).  A row that sees no key gets
+ *                  o = 0 and lse = -inf.
+ *   scale          finite float (any sign, 0 allowed).
+ *   piece_rows     query rows per piece (qb); 0 = one piece per sequence.
+ *                  Pieces are [p*qb, (p+1)*qb) within each sequence; no tile
+ *                  straddles a piece and the result does not depend on qb.
+ *   out            [total_q, num_heads_q, head_dim] of dtype, stride out_tok_stride.
+ *   lse            float [num_heads_q, total_q] or NULL (not written).
+ */
+int vea_attn_fwd(int dtype,
+                 const void* q, int64_t q_tok_stride,
+                 const void* k, int64_t k_tok_stride,
+                 const void* v, int64_t v_tok_stride,
+                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                 int batch, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                 int num_heads_q, int num_heads_kv, int head_dim,
+                 int causal, float scale, int piece_rows,
+                 void* out, int64_t out_tok_stride, float* lse,
+                 void* stream);
+
+/*
+ * vea_qkv_rope — split a fused QKV projection output and apply rotary position
+ * embedding to its Q and K heads (V is left in place for vea_attn_fwd to read
+ * through a strided pointer).
+ * Sources: the vision encoder's qkv_rope step [3090] section 二; the fused
+ * [T, 3*hidden] projection output [SGLang] section 3.1; trigonometry in at
+ * least fp32 [MI250] section 4.1 (here: angle and sin/cos in fp64, rotation in
+ * fp32, bf16 round-to-nearest-even output).
+ *
+ * Rotation: pair i of a rotated span of width d_r, (x[2i], x[2i+1]), turns by
+ * phi = pos * theta^(-2i/d_r).  pos_dims = 1: one span over the whole head,
+ * pos = positions[t].  pos_dims = 2 (patch grid): dims [0, d/2) turn with
+ * positions[t][0] (grid row), dims [d/2, d) with positions[t][1] (grid
+ * column), each a span of width d/2.
+ *
+ *   x_qkv       bf16 [num_tokens, (Hq + 2 Hkv) * head_dim] with columns
+ *               [Q heads | K heads | V heads], token stride x_tok_stride.
+ *   positions   device int32 [num_tokens] or [num_tokens, 2].
+ *   head_dim    even (pos_dims 1) or a multiple of 4 (pos_dims 2), and a
+ *               multiple of 8; at most 256.
+ *   theta       finite, > 0.
+ *   q, k        bf16 outputs [num_tokens, Hq, head_dim] and
+ *               [num_tokens, Hkv, head_dim], contiguous; must not overlap x_qkv.
+ */
+int vea_qkv_rope(const void* x_qkv, int64_t x_tok_stride,
+                 const int32_t* positions, int pos_dims,
+                 int num_tokens, int num_heads_q, int num_heads_kv, int head_dim, float theta,
+                 void* q, void* k, void* stream);
+
+/*
+ * vea_sparse_mqa_fwd — multi-query attention of each query row over its own
+ * top-k set of latent KV rows (all heads of a row share the gathered rows).
+ * Sources: sparse attention taking Q, the KV cache and an index [V32] section
+ * 实验方法和结果; the result depends on the index set, the order only changes
+ * rounding [V32] sections 结论 and 进一步探索 eq. (1)(2).  Each row's indices
+ * are sorted ascending on the device before use, so the output is bitwise
+ * invariant to the order of the indices within a row.
+ *
+ *   q          bf16 [num_rows, num_heads, d_qk], contiguous.
+ *   kv_latent  bf16 [n_kv, d_qk], contiguous; V is columns [0, d_v).
+ *   topk_idx   device int32 [num_rows, k].  Entries < 0 are padding and are
+ *              skipped; entries >= n_kv are skipped as well (and reported as
+ *              VEA_ERANGE under VEA_CHECK).  Repeated entries count with their
+ *              multiplicity.  A row with no valid entry gets o = 0, lse = -inf.
+ *   d_qk, d_v  compiled for d_qk = 576, d_v = 512.
+ *   k          1 .. 4096.
+ *   out        bf16 [num_rows, num_heads, d_v]; lse float [num_heads, num_rows]
+ *              or NULL.
+ */
+int vea_sparse_mqa_fwd(const void* q, const void* kv_latent, const int32_t* topk_idx,
+                       int num_rows, int num_heads, int n_kv, int d_qk, int d_v, int k,
+                       float scale, void* out, float* lse, void* stream);
+
+/*
+ * vea_attn_probs_piece — debug export (not on the timed path) of the
+ * probability matrix of one query piece of one head:
+ *     P[r][j] = exp(scale * q_{q0+r} . k_j - lse_{q0+r}),  r < rows, j < len_k,
+ * zero where the causal mask excludes the key.  The piece is written from the
+ * START of p_out (row r at p_out + r * p_row_stride): the piece-local
+ * addressing fix of [3090] section 三, and a buffer of rows x len_k floats is
+ * always enough.  Row sums of P are 1 up to rounding; [3090] section 四 prints
+ * 0.9997 .. 1.0003 for 1462 rows.
+ *
+ *   lse           the float [num_heads_q, lse_row_stride] output of vea_attn_fwd.
+ *   seq_begin_q   global row of the sequence's first query; len_q its length.
+ *   seq_begin_k   global row of the sequence's first key; len_k its length.
+ *   q0, rows      the piece: local rows [q0, q0 + rows) of the sequence.
+ */
+int vea_attn_probs_piece(int dtype,
+                         const void* q, int64_t q_tok_stride,
+                         const void* k, int64_t k_tok_stride,
+                         const float* lse, int64_t lse_row_stride,
+                         int head, int num_heads_q, int num_heads_kv, int head_dim,
+                         int seq_begin_q, int len_q, int seq_begin_k, int len_k,
+                         int q0, int rows, int causal, float scale,
+                         float* p_out, int64_t p_row_stride, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VEA_H */

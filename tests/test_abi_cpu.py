@@ -1,0 +1,179 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments with the documented status before
+any launch.  Also checks the oracle / HIP path separation."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vea.h")
+
+VEA_OK, VEA_EINVAL, VEA_EDTYPE, VEA_ESHAPE, VEA_EUNSUPPORTED = 0, -1, -2, -3, -4
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(vea_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from vision_encoder_attention_amd import _binding
+    if not os.path.exists(_binding.LIB_PATH):
+        pytest.fail("libvea.so is not built (run __graft_entry__.build())")
+    return _binding.load_library()
+
+
+def test_header_declares_the_four_operations():
+    names = _declared()
+    for n in ("vea_attn_fwd", "vea_qkv_rope", "vea_sparse_mqa_fwd", "vea_attn_probs_piece", "vea_status_str"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from vision_encoder_attention_amd import _binding
+    out = subprocess.run(["nm", "-D", "--defined-only", _binding.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (vea_[a-z0-9_]+)", out))
+    for n in _declared():
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_status_strings(lib):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7):
+        assert lib.vea_status_str(st).decode().startswith("VEA_")
+    assert lib.vea_version().decode().startswith("vea ")
+
+
+FAKE = 0x10000   # 16-byte aligned, never dereferenced: every call below fails validation first
+
+
+def _attn(lib, **kw):
+    a = dict(dtype=1, q=FAKE, qs=128, k=FAKE, ks=128, v=FAKE, vs=128, cuq=FAKE, cuk=FAKE, batch=1, tq=10, tk=10,
+             mq=10, mk=10, hq=2, hkv=2, d=64, causal=0, scale=0.125, qb=0, out=FAKE, os=128, lse=None)
+    a.update(kw)
+    return lib.vea_attn_fwd(a["dtype"], a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["cuq"], a["cuk"],
+                            a["batch"], a["tq"], a["tk"], a["mq"], a["mk"], a["hq"], a["hkv"], a["d"],
+                            a["causal"], a["scale"], a["qb"], a["out"], a["os"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), VEA_EDTYPE),
+    (dict(hq=3, hkv=2), VEA_ESHAPE),
+    (dict(hkv=0), VEA_ESHAPE),
+    (dict(batch=-1), VEA_ESHAPE),
+    (dict(qb=-5), VEA_ESHAPE),
+    (dict(d=96), VEA_EUNSUPPORTED),
+    (dict(dtype=0, d=128), VEA_EUNSUPPORTED),
+    (dict(scale=float("nan")), VEA_EINVAL),
+    (dict(scale=float("inf")), VEA_EINVAL),
+    (dict(causal=2), VEA_EINVAL),
+    (dict(q=None), VEA_EINVAL),
+    (dict(cuk=None), VEA_EINVAL),
+    (dict(q=FAKE + 2), VEA_EINVAL),
+    (dict(qs=100), VEA_ESHAPE),          # shorter than Hq * d
+    (dict(vs=132), VEA_EINVAL),          # not a multiple of 16 bytes
+    (dict(mq=11), VEA_ESHAPE),           # longer than total
+    (dict(batch=0), VEA_OK),             # nothing to do, nothing launched
+    (dict(tq=0, mq=0), VEA_OK),
+])
+def test_attn_fwd_validation(lib, kw, status):
+    assert _attn(lib, **kw) == status
+
+
+def _rope(lib, **kw):
+    a = dict(x=FAKE, xs=3 * 4 * 64, pos=FAKE, pd=2, t=5, hq=4, hkv=4, d=64, theta=1e4, q=FAKE, k=FAKE)
+    a.update(kw)
+    return lib.vea_qkv_rope(a["x"], a["xs"], a["pos"], a["pd"], a["t"], a["hq"], a["hkv"], a["d"], a["theta"],
+                            a["q"], a["k"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(pd=3), VEA_EINVAL),
+    (dict(theta=0.0), VEA_EINVAL),
+    (dict(theta=-1.0), VEA_EINVAL),
+    (dict(theta=float("nan")), VEA_EINVAL),
+    (dict(d=36, xs=3 * 4 * 36), VEA_EUNSUPPORTED),
+    (dict(d=512, xs=3 * 4 * 512), VEA_EUNSUPPORTED),
+    (dict(xs=100), VEA_ESHAPE),
+    (dict(x=None), VEA_EINVAL),
+    (dict(k=FAKE + 8), VEA_EINVAL),
+    (dict(t=-1), VEA_ESHAPE),
+    (dict(t=0), VEA_OK),
+])
+def test_qkv_rope_validation(lib, kw, status):
+    assert _rope(lib, **kw) == status
+
+
+def _sparse(lib, **kw):
+    a = dict(q=FAKE, kv=FAKE, idx=FAKE, r=3, h=128, nkv=100, dqk=576, dv=512, k=64, scale=0.04, out=FAKE, lse=None)
+    a.update(kw)
+    return lib.vea_sparse_mqa_fwd(a["q"], a["kv"], a["idx"], a["r"], a["h"], a["nkv"], a["dqk"], a["dv"], a["k"],
+                                  a["scale"], a["out"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dqk=512), VEA_EUNSUPPORTED),
+    (dict(dv=600), VEA_ESHAPE),
+    (dict(k=0), VEA_ESHAPE),
+    (dict(k=5000), VEA_EUNSUPPORTED),
+    (dict(scale=math.nan), VEA_EINVAL),
+    (dict(idx=None), VEA_EINVAL),
+    (dict(out=FAKE + 4), VEA_EINVAL),
+    (dict(r=0), VEA_OK),
+])
+def test_sparse_validation(lib, kw, status):
+    assert _sparse(lib, **kw) == status
+
+
+def test_probs_validation(lib):
+    f = lib.vea_attn_probs_piece
+    # piece beyond its sequence
+    assert f(1, FAKE, 128, FAKE, 128, FAKE, 50, 0, 2, 2, 64, 0, 10, 0, 10, 5, 6, 0, 0.1, FAKE, 10, None) == VEA_ESHAPE
+    # p_out rows shorter than the sequence's keys
+    assert f(1, FAKE, 128, FAKE, 128, FAKE, 50, 0, 2, 2, 64, 0, 10, 0, 10, 0, 5, 0, 0.1, FAKE, 9, None) == VEA_ESHAPE
+    assert f(1, FAKE, 128, FAKE, 128, FAKE, 50, 2, 2, 2, 64, 0, 10, 0, 10, 0, 5, 0, 0.1, FAKE, 10, None) == VEA_ESHAPE
+    assert f(5, FAKE, 128, FAKE, 128, FAKE, 50, 0, 2, 2, 64, 0, 10, 0, 10, 0, 5, 0, 0.1, FAKE, 10, None) == VEA_EDTYPE
+    assert f(1, FAKE, 128, FAKE, 128, FAKE, 50, 0, 2, 2, 64, 0, 10, 0, 10, 0, 0, 0, 0.1, FAKE, 10, None) == VEA_OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import vision_encoder_attention_amd as vea
+    q = torch.zeros(4, 1, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 4], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        vea.attn_fwd(q, q, q, cu, cu, False, 0.125, q.clone())
+
+
+# ------------------------------------------------------- separation checks
+
+def _py_files(d):
+    for base, _, files in os.walk(os.path.join(ROOT, d)):
+        for f in files:
+            if f.endswith(".py"):
+                yield os.path.join(base, f)
+
+
+def test_oracle_imports_nothing_from_the_hip_path():
+    for f in _py_files("oracle"):
+        src = open(f).read()
+        imports = re.findall(r"^\s*(?:import|from)\s+([\w.]+)", src, flags=re.M)
+        for mod in imports:
+            assert not mod.startswith(("vision_encoder_attention_amd", "ctypes", "torch")), (f, mod)
+        assert "libvea" not in src, f
+
+
+def test_product_path_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "vision_encoder_attention_amd")
+    for base, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                src = open(os.path.join(base, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", src, flags=re.M), f
+                assert "oracle/" not in src and "import oracle" not in src, f

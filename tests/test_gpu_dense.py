@@ -1,0 +1,249 @@
+"""GPU parity of the dense path (qkv_rope + attn_fwd) against the float64 oracle.
+
+All inputs are seeded.  bf16 tensors reach the oracle as the exact same
+values (bf16 -> float64 is exact).  Tolerances: see tests/gpu_util.py.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import assert_bf16_close, assert_f32_close, log, metrics
+from vision_encoder_attention_amd import runner as R
+from vision_encoder_attention_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_figures.json")
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    if not t.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import vision_encoder_attention_amd as vea
+    vea.load_library()
+    return t
+
+
+def _f64(t, dtype):
+    if dtype == "bf16":
+        return W.bf16_bits_to_f64(R.tensor_to_bits(t))
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def _inputs64(case, st):
+    """q, k, v as the attention kernel saw them (float64)."""
+    if case.x_qkv is not None:
+        q = W.bf16_bits_to_f64(R.tensor_to_bits(st.q))
+        k = W.bf16_bits_to_f64(R.tensor_to_bits(st.k))
+        v = W.bf16_bits_to_f64(case.v_from_x())
+    elif case.dtype == "bf16":
+        q, k, v = (W.bf16_bits_to_f64(a) for a in (case.q, case.k, case.v))
+    else:
+        q, k, v = (np.asarray(a, np.float64) for a in (case.q, case.k, case.v))
+    return q, k, v
+
+
+def _check_case(torch, case, piece_rows=None, rows=None):
+    log("case %s (piece_rows=%s)" % (case.name, case.piece_rows if piece_rows is None else piece_rows))
+    st = R.stage_dense(case)
+    R.run_dense(st, piece_rows)
+    torch.cuda.synchronize()
+    out = _f64(st.out, case.dtype)
+    lse = st.lse.cpu().numpy().astype(np.float64)
+    if case.x_qkv is not None:
+        q_ref, k_ref = oracle.qkv_rope(W.bf16_bits_to_f64(case.x_qkv), case.positions, case.theta,
+                                       case.num_heads_q, case.num_heads_kv, case.head_dim)
+        assert_bf16_close(_f64(st.q, "bf16"), q_ref, "rope q")
+        assert_bf16_close(_f64(st.k, "bf16"), k_ref, "rope k")
+    q, k, v = _inputs64(case, st)
+    o_ref, l_ref = oracle.attention(q, k, v, case.cu_seqlens_q, case.cu_seqlens_k, case.causal,
+                                    float(np.float32(case.scale)), rows=rows)
+    sel = slice(None) if rows is None else np.asarray(rows)
+    check = assert_f32_close if case.dtype == "f32" else assert_bf16_close
+    check(out[sel], o_ref[sel], "out")
+    check(lse[:, sel], l_ref[:, sel], "lse")
+    if case.x_qkv is not None:
+        # end to end from the fused projection, unrounded q/k (reported and gated alike)
+        v64 = W.bf16_bits_to_f64(case.v_from_x())
+        o_e2e, l_e2e = oracle.attention(q_ref, k_ref, v64, case.cu_seqlens_q, case.cu_seqlens_k, case.causal,
+                                        float(np.float32(case.scale)), rows=rows)
+        assert_bf16_close(out[sel], o_e2e[sel], "out (end to end)")
+        assert_bf16_close(lse[:, sel], l_e2e[:, sel], "lse (end to end)")
+    return st
+
+
+# ----------------------------------------------------------- small configs
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3])
+def test_small_workloads(torch, idx):
+    """Reduced versions of the four dense workloads (several tiles, several
+    pieces, ragged tails, empty and one-token sequences)."""
+    _check_case(torch, W.small_cases()[idx])
+
+
+def test_single_head_f32_full(torch):
+    """The fp32 workload at full size: N = 256, d = 64, 4 pieces of 64."""
+    _check_case(torch, W.single_head_f32())
+
+
+EDGE = [
+    # (lengths_q, lengths_k, hq, hkv, d, causal, dtype, piece_rows, scale, q_mul)
+    ([5, 300, 77], [9, 300, 200], 4, 4, 64, False, "bf16", 0, None, 1.0),      # L_q != L_k, non-causal
+    ([300, 64, 40], [200, 64, 100], 4, 2, 128, True, "bf16", 0, None, 1.0),    # L_q > L_k: fully masked rows
+    ([1], [1], 2, 1, 64, True, "bf16", 0, None, 1.0),                           # single key
+    ([0, 129, 0], [0, 129, 0], 8, 8, 128, True, "bf16", 0, None, 1.0),          # empty sequences around one
+    ([200], [0], 2, 2, 64, False, "bf16", 0, None, 1.0),                         # no keys at all
+    ([257], [257], 8, 1, 128, True, "bf16", 37, None, 1.0),                      # MQA, odd pieces
+    ([333], [333], 2, 2, 64, False, "bf16", 0, 0.0, 1.0),                        # scale 0: mean of V
+    ([190], [190], 2, 2, 128, True, "bf16", 64, -0.3, 1.0),                      # negative scale
+    ([1000], [1000], 2, 2, 128, True, "bf16", 0, None, 8.0),                     # very peaked logits
+    ([129, 63], [129, 63], 1, 1, 64, True, "f32", 0, None, 1.0),                 # fp32 causal
+    ([100, 3], [40, 3], 1, 1, 64, False, "f32", 7, None, 1.0),                   # fp32 pieces, L_q != L_k
+]
+
+
+@pytest.mark.parametrize("i", range(len(EDGE)))
+def test_edge_cases(torch, i):
+    lq, lk, hq, hkv, d, causal, dt, qb, scale, qm = EDGE[i]
+    case = W.random_dense(lq, lk, hq, hkv, d, causal, dt, seed=500 + i, piece_rows=qb, scale=scale, q_mul=qm)
+    _check_case(torch, case)
+
+
+# --------------------------------------------- invariances and determinism
+
+def test_piece_rows_do_not_change_results(torch):
+    """O and lse are bitwise identical for every piece size (the piece is a
+    scheduling unit only)."""
+    case = W.small_cases()[1]            # 667-token vision case
+    st = R.stage_dense(case)
+    R.run_dense(st, piece_rows=0)
+    torch.cuda.synchronize()
+    ref_o, ref_l = st.out.clone(), st.lse.clone()
+    for qb in (1, 7, 64, 127, 128, 129, 150, 300, 666, 667, 5000):
+        R.run_attn(st, piece_rows=qb)
+        torch.cuda.synchronize()
+        assert torch.equal(st.out, ref_o), qb
+        assert torch.equal(st.lse, ref_l), qb
+
+
+def test_packing_does_not_change_results(torch):
+    """A packed batch gives bitwise the same rows as each sequence alone."""
+    lens = [70, 129, 1, 260]
+    big = W.random_dense(lens, lens, 4, 2, 128, True, "bf16", seed=601)
+    st = R.stage_dense(big)
+    R.run_attn(st)
+    torch.cuda.synchronize()
+    cq = big.cu_seqlens_q
+    for b, n in enumerate(lens):
+        one = W.DenseCase("one", "bf16", 4, 2, 128, True, big.scale, 0, np.array([0, n], np.int32),
+                          np.array([0, n], np.int32), big.q[cq[b]:cq[b + 1]], big.k[cq[b]:cq[b + 1]],
+                          big.v[cq[b]:cq[b + 1]])
+        s1 = R.stage_dense(one)
+        R.run_attn(s1)
+        torch.cuda.synchronize()
+        assert torch.equal(s1.out, st.out[cq[b]:cq[b + 1]])
+        assert torch.equal(s1.lse, st.lse[:, cq[b]:cq[b + 1]])
+
+
+def test_repeated_runs_are_bitwise_identical(torch):
+    case = W.small_cases()[2]
+    st = R.stage_dense(case)
+    R.run_dense(st)
+    torch.cuda.synchronize()
+    o0, l0, q0 = st.out.clone(), st.lse.clone(), st.q.clone()
+    for _ in range(5):
+        st.out.fill_(0)
+        st.lse.fill_(0)
+        R.run_dense(st)
+        torch.cuda.synchronize()
+        assert torch.equal(st.q, q0) and torch.equal(st.out, o0) and torch.equal(st.lse, l0)
+
+
+def test_outputs_stay_inside_their_buffers(torch):
+    """Guard canaries of 64 KiB around out and lse stay untouched (the bug
+    class of an S/P buffer written past its end)."""
+    case = W.random_dense([300, 77], [300, 77], 4, 4, 64, False, "bf16", seed=602, piece_rows=100)
+    st = R.stage_dense(case)
+    guard = 32768
+    n_out = st.out.numel()
+    big = torch.full((guard + n_out + guard,), -7.0, dtype=torch.bfloat16, device="cuda")
+    out = big[guard:guard + n_out].view_as(st.out)
+    big_l = torch.full((guard + st.lse.numel() + guard,), 1234.5, dtype=torch.float32, device="cuda")
+    lse = big_l[guard:guard + st.lse.numel()].view_as(st.lse)
+    st.out, st.lse = out, lse
+    R.run_attn(st)
+    torch.cuda.synchronize()
+    assert bool((big[:guard] == -7.0).all()) and bool((big[guard + n_out:] == -7.0).all())
+    assert bool((big_l[:guard] == 1234.5).all()) and bool((big_l[guard + lse.numel():] == 1234.5).all())
+
+
+def test_probability_piece_export(torch):
+    """P of a non-first piece, exported from the start of a piece-sized
+    buffer: rows sum to 1 within the band printed for the fixed encoder
+    (0.9997 .. 1.0003) and match the oracle's P."""
+    import vision_encoder_attention_amd as vea
+    with open(GOLDEN) as f:
+        band = json.load(f)["row_sums_after_fix"]
+    case = W.vision(grid_rows=23, grid_cols=29, heads=4, d=64, piece_rows=150, seed=12)
+    st = R.stage_dense(case)
+    R.run_dense(st)
+    n = case.total_q
+    for causal in (False,):
+        for q0 in (150, 600):
+            rows = min(150, n - q0)
+            guard = 4096
+            buf = torch.full((guard + rows * n + guard,), -3.0, dtype=torch.float32, device="cuda")
+            p = buf[guard:guard + rows * n].view(rows, n)
+            vea.attn_probs_piece(st.q, st.k, st.lse, 2, 0, n, 0, n, q0, rows, causal, case.scale, p)
+            torch.cuda.synchronize()
+            assert bool((buf[:guard] == -3.0).all()) and bool((buf[guard + rows * n:] == -3.0).all())
+            pg = p.cpu().numpy().astype(np.float64)
+            sums = pg.sum(axis=1)
+            log("  piece q0=%d row sums in [%.6f, %.6f]" % (q0, sums.min(), sums.max()))
+            assert sums.min() >= band["lo"] and sums.max() <= band["hi"]
+            assert np.abs(sums - 1).max() < 1e-4
+            q64 = W.bf16_bits_to_f64(R.tensor_to_bits(st.q))
+            k64 = W.bf16_bits_to_f64(R.tensor_to_bits(st.k))
+            p_ref = oracle.attn_probs(q64, k64, case.cu_seqlens_q, case.cu_seqlens_k, causal,
+                                      float(np.float32(case.scale)), head=2, seq=0, q0=q0, rows=rows)
+            assert np.abs(pg - p_ref).max() < 1e-4
+
+
+# ------------------------------------------- full-size workloads, sampled
+
+def _sample_rows(case, per_seq=12, seed=7):
+    rng = np.random.default_rng(seed)
+    rows = []
+    cq = case.cu_seqlens_q
+    for b in range(case.batch):
+        lo, hi = int(cq[b]), int(cq[b + 1])
+        if hi <= lo:
+            continue
+        pick = set([lo, hi - 1, min(lo + 127, hi - 1), min(lo + 128, hi - 1)])
+        if case.piece_rows:
+            for p in range(lo + case.piece_rows, hi, case.piece_rows):
+                pick.update([p - 1, p])
+        pick.update(rng.integers(lo, hi, size=per_seq).tolist())
+        rows.extend(sorted(pick))
+    return np.array(sorted(set(rows)), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", ["vision", "varlen_gqa", "long_causal"])
+def test_full_size_sampled(torch, name):
+    """Full-size workloads in the benchmark's launch configuration, checked
+    on sampled rows (piece boundaries, tile boundaries, first/last rows and
+    random rows) for every head, plus run-to-run bitwise equality."""
+    case = W.full_case(name)
+    rows = _sample_rows(case, per_seq=24 if case.batch == 1 else 6)
+    st = _check_case(torch, case, rows=rows)
+    o0, l0 = st.out.clone(), st.lse.clone()
+    R.run_dense(st)
+    torch.cuda.synchronize()
+    assert torch.equal(st.out, o0) and torch.equal(st.lse, l0)
+    assert bool(torch.isfinite(st.out.float()).all())

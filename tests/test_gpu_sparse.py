@@ -1,0 +1,102 @@
+"""GPU parity of the top-k sparse MQA path against the float64 oracle."""
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import assert_bf16_close, log
+from vision_encoder_attention_amd import runner as R
+from vision_encoder_attention_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    if not t.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import vision_encoder_attention_amd as vea
+    vea.load_library()
+    return t
+
+
+def _run(torch, case, idx=None):
+    st = R.stage_sparse(case, idx=idx)
+    R.run_sparse(st)
+    torch.cuda.synchronize()
+    return st
+
+
+def _check(torch, case, idx=None, rows=None, name=""):
+    log("sparse case %s %s" % (case.name, name))
+    st = _run(torch, case, idx)
+    ix = case.topk_idx if idx is None else idx
+    o_ref, l_ref = oracle.sparse_mqa(W.bf16_bits_to_f64(case.q), W.bf16_bits_to_f64(case.kv_latent), ix, case.d_v,
+                                     float(np.float32(case.scale)), rows=rows)
+    sel = slice(None) if rows is None else np.asarray(rows)
+    out = W.bf16_bits_to_f64(R.tensor_to_bits(st.out))
+    lse = st.lse.cpu().numpy().astype(np.float64)
+    assert_bf16_close(out[sel], o_ref[sel], "out")
+    assert_bf16_close(lse[:, sel], l_ref[:, sel], "lse")
+    return st
+
+
+def test_small_sparse(torch):
+    _check(torch, W.small_cases()[4])
+
+
+def test_index_order_is_irrelevant_bitwise(torch):
+    """The same index sets in other orders give bitwise the same output (the
+    pages' kernel moved by 2^-8; here the rows are sorted on the device)."""
+    case = W.small_cases()[4]
+    a = _run(torch, case)
+    for seed in (105, 106):
+        b = _run(torch, case, W.permute_rows(case.topk_idx, seed))
+        assert torch.equal(a.out, b.out) and torch.equal(a.lse, b.lse)
+
+
+def test_padding_duplicates_and_out_of_range(torch):
+    """-1 padding and indices >= n_kv are skipped, repeated indices count
+    twice, an all-padding row gives o = 0 and lse = -inf, k = 1 selects one
+    row."""
+    case = W.sparse_mqa(rows=5, heads=64, n_kv=300, k=96, seed=16)
+    idx = case.topk_idx.copy()
+    idx[0, ::3] = -1
+    idx[1, :] = -1
+    idx[2, 10:20] = idx[2, 0:10]                   # duplicates
+    idx[3, 5] = 100000                             # out of range: skipped by the kernel
+    st = _run(torch, case, idx)
+    ref_idx = idx.copy()
+    ref_idx[3, 5] = -1                             # the oracle's view of a skipped entry
+    o_ref, l_ref = oracle.sparse_mqa(W.bf16_bits_to_f64(case.q), W.bf16_bits_to_f64(case.kv_latent), ref_idx,
+                                     case.d_v, float(np.float32(case.scale)))
+    out = W.bf16_bits_to_f64(R.tensor_to_bits(st.out))
+    lse = st.lse.cpu().numpy().astype(np.float64)
+    assert np.all(out[1] == 0) and np.all(lse[:, 1] == -np.inf)
+    assert_bf16_close(out, o_ref, "out")
+    assert_bf16_close(lse, l_ref, "lse")
+    one = W.SparseCase("k1", case.q, case.kv_latent, case.topk_idx[:, :1].copy(), case.d_v, case.scale)
+    st1 = _run(torch, one)
+    out1 = W.bf16_bits_to_f64(R.tensor_to_bits(st1.out))
+    kv = W.bf16_bits_to_f64(case.kv_latent)
+    for r in range(5):
+        assert np.array_equal(out1[r], np.broadcast_to(kv[one.topk_idx[r, 0], :case.d_v], out1[r].shape))
+
+
+def test_heads_not_a_multiple_of_the_workgroup(torch):
+    _check(torch, W.sparse_mqa(rows=3, heads=40, n_kv=200, k=70, seed=17), name="40 heads")
+
+
+def test_full_size_sampled(torch):
+    """The full workload (323 rows x 128 heads, k = 2048 of 2590) in the
+    benchmark's launch configuration: sampled rows against the oracle, every
+    row checked for permutation invariance, repeated runs bitwise equal."""
+    case = W.full_case("sparse_mqa")
+    rows = [0, 1, 100, 161, 254, 321, 322]
+    st = _check(torch, case, rows=rows, name="full")
+    o0, l0 = st.out.clone(), st.lse.clone()
+    R.run_sparse(st)
+    torch.cuda.synchronize()
+    assert torch.equal(st.out, o0) and torch.equal(st.lse, l0)
+    perm = _run(torch, case, W.permute_rows(case.topk_idx, 105))
+    assert torch.equal(perm.out, o0) and torch.equal(perm.lse, l0)

@@ -1,0 +1,18 @@
+"""MI355X-native (gfx950) tiled attention forward.
+
+The computation lives in hand-written HIP kernels inside ``libvea.so`` (C ABI
+in ``include/vea.h``); this package is a thin binding over it:
+
+* ``attn_fwd``        blockwise SDPA forward over a cu_seqlens-packed batch,
+                      causal or not, GQA, query pieces, fp32 online softmax;
+* ``qkv_rope``        fused QKV output split + 1D / 2D-grid RoPE;
+* ``sparse_mqa_fwd``  top-k sparse MQA over a shared latent KV;
+* ``attn_probs_piece`` debug export of one piece's probabilities.
+
+``workloads`` holds the seeded synthetic inputs; ``build`` compiles the library.
+"""
+from ._binding import (VeaError, attn_fwd, attn_probs_piece, lib_path, load_library,  # noqa: F401
+                       qkv_rope, sparse_mqa_fwd, status_str)
+
+__all__ = ["attn_fwd", "qkv_rope", "sparse_mqa_fwd", "attn_probs_piece", "VeaError", "load_library",
+           "lib_path", "status_str"]

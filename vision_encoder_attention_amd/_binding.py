@@ -1,0 +1,200 @@
+"""ctypes binding of libvea.so: argument marshalling only.
+
+Every function here takes torch tensors that already live on the GPU, reads
+their data pointers, element strides and the current HIP stream, and calls the
+C ABI declared in include/vea.h.  All computation happens in the HIP kernels;
+there is no Python or CPU fallback.  If the library is missing the first call
+raises, naming the build command.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libvea.so")
+
+VEA_F32, VEA_BF16 = 0, 1
+_lock = threading.Lock()
+_lib = None
+
+
+class VeaError(RuntimeError):
+    """A vea_* call returned a non-zero status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__("%s (status %d)" % (message, status))
+        self.status = status
+
+
+def lib_path() -> str:
+    return LIB_PATH
+
+
+def load_library():
+    """Load libvea.so once (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libvea.so not found at %s; build it with "
+                               "`python -m vision_encoder_attention_amd.build`" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        i32, i64, f32, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+        lib.vea_status_str.argtypes = [i32]
+        lib.vea_status_str.restype = ctypes.c_char_p
+        lib.vea_version.argtypes = []
+        lib.vea_version.restype = ctypes.c_char_p
+        lib.vea_attn_fwd.argtypes = [i32, vp, i64, vp, i64, vp, i64, vp, vp, i32, i32, i32, i32, i32,
+                                     i32, i32, i32, i32, f32, i32, vp, i64, vp, vp]
+        lib.vea_attn_fwd.restype = i32
+        lib.vea_qkv_rope.argtypes = [vp, i64, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp]
+        lib.vea_qkv_rope.restype = i32
+        lib.vea_sparse_mqa_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp]
+        lib.vea_sparse_mqa_fwd.restype = i32
+        lib.vea_attn_probs_piece.argtypes = [i32, vp, i64, vp, i64, vp, i64, i32, i32, i32, i32, i32, i32,
+                                             i32, i32, i32, i32, i32, f32, vp, i64, vp]
+        lib.vea_attn_probs_piece.restype = i32
+        _lib = lib
+        return lib
+
+
+def status_str(status: int) -> str:
+    return load_library().vea_status_str(int(status)).decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise VeaError(status, status_str(status))
+
+
+# ------------------------------------------------------------- marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return VEA_BF16
+    if t.dtype == torch.float32:
+        return VEA_F32
+    raise TypeError("unsupported dtype %s (bfloat16 or float32)" % t.dtype)
+
+
+def _token_major(t, name):
+    """[tokens, heads, dim] view with contiguous heads and dims; returns token stride."""
+    if t.dim() != 3:
+        raise ValueError("%s must be [tokens, heads, dim]" % name)
+    if t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+        raise ValueError("%s must have contiguous heads and head dims (token stride may differ)" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    return t.stride(0)
+
+
+def _int32_dev(t, name):
+    torch = _torch()
+    if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous int32 GPU tensor" % name)
+
+
+def attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, causal, scale, out, lse=None, *, piece_rows=0,
+             max_seqlen_q=None, max_seqlen_k=None):
+    """Blockwise attention forward (see vea_attn_fwd in include/vea.h).
+
+    q [total_q, Hq, d], k/v [total_k, Hkv, d] (token strides free), out like q,
+    lse float32 [Hq, total_q] or None.  max_seqlen_* default to the largest
+    sequence length, read from cu_seqlens with one host copy (synchronising).
+    """
+    lib = load_library()
+    qs, ks, vs, os_ = (_token_major(q, "q"), _token_major(k, "k"), _token_major(v, "v"),
+                       _token_major(out, "out"))
+    _int32_dev(cu_seqlens_q, "cu_seqlens_q")
+    _int32_dev(cu_seqlens_k, "cu_seqlens_k")
+    dt = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype or out.dtype != q.dtype:
+        raise TypeError("q, k, v and out must share a dtype")
+    if lse is not None:
+        torch = _torch()
+        if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (q.shape[1], q.shape[0]):
+            raise ValueError("lse must be contiguous float32 [Hq, total_q]")
+    batch = cu_seqlens_q.numel() - 1
+    if max_seqlen_q is None or max_seqlen_k is None:
+        lq = (cu_seqlens_q[1:] - cu_seqlens_q[:-1]).max().item() if batch > 0 else 0
+        lk = (cu_seqlens_k[1:] - cu_seqlens_k[:-1]).max().item() if batch > 0 else 0
+        max_seqlen_q = lq if max_seqlen_q is None else max_seqlen_q
+        max_seqlen_k = lk if max_seqlen_k is None else max_seqlen_k
+    st = lib.vea_attn_fwd(dt, _ptr(q), qs, _ptr(k), ks, _ptr(v), vs, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                          batch, q.shape[0], k.shape[0], int(max_seqlen_q), int(max_seqlen_k), q.shape[1],
+                          k.shape[1], q.shape[2], 1 if causal else 0, float(scale), int(piece_rows),
+                          _ptr(out), os_, _ptr(lse), _stream(q))
+    _check(st)
+    return out, lse
+
+
+def qkv_rope(x_qkv, positions, theta, q, k):
+    """Split the fused [T, (Hq+2Hkv) d] projection output into rotated q [T, Hq, d]
+    and k [T, Hkv, d] (see vea_qkv_rope); V stays in x_qkv."""
+    lib = load_library()
+    torch = _torch()
+    if x_qkv.dtype != torch.bfloat16 or q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16:
+        raise TypeError("qkv_rope works on bfloat16")
+    if x_qkv.dim() != 2 or x_qkv.stride(1) != 1:
+        raise ValueError("x_qkv must be [tokens, cols] with contiguous columns")
+    if not (q.is_contiguous() and k.is_contiguous()):
+        raise ValueError("q and k outputs must be contiguous")
+    _int32_dev(positions, "positions")
+    st = lib.vea_qkv_rope(_ptr(x_qkv), x_qkv.stride(0), _ptr(positions), positions.dim(), x_qkv.shape[0],
+                          q.shape[1], k.shape[1], q.shape[2], float(theta), _ptr(q), _ptr(k), _stream(x_qkv))
+    _check(st)
+    return q, k
+
+
+def sparse_mqa_fwd(q, kv_latent, topk_idx, k, scale, out, lse=None):
+    """Top-k sparse MQA (see vea_sparse_mqa_fwd): q [R, H, d_qk], kv_latent
+    [n_kv, d_qk], topk_idx int32 [R, k], out [R, H, d_v], lse [H, R] or None."""
+    lib = load_library()
+    torch = _torch()
+    for t, n in ((q, "q"), (kv_latent, "kv_latent"), (out, "out")):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("%s must be a contiguous bfloat16 GPU tensor" % n)
+    _int32_dev(topk_idx, "topk_idx")
+    if topk_idx.shape != (q.shape[0], k):
+        raise ValueError("topk_idx must be [rows, k]")
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (q.shape[1], q.shape[0])
+                            or not lse.is_contiguous()):
+        raise ValueError("lse must be contiguous float32 [heads, rows]")
+    st = lib.vea_sparse_mqa_fwd(_ptr(q), _ptr(kv_latent), _ptr(topk_idx), q.shape[0], q.shape[1],
+                                kv_latent.shape[0], q.shape[2], out.shape[2], int(k), float(scale), _ptr(out),
+                                _ptr(lse), _stream(q))
+    _check(st)
+    return out, lse
+
+
+def attn_probs_piece(q, k, lse, head, seq_begin_q, len_q, seq_begin_k, len_k, q0, rows, causal, scale, p_out):
+    """Debug export of P for one piece of one head into p_out [rows, >= len_k]
+    (see vea_attn_probs_piece)."""
+    lib = load_library()
+    qs, ks = _token_major(q, "q"), _token_major(k, "k")
+    if p_out.stride(1) != 1:
+        raise ValueError("p_out rows must be contiguous")
+    st = lib.vea_attn_probs_piece(_dtype_code(q), _ptr(q), qs, _ptr(k), ks, _ptr(lse), lse.stride(0), int(head),
+                                  q.shape[1], k.shape[1], q.shape[2], int(seq_begin_q), int(len_q),
+                                  int(seq_begin_k), int(len_k), int(q0), int(rows), 1 if causal else 0,
+                                  float(scale), _ptr(p_out), p_out.stride(0), _stream(q))
+    _check(st)
+    return p_out

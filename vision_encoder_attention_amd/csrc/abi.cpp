@@ -1,0 +1,206 @@
+// C ABI of the tiled-attention library: argument validation, launch shape,
+// dispatch to the kernel instances, and error reporting.  Declared in
+// include/vea.h.
+//
+// Validation runs entirely on the host and before any HIP call, so a bad
+// argument returns its status without touching the GPU.  Launch errors are
+// read back with hipGetLastError and returned as VEA_EHIP; they are never
+// swallowed (a swallowed error misled the debugging in
+// 「DeepSeek V4.1 上 4×RTX 3090：视觉链路的两个坑和修复」 section 三, "误导报错").
+#include "../../include/vea.h"
+#include "vea_internal.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <vector>
+
+using namespace vea;
+
+namespace {
+
+bool check_enabled() {
+  const char* e = getenv("VEA_CHECK");
+  return e != nullptr && e[0] != '\0' && strcmp(e, "0") != 0;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? VEA_OK : VEA_EHIP; }
+
+// VEA_CHECK: copy a device int32 array to the host after draining the stream.
+int fetch_ints(const int32_t* dev, size_t n, hipStream_t s, std::vector<int32_t>& host) {
+  host.resize(n);
+  if (n == 0) return VEA_OK;
+  if (hipStreamSynchronize(s) != hipSuccess) return VEA_EHIP;
+  if (hipMemcpy(host.data(), dev, n * sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess) return VEA_EHIP;
+  return VEA_OK;
+}
+
+int check_cu(const int32_t* cu, int batch, int total, int max_len, hipStream_t s) {
+  std::vector<int32_t> h;
+  int st = fetch_ints(cu, (size_t)batch + 1, s, h);
+  if (st != VEA_OK) return st;
+  if (h[0] != 0 || h[batch] != total) return VEA_ERANGE;
+  for (int b = 0; b < batch; ++b) {
+    const int len = h[b + 1] - h[b];
+    if (len < 0 || len > max_len) return VEA_ERANGE;
+  }
+  return VEA_OK;
+}
+
+int finish(int st, hipStream_t s) {
+  if (st != VEA_OK) return st;
+  if (check_enabled()) {
+    if (hipStreamSynchronize(s) != hipSuccess) return VEA_EHIP;
+  }
+  return VEA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* vea_status_str(int status) {
+  switch (status) {
+    case VEA_OK: return "VEA_OK";
+    case VEA_EINVAL: return "VEA_EINVAL: invalid argument (null pointer, non-finite scalar or misalignment)";
+    case VEA_EDTYPE: return "VEA_EDTYPE: dtype not supported by this call";
+    case VEA_ESHAPE: return "VEA_ESHAPE: inconsistent sizes";
+    case VEA_EUNSUPPORTED: return "VEA_EUNSUPPORTED: shape outside the compiled kernel set";
+    case VEA_ERANGE: return "VEA_ERANGE: index data out of range (VEA_CHECK)";
+    case VEA_EWORKSPACE: return "VEA_EWORKSPACE: workspace too small";
+    case VEA_EHIP: return "VEA_EHIP: HIP runtime error";
+    default: return "unknown vea status";
+  }
+}
+
+const char* vea_version(void) { return "vea 0.1.0 gfx950"; }
+
+int vea_attn_fwd(int dtype, const void* q, int64_t q_tok_stride, const void* k, int64_t k_tok_stride,
+                 const void* v, int64_t v_tok_stride, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                 int batch, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int num_heads_q,
+                 int num_heads_kv, int head_dim, int causal, float scale, int piece_rows, void* out,
+                 int64_t out_tok_stride, float* lse, void* stream) {
+  // ---- validation (host only)
+  if (dtype != VEA_BF16 && dtype != VEA_F32) return VEA_EDTYPE;
+  if (batch < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || piece_rows < 0)
+    return VEA_ESHAPE;
+  if (num_heads_q <= 0 || num_heads_kv <= 0 || num_heads_q % num_heads_kv != 0) return VEA_ESHAPE;
+  if (!isfinite(scale)) return VEA_EINVAL;
+  if (causal != 0 && causal != 1) return VEA_EINVAL;
+  if (dtype == VEA_BF16 && head_dim != 64 && head_dim != 128) return VEA_EUNSUPPORTED;
+  if (dtype == VEA_F32 && head_dim != 64) return VEA_EUNSUPPORTED;
+  if (batch == 0 || total_q == 0) return VEA_OK;                 // nothing to compute
+  if (!q || !k || !v || !out || !cu_seqlens_q || !cu_seqlens_k) return VEA_EINVAL;
+  const int64_t esz = dtype == VEA_BF16 ? 2 : 4;
+  const int64_t qrow = (int64_t)num_heads_q * head_dim, krow = (int64_t)num_heads_kv * head_dim;
+  if (q_tok_stride < qrow || out_tok_stride < qrow || k_tok_stride < krow || v_tok_stride < krow) return VEA_ESHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return VEA_EINVAL;
+  if ((q_tok_stride * esz) % 16 || (k_tok_stride * esz) % 16 || (v_tok_stride * esz) % 16 ||
+      (out_tok_stride * esz) % 16)
+    return VEA_EINVAL;
+  if (max_seqlen_q > total_q || max_seqlen_k > total_k) return VEA_ESHAPE;
+  hipStream_t s = (hipStream_t)stream;
+
+  if (check_enabled()) {
+    int st = check_cu(cu_seqlens_q, batch, total_q, max_seqlen_q, s);
+    if (st == VEA_OK) st = check_cu(cu_seqlens_k, batch, total_k, max_seqlen_k, s);
+    if (st != VEA_OK) return st;
+  }
+  if (max_seqlen_q == 0) return finish(VEA_OK, s);
+
+  // ---- launch shape: (sequence, piece, tile, head) units
+  DenseParams p;
+  p.q = q; p.k = k; p.v = v; p.out = out; p.lse = lse;
+  p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k;
+  p.q_stride = q_tok_stride; p.k_stride = k_tok_stride; p.v_stride = v_tok_stride; p.o_stride = out_tok_stride;
+  p.batch = batch; p.total_q = total_q; p.total_k = total_k;
+  p.hq = num_heads_q; p.hkv = num_heads_kv; p.group = num_heads_q / num_heads_kv;
+  p.qb = (piece_rows > 0 && piece_rows < max_seqlen_q) ? piece_rows : max_seqlen_q;
+  p.tiles_per_piece = (p.qb + kDenseBM - 1) / kDenseBM;
+  const int64_t pieces = ((int64_t)max_seqlen_q + p.qb - 1) / p.qb;
+  const int64_t tps = pieces * p.tiles_per_piece;
+  const int64_t units = (int64_t)batch * tps * num_heads_q;
+  if (units > 0x7fffffff) return VEA_EUNSUPPORTED;
+  p.tiles_per_seq = (int)tps;
+  p.units = (int)units;
+  p.xcd_map = (num_heads_kv % 8 == 0) ? 1 : 0;
+  p.scale = scale;
+
+  hipError_t e = dtype == VEA_BF16 ? launch_attn_fwd_bf16(p, head_dim, causal != 0, s)
+                                   : launch_attn_fwd_f32(p, head_dim, causal != 0, s);
+  return finish(hip_status(e), s);
+}
+
+int vea_qkv_rope(const void* x_qkv, int64_t x_tok_stride, const int32_t* positions, int pos_dims, int num_tokens,
+                 int num_heads_q, int num_heads_kv, int head_dim, float theta, void* q, void* k, void* stream) {
+  if (num_tokens < 0 || num_heads_q <= 0 || num_heads_kv <= 0 || head_dim <= 0) return VEA_ESHAPE;
+  if (pos_dims != 1 && pos_dims != 2) return VEA_EINVAL;
+  if (!isfinite(theta) || !(theta > 0.f)) return VEA_EINVAL;
+  if (head_dim % 8 != 0 || head_dim > 256 || (pos_dims == 2 && head_dim % 4 != 0)) return VEA_EUNSUPPORTED;
+  if (num_tokens == 0) return VEA_OK;
+  if (!x_qkv || !positions || !q || !k) return VEA_EINVAL;
+  if (x_tok_stride < (int64_t)(num_heads_q + 2 * num_heads_kv) * head_dim) return VEA_ESHAPE;
+  if (!aligned16(x_qkv) || !aligned16(q) || !aligned16(k) || (x_tok_stride * 2) % 16) return VEA_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  RopeParams p;
+  p.x = (const uint16_t*)x_qkv; p.pos = positions; p.q = (uint16_t*)q; p.k = (uint16_t*)k;
+  p.x_stride = x_tok_stride; p.tokens = num_tokens; p.hq = num_heads_q; p.hkv = num_heads_kv;
+  p.d = head_dim; p.pos_dims = pos_dims; p.theta = (double)theta;
+  return finish(hip_status(launch_qkv_rope(p, s)), s);
+}
+
+int vea_sparse_mqa_fwd(const void* q, const void* kv_latent, const int32_t* topk_idx, int num_rows, int num_heads,
+                       int n_kv, int d_qk, int d_v, int k, float scale, void* out, float* lse, void* stream) {
+  if (num_rows < 0 || num_heads <= 0 || n_kv < 0 || k <= 0) return VEA_ESHAPE;
+  if (d_v <= 0 || d_qk <= 0 || d_v > d_qk) return VEA_ESHAPE;
+  if (!isfinite(scale)) return VEA_EINVAL;
+  if (d_qk != 576 || d_v != 512 || k > 4096) return VEA_EUNSUPPORTED;
+  if (num_rows == 0) return VEA_OK;
+  if (!q || !topk_idx || !out || (n_kv > 0 && !kv_latent)) return VEA_EINVAL;
+  if (!aligned16(q) || !aligned16(out) || (kv_latent && !aligned16(kv_latent))) return VEA_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  if (check_enabled()) {
+    std::vector<int32_t> h;
+    int st = fetch_ints(topk_idx, (size_t)num_rows * k, s, h);
+    if (st != VEA_OK) return st;
+    for (int32_t x : h)
+      if (x >= n_kv) return VEA_ERANGE;
+  }
+  SparseParams p;
+  p.q = (const uint16_t*)q; p.kv = (const uint16_t*)kv_latent; p.idx = topk_idx; p.out = (uint16_t*)out;
+  p.lse = lse; p.rows = num_rows; p.heads = num_heads; p.n_kv = n_kv; p.k = k;
+  p.head_blocks = (num_heads + kSparseHeadsPerWG - 1) / kSparseHeadsPerWG;
+  p.scale = scale;
+  if ((int64_t)num_rows * p.head_blocks > 0x7fffffff) return VEA_EUNSUPPORTED;
+  return finish(hip_status(launch_sparse_mqa(p, d_qk, d_v, s)), s);
+}
+
+int vea_attn_probs_piece(int dtype, const void* q, int64_t q_tok_stride, const void* k, int64_t k_tok_stride,
+                         const float* lse, int64_t lse_row_stride, int head, int num_heads_q, int num_heads_kv,
+                         int head_dim, int seq_begin_q, int len_q, int seq_begin_k, int len_k, int q0, int rows,
+                         int causal, float scale, float* p_out, int64_t p_row_stride, void* stream) {
+  if (dtype != VEA_BF16 && dtype != VEA_F32) return VEA_EDTYPE;
+  if (num_heads_q <= 0 || num_heads_kv <= 0 || num_heads_q % num_heads_kv) return VEA_ESHAPE;
+  if (head < 0 || head >= num_heads_q || head_dim <= 0) return VEA_ESHAPE;
+  if (seq_begin_q < 0 || seq_begin_k < 0 || len_q < 0 || len_k < 0 || q0 < 0 || rows < 0 || q0 + rows > len_q)
+    return VEA_ESHAPE;
+  if (p_row_stride < len_k || lse_row_stride < seq_begin_q + len_q) return VEA_ESHAPE;
+  if (q_tok_stride < (int64_t)num_heads_q * head_dim || k_tok_stride < (int64_t)num_heads_kv * head_dim)
+    return VEA_ESHAPE;
+  if (!isfinite(scale) || (causal != 0 && causal != 1)) return VEA_EINVAL;
+  if (rows == 0 || len_k == 0) return VEA_OK;
+  if (!q || !k || !lse || !p_out) return VEA_EINVAL;
+  ProbsParams p;
+  p.q = q; p.k = k; p.lse = lse; p.p = p_out;
+  p.q_stride = q_tok_stride; p.k_stride = k_tok_stride; p.lse_stride = lse_row_stride; p.p_stride = p_row_stride;
+  p.head = head; p.kv_head = head / (num_heads_q / num_heads_kv); p.d = head_dim;
+  p.seq_q = seq_begin_q; p.len_q = len_q; p.seq_k = seq_begin_k; p.len_k = len_k; p.q0 = q0; p.rows = rows;
+  p.causal = causal; p.scale = scale;
+  hipStream_t s = (hipStream_t)stream;
+  return finish(hip_status(launch_attn_probs(p, dtype == VEA_BF16, s)), s);
+}
+
+}  // extern "C"

@@ -1,0 +1,553 @@
+// Blockwise scaled-dot-product attention forward for gfx950 (CDNA4, wave64).
+//
+// What is computed (per sequence b of a cu_seqlens-packed batch, query head h,
+// key/value head g = h / (Hq/Hkv), query row i):
+//   o_i = sum_j softmax_j(scale * q_i.k_j) v_j over the allowed keys j,
+//   lse_i = ln sum_j exp(scale * q_i.k_j)
+// Page titles cited:
+//   [3090]   「DeepSeek V4.1 上 4×RTX 3090：视觉链路的两个坑和修复」
+//   [MI250]  「AMD MI250部署DeepSeek-V4-Flash：先修正确性再谈性能」
+//   [SGLang] 「从 SGLang Kernel源码到 GPU Trace：DeepSeek V4.1 Flash - Prefill」
+//   [V32]    「推理引擎的“蝴蝶效应” -- 从V32 模型的输出不一致说起」
+//
+// Structure (bf16 path):
+//   * One workgroup = 4 waves = BM (128) query rows of one (sequence, piece,
+//     head).  Query pieces of qb rows are the scheduling unit of [3090]
+//     section 三; a tile never straddles a piece and all addressing inside a
+//     piece is relative to the piece's own rows (there is no S/P buffer in
+//     global memory at all: S and P live in registers).
+//   * The key loop walks BN = 64 keys per step up to the sequence's own key
+//     bound (the varlen loop of [SGLang] section 3.2), K and V tiles staged
+//     through LDS, double buffered, with 16-byte coalesced global loads.
+//   * Each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (fp32
+//     accumulation, [MI250] sections 3.1 / 4.1): the accumulator layout gives
+//     each lane ONE query row and 32 of the step's keys, so the row max needs
+//     a single cross-lane exchange and the row sum is lane-local until the end.
+//   * Online softmax in fp32 ([V32] section 进一步探索 eq. (1)(2)): running max
+//     m, rescale alpha = 2^(m_old - m_new), running sum l; exponentials via
+//     v_exp_f32 with log2(e) folded into the scale.
+//   * O^T += V^T P^T with the same MFMA; P is rounded to bf16 (RNE) in
+//     registers, V is stored transposed in LDS so each lane reads 4 keys of one
+//     column as one 8-byte LDS read.  O^T's layout again gives each lane one
+//     query row, so the per-row rescale touches only the lane's own registers.
+//   * Masking excludes keys (weight exactly 0) rather than adding a bias
+//     ([MI250] section 3.3); only tiles that cross the causal diagonal or the
+//     key tail evaluate the mask.
+//   * No atomics; each output element and each lse entry has one writer, so
+//     runs are bitwise reproducible ([MI250] section 3.2).
+#include "vea_internal.h"
+
+#include <float.h>
+#include <math.h>
+
+namespace vea {
+namespace {
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  // Round-to-nearest-even conversion; gfx950 emits v_cvt_pk_bf16_f32.
+  __bf16 a = (__bf16)lo;
+  __bf16 b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+// Decode the workgroup id into (sequence b, query head h, tile t).  Tiles are
+// issued heaviest-first (largest tile index first: under a causal mask it has
+// the most keys).  With xcd_map, all query heads of one key/value head are
+// kept on one XCD (workgroups are dispatched round-robin over the 8 XCDs), so
+// the workgroups that stream the same K/V share that XCD's L2.
+__device__ __forceinline__ void decode_unit(const DenseParams& p, int id, int& b, int& h, int& t) {
+  int trev;
+  if (p.xcd_map) {
+    const int xcd = id & 7, j = id >> 3;
+    const int nh = p.hq >> 3;
+    const int per_t = p.batch * nh;
+    trev = j / per_t;
+    const int rem = j - trev * per_t;
+    b = rem / nh;
+    const int hl = rem - b * nh;
+    const int a = hl / p.group, gi = hl - a * p.group;
+    h = (xcd + 8 * a) * p.group + gi;
+  } else {
+    const int per_t = p.batch * p.hq;
+    trev = id / per_t;
+    const int rem = id - trev * per_t;
+    b = rem / p.hq;
+    h = rem - b * p.hq;
+  }
+  t = p.tiles_per_seq - 1 - trev;
+}
+
+struct TileRange {
+  int qs, ks, len_q, len_k;   // sequence base rows and lengths
+  int row0, row_end;          // local query rows [row0, row_end) of this tile
+  int kend;                   // keys [0, kend) are needed by some row
+  int kfull;                  // keys [0, kfull) are allowed for every row
+};
+
+__device__ __forceinline__ bool tile_range(const DenseParams& p, int b, int t, int bm, bool causal, TileRange& r) {
+  const int qs = clampi(p.cu_q[b], 0, p.total_q);
+  const int qe = clampi(p.cu_q[b + 1], qs, p.total_q);
+  const int ks = clampi(p.cu_k[b], 0, p.total_k);
+  const int ke = clampi(p.cu_k[b + 1], ks, p.total_k);
+  r.qs = qs;
+  r.ks = ks;
+  r.len_q = qe - qs;
+  r.len_k = ke - ks;
+  const int piece = t / p.tiles_per_piece;
+  const int tip = t - piece * p.tiles_per_piece;
+  const int pbase = piece * p.qb;                       // piece-local row base
+  const int row_lim = min(pbase + p.qb, r.len_q);
+  r.row0 = pbase + tip * bm;
+  if (r.row0 >= row_lim) return false;
+  r.row_end = min(r.row0 + bm, row_lim);
+  if (causal) {
+    const int off = r.len_k - r.len_q;                  // bottom-right alignment
+    r.kend = clampi(r.row_end + off, 0, r.len_k);
+    r.kfull = clampi(r.row0 + off + 1, 0, r.len_k);
+  } else {
+    r.kend = r.len_k;
+    r.kfull = r.len_k;
+  }
+  return true;
+}
+
+// =============================================================== bf16 path
+
+template <int D>
+struct Cfg {
+  static constexpr int BM = kDenseBM;         // 4 waves x 32 rows
+  static constexpr int BN = 64;               // keys per step
+  static constexpr int THREADS = 256;
+  static constexpr int KROW = D + 8;          // K row in LDS (bf16), padded: conflict-free 16-B reads
+  static constexpr int VROW = BN + 4;         // V^T row in LDS (bf16), 136 B: conflict-free 8-B reads
+  static constexpr int K_ELEMS = BN * KROW;
+  static constexpr int V_ELEMS = D * VROW;
+  static constexpr int BUF = K_ELEMS + V_ELEMS;
+  static constexpr int DCH = D / 8;           // 16-byte chunks per row
+  static constexpr int CPT = BN * DCH / THREADS;   // chunks per thread per tensor (4 or 2)
+  static_assert(CPT == 2 || CPT == 4, "tile/thread split");
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(DenseParams p) {
+  using C = Cfg<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::BUF];
+
+  int b, h, t;
+  decode_unit(p, blockIdx.x, b, h, t);
+  TileRange tr;
+  if (!tile_range(p, b, t, C::BM, CAUSAL, tr)) return;   // uniform over the workgroup
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int g2 = lane >> 5;                 // 0/1: which half of the wave
+  const int kvh = h / p.group;
+
+  const uint16_t* __restrict__ qg = (const uint16_t*)p.q;
+  const uint16_t* __restrict__ kg = (const uint16_t*)p.k;
+  const uint16_t* __restrict__ vg = (const uint16_t*)p.v;
+
+  // ---- this lane's query row (local index in the sequence)
+  const int qi = tr.row0 + wave * 32 + l32;
+  const bool qvalid = qi < tr.row_end;
+
+  // ---- Q fragment (B operand of S^T = K Q^T): Q[qi][16 ks + 8 g2 .. +7]
+  u32x4 qf[D / 16];
+  {
+    const uint16_t* src = qg + (int64_t)(tr.qs + (qvalid ? qi : tr.row0)) * p.q_stride + (int64_t)h * D + 8 * g2;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      u32x4 v = *(const u32x4*)(src + 16 * ks);
+      qf[ks] = qvalid ? v : (u32x4){0u, 0u, 0u, 0u};
+    }
+  }
+  // Negative scale: negate Q (exact, a sign-bit flip) so the exponent scale is positive.
+  float c = fabsf(p.scale) * kLog2e;
+  if (p.scale < 0.f) {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) qf[ks] ^= (u32x4){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+  }
+  c = fmaxf(c, FLT_MIN);   // scale 0: every logit becomes ~0, masked ones stay -inf
+
+  // Per-row key bound for the causal mask (keys j < kend_i are allowed).
+  const int kend_i = CAUSAL ? clampi(qi + tr.len_k - tr.len_q + 1, 0, tr.len_k) : tr.len_k;
+
+  floatx16 o[D / 32];
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb) o[nb] = (floatx16){};
+  float m_run = -INFINITY;   // running max, already multiplied by c (log2 domain)
+  float l_run = 0.f;         // lane-partial running sum
+
+  const int n_tiles = (tr.kend + C::BN - 1) / C::BN;
+
+  // ---- global -> register staging of one K/V tile
+  const int kdc = tid % C::DCH;                    // K: chunk column
+  const int krow = tid / C::DCH;                   // K: first key row (+ i * THREADS/DCH)
+  const int vdc = tid % C::DCH;                    // V: chunk column
+  const int vkg = tid / C::DCH;                    // V: key group of CPT consecutive keys
+  u32x4 kreg[C::CPT], vreg[C::CPT];
+
+  auto load_tile = [&](int kt) {
+    const int kbase = kt * C::BN;
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int key = kbase + krow + i * (C::THREADS / C::DCH);
+      const bool ok = key < tr.kend;
+      const uint16_t* src = kg + (int64_t)(tr.ks + (ok ? key : 0)) * p.k_stride + (int64_t)kvh * D + 8 * kdc;
+      u32x4 v = *(const u32x4*)src;
+      kreg[i] = ok ? v : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int key = kbase + vkg * C::CPT + i;
+      const bool ok = key < tr.kend;
+      const uint16_t* src = vg + (int64_t)(tr.ks + (ok ? key : 0)) * p.v_stride + (int64_t)kvh * D + 8 * vdc;
+      u32x4 v = *(const u32x4*)src;
+      vreg[i] = ok ? v : (u32x4){0u, 0u, 0u, 0u};   // zero rows: masked P (=0) times finite V
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+    uint16_t* ks_ = smem + buf * C::BUF;
+    uint16_t* vs_ = ks_ + C::K_ELEMS;
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int r = krow + i * (C::THREADS / C::DCH);
+      *(u32x4*)(ks_ + r * C::KROW + 8 * kdc) = kreg[i];
+    }
+    // V^T[d][key]: element e of this thread's chunk column, CPT consecutive keys.
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int w = e >> 1, sh = (e & 1) * 16;
+      uint16_t* dst = vs_ + (8 * vdc + e) * C::VROW + vkg * C::CPT;
+      if constexpr (C::CPT == 4) {
+        const uint32_t a0 = (vreg[0][w] >> sh) & 0xFFFFu, a1 = (vreg[1][w] >> sh) & 0xFFFFu;
+        const uint32_t a2 = (vreg[2][w] >> sh) & 0xFFFFu, a3 = (vreg[3][w] >> sh) & 0xFFFFu;
+        *(u32x2*)dst = (u32x2){a0 | (a1 << 16), a2 | (a3 << 16)};
+      } else {
+        const uint32_t a0 = (vreg[0][w] >> sh) & 0xFFFFu, a1 = (vreg[1][w] >> sh) & 0xFFFFu;
+        *(uint32_t*)dst = a0 | (a1 << 16);
+      }
+    }
+  };
+
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+  }
+
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < n_tiles) load_tile(kt + 1);
+
+    const uint16_t* ks_ = smem + buf * C::BUF;
+    const uint16_t* vs_ = ks_ + C::K_ELEMS;
+
+    // ---- S^T = K Q^T for two 32-key blocks
+    floatx16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = (floatx16){};
+      const uint16_t* ka = ks_ + (32 * kb + l32) * C::KROW + 8 * g2;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const u32x4 a = *(const u32x4*)(ka + 16 * ks);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qf[ks]), s[kb], 0, 0, 0);
+      }
+    }
+
+    // ---- mask (only tiles crossing the causal diagonal or the key tail)
+    const int kbase = kt * C::BN;
+    if (kbase + C::BN > tr.kfull) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = kbase + 32 * kb + 8 * (r >> 2) + 4 * g2 + (r & 3);
+          if (j >= kend_i) s[kb][r] = -INFINITY;
+        }
+    }
+
+    // ---- online softmax (fp32)
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mx_sc = (mx == -INFINITY) ? -INFINITY : mx * c;
+    const float m_new = fmaxf(m_run, mx_sc);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = fast_exp2(fmaf(s[kb][r], c, -m_use));
+        s[kb][r] = e;
+        psum += e;
+      }
+    l_run = fmaf(alpha, l_run, psum);
+
+    // Rescale O only when some row's max moved (alpha == 1 otherwise).
+    if (__builtin_amdgcn_read_exec() && __any(alpha != 1.f)) {
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb) o[nb] *= alpha;
+    }
+
+    // ---- P -> bf16 (B operand of O^T += V^T P^T), 4 k-steps of 16 keys
+    u32x4 pb[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int r0 = 8 * hf;
+        pb[2 * kb + hf] = (u32x4){pack_bf16x2(s[kb][r0 + 0], s[kb][r0 + 1]), pack_bf16x2(s[kb][r0 + 2], s[kb][r0 + 3]),
+                                  pack_bf16x2(s[kb][r0 + 4], s[kb][r0 + 5]), pack_bf16x2(s[kb][r0 + 6], s[kb][r0 + 7])};
+      }
+
+    // ---- O^T += V^T P^T.  k-slot j of lane half g2 in step (kb, hf) is key
+    //      32 kb + 16 hf + 8 (j / 4) + 4 g2 + (j % 4): the same keys the lane's
+    //      P registers hold, so both operands agree on the contraction order.
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) {
+      const uint16_t* va = vs_ + (32 * nb + l32) * C::VROW + 4 * g2;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int koff = 16 * st;                // = 32 kb + 16 hf
+        const u32x2 lo = *(const u32x2*)(va + koff);
+        const u32x2 hi = *(const u32x2*)(va + koff + 8);
+        const u32x4 a = (u32x4){lo[0], lo[1], hi[0], hi[1]};
+        o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pb[st]), o[nb], 0, 0, 0);
+      }
+    }
+
+    if (kt + 1 < n_tiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O / l (bf16 RNE), lse = ln 2 * (m + log2 l)
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qvalid) {
+    uint16_t* dst = (uint16_t*)p.out + (int64_t)(tr.qs + qi) * p.o_stride + (int64_t)h * D + 4 * g2;
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const floatx16& ov = o[nb];
+        const u32x2 w = (u32x2){pack_bf16x2(ov[4 * r4 + 0] * inv, ov[4 * r4 + 1] * inv),
+                                pack_bf16x2(ov[4 * r4 + 2] * inv, ov[4 * r4 + 3] * inv)};
+        *(u32x2*)(dst + 32 * nb + 8 * r4) = w;
+      }
+    if (p.lse != nullptr && g2 == 0)
+      p.lse[(int64_t)h * p.total_q + tr.qs + qi] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+// ================================================================ fp32 path
+// Same decomposition with v_mfma_f32_32x32x2_f32: each lane holds one k value
+// per MFMA, so K and V are read row-major from LDS (no transpose needed).
+
+template <int D>
+struct CfgF32 {
+  static constexpr int BM = kDenseBM;
+  static constexpr int BN = 32;
+  static constexpr int THREADS = 256;
+  static constexpr int ROW = D + 4;           // floats per LDS row
+  static constexpr int DCH = D / 4;           // 16-byte chunks per row
+  static constexpr int CPT = BN * DCH / THREADS;
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void attn_fwd_f32_kernel(DenseParams p) {
+  using C = CfgF32<D>;
+  __shared__ __attribute__((aligned(16))) float ksm[C::BN * C::ROW];
+  __shared__ __attribute__((aligned(16))) float vsm[C::BN * C::ROW];
+
+  int b, h, t;
+  decode_unit(p, blockIdx.x, b, h, t);
+  TileRange tr;
+  if (!tile_range(p, b, t, C::BM, CAUSAL, tr)) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int g2 = lane >> 5;
+  const int kvh = h / p.group;
+  const float* __restrict__ qg = (const float*)p.q;
+  const float* __restrict__ kg = (const float*)p.k;
+  const float* __restrict__ vg = (const float*)p.v;
+
+  const int qi = tr.row0 + wave * 32 + l32;
+  const bool qvalid = qi < tr.row_end;
+  // B operand of the 32x32x2 MFMA: lane holds Q[qi][2 ks + g2]
+  float qf[D / 2];
+  {
+    const float* src = qg + (int64_t)(tr.qs + (qvalid ? qi : tr.row0)) * p.q_stride + (int64_t)h * D + g2;
+#pragma unroll
+    for (int ks = 0; ks < D / 2; ++ks) qf[ks] = qvalid ? src[2 * ks] : 0.f;
+  }
+  float c = fabsf(p.scale) * kLog2e;
+  if (p.scale < 0.f) {
+#pragma unroll
+    for (int ks = 0; ks < D / 2; ++ks) qf[ks] = -qf[ks];
+  }
+  c = fmaxf(c, FLT_MIN);
+  const int kend_i = CAUSAL ? clampi(qi + tr.len_k - tr.len_q + 1, 0, tr.len_k) : tr.len_k;
+
+  floatx16 o[D / 32];
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb) o[nb] = (floatx16){};
+  float m_run = -INFINITY, l_run = 0.f;
+  const int n_tiles = (tr.kend + C::BN - 1) / C::BN;
+
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const int kbase = kt * C::BN;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int cidx = tid + i * C::THREADS;
+      const int r = cidx / C::DCH, dc = cidx % C::DCH;
+      const int key = kbase + r;
+      const bool ok = key < tr.kend;
+      const int64_t row = tr.ks + (ok ? key : 0);
+      floatx4 kv = *(const floatx4*)(kg + row * p.k_stride + (int64_t)kvh * D + 4 * dc);
+      floatx4 vv = *(const floatx4*)(vg + row * p.v_stride + (int64_t)kvh * D + 4 * dc);
+      if (!ok) { kv = (floatx4){}; vv = (floatx4){}; }
+      *(floatx4*)(ksm + r * C::ROW + 4 * dc) = kv;
+      *(floatx4*)(vsm + r * C::ROW + 4 * dc) = vv;
+    }
+    __syncthreads();
+
+    floatx16 s = (floatx16){};
+    {
+      const float* ka = ksm + l32 * C::ROW + g2;
+#pragma unroll
+      for (int ks = 0; ks < D / 2; ++ks)
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(ka[2 * ks], qf[ks], s, 0, 0, 0);
+    }
+    if (kbase + C::BN > tr.kfull) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = kbase + 8 * (r >> 2) + 4 * g2 + (r & 3);
+        if (j >= kend_i) s[r] = -INFINITY;
+      }
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mx_sc = (mx == -INFINITY) ? -INFINITY : mx * c;
+    const float m_new = fmaxf(m_run, mx_sc);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float e = fast_exp2(fmaf(s[r], c, -m_use));
+      s[r] = e;
+      psum += e;
+    }
+    l_run = fmaf(alpha, l_run, psum);
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) o[nb] *= alpha;
+    // O^T += V^T P^T: MFMA step r uses key 8 (r/4) + 4 g2 + r%4 in lane half g2.
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r >> 2) + 4 * g2 + (r & 3);
+        o[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(vsm[key * C::ROW + 32 * nb + l32], s[r], o[nb], 0, 0, 0);
+      }
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qvalid) {
+    float* dst = (float*)p.out + (int64_t)(tr.qs + qi) * p.o_stride + (int64_t)h * D + 4 * g2;
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const floatx16& ov = o[nb];
+        *(floatx4*)(dst + 32 * nb + 8 * r4) =
+            (floatx4){ov[4 * r4] * inv, ov[4 * r4 + 1] * inv, ov[4 * r4 + 2] * inv, ov[4 * r4 + 3] * inv};
+      }
+    if (p.lse != nullptr && g2 == 0)
+      p.lse[(int64_t)h * p.total_q + tr.qs + qi] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+// ======================================================= debug probabilities
+// P[r][j] = exp(scale q.k - lse) for one piece of one head, written from the
+// start of the caller's buffer (piece-local addressing, [3090] section 三).
+template <bool BF16>
+__global__ __launch_bounds__(256) void attn_probs_kernel(ProbsParams p) {
+  const int r = blockIdx.y;
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= p.rows || j >= p.len_k) return;
+  const int i = p.q0 + r;                                   // local query row
+  float* dst = p.p + (int64_t)r * p.p_stride + j;
+  if (p.causal && j > i + p.len_k - p.len_q) { *dst = 0.f; return; }
+  float dot = 0.f;
+  if (BF16) {
+    const uint16_t* qq = (const uint16_t*)p.q + (int64_t)(p.seq_q + i) * p.q_stride + (int64_t)p.head * p.d;
+    const uint16_t* kk = (const uint16_t*)p.k + (int64_t)(p.seq_k + j) * p.k_stride + (int64_t)p.kv_head * p.d;
+    for (int c = 0; c < p.d; ++c)
+      dot = fmaf(__uint_as_float((uint32_t)qq[c] << 16), __uint_as_float((uint32_t)kk[c] << 16), dot);
+  } else {
+    const float* qq = (const float*)p.q + (int64_t)(p.seq_q + i) * p.q_stride + (int64_t)p.head * p.d;
+    const float* kk = (const float*)p.k + (int64_t)(p.seq_k + j) * p.k_stride + (int64_t)p.kv_head * p.d;
+    for (int c = 0; c < p.d; ++c) dot = fmaf(qq[c], kk[c], dot);
+  }
+  const float l = p.lse[(int64_t)p.head * p.lse_stride + p.seq_q + i];
+  *dst = expf(p.scale * dot - l);
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd_bf16(const DenseParams& p, int head_dim, bool causal, hipStream_t s) {
+  const dim3 grid(p.units), block(256);
+  if (head_dim == 64) {
+    if (causal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, false>), grid, block, 0, s, p);
+  } else if (head_dim == 128) {
+    if (causal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, false>), grid, block, 0, s, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd_f32(const DenseParams& p, int head_dim, bool causal, hipStream_t s) {
+  const dim3 grid(p.units), block(256);
+  if (head_dim != 64) return hipErrorInvalidValue;
+  if (causal) hipLaunchKernelGGL((attn_fwd_f32_kernel<64, true>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((attn_fwd_f32_kernel<64, false>), grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_probs(const ProbsParams& p, bool bf16, hipStream_t s) {
+  const dim3 grid((p.len_k + 255) / 256, p.rows), block(256);
+  if (bf16) hipLaunchKernelGGL((attn_probs_kernel<true>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((attn_probs_kernel<false>), grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace vea

@@ -1,0 +1,99 @@
+// Fused-QKV split + rotary position embedding for gfx950.
+//
+// The vision encoder's qkv_rope step (「DeepSeek V4.1 上 4×RTX 3090：视觉链路的两个坑和修复」,
+// section 二) rotated Q and K in place, and two threads touched the same
+// memory.  This kernel is out-of-place and every output element has exactly
+// one writer: a thread owns whole 16-byte chunks (4 rotation pairs), so no
+// pair is ever split between threads and nothing needs synchronising except
+// the per-token angle table, written before one barrier and read after it.
+//
+// Layout of the fused projection output ([T, 3*hidden] in
+// 「从 SGLang Kernel源码到 GPU Trace：DeepSeek V4.1 Flash - Prefill」 section 3.1):
+// columns [Q heads | K heads | V heads], each head `d` contiguous bf16 values.
+// Q and K are contiguous in a row, so the (Hq + Hkv) * d / 8 chunks of a token
+// are read as one coalesced run; V is not touched (the attention kernel reads
+// it in place through a strided pointer).
+//
+// Precision (trigonometry in at least fp32:
+// 「AMD MI250部署DeepSeek-V4-Flash：先修正确性再谈性能」 section 4.1): the
+// frequency theta^(-2i/d_r) and the angle pos * freq are formed in fp64, sin and
+// cos are taken in fp64 and rounded to fp32, the rotation is done in fp32 and
+// the result rounded to bf16 (nearest even).  At position 8191 an fp32 angle
+// would carry ~5e-4 rad of error; the fp64 angle keeps it below 1e-11.
+#include "vea_internal.h"
+
+#include <math.h>
+
+namespace vea {
+namespace {
+
+constexpr int kRopeMaxHalf = 128;   // head_dim <= 256
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__global__ __launch_bounds__(256) void qkv_rope_kernel(RopeParams p) {
+  __shared__ float cs[kRopeMaxHalf];
+  __shared__ float sn[kRopeMaxHalf];
+  const int t = blockIdx.x;
+  const int half = p.d >> 1;
+  const double log2_theta = log2(p.theta);
+
+  // Angle table of this token, indexed by the pair's index inside the head.
+  for (int i = threadIdx.x; i < half; i += blockDim.x) {
+    double pos, expo;
+    if (p.pos_dims == 1) {
+      pos = (double)p.pos[t];
+      expo = -2.0 * (double)i / (double)p.d;                 // span d
+    } else {
+      const int q4 = p.d >> 2;                               // pairs per half-head
+      const int axis = i >= q4 ? 1 : 0;                      // 0: grid row, 1: grid column
+      const int ii = i - axis * q4;
+      pos = (double)p.pos[2 * (int64_t)t + axis];
+      expo = -2.0 * (double)ii / (double)(p.d >> 1);         // span d/2
+    }
+    const double ang = pos * exp2(expo * log2_theta);
+    double s, c;
+    sincos(ang, &s, &c);
+    cs[i] = (float)c;
+    sn[i] = (float)s;
+  }
+  __syncthreads();
+
+  const int cph = p.d >> 3;                                  // 16-byte chunks per head
+  const int nchunks = (p.hq + p.hkv) * cph;
+  const uint16_t* src = p.x + (int64_t)t * p.x_stride;
+  for (int ci = threadIdx.x; ci < nchunks; ci += blockDim.x) {
+    const int head = ci / cph;
+    const int ch = ci - head * cph;
+    const u32x4 v = *(const u32x4*)(src + 8 * ci);
+    u32x4 o;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int pi = 4 * ch + w;                             // pair index inside the head
+      const float x0 = bf16lo(v[w]), x1 = bf16hi(v[w]);
+      const float c = cs[pi], s = sn[pi];
+      const float y0 = fmaf(x0, c, -(x1 * s));
+      const float y1 = fmaf(x0, s, x1 * c);
+      o[w] = pack2(y0, y1);
+    }
+    uint16_t* dst = head < p.hq ? p.q + ((int64_t)t * p.hq + head) * p.d + 8 * ch
+                                : p.k + ((int64_t)t * p.hkv + (head - p.hq)) * p.d + 8 * ch;
+    *(u32x4*)dst = o;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_qkv_rope(const RopeParams& p, hipStream_t s) {
+  if (p.tokens == 0) return hipSuccess;
+  hipLaunchKernelGGL(qkv_rope_kernel, dim3(p.tokens), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace vea

@@ -1,0 +1,84 @@
+// Internal declarations shared by the HIP kernels and the C ABI layer.
+// Target: gfx950 (CDNA4), wave64.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vea {
+
+// ---------------------------------------------------------------- vector types
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ------------------------------------------------------------ launch params
+struct DenseParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;                // nullable
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int64_t q_stride, k_stride, v_stride, o_stride;   // elements per token
+  int batch, total_q, total_k;
+  int hq, hkv, group;        // group = hq / hkv
+  int qb;                    // rows per piece (> 0, already resolved)
+  int tiles_per_piece, tiles_per_seq;
+  int units;                 // batch * tiles_per_seq * hq
+  int xcd_map;               // 1: spread kv heads over the 8 XCDs
+  float scale;
+};
+
+struct RopeParams {
+  const uint16_t* x;
+  const int32_t* pos;
+  uint16_t* q;
+  uint16_t* k;
+  int64_t x_stride;
+  int tokens, hq, hkv, d, pos_dims;
+  double theta;
+};
+
+struct SparseParams {
+  const uint16_t* q;
+  const uint16_t* kv;
+  const int32_t* idx;
+  uint16_t* out;
+  float* lse;                // nullable
+  int rows, heads, n_kv, k;
+  int head_blocks;           // ceil(heads / heads per workgroup)
+  float scale;
+};
+
+struct ProbsParams {
+  const void* q;
+  const void* k;
+  const float* lse;
+  float* p;
+  int64_t q_stride, k_stride, lse_stride, p_stride;
+  int head, kv_head, d;
+  int seq_q, len_q, seq_k, len_k, q0, rows, causal;
+  float scale;
+};
+
+// Launchers (one per kernel family).  Each returns the hipError_t of the launch.
+hipError_t launch_attn_fwd_bf16(const DenseParams& p, int head_dim, bool causal, hipStream_t s);
+hipError_t launch_attn_fwd_f32(const DenseParams& p, int head_dim, bool causal, hipStream_t s);
+hipError_t launch_qkv_rope(const RopeParams& p, hipStream_t s);
+hipError_t launch_sparse_mqa(const SparseParams& p, int d_qk, int d_v, hipStream_t s);
+hipError_t launch_attn_probs(const ProbsParams& p, bool bf16, hipStream_t s);
+
+// Tile shape of the dense bf16/f32 kernels (query rows per workgroup); the
+// host uses it to size the launch.
+constexpr int kDenseBM = 128;
+constexpr int kSparseHeadsPerWG = 64;
+
+}  // namespace vea
