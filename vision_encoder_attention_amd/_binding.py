@@ -99,6 +99,8 @@ def _token_major(t, name):
     """[tokens, heads, dim] view with contiguous heads and dims; returns token stride."""
     if t.dim() != 3:
         raise ValueError("%s must be [tokens, heads, dim]" % name)
+    if t.numel() == 0:
+        return t.shape[1] * t.shape[2]          # empty: strides are meaningless, nothing is read
     if t.stride(2) != 1 or t.stride(1) != t.shape[2]:
         raise ValueError("%s must have contiguous heads and head dims (token stride may differ)" % name)
     if not t.is_cuda:

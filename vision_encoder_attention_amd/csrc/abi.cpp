@@ -93,7 +93,8 @@ int vea_attn_fwd(int dtype, const void* q, int64_t q_tok_stride, const void* k, 
   if (dtype == VEA_BF16 && head_dim != 64 && head_dim != 128) return VEA_EUNSUPPORTED;
   if (dtype == VEA_F32 && head_dim != 64) return VEA_EUNSUPPORTED;
   if (batch == 0 || total_q == 0) return VEA_OK;                 // nothing to compute
-  if (!q || !k || !v || !out || !cu_seqlens_q || !cu_seqlens_k) return VEA_EINVAL;
+  if (!q || !out || !cu_seqlens_q || !cu_seqlens_k) return VEA_EINVAL;
+  if (total_k > 0 && (!k || !v)) return VEA_EINVAL;               // no keys: k/v are never read
   const int64_t esz = dtype == VEA_BF16 ? 2 : 4;
   const int64_t qrow = (int64_t)num_heads_q * head_dim, krow = (int64_t)num_heads_kv * head_dim;
   if (q_tok_stride < qrow || out_tok_stride < qrow || k_tok_stride < krow || v_tok_stride < krow) return VEA_ESHAPE;
