@@ -40,17 +40,24 @@
 #include <float.h>
 #include <math.h>
 
+#include <type_traits>
+
 namespace vea {
 namespace {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  // Round-to-nearest-even conversion; gfx950 emits v_cvt_pk_bf16_f32.
-  __bf16 a = (__bf16)lo;
-  __bf16 b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  // Round-to-nearest-even conversion of a pair: one v_cvt_pk_bf16_f32.
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2v));
 }
+
+// IEEE maximum (NaN-propagating); maps to v_maximum3_f32 without the
+// canonicalising moves fmaxf needs.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -119,25 +126,47 @@ __device__ __forceinline__ bool tile_range(const DenseParams& p, int b, int t, i
 
 // =============================================================== bf16 path
 
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Transposed LDS read: within each group of 16 lanes, lane i points at 8 bytes
+// (row i/4, columns 4(i%4)..+3 of a 4 x 16 bf16 block) and receives column i
+// of that block (its 4 rows).
+__device__ __forceinline__ u32x2 lds_read_tr(const void* p) {
+  shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) shortx4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ float lane_swap_max(float x) {
+  // max with the lane 32 apart (the other half of the wave holds the same row)
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float lane_swap_add(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int D>
 struct Cfg {
-  static constexpr int BM = kDenseBM;         // 4 waves x 32 rows
-  static constexpr int BN = 64;               // keys per step
+  static constexpr int BM = kDenseBM;                   // 4 waves x 32 query rows
+  static constexpr int BN = 64;                         // keys per step
   static constexpr int THREADS = 256;
-  static constexpr int KROW = D + 8;          // K row in LDS (bf16), padded: conflict-free 16-B reads
-  static constexpr int VROW = BN + 4;         // V^T row in LDS (bf16), 136 B: conflict-free 8-B reads
-  static constexpr int K_ELEMS = BN * KROW;
-  static constexpr int V_ELEMS = D * VROW;
-  static constexpr int BUF = K_ELEMS + V_ELEMS;
-  static constexpr int DCH = D / 8;           // 16-byte chunks per row
-  static constexpr int CPT = BN * DCH / THREADS;   // chunks per thread per tensor (4 or 2)
-  static_assert(CPT == 2 || CPT == 4, "tile/thread split");
+  static constexpr int CPR = D / 8;                     // 16-byte chunks per K/V row
+  static constexpr int TILE = BN * D * 2;               // bytes of one K (or V) tile
+  static constexpr int STAGE = 2 * TILE;                // K + V
+  static constexpr int LOADS = TILE / (THREADS * 16);   // 16-byte DMA loads per lane per tile
+  static_assert(LOADS == 2 || LOADS == 4, "tile split");
+  // XOR swizzle of the 16-byte chunks of a row: the 32 rows read together by
+  // one MFMA operand land on distinct bank groups.
+  static __device__ __forceinline__ int swz(int r) { return D == 64 ? ((r >> 1) & 7) : (r & 15); }
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(DenseParams p) {
+__global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(DenseParams p) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::BUF];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * C::STAGE];
 
   int b, h, t;
   decode_unit(p, blockIdx.x, b, h, t);
@@ -148,12 +177,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(DenseParams p) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l32 = lane & 31;
-  const int g2 = lane >> 5;                 // 0/1: which half of the wave
+  const int g2 = lane >> 5;                 // which half of the wave
   const int kvh = h / p.group;
-
-  const uint16_t* __restrict__ qg = (const uint16_t*)p.q;
-  const uint16_t* __restrict__ kg = (const uint16_t*)p.k;
-  const uint16_t* __restrict__ vg = (const uint16_t*)p.v;
 
   // ---- this lane's query row (local index in the sequence)
   const int qi = tr.row0 + wave * 32 + l32;
@@ -162,14 +187,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(DenseParams p) {
   // ---- Q fragment (B operand of S^T = K Q^T): Q[qi][16 ks + 8 g2 .. +7]
   u32x4 qf[D / 16];
   {
-    const uint16_t* src = qg + (int64_t)(tr.qs + (qvalid ? qi : tr.row0)) * p.q_stride + (int64_t)h * D + 8 * g2;
+    const uint16_t* src = (const uint16_t*)p.q + (int64_t)(tr.qs + (qvalid ? qi : tr.row0)) * p.q_stride +
+                          (int64_t)h * D + 8 * g2;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      u32x4 v = *(const u32x4*)(src + 16 * ks);
+      const u32x4 v = *(const u32x4*)(src + 16 * ks);
       qf[ks] = qvalid ? v : (u32x4){0u, 0u, 0u, 0u};
     }
   }
-  // Negative scale: negate Q (exact, a sign-bit flip) so the exponent scale is positive.
+  // Negative scale: negate Q (exact sign-bit flip) so the exponent scale is positive.
   float c = fabsf(p.scale) * kLog2e;
   if (p.scale < 0.f) {
 #pragma unroll
@@ -177,169 +203,157 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(DenseParams p) {
   }
   c = fmaxf(c, FLT_MIN);   // scale 0: every logit becomes ~0, masked ones stay -inf
 
-  // Per-row key bound for the causal mask (keys j < kend_i are allowed).
   const int kend_i = CAUSAL ? clampi(qi + tr.len_k - tr.len_q + 1, 0, tr.len_k) : tr.len_k;
+
+  // ---- DMA of K/V tiles straight into LDS (buffer loads, no register staging).
+  // Lane slot sl of the wave's 1 KB destination block holds row sl / CPR,
+  // physical chunk sl % CPR = logical chunk ^ swz(row).  Rows past the needed
+  // key range read as zeros (beyond the buffer's record count).
+  const int64_t ksb = p.k_stride * 2, vsb = p.v_stride * 2;
+  int voff_k[C::LOADS], voff_v[C::LOADS];
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i) {
+    const int sl = (wave * C::LOADS + i) * 64 + lane;
+    const int r = sl / C::CPR, ch = (sl % C::CPR) ^ C::swz(r);
+    voff_k[i] = (int)(r * ksb) + 16 * ch;
+    voff_v[i] = (int)(r * vsb) + 16 * ch;
+  }
+  const unsigned char* kbase_ptr = (const unsigned char*)p.k + ((int64_t)tr.ks * p.k_stride + (int64_t)kvh * D) * 2;
+  const unsigned char* vbase_ptr = (const unsigned char*)p.v + ((int64_t)tr.ks * p.v_stride + (int64_t)kvh * D) * 2;
+
+  auto issue = [&](int kt, int buf) {
+    const int rows = min(tr.kend - kt * C::BN, C::BN);
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase_ptr + (int64_t)kt * C::BN * ksb), (short)0,
+                                          (int)(rows * ksb), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase_ptr + (int64_t)kt * C::BN * vsb), (short)0,
+                                          (int)(rows * vsb), 0x00020000);
+    unsigned char* dk = smem + buf * C::STAGE + wave * C::LOADS * 1024;
+    unsigned char* dv = dk + C::TILE;
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(dk + i * 1024), 16,
+                                               (unsigned)voff_k[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(dv + i * 1024), 16,
+                                               (unsigned)voff_v[i], 0, 0, 0);
+    }
+  };
+
+  // ---- per-lane LDS read offsets (loop invariant)
+  const int sw = C::swz(l32);                         // same for rows l32 and 32 + l32
+  int koff[D / 16];                                   // K rows l32 (+32), chunk 2 ks + g2
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = l32 * D * 2 + 16 * ((2 * ks + g2) ^ sw);
+  const int i16 = lane & 15, G16 = lane >> 4, nhalf = G16 & 1;
+  const int vr0 = 4 * g2 + (i16 >> 2);                // key row of the first 4-key read (+ 16 st)
+  int voff0[D / 32], voff1[D / 32];                   // V rows vr0 and vr0 + 8
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb) {
+    const int chunk = 4 * nb + 2 * nhalf + ((i16 & 3) >> 1);
+    voff0[nb] = vr0 * D * 2 + 16 * (chunk ^ C::swz(vr0)) + 8 * (i16 & 1);
+    voff1[nb] = (vr0 + 8) * D * 2 + 16 * (chunk ^ C::swz(vr0 + 8)) + 8 * (i16 & 1);
+  }
 
   floatx16 o[D / 32];
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb) o[nb] = (floatx16){};
-  float m_run = -INFINITY;   // running max, already multiplied by c (log2 domain)
-  float l_run = 0.f;         // lane-partial running sum
+  float m_used = -INFINITY;  // max used for exponentiation (times c, log2 domain)
+  float l_run = 0.f;         // lane-partial sum of the bf16-rounded P
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   const int n_tiles = (tr.kend + C::BN - 1) / C::BN;
+  const int n_full = min(n_tiles, tr.kfull / C::BN);   // tiles no row needs masked
 
-  // ---- global -> register staging of one K/V tile
-  const int kdc = tid % C::DCH;                    // K: chunk column
-  const int krow = tid / C::DCH;                   // K: first key row (+ i * THREADS/DCH)
-  const int vdc = tid % C::DCH;                    // V: chunk column
-  const int vkg = tid / C::DCH;                    // V: key group of CPT consecutive keys
-  u32x4 kreg[C::CPT], vreg[C::CPT];
-
-  auto load_tile = [&](int kt) {
-    const int kbase = kt * C::BN;
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int key = kbase + krow + i * (C::THREADS / C::DCH);
-      const bool ok = key < tr.kend;
-      const uint16_t* src = kg + (int64_t)(tr.ks + (ok ? key : 0)) * p.k_stride + (int64_t)kvh * D + 8 * kdc;
-      u32x4 v = *(const u32x4*)src;
-      kreg[i] = ok ? v : (u32x4){0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int key = kbase + vkg * C::CPT + i;
-      const bool ok = key < tr.kend;
-      const uint16_t* src = vg + (int64_t)(tr.ks + (ok ? key : 0)) * p.v_stride + (int64_t)kvh * D + 8 * vdc;
-      u32x4 v = *(const u32x4*)src;
-      vreg[i] = ok ? v : (u32x4){0u, 0u, 0u, 0u};   // zero rows: masked P (=0) times finite V
-    }
-  };
-
-  auto store_tile = [&](int buf) {
-    uint16_t* ks_ = smem + buf * C::BUF;
-    uint16_t* vs_ = ks_ + C::K_ELEMS;
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int r = krow + i * (C::THREADS / C::DCH);
-      *(u32x4*)(ks_ + r * C::KROW + 8 * kdc) = kreg[i];
-    }
-    // V^T[d][key]: element e of this thread's chunk column, CPT consecutive keys.
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1, sh = (e & 1) * 16;
-      uint16_t* dst = vs_ + (8 * vdc + e) * C::VROW + vkg * C::CPT;
-      if constexpr (C::CPT == 4) {
-        const uint32_t a0 = (vreg[0][w] >> sh) & 0xFFFFu, a1 = (vreg[1][w] >> sh) & 0xFFFFu;
-        const uint32_t a2 = (vreg[2][w] >> sh) & 0xFFFFu, a3 = (vreg[3][w] >> sh) & 0xFFFFu;
-        *(u32x2*)dst = (u32x2){a0 | (a1 << 16), a2 | (a3 << 16)};
-      } else {
-        const uint32_t a0 = (vreg[0][w] >> sh) & 0xFFFFu, a1 = (vreg[1][w] >> sh) & 0xFFFFu;
-        *(uint32_t*)dst = a0 | (a1 << 16);
-      }
-    }
-  };
-
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-  }
-
-  for (int kt = 0; kt < n_tiles; ++kt) {
+  auto step = [&](int kt, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int buf = kt & 1;
-    if (kt + 1 < n_tiles) load_tile(kt + 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this lane's DMA of tile kt landed
+    __syncthreads();                                   // everyone's landed; tile kt-1 fully consumed
+    if (kt + 1 < n_tiles) issue(kt + 1, buf ^ 1);
+    const unsigned char* ks_ = smem + buf * C::STAGE;
+    const unsigned char* vs_ = ks_ + C::TILE;
 
-    const uint16_t* ks_ = smem + buf * C::BUF;
-    const uint16_t* vs_ = ks_ + C::K_ELEMS;
-
-    // ---- S^T = K Q^T for two 32-key blocks
-    floatx16 s[2];
+    // S^T = K Q^T: two independent 32-key accumulators, interleaved
+    floatx16 s0 = (floatx16){}, s1 = (floatx16){};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = (floatx16){};
-      const uint16_t* ka = ks_ + (32 * kb + l32) * C::KROW + 8 * g2;
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const u32x4 a = *(const u32x4*)(ka + 16 * ks);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qf[ks]), s[kb], 0, 0, 0);
-      }
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const u32x4 a0 = *(const u32x4*)(ks_ + koff[ks]);
+      const u32x4 a1 = *(const u32x4*)(ks_ + 32 * D * 2 + koff[ks]);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), as_bf16x8(qf[ks]), s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), as_bf16x8(qf[ks]), s1, 0, 0, 0);
     }
-
-    // ---- mask (only tiles crossing the causal diagonal or the key tail)
-    const int kbase = kt * C::BN;
-    if (kbase + C::BN > tr.kfull) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = kbase + 32 * kb + 8 * (r >> 2) + 4 * g2 + (r & 3);
-          if (j >= kend_i) s[kb][r] = -INFINITY;
-        }
-    }
-
-    // ---- online softmax (fp32)
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mx_sc = (mx == -INFINITY) ? -INFINITY : mx * c;
-    const float m_new = fmaxf(m_run, mx_sc);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
-
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    if constexpr (MASK) {
+      const int j0 = kt * C::BN + 4 * g2;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(fmaf(s[kb][r], c, -m_use));
-        s[kb][r] = e;
-        psum += e;
+        const int j = j0 + 8 * (r >> 2) + (r & 3);
+        if (j >= kend_i) s0[r] = -INFINITY;
+        if (j + 32 >= kend_i) s1[r] = -INFINITY;
       }
-    l_run = fmaf(alpha, l_run, psum);
-
-    // Rescale O only when some row's max moved (alpha == 1 otherwise).
-    if (__builtin_amdgcn_read_exec() && __any(alpha != 1.f)) {
-#pragma unroll
-      for (int nb = 0; nb < D / 32; ++nb) o[nb] *= alpha;
     }
 
-    // ---- P -> bf16 (B operand of O^T += V^T P^T), 4 k-steps of 16 keys
+    // online softmax with a lazily moved reference max: a row's reference is
+    // raised only when its tile max exceeds it by more than 8 (log2 units), so
+    // P stays below 2^8; the final lse uses the same reference, so the result
+    // is exact in real arithmetic.
+    float mx = vmax(s0[0], s1[0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = vmax(vmax(mx, s0[r]), s1[r]);
+    mx = lane_swap_max(mx);
+    const float mx_sc = (mx == -INFINITY) ? -INFINITY : mx * c;
+    const bool upd = mx_sc > m_used + 8.0f;
+    const float m_new = upd ? mx_sc : m_used;
+    const float alpha = upd ? fast_exp2(m_used - m_new) : 1.0f;
+    m_used = m_new;
+    const float m_use = (m_used == -INFINITY) ? 0.f : m_used;
+    if (__any(upd)) {
+      asm volatile("; rare: rescale O and l" ::);   // keeps this a real branch (not if-converted)
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb) o[nb] *= alpha;
+      l_run *= alpha;
+    }
+    // P = 2^(s c - m), rounded to bf16 and packed for the P V step; the row
+    // sum adds the same rounded values (v_dot2 with ones).
     u32x4 pb[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      const floatx16& sv = kb == 0 ? s0 : s1;
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const int r0 = 8 * hf;
-        pb[2 * kb + hf] = (u32x4){pack_bf16x2(s[kb][r0 + 0], s[kb][r0 + 1]), pack_bf16x2(s[kb][r0 + 2], s[kb][r0 + 3]),
-                                  pack_bf16x2(s[kb][r0 + 4], s[kb][r0 + 5]), pack_bf16x2(s[kb][r0 + 6], s[kb][r0 + 7])};
+        u32x4 w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float e0 = fast_exp2(fmaf(sv[8 * hf + 2 * q], c, -m_use));
+          const float e1 = fast_exp2(fmaf(sv[8 * hf + 2 * q + 1], c, -m_use));
+          w[q] = pack_bf16x2(e0, e1);
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[q]), ones, l_run, false);
+        }
+        pb[2 * kb + hf] = w;
       }
+    }
 
-    // ---- O^T += V^T P^T.  k-slot j of lane half g2 in step (kb, hf) is key
-    //      32 kb + 16 hf + 8 (j / 4) + 4 g2 + (j % 4): the same keys the lane's
-    //      P registers hold, so both operands agree on the contraction order.
+    // O^T += V^T P^T.  k-slot j of lane half g2 in step st is key
+    // 16 st + 8 (j / 4) + 4 g2 + j % 4 for both operands.
 #pragma unroll
-    for (int nb = 0; nb < D / 32; ++nb) {
-      const uint16_t* va = vs_ + (32 * nb + l32) * C::VROW + 4 * g2;
+    for (int st = 0; st < 4; ++st) {
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const int koff = 16 * st;                // = 32 kb + 16 hf
-        const u32x2 lo = *(const u32x2*)(va + koff);
-        const u32x2 hi = *(const u32x2*)(va + koff + 8);
+      for (int nb = 0; nb < D / 32; ++nb) {
+        const u32x2 lo = lds_read_tr(vs_ + st * 16 * D * 2 + voff0[nb]);
+        const u32x2 hi = lds_read_tr(vs_ + st * 16 * D * 2 + voff1[nb]);
         const u32x4 a = (u32x4){lo[0], lo[1], hi[0], hi[1]};
         o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pb[st]), o[nb], 0, 0, 0);
       }
     }
+  };
 
-    if (kt + 1 < n_tiles) store_tile(buf ^ 1);
-    __syncthreads();
-  }
+  if (n_tiles > 0) issue(0, 0);
+  int kt = 0;
+  for (; kt < n_full; ++kt) step(kt, std::false_type{});
+  for (; kt < n_tiles; ++kt) step(kt, std::true_type{});
 
   // ---- epilogue: O / l (bf16 RNE), lse = ln 2 * (m + log2 l)
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = lane_swap_add(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qvalid) {
     uint16_t* dst = (uint16_t*)p.out + (int64_t)(tr.qs + qi) * p.o_stride + (int64_t)h * D + 4 * g2;
@@ -353,7 +367,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(DenseParams p) {
         *(u32x2*)(dst + 32 * nb + 8 * r4) = w;
       }
     if (p.lse != nullptr && g2 == 0)
-      p.lse[(int64_t)h * p.total_q + tr.qs + qi] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+      p.lse[(int64_t)h * p.total_q + tr.qs + qi] = l_tot > 0.f ? (m_used + log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
