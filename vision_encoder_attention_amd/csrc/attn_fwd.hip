@@ -166,10 +166,12 @@ struct Cfg {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(DenseParams p) {
   using C = Cfg<D>;
-  // Two stages in distinct arrays: the compiler can then see that the DMA into
-  // one stage never aliases the reads of the other, and does not wait on it.
-  __shared__ __attribute__((aligned(1024))) unsigned char stage0[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char stage1[C::STAGE];
+  // Two K stages and two V stages in distinct arrays: the compiler can then see
+  // that a DMA into one stage never aliases reads of another, and does not wait.
+  __shared__ __attribute__((aligned(1024))) unsigned char kst0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char kst1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char vst0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char vst1[C::TILE];
 
   int b, h, t;
   decode_unit(p, blockIdx.x, b, h, t);
@@ -224,24 +226,18 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
   const unsigned char* kbase_ptr = (const unsigned char*)p.k + ((int64_t)tr.ks * p.k_stride + (int64_t)kvh * D) * 2;
   const unsigned char* vbase_ptr = (const unsigned char*)p.v + ((int64_t)tr.ks * p.v_stride + (int64_t)kvh * D) * 2;
 
-  auto issue = [&](int kt, unsigned char* stage) {
+  auto issue_tile = [&](int kt, const unsigned char* base, int64_t sb, const int* voff, unsigned char* stage) {
     const int rows = min(tr.kend - kt * C::BN, C::BN);
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase_ptr + (int64_t)kt * C::BN * ksb), (short)0,
-                                          (int)(rows * ksb), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase_ptr + (int64_t)kt * C::BN * vsb), (short)0,
-                                          (int)(rows * vsb), 0x00020000);
-    unsigned char* dk = stage + wave * C::LOADS * 1024;
-    unsigned char* dv = dk + C::TILE;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(base + (int64_t)kt * C::BN * sb), (short)0, (int)(rows * sb), 0x00020000);
+    unsigned char* dst = stage + wave * C::LOADS * 1024;
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(dk + i * 1024), 16,
-                                               (unsigned)voff_k[i], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(dv + i * 1024), 16,
-                                               (unsigned)voff_v[i], 0, 0, 0);
-    }
+    for (int i = 0; i < C::LOADS; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16,
+                                               (unsigned)voff[i], 0, 0, 0);
   };
+  auto issue_k = [&](int kt, unsigned char* stage) { issue_tile(kt, kbase_ptr, ksb, voff_k, stage); };
+  auto issue_v = [&](int kt, unsigned char* stage) { issue_tile(kt, vbase_ptr, vsb, voff_v, stage); };
 
   // ---- per-lane LDS read offsets (loop invariant)
   const int sw = C::swz(l32);                         // same for rows l32 and 32 + l32
@@ -268,19 +264,10 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
   const int n_tiles = (tr.kend + C::BN - 1) / C::BN;
   const int n_full = min(n_tiles, tr.kfull / C::BN);   // tiles no row needs masked
 
-  auto step = [&](int kt, auto mask_tag, auto odd_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    constexpr bool ODD = decltype(odd_tag)::value;     // tile kt lives in stage kt & 1
-    unsigned char* cur = ODD ? stage1 : stage0;
-    unsigned char* nxt = ODD ? stage0 : stage1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this lane's DMA of tile kt landed
-    __syncthreads();                                   // everyone's landed; tile kt-1 fully consumed
-    if (kt + 1 < n_tiles) issue(kt + 1, nxt);
-    const unsigned char* ks_ = cur;
-    const unsigned char* vs_ = cur + C::TILE;
-
-    // S^T = K Q^T: two independent 32-key accumulators, interleaved
-    floatx16 s0 = (floatx16){}, s1 = (floatx16){};
+  // S^T = K Q^T for one tile: two independent 32-key accumulators, interleaved.
+  auto qk = [&](const unsigned char* ks_, floatx16& s0, floatx16& s1) {
+    s0 = (floatx16){};
+    s1 = (floatx16){};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       const u32x4 a0 = *(const u32x4*)(ks_ + koff[ks]);
@@ -288,39 +275,46 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), as_bf16x8(qf[ks]), s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), as_bf16x8(qf[ks]), s1, 0, 0, 0);
     }
-    if constexpr (MASK) {
-      const int j0 = kt * C::BN + 4 * g2;
+  };
+  // Keys past a row's bound (tail of the sequence, causal diagonal) -> -inf.
+  auto mask = [&](int kt, floatx16& s0, floatx16& s1) {
+    const int j0 = kt * C::BN + 4 * g2;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = j0 + 8 * (r >> 2) + (r & 3);
-        if (j >= kend_i) s0[r] = -INFINITY;
-        if (j + 32 >= kend_i) s1[r] = -INFINITY;
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int j = j0 + 8 * (r >> 2) + (r & 3);
+      if (j >= kend_i) s0[r] = -INFINITY;
+      if (j + 32 >= kend_i) s1[r] = -INFINITY;
     }
-
-    // online softmax with a lazily moved reference max: a row's reference is
-    // raised only when its tile max exceeds it by more than 8 (log2 units), so
-    // P stays below 2^8; the final lse uses the same reference, so the result
-    // is exact in real arithmetic.
+  };
+  // Online softmax, part 1: row max of a finished tile's logits and the
+  // (rare) move of the reference max.  The reference max of a row moves
+  // lazily: only when the tile max exceeds it by more than 8 (log2 units), so
+  // P stays below 2^8; the final lse uses the same reference, so the result
+  // is exact in real arithmetic.  Returns the reference to subtract.
+  auto softmax_ref = [&](const floatx16& s0, const floatx16& s1) -> float {
     float mx = vmax(s0[0], s1[0]);
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = vmax(vmax(mx, s0[r]), s1[r]);
     mx = lane_swap_max(mx);
     const float mx_sc = (mx == -INFINITY) ? -INFINITY : mx * c;
     const bool upd = mx_sc > m_used + 8.0f;
-    const float m_new = upd ? mx_sc : m_used;
-    const float alpha = upd ? fast_exp2(m_used - m_new) : 1.0f;
-    m_used = m_new;
-    const float m_use = (m_used == -INFINITY) ? 0.f : m_used;
     if (__any(upd)) {
-      asm volatile("; rare: rescale O and l" ::);   // keeps this a real branch (not if-converted)
+      asm volatile("; rare: move the reference max, rescale O and l" ::);
+      const float m_new = upd ? mx_sc : m_used;
+      const float alpha = upd ? fast_exp2(m_used - m_new) : 1.0f;
+      m_used = m_new;
 #pragma unroll
       for (int nb = 0; nb < D / 32; ++nb) o[nb] *= alpha;
       l_run *= alpha;
       l_odd *= alpha;
     }
-    // P = 2^(s c - m): summed in fp32 for l (so lse is the log-sum-exp of the
-    // logits themselves), rounded to bf16 and packed for the P V step.
+    return (m_used == -INFINITY) ? 0.f : m_used;
+  };
+  // Part 2: P = 2^(s c - m) summed in fp32 for l (so lse is the log-sum-exp of
+  // the logits themselves), rounded to bf16 and packed; then O^T += V^T P^T
+  // with V read transposed from a V stage.  k-slot j of lane half g2 in step
+  // st is key 16 st + 8 (j / 4) + 4 g2 + j % 4 for both operands.
+  auto softmax_pv = [&](const floatx16& s0, const floatx16& s1, float m_use, const unsigned char* vs_) {
     u32x4 pb[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -339,9 +333,6 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
         pb[2 * kb + hf] = (u32x4){w[0], w[1], w[2], w[3]};
       }
     }
-
-    // O^T += V^T P^T.  k-slot j of lane half g2 in step st is key
-    // 16 st + 8 (j / 4) + 4 g2 + j % 4 for both operands.
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
 #pragma unroll
@@ -354,16 +345,61 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
     }
   };
 
-  if (n_tiles > 0) issue(0, stage0);
-  int kt = 0;
-  for (; kt + 2 <= n_full; kt += 2) {                  // unmasked tiles, two stages per trip
-    step(kt, std::false_type{}, std::false_type{});
-    step(kt + 1, std::false_type{}, std::true_type{});
-  }
-  if (kt < n_full) { step(kt, std::false_type{}, std::false_type{}); ++kt; }
-  for (; kt < n_tiles; ++kt) {                         // tiles crossing the diagonal or the key tail
-    if (kt & 1) step(kt, std::true_type{}, std::true_type{});
-    else step(kt, std::true_type{}, std::false_type{});
+  // ---- software pipeline over key tiles.  Iteration kt (1 <= kt <= n_tiles)
+  // computes S of tile kt while it finishes tile kt-1 (softmax + P V), so the
+  // QK^T MFMAs run under the softmax VALU work of the same wave.  K is staged
+  // one tile ahead of V: iteration kt reads K(kt) and V(kt-1), and its DMA
+  // refills the K stage of tile kt-1 with K(kt+1) and the V stage of tile
+  // kt-2 with V(kt).  Stage parity is static per iteration (unrolled by two),
+  // so the compiler sees that the DMA never aliases the stages being read.
+  floatx16 sp0, sp1;                                  // logits of the tile being finished
+  auto iter = [&](int kt, auto odd_tag, auto has_s_tag) {
+    constexpr bool ODD = decltype(odd_tag)::value;      // parity of kt
+    constexpr bool HAS_S = decltype(has_s_tag)::value;  // kt < n_tiles
+    unsigned char* k_rd = ODD ? kst1 : kst0;          // K(kt)
+    unsigned char* k_wr = ODD ? kst0 : kst1;          // K(kt+1)
+    unsigned char* v_rd = ODD ? vst0 : vst1;          // V(kt-1)
+    unsigned char* v_wr = ODD ? vst1 : vst0;          // V(kt)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this lane's DMA of K(kt), V(kt-1) landed
+    __syncthreads();                                  // everyone's landed; the stages refilled below are consumed
+    floatx16 sn0, sn1;
+    if constexpr (HAS_S) {
+      if (kt + 1 < n_tiles) issue_k(kt + 1, k_wr);
+      issue_v(kt, v_wr);
+    }
+    const float m_use = softmax_ref(sp0, sp1);
+    // one branch-free block: QK^T of tile kt, softmax and P V of tile kt-1
+    if constexpr (HAS_S) qk(k_rd, sn0, sn1);
+    softmax_pv(sp0, sp1, m_use, v_rd);
+    if constexpr (HAS_S) {
+      if (kt >= n_full) {
+        asm volatile("; masked tile" ::);
+        mask(kt, sn0, sn1);
+      }
+      sp0 = sn0;
+      sp1 = sn1;
+    }
+  };
+
+  if (n_tiles > 0) {
+    issue_k(0, kst0);
+    issue_v(0, vst0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (1 < n_tiles) issue_k(1, kst1);
+    qk(kst0, sp0, sp1);
+    if (0 >= n_full) mask(0, sp0, sp1);
+    int kt = 1;
+    for (; kt + 1 < n_tiles; kt += 2) {                // kt odd here
+      iter(kt, std::true_type{}, std::true_type{});
+      iter(kt + 1, std::false_type{}, std::true_type{});
+    }
+    if (kt < n_tiles) {                                // one more tile with S (odd), then drain (even)
+      iter(kt, std::true_type{}, std::true_type{});
+      iter(kt + 1, std::false_type{}, std::false_type{});
+    } else {                                           // drain at an odd kt
+      iter(kt, std::true_type{}, std::false_type{});
+    }
   }
 
   // ---- epilogue: O / l (bf16 RNE), lse = ln 2 * (m + log2 l)
