@@ -103,12 +103,14 @@ def bench_vision(torch, args):
     return case, tm, wall_ms
 
 
-def bench_other(torch, steps):
+def bench_other(torch, steps, only=None):
     """The remaining workloads: one timed kernel family each."""
     from vision_encoder_attention_amd import runner as R
     from vision_encoder_attention_amd import workloads as W
     res = {}
     for name in ("varlen_gqa", "long_causal"):
+        if only is not None and name != only:
+            continue
         case = W.full_case(name)
         st = R.stage_dense(case)
         R.run_dense(st)
@@ -133,6 +135,8 @@ def bench_other(torch, steps):
         res[case.name] = ent
         del st
         torch.cuda.empty_cache()
+    if only is not None and only != "sparse_mqa":
+        return res
     # sparse MQA: evict L2 / MALL between timed launches (untimed fill of 1 GiB)
     case = W.full_case("sparse_mqa")
     st = R.stage_sparse(case)
@@ -147,10 +151,40 @@ def bench_other(torch, steps):
     by, fl = sparse_bytes(case), sparse_flops(case)
     res[case.name] = {"sparse_mqa_ms": round(s_ms, 4), "sparse_mqa_min_ms": round(s_min, 4),
                       "gbs": round(by / s_ms / 1e6, 1), "frac_hbm": round(by / s_ms / 1e6 / PEAK_HBM_GBS, 4),
-                      "tflops": round(fl / s_ms / 1e9, 2), "bytes": by, "flops": fl}
+                      "tflops": round(fl / s_ms / 1e9, 2), "bytes": by, "flops": fl,
+                      "hbm_traffic_counter_bytes": committed_traffic("sparse_mqa_hbm_counters.txt")}
     del scratch, st
     torch.cuda.empty_cache()
     return res
+
+
+def source_digest(paths) -> str:
+    """sha256 over the given source files (identifies the kernel build a
+    committed counter summary belongs to)."""
+    import hashlib
+    h = hashlib.sha256()
+    for pth in paths:
+        with open(os.path.join(ROOT, pth), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(profile: str):
+    """HBM bytes per launch recorded in a committed counter summary under
+    profiles/ (FETCH_SIZE and WRITE_SIZE, each scaled by what the same counter
+    reads for a plain copy of known size), or None when the kernel source has
+    changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", profile)
+    if not os.path.exists(path):
+        return None
+    rec = None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("RESULT "):
+                rec = json.loads(line[len("RESULT "):])
+    if not rec or rec.get("source_digest") != source_digest(rec["sources"]):
+        return None
+    return rec["hbm_bytes_per_launch"]
 
 
 def cpu_baseline():
@@ -189,6 +223,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--only", choices=["varlen_gqa", "long_causal", "sparse_mqa"],
+                    help="only run one of the other workloads (for profiling one kernel family)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         err("bench.py measures one GPU: this library's path runs on a single MI355X "
@@ -206,6 +242,10 @@ def main():
     props = torch.cuda.get_device_properties(0)
     err("device: %s, %d CUs" % (props.name, props.multi_processor_count))
 
+    if args.only:
+        res = bench_other(torch, max(3, min(args.steps, 20)), only=args.only)
+        err(json.dumps(res))
+        return
     if args.calibrate_copy:
         n = 512 << 20
         a = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -246,7 +286,9 @@ def main():
                     "qkv_rope_frac_hbm": round(rb / r_ms / 1e6 / PEAK_HBM_GBS, 4)},
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_bf16_kernel<64,false>", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": committed_traffic("attn_fwd_vision_hbm_counters.txt"),
+                     "traffic_unit": "bytes per launch (HBM, counter-measured)",
+                     "algorithmic_bytes": 4 * case.total_q * case.num_heads_q * case.head_dim * 2},
     }
     if not args.no_extra:
         line["workloads"] = bench_other(torch, max(5, min(args.steps, 20)))
