@@ -158,9 +158,24 @@ struct Cfg {
   static constexpr int STAGE = 2 * TILE;                // K + V
   static constexpr int LOADS = TILE / (THREADS * 16);   // 16-byte DMA loads per lane per tile
   static_assert(LOADS == 2 || LOADS == 4, "tile split");
-  // XOR swizzle of the 16-byte chunks of a row: the 32 rows read together by
-  // one MFMA operand land on distinct bank groups.
-  static __device__ __forceinline__ int swz(int r) { return D == 64 ? ((r >> 1) & 7) : (r & 15); }
+  // XOR swizzle of the 16-byte chunks of a row.  The LDS has 64 four-byte
+  // banks and a ds_read_b64_tr_b16 serves 32 lanes per cycle.
+  //  * V^T reads: 4 rows x 4 logical chunks per 32 lanes; rows r and r + 2
+  //    (same bank half for d = 64; for d = 128 every row spans all banks)
+  //    need disjoint physical chunk sets, so their swizzles differ in a bit
+  //    above the low two.
+  //  * K reads (ds_read_b128): 16 rows x one logical chunk, each row pair on
+  //    a distinct chunk.
+  // Both read kinds measure zero SQ_LDS_BANK_CONFLICT cycles with these
+  // swizzles (the plain (r / 2) % 8 and r % 16 cost every V^T read 2 and 6).
+  // The period is 16 rows, so rows r, r + 16 and r + 32 share a swizzle.
+  static __device__ __forceinline__ int swz(int r) {
+    if (D == 64) {
+      const int x = (r >> 1) & 7;                       // bit-reversed row pair
+      return ((x & 1) << 2) | (x & 2) | ((x >> 2) & 1);
+    }
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  }
 };
 
 template <int D, bool CAUSAL>

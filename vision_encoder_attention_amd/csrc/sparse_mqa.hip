@@ -72,10 +72,20 @@ struct SCfg {
   static_assert(DQK % 64 == 0 && DV % 32 == 0 && DV <= DQK, "latent dims");
   static_assert((DV / 2) % 64 == 0, "each half of d_v starts on an 8-chunk boundary");
   static_assert(HEADS == kSparseHeadsPerWG, "host launch shape");
-  // Chunk swizzle: rows r and r + 1 sit 32 banks apart (1152-byte rows), so
-  // XOR with (r / 2) % 8 spreads the 16 rows read by one MFMA operand over
-  // all 16 bank groups.
-  static __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+  // Chunk swizzle.  Rows r and r + 1 sit 32 banks apart (1152-byte rows), so
+  // the swizzle works on the row pair x = (r / 2) % 8 and permutes the low 3
+  // bits of a chunk index (it stays inside aligned groups of 8 chunks).
+  //  * V^T reads (ds_read_b64_tr_b16: 32 lanes per cycle, rows 0..7 x one
+  //    chunk pair) need the four rows of one bank half on disjoint chunk
+  //    pairs: the permutation must map x = 0..3 (and 4..7) to distinct x / 2.
+  //  * K reads (ds_read_b128, 16 rows x one logical chunk) were measured with
+  //    the SQ_LDS_BANK_CONFLICT counter for candidate permutations: x ^ (2x & 6)
+  //    is conflict-free for both read kinds (the bit reversal and the
+  //    rotation, which also satisfy the V^T rule, cost K reads 4 cycles).
+  static __device__ __forceinline__ int swz(int r) {
+    const int x = (r >> 1) & 7;
+    return x ^ ((x << 1) & 6);
+  }
 };
 
 // One workgroup = 8 waves = 64 heads of one query row.  The two waves of a
