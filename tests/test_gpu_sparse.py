@@ -100,3 +100,31 @@ def test_full_size_sampled(torch):
     assert torch.equal(st.out, o0) and torch.equal(st.lse, l0)
     perm = _run(torch, case, W.permute_rows(case.topk_idx, 105))
     assert torch.equal(perm.out, o0) and torch.equal(perm.lse, l0)
+
+
+def test_large_cache_uses_the_sorting_network(torch):
+    """A latent cache too large for the in-LDS counting sort (80000 rows) takes
+    the bitonic path: same results, padding / duplicates / out-of-range entries
+    handled the same way, still bitwise invariant to index order."""
+    case = W.sparse_mqa(rows=3, heads=128, n_kv=80000, k=300, seed=18)
+    idx = case.topk_idx.copy()
+    idx[0, ::5] = -1
+    idx[1, 20:40] = idx[1, 0:20]                   # duplicates
+    idx[2, 7] = 80000                              # out of range: skipped
+    st = _run(torch, case, idx)
+    ref_idx = idx.copy()
+    ref_idx[2, 7] = -1
+    o_ref, l_ref = oracle.sparse_mqa(W.bf16_bits_to_f64(case.q), W.bf16_bits_to_f64(case.kv_latent), ref_idx,
+                                     case.d_v, float(np.float32(case.scale)))
+    assert_bf16_close(W.bf16_bits_to_f64(R.tensor_to_bits(st.out)), o_ref, "out")
+    assert_bf16_close(st.lse.cpu().numpy().astype(np.float64), l_ref, "lse")
+    perm = _run(torch, case, W.permute_rows(idx, 107))
+    assert torch.equal(perm.out, st.out) and torch.equal(perm.lse, st.lse)
+
+
+def test_more_than_2048_indices(torch):
+    """k in (2048, 4096] uses the three-stage variant of the kernel."""
+    case = W.sparse_mqa(rows=2, heads=128, n_kv=3500, k=3000, seed=19)
+    st = _check(torch, case, name="k3000")
+    perm = _run(torch, case, W.permute_rows(case.topk_idx, 108))
+    assert torch.equal(perm.out, st.out) and torch.equal(perm.lse, st.lse)

@@ -8,21 +8,28 @@
 // LDS before use, so the blocks always arrive in one canonical order and the
 // output is bitwise independent of the order the caller supplies.
 //
-// One workgroup = 8 waves = 64 query heads of one query row; all heads share
-// the row's gathered latent rows (multi-query).  Per step of BN = 32 sorted
-// indices:
-//   gather   32 latent rows (d_qk bf16 each) straight into LDS by buffer
-//            loads with the LDS bit (per-lane row addresses; entries past the
-//            valid count read as zeros through the buffer's record bound),
-//            double buffered, 16-byte chunks XOR-swizzled within each row;
-//   S^T      = K Q^T over d_qk with v_mfma_f32_16x16x32_bf16, Q^T held in
-//            registers; a pair of waves splits d_qk (and later d_v) between
-//            them and adds its partial logits through LDS; fp32 accumulation;
-//   softmax  fp32 online update with a lazily moved reference max;
-//   O^T     += V^T P^T over d_v with the same MFMA.  V is the first d_v
-//            columns of the gathered rows; V^T operands come straight from the
-//            row-major tile with ds_read_b64_tr_b16 (each 16-lane group reads
-//            a 4-key x 16-column block and receives it transposed).
+// Per query row r the work is a small dense attention whose "query rows" are
+// the heads: S = Q_r K_r^T over d_qk (heads x k), softmax per head, O = P V_r
+// over d_v, with K_r the gathered latent rows and V_r their first d_v columns.
+//
+// One workgroup = 4 waves = 128 heads of one query row, so each latent row is
+// gathered once per query row.  Each wave owns 32 heads over the full d_qk and
+// d_v, with v_mfma_f32_32x32x16_bf16 tiles whose N dimension is the 32 heads:
+// every 16-byte K or V operand read from LDS feeds 32 heads (32 flops per LDS
+// byte; a 16-head tile would make the kernel LDS-bound).  Q^T (36 k-steps) sits
+// in VGPRs and O^T (16 tiles of 32 d_v x 32 heads) in accumulation registers:
+// one wave per SIMD.  Per step of BN = 32 sorted indices:
+//   gather   32 latent rows straight into LDS by buffer loads with the LDS bit
+//            (per-lane row addresses; entries past the valid count read as
+//            zeros through the buffer's record bound), into a ring of stages
+//            filled ahead of use, 16-byte chunks XOR-swizzled within each row;
+//   S^T      = K Q^T, fp32 accumulation;
+//   softmax  fp32 online update with a lazily moved reference max, one step
+//            behind the MFMAs: the exponentials of tile t-1 run under the
+//            QK^T MFMAs of tile t;
+//   O^T     += V^T P^T; the V^T operands come straight from the row-major tile
+//            with ds_read_b64_tr_b16 (each 16-lane group reads a 4-key x
+//            16-column block and receives it transposed).
 // Entries < 0 or >= n_kv are skipped.  No atomics: every output element and
 // lse entry has one writer.
 #include "vea_internal.h"
@@ -37,10 +44,10 @@ namespace vea {
 namespace {
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2v));
@@ -54,254 +61,521 @@ __device__ __forceinline__ u32x2 lds_read_tr(const void* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// The MFMAs are emitted as inline asm so that the register class of each
+// accumulator is fixed: O^T in AGPRs (256 of them), S^T in VGPRs next to the
+// softmax that reads it.  The compiler does not see these as MFMAs, so the
+// wait states the CDNA3/4 ISA requires around matrix instructions are issued
+// here by hand (at most 18 for an XDL result read or overwritten by a VALU,
+// LDS or memory instruction, 2 for a VALU result read by an XDL instruction;
+// a margin on both).  The asm is not volatile, so LDS reads can still be
+// scheduled ahead of the MFMAs that use them; every wait is ordered against
+// the MFMAs by a register dependency (the wait "rewrites" the registers it
+// guards), never by volatility.
+__device__ __forceinline__ void mfma_s_first(floatx16& d, const u32x4& a, const u32x4& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_s(floatx16& d, const u32x4& a, const u32x4& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_o(floatx16& d, const u32x4& a, const u32x4& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+}
+// XDL result in VGPRs -> any other reader: 20 wait states.
+__device__ __forceinline__ void xdl_drain_v(floatx16& d) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(d));
+}
+// The 16 O^T accumulators (AGPRs) after the last MFMA that wrote them, before
+// anything else reads or writes them: 20 wait states.
+#define VEA_O16(o) "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]), "+a"(o[6]), \
+    "+a"(o[7]), "+a"(o[8]), "+a"(o[9]), "+a"(o[10]), "+a"(o[11]), "+a"(o[12]), "+a"(o[13]), "+a"(o[14]), "+a"(o[15])
+__device__ __forceinline__ void xdl_drain_o(floatx16 (&o)[16]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : VEA_O16(o));
+}
+// VALU writes of the O^T accumulators -> the next MFMA reading them: 5 wait states.
+__device__ __forceinline__ void valu_to_xdl_o(floatx16 (&o)[16]) {
+  asm volatile("s_nop 4" : VEA_O16(o));
+}
+#undef VEA_O16
+// VALU result -> XDL operand: 5 wait states.
+__device__ __forceinline__ void valu_to_xdl(u32x4& x, u32x4& y) {
+  asm volatile("s_nop 4" : "+v"(x), "+v"(y));
+}
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+__device__ __forceinline__ float lane_swap_max(float x) {
+  // max with the lane 32 apart (the other half of the wave holds the same head)
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 template <int DQK, int DV, int MAXK>
 struct SCfg {
-  static constexpr int WAVES = 8;
+  static constexpr int WAVES = 4;
   static constexpr int THREADS = WAVES * 64;
-  static constexpr int HPW = 16;                       // heads per wave pair (MFMA N)
-  static constexpr int HEADS = (WAVES / 2) * HPW;      // heads per workgroup
+  static constexpr int HPW = 32;                       // heads per wave (MFMA N)
+  static constexpr int HEADS = WAVES * HPW;            // heads per workgroup
   static constexpr int BN = 32;                        // sorted indices per step
   static constexpr int ROWB = DQK * 2;                 // bytes per latent row (no padding)
   static constexpr int TILE = BN * ROWB;
   static constexpr int CPR = DQK / 8;                  // 16-byte chunks per row
   static constexpr int BLOCKS = TILE / 1024;           // 1 KB DMA blocks per tile
-  static constexpr int KS_HALF = DQK / 64;             // 32-wide k-steps per half of d_qk
-  static constexpr int NT_HALF = DV / 32;              // 16-wide n-tiles per half of d_v
-  static_assert(TILE % 1024 == 0, "tile in whole 1 KB DMA blocks");
+  static constexpr int BPW = BLOCKS / WAVES;           // DMA blocks per wave per tile
+  static constexpr int KSTEPS = DQK / 16;              // k-steps of S^T
+  static constexpr int NT = DV / 32;                   // 32-wide d_v tiles of O^T
+  // Ring of LDS stages.  The DMA of tile t + DIST is issued at step t, while
+  // QK^T reads tile t and P V reads tile t - 1, so NSTAGE = DIST + 2.  Up to
+  // 2048 indices the sorted list leaves room for four stages (prefetch two
+  // tiles ahead); up to 4096, three.
+  static constexpr int NSTAGE = MAXK <= 2048 ? 4 : 3;
+  static constexpr int DIST = NSTAGE - 2;
+  static_assert(TILE % 1024 == 0 && BLOCKS % WAVES == 0, "tile in whole 1 KB DMA blocks per wave");
   static_assert(CPR % 8 == 0, "swizzle stays inside aligned groups of 8 chunks");
-  static_assert(DQK % 64 == 0 && DV % 32 == 0 && DV <= DQK, "latent dims");
-  static_assert((DV / 2) % 64 == 0, "each half of d_v starts on an 8-chunk boundary");
+  static_assert(DQK % 32 == 0 && DV % 64 == 0 && DV <= DQK, "latent dims");
   static_assert(HEADS == kSparseHeadsPerWG, "host launch shape");
+  static_assert(NT == 16, "the accumulator waits name 16 O^T tiles");
+  static_assert(NSTAGE * TILE + MAXK * 4 + WAVES * 4 <= 160 * 1024, "LDS budget");
   // Chunk swizzle.  Rows r and r + 1 sit 32 banks apart (1152-byte rows), so
   // the swizzle works on the row pair x = (r / 2) % 8 and permutes the low 3
-  // bits of a chunk index (it stays inside aligned groups of 8 chunks).
-  //  * V^T reads (ds_read_b64_tr_b16: 32 lanes per cycle, rows 0..7 x one
-  //    chunk pair) need the four rows of one bank half on disjoint chunk
-  //    pairs: the permutation must map x = 0..3 (and 4..7) to distinct x / 2.
-  //  * K reads (ds_read_b128, 16 rows x one logical chunk) were measured with
-  //    the SQ_LDS_BANK_CONFLICT counter for candidate permutations: x ^ (2x & 6)
-  //    is conflict-free for both read kinds (the bit reversal and the
-  //    rotation, which also satisfy the V^T rule, cost K reads 4 cycles).
+  // bits of a chunk index (it stays inside aligned groups of 8 chunks; rows r
+  // and r + 16 share a swizzle).
+  //  * K reads (ds_read_b128, 16 lanes = 16 consecutive rows x one logical
+  //    chunk): the swizzle must be a permutation of x = 0..7.
+  //  * V^T reads (ds_read_b64_tr_b16, 32 lanes = 4 consecutive rows x 4
+  //    logical chunks 4n..4n+3): the two row pairs of an aligned group of 4
+  //    rows need swizzles that differ in bit 2.
+  // x -> (x & 1) << 2 | x >> 1 satisfies both.
   static __device__ __forceinline__ int swz(int r) {
     const int x = (r >> 1) & 7;
-    return x ^ ((x << 1) & 6);
+    return ((x & 1) << 2) | (x >> 1);
   }
 };
 
-// One workgroup = 8 waves = 64 heads of one query row.  The two waves of a
-// pair serve the same 16 heads: wave half hh computes the logits over its half
-// of d_qk and keeps the output for its half of d_v.  After the QK^T MFMAs the
-// pair adds its two partial logit tiles through LDS (the sum is commutative,
-// so both waves hold bitwise the same logits and run the same softmax).  This
-// keeps a wave at 36 Q + 64 O registers.
+// One 16-byte DMA per lane from global memory straight into LDS: lane l's
+// chunk lands at lds_block + 16 l.  Written as asm so that the compiler does
+// not track it: it would otherwise stop every LDS read of another stage until
+// the DMA lands (it cannot tell the stages of the ring apart).  The kernel
+// orders these DMAs itself (s_waitcnt vmcnt before the barrier that precedes
+// the reads).  Offsets past num_records read as zeros.
+__device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t lds_block, uint32_t voffset) {
+  // M0 is saved and restored around the DMA (it is a reserved register); one
+  // wait state separates the M0 write from the DMA that reads it.
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voffset), "s"(lds_block), "s"(rsrc));
+}
+
 template <int DQK, int DV, int MAXK>
-__global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(SparseParams p) {
+__global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
   using C = SCfg<DQK, DV, MAXK>;
-  __shared__ __attribute__((aligned(1024))) unsigned char tile0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char tile1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[C::NSTAGE * C::TILE];
   __shared__ int sidx[MAXK];
-  __shared__ float xs[C::WAVES][8][64];                 // partial logits, exchanged within a pair
+  __shared__ int wsum[C::WAVES];
 
   const int row = blockIdx.x / p.head_blocks;
   const int hb = blockIdx.x - row * p.head_blocks;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar) value
-  const int hh = wave & 1;                              // which half of d_qk / d_v
-  const int pr = wave >> 1;                             // pair: 16 heads
-  const int l16 = lane & 15;
-  const int G = lane >> 4;                              // lane group 0..3
+  const int l32 = lane & 31;
+  const int g2 = lane >> 5;                             // which half of the wave
 
-  // ---- canonical order: load the row's indices and sort them ascending
-  int n2 = 1;
-  while (n2 < p.k) n2 <<= 1;
+  // ---- canonical order: the row's valid indices in ascending order (with
+  // their multiplicity) in sidx[0, nvalid).
+  int nvalid;
   const int32_t* irow = p.idx + (int64_t)row * p.k;
-  for (int i = tid; i < n2; i += C::THREADS) {
-    int v = INT_MAX;
-    if (i < p.k) {
+  if (p.n_kv <= C::NSTAGE * C::TILE / 2) {
+    // Counting sort in the stage ring (idle until the key loop): a 16-bit
+    // count per latent row (two per word; k <= 4096 cannot overflow one),
+    // incremented by LDS atomics (the counts do not depend on their order),
+    // then one block-wide exclusive scan over runs of consecutive rows and a
+    // scatter of each row's index count times.
+    uint32_t* cnt = (uint32_t*)ring;
+    const int nw = (p.n_kv + 1) >> 1;
+    for (int i = tid; i < nw; i += C::THREADS) cnt[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < p.k; i += C::THREADS) {
       const int x = irow[i];
-      v = (x >= 0 && x < p.n_kv) ? x : INT_MAX;        // padding / out of range: skipped
+      if (x >= 0 && x < p.n_kv) atomicAdd(&cnt[x >> 1], 1u << (16 * (x & 1)));   // padding / out of range: skipped
     }
-    sidx[i] = v;
-  }
-  __syncthreads();
-  for (int size = 2; size <= n2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = tid; t < (n2 >> 1); t += C::THREADS) {
-        const int i = 2 * t - (t & (stride - 1));
-        const int j = i + stride;
-        const bool up = (i & size) == 0;
-        const int a = sidx[i], b = sidx[j];
-        if ((a > b) == up) { sidx[i] = b; sidx[j] = a; }
-      }
-      __syncthreads();
-    }
-  }
-  // number of valid entries: first position holding INT_MAX (binary search)
-  int lo = 0, hi = n2;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (sidx[mid] == INT_MAX) hi = mid; else lo = mid + 1;
-  }
-  const int nvalid = lo;
-
-  // ---- Q^T fragment: this pair's 16 heads, this wave's half of d_qk
-  const int head = hb * C::HEADS + pr * C::HPW + l16;
-  const bool hvalid = head < p.heads;
-  const int dq0 = hh * (DQK / 2);
-  u32x4 qf[C::KS_HALF];
-  {
-    const uint16_t* src = p.q + ((int64_t)row * p.heads + (hvalid ? head : 0)) * DQK + dq0 + 8 * G;
+    __syncthreads();
+    auto count = [&](int v) -> int { return (int)((cnt[v >> 1] >> (16 * (v & 1))) & 0xFFFFu); };
+    const int per = (p.n_kv + C::THREADS - 1) / C::THREADS;
+    const int v0 = min(tid * per, p.n_kv), v1 = min(v0 + per, p.n_kv);
+    int tot = 0;
+    for (int v = v0; v < v1; ++v) tot += count(v);
+    int incl = tot;                                     // inclusive scan over the wave
 #pragma unroll
-    for (int ks = 0; ks < C::KS_HALF; ++ks) {
-      const u32x4 v = *(const u32x4*)(src + 32 * ks);
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int base = incl - tot;
+    nvalid = 0;
+#pragma unroll
+    for (int w = 0; w < C::WAVES; ++w) {
+      if (w < wave) base += wsum[w];
+      nvalid += wsum[w];
+    }
+    for (int v = v0; v < v1; ++v)
+      for (int c = count(v); c > 0; --c) sidx[base++] = v;
+    __syncthreads();
+  } else {
+    // Bitonic sorting network in LDS; padding and out-of-range entries become
+    // INT_MAX and sort to the end.
+    int n2 = 1;
+    while (n2 < p.k) n2 <<= 1;
+    for (int i = tid; i < n2; i += C::THREADS) {
+      int v = INT_MAX;
+      if (i < p.k) {
+        const int x = irow[i];
+        v = (x >= 0 && x < p.n_kv) ? x : INT_MAX;
+      }
+      sidx[i] = v;
+    }
+    __syncthreads();
+    for (int size = 2; size <= n2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int t = tid; t < (n2 >> 1); t += C::THREADS) {
+          const int i = 2 * t - (t & (stride - 1));
+          const int j = i + stride;
+          const bool up = (i & size) == 0;
+          const int a = sidx[i], b = sidx[j];
+          if ((a > b) == up) { sidx[i] = b; sidx[j] = a; }
+        }
+        __syncthreads();
+      }
+    }
+    // number of valid entries: first position holding INT_MAX (binary search)
+    int lo = 0, hi = n2;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (sidx[mid] == INT_MAX) hi = mid; else lo = mid + 1;
+    }
+    nvalid = lo;
+  }
+  const int n_tiles = (nvalid + C::BN - 1) / C::BN;
+
+  // ---- Q^T fragment (B operand of S^T = K Q^T): head l32 of this wave,
+  // dims 16 ks + 8 g2 .. +7
+  const int head0 = hb * C::HEADS + wave * C::HPW;      // wave-uniform
+  const bool active = head0 < p.heads;                  // wave has at least one head
+  const int head = head0 + l32;
+  const bool hvalid = head < p.heads;
+  u32x4 qf[C::KSTEPS];
+  {
+    const uint16_t* src = p.q + ((int64_t)row * p.heads + (hvalid ? head : 0)) * DQK + 8 * g2;
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+      const u32x4 v = *(const u32x4*)(src + 16 * ks);
       qf[ks] = hvalid ? v : (u32x4){0u, 0u, 0u, 0u};
     }
   }
   float c = fabsf(p.scale) * kLog2e;
   if (p.scale < 0.f) {
 #pragma unroll
-    for (int ks = 0; ks < C::KS_HALF; ++ks) qf[ks] ^= (u32x4){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+    for (int ks = 0; ks < C::KSTEPS; ++ks) qf[ks] ^= (u32x4){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
   }
   c = fmaxf(c, FLT_MIN);
+  // Retire the Q loads here: otherwise the compiler waits for them (vmcnt(0),
+  // which would also drain the in-flight tile DMAs) at their first use inside
+  // the key loop, on every iteration.
+#pragma unroll
+  for (int ks = 0; ks < C::KSTEPS; ++ks) asm volatile("" : "+v"(qf[ks]));
 
-  // ---- gather by DMA: 1 KB block bk of a tile is filled by wave bk % 8;
+  // ---- gather by DMA: 1 KB block bk of a tile is filled by wave bk % WAVES;
   // slot sl of the tile holds row sl / CPR, physical chunk sl % CPR =
   // logical chunk ^ swz(row).
-  const __amdgpu_buffer_rsrc_t kv_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)p.kv, (short)0, (int)((int64_t)p.n_kv * C::ROWB), 0x00020000);
-  auto gather = [&](int kt, unsigned char* dst) {
+  const uint64_t kv_addr = (uint64_t)(uintptr_t)p.kv;
+  const i32x4 kv_rsrc = (i32x4){(int)(uint32_t)kv_addr, (int)(uint32_t)(kv_addr >> 32) & 0xFFFF,
+                                (int)((int64_t)p.n_kv * C::ROWB), 0x00020000};
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)ring;
+  // Slot (row, byte column) of each of this lane's DMA blocks, packed
+  // row << 16 | column; the same for every tile.
+  int g_rc[C::BPW];
 #pragma unroll
-    for (int bi = 0; bi < (C::BLOCKS + C::WAVES - 1) / C::WAVES; ++bi) {
-      const int bk = bi * C::WAVES + wave;              // wave-uniform
-      if (bk < C::BLOCKS) {
-        const int sl = bk * 64 + lane;
-        const int r = sl / C::CPR;
-        const int col = 16 * ((sl - r * C::CPR) ^ C::swz(r));
-        const int j = kt * C::BN + r;
-        const unsigned off = j < nvalid ? (unsigned)sidx[j] * C::ROWB + col : 0xFFFFFFF0u;   // past the end: zeros
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, (__attribute__((address_space(3))) void*)(dst + bk * 1024),
-                                                 16, off, 0, 0, 0);
-      }
+  for (int bi = 0; bi < C::BPW; ++bi) {
+    const int sl = (bi * C::WAVES + wave) * 64 + lane;
+    const int r = sl / C::CPR;
+    const int ph = sl - r * C::CPR;
+    g_rc[bi] = (r << 16) | (16 * ((ph & ~7) | ((ph & 7) ^ C::swz(r))));
+  }
+  auto gather = [&](int kt) {
+    const uint32_t dst = ring_lds + (uint32_t)((kt % C::NSTAGE) * C::TILE);
+    int x[C::BPW];                                      // all index reads first: one LDS wait
+#pragma unroll
+    for (int bi = 0; bi < C::BPW; ++bi) x[bi] = sidx[min(kt * C::BN + (g_rc[bi] >> 16), MAXK - 1)];
+#pragma unroll
+    for (int bi = 0; bi < C::BPW; ++bi) asm volatile("" : "+v"(x[bi]));   // keep the reads unconditional
+#pragma unroll
+    for (int bi = 0; bi < C::BPW; ++bi) {
+      const int j = kt * C::BN + (g_rc[bi] >> 16);
+      const uint32_t off = __umul24((uint32_t)x[bi], (uint32_t)C::ROWB) + (uint32_t)(g_rc[bi] & 0xFFFF);
+      dma16(kv_rsrc, __builtin_amdgcn_readfirstlane(dst + (uint32_t)((bi * C::WAVES + wave) * 1024)),
+            j < nvalid ? off : 0xFFFFFFF0u);              // past the end: zeros
     }
   };
 
-  // ---- per-lane LDS read offsets.  The swizzle only permutes the low 3 bits
-  // of a chunk index, so chunk 8 a + x (x < 8) sits at 16 (8 a + (x ^ swz)):
-  // one per-lane base per x class plus a compile-time 128 a offset.
-  const int ksw = C::swz(l16);                           // same for rows l16 and 16 + l16
-  int kbase[2];                                          // K chunk dq0/8 + 4 ks + G, ks = 2 a + b
+
+  // ---- per-lane LDS read offsets.  Chunk 8 a + b (b < 8) sits at
+  // 16 (8 a + (b ^ swz)): a per-lane base per low-bit class plus 128 a.
+  const int ksw = C::swz(l32);                          // same for rows l32 and l32 + 16
+  int kb[4];                                            // K row l32, chunk 2 ks + g2, ks = 4 a + b
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int c0 = dq0 / 8 + 4 * b + G;                  // chunk at a = 0 (dq0/8 need not be 8-aligned)
-    kbase[b] = l16 * C::ROWB + 16 * ((c0 & ~7) | ((c0 & 7) ^ ksw));
-  }
-  const int vr0 = 4 * G + (l16 >> 2);                    // first of the 4 keys read transposed
-  const int vx = (l16 & 3) >> 1;                         // chunk dv0/8 + 2 nt + vx, nt = 4 a + b
-  const int dv0 = hh * (DV / 2);
-  int vbase0[4], vbase1[4];
+  for (int b = 0; b < 4; ++b) kb[b] = l32 * C::ROWB + 16 * ((2 * b + g2) ^ ksw);
+  const int i16 = lane & 15, nh = (lane >> 4) & 1;
+  const int vr0 = 4 * g2 + (i16 >> 2);                 // key row of the first 4-key read (+ 16 kst)
+  const int vx = 2 * nh + ((i16 & 3) >> 1);            // low chunk bits within a 32-column tile
+  int vb0[2], vb1[2];                                   // V rows vr0 and vr0 + 8; nt & 1 selects
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    vbase0[b] = vr0 * C::ROWB + dv0 * 2 + 16 * ((2 * b + vx) ^ C::swz(vr0)) + 8 * (l16 & 1);
-    vbase1[b] = (vr0 + 16) * C::ROWB + dv0 * 2 + 16 * ((2 * b + vx) ^ C::swz(vr0 + 16)) + 8 * (l16 & 1);
+  for (int e = 0; e < 2; ++e) {
+    vb0[e] = vr0 * C::ROWB + 16 * ((4 * e + vx) ^ C::swz(vr0)) + 8 * (i16 & 1);
+    vb1[e] = (vr0 + 8) * C::ROWB + 16 * ((4 * e + vx) ^ C::swz(vr0 + 8)) + 8 * (i16 & 1);
   }
 
-  floatx4 o[C::NT_HALF];
+  floatx16 o[C::NT];
 #pragma unroll
-  for (int nt = 0; nt < C::NT_HALF; ++nt) o[nt] = (floatx4){};
-  float m_used = -INFINITY, l_run = 0.f;
-  const int n_tiles = (nvalid + C::BN - 1) / C::BN;
+  for (int nt = 0; nt < C::NT; ++nt) {
+    o[nt] = (floatx16){};
+    asm("" : "+a"(o[nt]));                              // O^T lives in AGPRs from the start
+  }
+  float m_used = -INFINITY;  // reference max (times c, log2 domain)
+  float l_run = 0.f;         // this lane's partial sum of P
 
-  auto step = [&](int kt, auto odd_tag) {
-    constexpr bool ODD = decltype(odd_tag)::value;
-    unsigned char* cur = ODD ? tile1 : tile0;
-    unsigned char* nxt = ODD ? tile0 : tile1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this lane's gather of tile kt landed
-    __syncthreads();                                   // everyone's landed; tile kt-1 fully consumed
-    if (kt + 1 < n_tiles) gather(kt + 1, nxt);
-
-    // partial S^T[key 16 kb + 4 G + i][head l16] over this wave's half of d_qk
-    floatx4 s0 = (floatx4){}, s1 = (floatx4){};
-#pragma unroll
-    for (int ks = 0; ks < C::KS_HALF; ++ks) {
-      const unsigned char* kp = cur + kbase[ks & 1] + 128 * (ks >> 1);
-      const u32x4 a0 = *(const u32x4*)(kp);
-      const u32x4 a1 = *(const u32x4*)(kp + 16 * C::ROWB);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), as_bf16x8(qf[ks]), s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), as_bf16x8(qf[ks]), s1, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      xs[wave][i][lane] = s0[i];
-      xs[wave][4 + i][lane] = s1[i];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {                      // own + partner: the same sum in both waves
-      s0[i] += xs[wave ^ 1][i][lane];
-      s1[i] += xs[wave ^ 1][4 + i][lane];
-    }
+  auto mask_tail = [&](int kt, floatx16& s) {
     if ((kt + 1) * C::BN > nvalid) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (kt * C::BN + 4 * G + i >= nvalid) s0[i] = -INFINITY;
-        if (kt * C::BN + 16 + 4 * G + i >= nvalid) s1[i] = -INFINITY;
-      }
-    }
-    float mx = vmax(vmax(s0[0], s0[1]), vmax(s0[2], s0[3]));
-    mx = vmax(mx, vmax(vmax(s1[0], s1[1]), vmax(s1[2], s1[3])));
-    mx = vmax(mx, __shfl_xor(mx, 16));
-    mx = vmax(mx, __shfl_xor(mx, 32));
-    const float mx_sc = (mx == -INFINITY) ? -INFINITY : mx * c;
-    const bool upd = mx_sc > m_used + 8.0f;            // lazy reference max (P < 2^8)
-    if (__any(upd)) {
-      asm volatile("; rare: move the reference max, rescale O and l" ::);
-      const float m_new = upd ? mx_sc : m_used;
-      const float alpha = upd ? fast_exp2(m_used - m_new) : 1.0f;
-      m_used = m_new;
-#pragma unroll
-      for (int nt = 0; nt < C::NT_HALF; ++nt) o[nt] *= alpha;
-      l_run *= alpha;
-    }
-    const float m_use = (m_used == -INFINITY) ? 0.f : m_used;
-    float e[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      e[i] = fast_exp2(fmaf(s0[i], c, -m_use));
-      e[4 + i] = fast_exp2(fmaf(s1[i], c, -m_use));
-    }
-    l_run += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-    // B operand: k-slot j of lane group G is key 16 (j/4) + 4 G + j%4.
-    const u32x4 pb = (u32x4){pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]),
-                             pack_bf16x2(e[4], e[5]), pack_bf16x2(e[6], e[7])};
-    // A operand V^T[n][keys]: transposed read of rows vr0 (+16), this wave's d_v half.
-#pragma unroll
-    for (int nt = 0; nt < C::NT_HALF; ++nt) {
-      const u32x2 a = lds_read_tr(cur + vbase0[nt & 3] + 128 * (nt >> 2));
-      const u32x2 b = lds_read_tr(cur + vbase1[nt & 3] + 128 * (nt >> 2));
-      o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8((u32x4){a[0], a[1], b[0], b[1]}), as_bf16x8(pb),
-                                                      o[nt], 0, 0, 0);
+      for (int r = 0; r < 16; ++r)
+        if (kt * C::BN + 8 * (r >> 2) + 4 * g2 + (r & 3) >= nvalid) s[r] = -INFINITY;
     }
   };
+  // ---- one step of the key loop, as an explicitly scheduled sequence of
+  // MFMA slots: slots 0..KSTEPS-1 are the QK^T k-steps of tile t (S^T[key
+  // 8 (r/4) + 4 g2 + r%4][head l32] accumulates in s), the next 2 NT slots
+  // the P V MFMAs of tile t-1 (P already packed in pb).  Each slot issues the
+  // LDS read of the operand PD slots ahead and ends in a scheduling barrier,
+  // so the register footprint stays fixed (the compiler would otherwise hoist
+  // every read of the step).  The softmax of tile t runs on the VALU under
+  // the P V MFMAs of tile t-1:
+  //   * head max of the tile; the reference max moves only when the tile max
+  //     exceeds it by more than 8 (log2 units), so P stays below 2^8 (lazy
+  //     rescaling); the final lse uses the same reference, so the result is
+  //     exact in real arithmetic;
+  //   * l is rescaled at once; O (which P V of tile t-1 is still writing) is
+  //     rescaled after the step's last MFMA, in a rare branch;
+  //   * P = 2^(s c - m) with an fp32 sum for l, rounded to bf16 and packed:
+  //     k-slot j of lane half g2 in P V k-step kst is key 16 kst + 8 (j / 4) +
+  //     4 g2 + j % 4, i.e. accumulator entry 8 kst + j, for both the P^T and
+  //     the V^T operand.
+  constexpr int PD = 4;
+  constexpr int NQK = C::KSTEPS, NPV = 2 * C::NT;
+  auto load_op = [&](const unsigned char* kst, const unsigned char* vst, auto slot_tag) -> u32x4 {
+    constexpr int SL = decltype(slot_tag)::value;
+    if constexpr (SL < NQK) {
+      return *(const u32x4*)(kst + kb[SL & 3] + 128 * (SL >> 2));
+    } else {
+      constexpr int J = SL - NQK, KS = J / C::NT, NTI = J % C::NT;
+      constexpr int OFF = KS * 16 * C::ROWB + 128 * (NTI >> 1);   // 16 key rows per k-step; 8 chunks per tile pair
+      const u32x2 lo = lds_read_tr(vst + vb0[NTI & 1] + OFF);
+      const u32x2 hi = lds_read_tr(vst + vb1[NTI & 1] + OFF);
+      return (u32x4){lo[0], lo[1], hi[0], hi[1]};
+    }
+  };
+  // Softmax of the tile in s, cut into small VALU pieces that the P V slots
+  // interleave, one per slot: with one wave per SIMD nothing else hides the
+  // latency of a dependent VALU chain, so each piece only consumes values
+  // produced at least one slot earlier.
+  struct Soft {
+    float mx[4], alpha, m_use;
+    bool any_upd;
+    float e[16];
+    uint32_t w[8];
+  };
+  auto soft_piece = [&](floatx16& s, Soft& sf, auto piece_tag) {
+    constexpr int P = decltype(piece_tag)::value;
+    if constexpr (P == 0) {                             // head max: four partial trees
+      sf.mx[0] = vmax(vmax(s[0], s[1]), s[2]);
+      sf.mx[1] = vmax(vmax(s[3], s[4]), s[5]);
+      sf.mx[2] = vmax(vmax(s[6], s[7]), s[8]);
+      sf.mx[3] = vmax(vmax(s[9], s[10]), s[11]);
+    } else if constexpr (P == 1) {
+      sf.mx[0] = vmax(vmax(sf.mx[0], sf.mx[1]), s[12]);
+      sf.mx[2] = vmax(vmax(sf.mx[2], sf.mx[3]), vmax(vmax(s[13], s[14]), s[15]));
+    } else if constexpr (P == 2) {
+      sf.mx[0] = lane_swap_max(vmax(sf.mx[0], sf.mx[2]));
+    } else if constexpr (P == 3) {                      // reference update (lazy: only beyond 2^8)
+      const float mx_sc = (sf.mx[0] == -INFINITY) ? -INFINITY : sf.mx[0] * c;
+      const bool upd = mx_sc > m_used + 8.0f;
+      sf.any_upd = __any(upd);
+      const float m_new = upd ? mx_sc : m_used;
+      sf.alpha = upd ? fast_exp2(m_used - m_new) : 1.0f;
+      sf.m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      m_used = m_new;
+    } else if constexpr (P == 4) {
+      l_run *= sf.alpha;
+      sf.e[0] = fast_exp2(fmaf(s[0], c, -sf.m_use));
+      sf.e[1] = fast_exp2(fmaf(s[1], c, -sf.m_use));
+    } else if constexpr (P < 12) {                      // pieces 5..11: two probabilities, pack / sum the previous two
+      constexpr int R = 2 * (P - 4);
+      sf.e[R] = fast_exp2(fmaf(s[R], c, -sf.m_use));
+      sf.e[R + 1] = fast_exp2(fmaf(s[R + 1], c, -sf.m_use));
+      sf.w[(R - 2) >> 1] = pack_bf16x2(sf.e[R - 2], sf.e[R - 1]);
+      l_run += sf.e[R - 2] + sf.e[R - 1];
+    } else if constexpr (P == 12) {
+      sf.w[7] = pack_bf16x2(sf.e[14], sf.e[15]);
+      l_run += sf.e[14] + sf.e[15];
+    }
+  };
+  auto rescale_o = [&](const Soft& sf) {
+    if (sf.any_upd) {
+      asm volatile("; rare: the reference max moved, rescale O" ::);
+      xdl_drain_o(o);
+#pragma unroll
+      for (int nt = 0; nt < C::NT; ++nt) {              // one tile at a time through VGPRs
+        o[nt] *= sf.alpha;
+        asm volatile("" : "+a"(o[nt]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      valu_to_xdl_o(o);
+    }
+  };
+  // QK: the QK^T slots of the tile in kst into s, then (PV) the P V slots of
+  // the previous tile (pb, V from vst) with the softmax of s under them.
+  // Returns the packed P of s in pb.
+  // `issue` runs between the first operand reads and the first MFMA (the
+  // next tile's DMA issue hides their latency).
+  auto step_mma = [&](int kt, const unsigned char* kst, const unsigned char* vst, floatx16& s, u32x4* pb, Soft& sf,
+                      auto pv_tag, auto&& issue) {
+    constexpr bool PV = decltype(pv_tag)::value;
+    constexpr int LAST = PV ? NQK + NPV : NQK;
+    u32x4 opr[PD];
+    floatx16 s1;
+    static_for<0, PD>([&](auto i) { opr[i.value] = load_op(kst, vst, i); });
+    issue();
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, LAST>([&](auto slot_tag) {
+      constexpr int SL = decltype(slot_tag)::value;
+      const u32x4 a = opr[SL % PD];
+      if constexpr (SL + PD < LAST) opr[SL % PD] = load_op(kst, vst, std::integral_constant<int, SL + PD>{});
+      if constexpr (SL < NQK) {
+        // two accumulators (even / odd k-steps): back-to-back MFMAs never
+        // wait on each other's result
+        if constexpr (SL == 0) mfma_s_first(s, a, qf[0]);
+        else if constexpr (SL == 1) mfma_s_first(s1, a, qf[1]);
+        else if constexpr (SL & 1) mfma_s(s1, a, qf[SL]);
+        else mfma_s(s, a, qf[SL]);
+        if constexpr (SL == NQK - 1 && !PV) {
+          xdl_drain_v(s1);
+          s += s1;
+          mask_tail(kt, s);                             // keys past the valid count -> -inf
+        }
+      } else {
+        constexpr int J = SL - NQK, KS = J / C::NT, NTI = J % C::NT;
+        mfma_o(o[NTI], a, pb[KS]);
+        if constexpr (J == 0) {                         // under the first P V MFMA: finish S^T
+          xdl_drain_v(s1);
+          s += s1;
+          mask_tail(kt, s);                             // keys past the valid count -> -inf
+        }
+        // softmax pieces under P V slots 1 .. 13
+        if constexpr (J >= 1 && J <= 13) soft_piece(s, sf, std::integral_constant<int, J - 1>{});
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if constexpr (!PV) static_for<0, 13>([&](auto piece) { soft_piece(s, sf, piece); });
+  };
+  auto pack_p = [&](const Soft& sf, u32x4* pb) {
+    pb[0] = (u32x4){sf.w[0], sf.w[1], sf.w[2], sf.w[3]};
+    pb[1] = (u32x4){sf.w[4], sf.w[5], sf.w[6], sf.w[7]};
+    valu_to_xdl(pb[0], pb[1]);
+  };
+  // Last P V (no QK^T slots).
+  auto last_pv = [&](const unsigned char* vst, const u32x4* pb) {
+    u32x4 opr[PD];
+    static_for<0, PD>([&](auto i) { opr[i.value] = load_op(vst, vst, std::integral_constant<int, NQK + i.value>{}); });
+    static_for<NQK, NQK + NPV>([&](auto slot_tag) {
+      constexpr int SL = decltype(slot_tag)::value;
+      const u32x4 a = opr[SL % PD];
+      if constexpr (SL + PD < NQK + NPV) opr[SL % PD] = load_op(vst, vst, std::integral_constant<int, SL + PD>{});
+      constexpr int J = SL - NQK, KS = J / C::NT, NTI = J % C::NT;
+      mfma_o(o[NTI], a, pb[KS]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
 
-  if (n_tiles > 0) gather(0, tile0);
-  int kt = 0;
-  for (; kt + 2 <= n_tiles; kt += 2) {
-    step(kt, std::false_type{});
-    step(kt + 1, std::true_type{});
+  // Wait until this lane's DMA of tile t has landed (the DMAs of later tiles
+  // may stay in flight; vector memory loads complete in issue order), then
+  // for every wave's.  The barrier also retires the reads of the stage the
+  // next DMA refills.
+  auto wait_tile = [&](int t) {
+    if (C::DIST == 2 && t + 1 < n_tiles) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::BPW) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  auto stage_ptr = [&](int t) -> const unsigned char* { return ring + (t % C::NSTAGE) * C::TILE; };
+
+  if (n_tiles > 0) {
+    gather(0);
+    if (C::DIST == 2 && 1 < n_tiles) gather(1);
+    u32x4 pb[2];                                        // packed P of the previous tile
+    // step 0: QK^T and softmax of tile 0
+    wait_tile(0);
+    auto issue0 = [&] { if (C::DIST < n_tiles) gather(C::DIST); };
+    if (active) {
+      floatx16 s;
+      Soft sf;
+      step_mma(0, stage_ptr(0), stage_ptr(0), s, pb, sf, std::false_type{}, issue0);
+      pack_p(sf, pb);
+    } else {
+      issue0();
+    }
+    // steps 1 .. n_tiles-1: QK^T and softmax of tile t under P V of tile t-1
+    for (int t = 1; t < n_tiles; ++t) {
+      wait_tile(t);
+      auto issue = [&] { if (t + C::DIST < n_tiles) gather(t + C::DIST); };
+      if (active) {
+        floatx16 s;
+        Soft sf;
+        step_mma(t, stage_ptr(t), stage_ptr(t - 1), s, pb, sf, std::true_type{}, issue);
+        rescale_o(sf);
+        pack_p(sf, pb);
+      } else {
+        issue();
+      }
+    }
+    // last step: P V of tile n_tiles-1
+    if (active) last_pv(stage_ptr(n_tiles - 1), pb);
   }
-  if (kt < n_tiles) step(kt, std::false_type{});
 
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  // ---- epilogue: O / l (bf16 RNE), lse = ln 2 * (m + log2 l)
+  xdl_drain_o(o);
+  float l_tot = l_run;
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_tot), __float_as_uint(l_tot), false, false);
+    l_tot = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (hvalid) {
-    uint16_t* dst = p.out + ((int64_t)row * p.heads + head) * DV + dv0 + 4 * G;
+    uint16_t* dst = p.out + ((int64_t)row * p.heads + head) * DV + 4 * g2;
 #pragma unroll
-    for (int nt = 0; nt < C::NT_HALF; ++nt)
-      *(u32x2*)(dst + 16 * nt) = (u32x2){pack_bf16x2(o[nt][0] * inv, o[nt][1] * inv),
-                                         pack_bf16x2(o[nt][2] * inv, o[nt][3] * inv)};
-    if (p.lse != nullptr && G == 0 && hh == 0)
+    for (int nt = 0; nt < C::NT; ++nt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *(u32x2*)(dst + 32 * nt + 8 * r4) = (u32x2){pack_bf16x2(o[nt][4 * r4] * inv, o[nt][4 * r4 + 1] * inv),
+                                                    pack_bf16x2(o[nt][4 * r4 + 2] * inv, o[nt][4 * r4 + 3] * inv)};
+    if (p.lse != nullptr && g2 == 0)
       p.lse[(int64_t)head * p.rows + row] = l_tot > 0.f ? (m_used + log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
@@ -312,7 +586,7 @@ hipError_t launch_sparse_mqa(const SparseParams& p, int d_qk, int d_v, hipStream
   if (d_qk != 576 || d_v != 512) return hipErrorInvalidValue;
   if (p.k > 4096) return hipErrorInvalidValue;
   if (p.rows == 0) return hipSuccess;
-  const dim3 grid(p.rows * p.head_blocks), block(512);
+  const dim3 grid(p.rows * p.head_blocks), block(256);
   if (p.k <= 2048) hipLaunchKernelGGL((sparse_mqa_kernel<576, 512, 2048>), grid, block, 0, s, p);
   else hipLaunchKernelGGL((sparse_mqa_kernel<576, 512, 4096>), grid, block, 0, s, p);
   return hipGetLastError();

@@ -79,6 +79,6 @@ hipError_t launch_attn_probs(const ProbsParams& p, bool bf16, hipStream_t s);
 // Tile shape of the dense bf16/f32 kernels (query rows per workgroup); the
 // host uses it to size the launch.
 constexpr int kDenseBM = 128;
-constexpr int kSparseHeadsPerWG = 64;
+constexpr int kSparseHeadsPerWG = 128;
 
 }  // namespace vea
