@@ -9,7 +9,8 @@
  *
  * Conventions shared by every call
  *   - All tensor pointers are DEVICE pointers, row-major, owned by the caller.
- *     The library allocates nothing and keeps no state between calls.
+ *     The library allocates nothing and keeps no state between calls; a call
+ *     that can use scratch memory takes it as a caller workspace.
  *   - Strides are in ELEMENTS.  Within a token, heads are contiguous and each
  *     head holds head_dim contiguous elements.
  *   - 16-byte vector loads are used: every tensor pointer must be 16-byte
@@ -32,6 +33,7 @@
 #ifndef VEA_H
 #define VEA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -45,7 +47,7 @@ typedef enum vea_status {
   VEA_ESHAPE = -3,       /* inconsistent sizes (negative counts, Hq % Hkv != 0, short stride) */
   VEA_EUNSUPPORTED = -4, /* valid request outside the compiled kernel set (e.g. head_dim) */
   VEA_ERANGE = -5,       /* VEA_CHECK only: bad cu_seqlens or top-k index found on the host */
-  VEA_EWORKSPACE = -6,   /* reserved for calls that take a caller workspace */
+  VEA_EWORKSPACE = -6,   /* caller workspace smaller than the call needs, or misaligned */
   VEA_EHIP = -7          /* the HIP runtime reported an error (launch or VEA_CHECK sync) */
 } vea_status;
 
@@ -153,10 +155,32 @@ int vea_qkv_rope(const void* x_qkv, int64_t x_tok_stride,
  *   k          1 .. 4096.
  *   out        bf16 [num_rows, num_heads, d_v]; lse float [num_heads, num_rows]
  *              or NULL.
+ *   workspace  NULL (workspace_bytes ignored), or device memory of at least
+ *              vea_sparse_mqa_workspace_size bytes for the same sizes on the
+ *              current device, 16-byte aligned; else VEA_EWORKSPACE.  Its
+ *              contents need no initialisation and are garbage afterwards.
+ *              With a workspace, the (row, 128-head block) units of the last,
+ *              partial round of workgroups over the device's CUs are split
+ *              into key ranges of the sorted indices that run on otherwise
+ *              idle CUs and are merged in range order (the same merge).  The
+ *              rounding of those rows then depends on num_rows, num_heads and
+ *              the CU count; without a workspace every row is computed alone,
+ *              so a row's bits do not depend on the rest of the batch.  Both
+ *              modes are deterministic and order-invariant.  Calls that share
+ *              a workspace must be ordered (same stream).
  */
 int vea_sparse_mqa_fwd(const void* q, const void* kv_latent, const int32_t* topk_idx,
                        int num_rows, int num_heads, int n_kv, int d_qk, int d_v, int k,
-                       float scale, void* out, float* lse, void* stream);
+                       float scale, void* out, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * vea_sparse_mqa_workspace_size — bytes of workspace vea_sparse_mqa_fwd uses
+ * for these sizes on the current HIP device (0 when no split pays off, e.g.
+ * when the units fill whole rounds of the CUs).  Validates like
+ * vea_sparse_mqa_fwd; VEA_EHIP if the device cannot be queried.
+ */
+int vea_sparse_mqa_workspace_size(int num_rows, int num_heads, int d_qk, int d_v, int k, size_t* bytes);
 
 /*
  * vea_attn_probs_piece — debug export (not on the timed path) of the

@@ -12,7 +12,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "vea.h")
 
-VEA_OK, VEA_EINVAL, VEA_EDTYPE, VEA_ESHAPE, VEA_EUNSUPPORTED = 0, -1, -2, -3, -4
+VEA_OK, VEA_EINVAL, VEA_EDTYPE, VEA_ESHAPE, VEA_EUNSUPPORTED, VEA_EWORKSPACE = 0, -1, -2, -3, -4, -6
 
 
 def _declared():
@@ -29,9 +29,10 @@ def lib():
     return _binding.load_library()
 
 
-def test_header_declares_the_four_operations():
+def test_header_declares_the_operations():
     names = _declared()
-    for n in ("vea_attn_fwd", "vea_qkv_rope", "vea_sparse_mqa_fwd", "vea_attn_probs_piece", "vea_status_str"):
+    for n in ("vea_attn_fwd", "vea_qkv_rope", "vea_sparse_mqa_fwd", "vea_sparse_mqa_workspace_size",
+              "vea_attn_probs_piece", "vea_status_str"):
         assert n in names
 
 
@@ -111,10 +112,11 @@ def test_qkv_rope_validation(lib, kw, status):
 
 
 def _sparse(lib, **kw):
-    a = dict(q=FAKE, kv=FAKE, idx=FAKE, r=3, h=128, nkv=100, dqk=576, dv=512, k=64, scale=0.04, out=FAKE, lse=None)
+    a = dict(q=FAKE, kv=FAKE, idx=FAKE, r=3, h=128, nkv=100, dqk=576, dv=512, k=64, scale=0.04, out=FAKE, lse=None,
+             ws=None, wsb=0)
     a.update(kw)
     return lib.vea_sparse_mqa_fwd(a["q"], a["kv"], a["idx"], a["r"], a["h"], a["nkv"], a["dqk"], a["dv"], a["k"],
-                                  a["scale"], a["out"], a["lse"], None)
+                                  a["scale"], a["out"], a["lse"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -126,9 +128,26 @@ def _sparse(lib, **kw):
     (dict(idx=None), VEA_EINVAL),
     (dict(out=FAKE + 4), VEA_EINVAL),
     (dict(r=0), VEA_OK),
+    (dict(ws=FAKE + 8, wsb=1 << 20), VEA_EWORKSPACE),
+    (dict(nkv=-1), VEA_ESHAPE),
 ])
 def test_sparse_validation(lib, kw, status):
     assert _sparse(lib, **kw) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((3, 128, 512, 512, 64), VEA_EUNSUPPORTED),
+    ((3, 128, 576, 600, 64), VEA_ESHAPE),
+    ((3, 0, 576, 512, 64), VEA_ESHAPE),
+    ((3, 128, 576, 512, 0), VEA_ESHAPE),
+    ((3, 128, 576, 512, 4097), VEA_EUNSUPPORTED),
+    ((0, 128, 576, 512, 64), VEA_OK),
+])
+def test_sparse_workspace_size_validation(lib, args, status):
+    n = ctypes.c_size_t(12345)
+    assert lib.vea_sparse_mqa_workspace_size(*args, ctypes.byref(n)) == status
+    assert n.value == 0
+    assert lib.vea_sparse_mqa_workspace_size(*args, None) == VEA_EINVAL
 
 
 def test_probs_validation(lib):

@@ -20,16 +20,16 @@ def torch():
     return t
 
 
-def _run(torch, case, idx=None):
-    st = R.stage_sparse(case, idx=idx)
+def _run(torch, case, idx=None, split=True):
+    st = R.stage_sparse(case, idx=idx, split=split)
     R.run_sparse(st)
     torch.cuda.synchronize()
     return st
 
 
-def _check(torch, case, idx=None, rows=None, name=""):
-    log("sparse case %s %s" % (case.name, name))
-    st = _run(torch, case, idx)
+def _check(torch, case, idx=None, rows=None, name="", split=True):
+    log("sparse case %s %s split=%s" % (case.name, name, split))
+    st = _run(torch, case, idx, split)
     ix = case.topk_idx if idx is None else idx
     o_ref, l_ref = oracle.sparse_mqa(W.bf16_bits_to_f64(case.q), W.bf16_bits_to_f64(case.kv_latent), ix, case.d_v,
                                      float(np.float32(case.scale)), rows=rows)
@@ -128,3 +128,82 @@ def test_more_than_2048_indices(torch):
     st = _check(torch, case, name="k3000")
     perm = _run(torch, case, W.permute_rows(case.topk_idx, 108))
     assert torch.equal(perm.out, st.out) and torch.equal(perm.lse, st.lse)
+
+
+# ---- the split of the last, partial round of workgroups (a caller workspace)
+
+def _cus(torch):
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def test_without_workspace_rows_are_batch_invariant(torch):
+    """Without a workspace every row runs whole: right against the oracle, and
+    a row's bits do not depend on the other rows of the batch."""
+    case = W.sparse_mqa(rows=5, heads=128, n_kv=700, k=256, seed=21)
+    st = _check(torch, case, split=False, name="unsplit")
+    assert st.ws is None
+    sub = W.SparseCase("rows 2..3", case.q[2:4].copy(), case.kv_latent, case.topk_idx[2:4].copy(), case.d_v,
+                       case.scale)
+    st2 = _run(torch, sub, split=False)
+    assert torch.equal(st2.out, st.out[2:4]) and torch.equal(st2.lse, st.lse[:, 2:4])
+
+
+def test_split_matches_unsplit_within_rounding(torch):
+    """Split rows differ from whole rows only by the rounding of the merge."""
+    case = W.sparse_mqa(rows=3, heads=128, n_kv=2600, k=2048, seed=22)
+    a = _check(torch, case, name="split")
+    assert a.ws is not None and a.ws.numel() > 0
+    b = _check(torch, case, split=False, name="unsplit")
+    ao, bo = W.bf16_bits_to_f64(R.tensor_to_bits(a.out)), W.bf16_bits_to_f64(R.tensor_to_bits(b.out))
+    assert_bf16_close(ao, bo, "split vs unsplit")
+
+
+def test_split_empty_chunks_and_padding(torch):
+    """k = 64 (two tiles, so two key ranges): a row with 5 valid entries (its
+    first range is empty), an all-padding row (both empty: o = 0, lse =
+    -inf), a row with one partial tile past a full one, a full row."""
+    case = W.sparse_mqa(rows=4, heads=128, n_kv=500, k=64, seed=23)
+    idx = case.topk_idx.copy()
+    idx[0, 5:] = -1
+    idx[1, :] = -1
+    idx[2, 33:] = -1
+    st = _check(torch, case, idx=idx, name="empty chunks")
+    assert st.ws is not None
+    out = W.bf16_bits_to_f64(R.tensor_to_bits(st.out))
+    assert np.all(out[1] == 0) and np.all(st.lse[:, 1].cpu().numpy() == -np.inf)
+
+
+def test_split_order_invariant_and_repeatable_bitwise(torch):
+    """Key ranges are cut in sorted order, so the split output is still
+    bitwise independent of the index order, and bitwise repeatable."""
+    case = W.sparse_mqa(rows=3, heads=128, n_kv=2600, k=2048, seed=24)
+    a = _run(torch, case)
+    o0, l0 = a.out.clone(), a.lse.clone()
+    R.run_sparse(a)
+    torch.cuda.synchronize()
+    assert torch.equal(a.out, o0) and torch.equal(a.lse, l0)
+    for seed in (109, 110):
+        b = _run(torch, case, W.permute_rows(case.topk_idx, seed))
+        assert torch.equal(b.out, o0) and torch.equal(b.lse, l0)
+
+
+def test_split_at_a_round_boundary(torch):
+    """CUs + 3 rows: the first CUs rows run whole, the last 3 are split; both
+    sides of the boundary against the oracle, two head blocks (200 heads)."""
+    cus = _cus(torch)
+    case = W.sparse_mqa(rows=cus + 3, heads=200, n_kv=900, k=320, seed=25)
+    rows = [0, cus // 2 - 1, cus // 2, cus // 2 + 1, cus - 1, cus, cus + 1, cus + 2]
+    st = _check(torch, case, rows=rows, name="round boundary")
+    assert st.ws is not None
+
+
+def test_workspace_too_small_is_rejected(torch):
+    import vision_encoder_attention_amd as vea
+    case = W.sparse_mqa(rows=3, heads=128, n_kv=500, k=256, seed=26)
+    st = R.stage_sparse(case)
+    need = vea.sparse_mqa_workspace_size(3, 128, case.d_qk, case.d_v, 256)
+    assert need > 0 and st.ws.numel() == need
+    small = torch.empty(need - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(vea.VeaError) as e:
+        vea.sparse_mqa_fwd(st.q, st.kv, st.idx, 256, case.scale, st.out, st.lse, workspace=small)
+    assert e.value.status == -6

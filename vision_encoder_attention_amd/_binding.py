@@ -52,8 +52,11 @@ def load_library():
         lib.vea_attn_fwd.restype = i32
         lib.vea_qkv_rope.argtypes = [vp, i64, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp]
         lib.vea_qkv_rope.restype = i32
-        lib.vea_sparse_mqa_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp]
+        lib.vea_sparse_mqa_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp,
+                                           ctypes.c_size_t, vp]
         lib.vea_sparse_mqa_fwd.restype = i32
+        lib.vea_sparse_mqa_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+        lib.vea_sparse_mqa_workspace_size.restype = i32
         lib.vea_attn_probs_piece.argtypes = [i32, vp, i64, vp, i64, vp, i64, i32, i32, i32, i32, i32, i32,
                                              i32, i32, i32, i32, i32, f32, vp, i64, vp]
         lib.vea_attn_probs_piece.restype = i32
@@ -166,9 +169,22 @@ def qkv_rope(x_qkv, positions, theta, q, k):
     return q, k
 
 
-def sparse_mqa_fwd(q, kv_latent, topk_idx, k, scale, out, lse=None):
+def sparse_mqa_workspace_size(rows, heads, d_qk, d_v, k) -> int:
+    """Workspace bytes vea_sparse_mqa_fwd uses for these sizes on the current
+    device (0: no split)."""
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    _check(lib.vea_sparse_mqa_workspace_size(int(rows), int(heads), int(d_qk), int(d_v), int(k), ctypes.byref(n)))
+    return int(n.value)
+
+
+def sparse_mqa_fwd(q, kv_latent, topk_idx, k, scale, out, lse=None, workspace="auto"):
     """Top-k sparse MQA (see vea_sparse_mqa_fwd): q [R, H, d_qk], kv_latent
-    [n_kv, d_qk], topk_idx int32 [R, k], out [R, H, d_v], lse [H, R] or None."""
+    [n_kv, d_qk], topk_idx int32 [R, k], out [R, H, d_v], lse [H, R] or None.
+
+    workspace: "auto" allocates the size the call asks for (split of the last
+    round of workgroups), None runs every row alone (batch-invariant bits), or
+    a contiguous uint8 GPU tensor to use."""
     lib = load_library()
     torch = _torch()
     for t, n in ((q, "q"), (kv_latent, "kv_latent"), (out, "out")):
@@ -180,9 +196,19 @@ def sparse_mqa_fwd(q, kv_latent, topk_idx, k, scale, out, lse=None):
     if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (q.shape[1], q.shape[0])
                             or not lse.is_contiguous()):
         raise ValueError("lse must be contiguous float32 [heads, rows]")
-    st = lib.vea_sparse_mqa_fwd(_ptr(q), _ptr(kv_latent), _ptr(topk_idx), q.shape[0], q.shape[1],
-                                kv_latent.shape[0], q.shape[2], out.shape[2], int(k), float(scale), _ptr(out),
-                                _ptr(lse), _stream(q))
+    with torch.cuda.device(q.device):
+        if isinstance(workspace, str):
+            if workspace != "auto":
+                raise ValueError('workspace must be "auto", None or a uint8 GPU tensor')
+            nbytes = sparse_mqa_workspace_size(q.shape[0], q.shape[1], q.shape[2], out.shape[2], k)
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
+        if workspace is not None and (workspace.dtype != torch.uint8 or not workspace.is_contiguous()
+                                      or workspace.device != q.device):
+            raise ValueError("workspace must be a contiguous uint8 tensor on q's device")
+        st = lib.vea_sparse_mqa_fwd(_ptr(q), _ptr(kv_latent), _ptr(topk_idx), q.shape[0], q.shape[1],
+                                    kv_latent.shape[0], q.shape[2], out.shape[2], int(k), float(scale), _ptr(out),
+                                    _ptr(lse), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                    _stream(q))
     _check(st)
     return out, lse
 

@@ -153,29 +153,81 @@ int vea_qkv_rope(const void* x_qkv, int64_t x_tok_stride, const int32_t* positio
   return finish(hip_status(launch_qkv_rope(p, s)), s);
 }
 
-int vea_sparse_mqa_fwd(const void* q, const void* kv_latent, const int32_t* topk_idx, int num_rows, int num_heads,
-                       int n_kv, int d_qk, int d_v, int k, float scale, void* out, float* lse, void* stream) {
-  if (num_rows < 0 || num_heads <= 0 || n_kv < 0 || k <= 0) return VEA_ESHAPE;
+namespace {
+
+int sparse_shape_status(int num_rows, int num_heads, int d_qk, int d_v, int k) {
+  if (num_rows < 0 || num_heads <= 0 || k <= 0) return VEA_ESHAPE;
   if (d_v <= 0 || d_qk <= 0 || d_v > d_qk) return VEA_ESHAPE;
-  if (!isfinite(scale)) return VEA_EINVAL;
   if (d_qk != 576 || d_v != 512 || k > 4096) return VEA_EUNSUPPORTED;
+  const int64_t units = (int64_t)num_rows * ((num_heads + kSparseHeadsPerWG - 1) / kSparseHeadsPerWG);
+  if (units * 8 > 0x7fffffff) return VEA_EUNSUPPORTED;
+  return VEA_OK;
+}
+
+// CU count of the current device (the split plan's round size).
+int current_cus(int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return VEA_EHIP;
+  if (hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return VEA_EHIP;
+  return VEA_OK;
+}
+
+}  // namespace
+
+int vea_sparse_mqa_workspace_size(int num_rows, int num_heads, int d_qk, int d_v, int k, size_t* bytes) {
+  if (bytes == nullptr) return VEA_EINVAL;
+  *bytes = 0;
+  int st = sparse_shape_status(num_rows, num_heads, d_qk, d_v, k);
+  if (st != VEA_OK) return st;
+  if (num_rows == 0) return VEA_OK;
+  int cus = 0;
+  st = current_cus(&cus);
+  if (st != VEA_OK) return st;
+  const int head_blocks = (num_heads + kSparseHeadsPerWG - 1) / kSparseHeadsPerWG;
+  const SparseSplit plan = sparse_split_plan(num_rows * head_blocks, k, cus);
+  *bytes = (size_t)plan.chunks * sparse_chunk_bytes(d_v);
+  return VEA_OK;
+}
+
+int vea_sparse_mqa_fwd(const void* q, const void* kv_latent, const int32_t* topk_idx, int num_rows, int num_heads,
+                       int n_kv, int d_qk, int d_v, int k, float scale, void* out, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (n_kv < 0) return VEA_ESHAPE;
+  int st = sparse_shape_status(num_rows, num_heads, d_qk, d_v, k);
+  if (st != VEA_OK) return st;
+  if (!isfinite(scale)) return VEA_EINVAL;
   if (num_rows == 0) return VEA_OK;
   if (!q || !topk_idx || !out || (n_kv > 0 && !kv_latent)) return VEA_EINVAL;
   if (!aligned16(q) || !aligned16(out) || (kv_latent && !aligned16(kv_latent))) return VEA_EINVAL;
-  hipStream_t s = (hipStream_t)stream;
-  if (check_enabled()) {
-    std::vector<int32_t> h;
-    int st = fetch_ints(topk_idx, (size_t)num_rows * k, s, h);
-    if (st != VEA_OK) return st;
-    for (int32_t x : h)
-      if (x >= n_kv) return VEA_ERANGE;
-  }
+  if (workspace != nullptr && !aligned16(workspace)) return VEA_EWORKSPACE;
   SparseParams p;
   p.q = (const uint16_t*)q; p.kv = (const uint16_t*)kv_latent; p.idx = topk_idx; p.out = (uint16_t*)out;
   p.lse = lse; p.rows = num_rows; p.heads = num_heads; p.n_kv = n_kv; p.k = k;
   p.head_blocks = (num_heads + kSparseHeadsPerWG - 1) / kSparseHeadsPerWG;
   p.scale = scale;
-  if ((int64_t)num_rows * p.head_blocks > 0x7fffffff) return VEA_EUNSUPPORTED;
+  p.full_units = num_rows * p.head_blocks;
+  p.nsplit = 1;
+  p.ws = nullptr;
+  if (workspace != nullptr) {
+    int cus = 0;
+    st = current_cus(&cus);
+    if (st != VEA_OK) return st;
+    const SparseSplit plan = sparse_split_plan(p.full_units, k, cus);
+    if (plan.nsplit > 1) {
+      if (workspace_bytes < (size_t)plan.chunks * sparse_chunk_bytes(d_v)) return VEA_EWORKSPACE;
+      p.full_units = plan.full_units;
+      p.nsplit = plan.nsplit;
+      p.ws = (float*)workspace;
+    }
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if (check_enabled()) {
+    std::vector<int32_t> h;
+    st = fetch_ints(topk_idx, (size_t)num_rows * k, s, h);
+    if (st != VEA_OK) return st;
+    for (int32_t x : h)
+      if (x >= n_kv) return VEA_ERANGE;
+  }
   return finish(hip_status(launch_sparse_mqa(p, d_qk, d_v, s)), s);
 }
 

@@ -32,12 +32,20 @@
 //            16-column block and receives it transposed).
 // Entries < 0 or >= n_kv are skipped.  No atomics: every output element and
 // lse entry has one writer.
+//
+// Workgroups run one per CU, so rows x head blocks units fill whole rounds of
+// the chip plus a last, partial one.  With a workspace, each unit of that last
+// round is split into nsplit workgroups over consecutive ranges of its SORTED
+// tiles (so the split, like the sort, ignores the caller's order); each writes
+// its unnormalized O, reference max and sum, and a second kernel merges the
+// ranges in range order.
 #include "vea_internal.h"
 
 #include <float.h>
 #include <limits.h>
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 namespace vea {
@@ -182,8 +190,17 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
   __shared__ int sidx[MAXK];
   __shared__ int wsum[C::WAVES];
 
-  const int row = blockIdx.x / p.head_blocks;
-  const int hb = blockIdx.x - row * p.head_blocks;
+  // workgroup unit (row, head block) and, for a split unit, its chunk
+  int unit = blockIdx.x, chunk = 0;
+  const bool split = unit >= p.full_units;
+  if (split) {
+    const int u2 = unit - p.full_units;
+    const int tu = u2 / p.nsplit;
+    chunk = u2 - tu * p.nsplit;
+    unit = p.full_units + tu;
+  }
+  const int row = unit / p.head_blocks;
+  const int hb = unit - row * p.head_blocks;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar) value
@@ -266,7 +283,19 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
     }
     nvalid = lo;
   }
-  const int n_tiles = (nvalid + C::BN - 1) / C::BN;
+  // Tiles [t0, t0 + n_tiles) of the sorted list: all of them, or this
+  // chunk's share of a split unit.  The key loop sees the list from entry
+  // t0 BN on (srow) and the valid count from there (nloc).
+  nvalid = __builtin_amdgcn_readfirstlane(nvalid);
+  const int n_all = (nvalid + C::BN - 1) / C::BN;
+  int t0 = 0, n_tiles = n_all;
+  if (split) {
+    t0 = (n_all * chunk) / p.nsplit;
+    n_tiles = (n_all * (chunk + 1)) / p.nsplit - t0;
+  }
+  const int nloc = nvalid - t0 * C::BN;
+  const int* srow = sidx + t0 * C::BN;
+  const int slim = MAXK - 1 - t0 * C::BN;               // last entry of sidx, from srow
 
   // ---- Q^T fragment (B operand of S^T = K Q^T): head l32 of this wave,
   // dims 16 ks + 8 g2 .. +7
@@ -316,7 +345,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
     const uint32_t dst = ring_lds + (uint32_t)((kt % C::NSTAGE) * C::TILE);
     int x[C::BPW];                                      // all index reads first: one LDS wait
 #pragma unroll
-    for (int bi = 0; bi < C::BPW; ++bi) x[bi] = sidx[min(kt * C::BN + (g_rc[bi] >> 16), MAXK - 1)];
+    for (int bi = 0; bi < C::BPW; ++bi) x[bi] = srow[min(kt * C::BN + (g_rc[bi] >> 16), slim)];
 #pragma unroll
     for (int bi = 0; bi < C::BPW; ++bi) asm volatile("" : "+v"(x[bi]));   // keep the reads unconditional
 #pragma unroll
@@ -324,7 +353,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
       const int j = kt * C::BN + (g_rc[bi] >> 16);
       const uint32_t off = __umul24((uint32_t)x[bi], (uint32_t)C::ROWB) + (uint32_t)(g_rc[bi] & 0xFFFF);
       dma16(kv_rsrc, __builtin_amdgcn_readfirstlane(dst + (uint32_t)((bi * C::WAVES + wave) * 1024)),
-            j < nvalid ? off : 0xFFFFFFF0u);              // past the end: zeros
+            j < nloc ? off : 0xFFFFFFF0u);                // past the end: zeros
     }
   };
 
@@ -355,10 +384,10 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
   float l_run = 0.f;         // this lane's partial sum of P
 
   auto mask_tail = [&](int kt, floatx16& s) {
-    if ((kt + 1) * C::BN > nvalid) {
+    if ((kt + 1) * C::BN > nloc) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (kt * C::BN + 8 * (r >> 2) + 4 * g2 + (r & 3) >= nvalid) s[r] = -INFINITY;
+        if (kt * C::BN + 8 * (r >> 2) + 4 * g2 + (r & 3) >= nloc) s[r] = -INFINITY;
     }
   };
   // ---- one step of the key loop, as an explicitly scheduled sequence of
@@ -566,29 +595,136 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_tot), __float_as_uint(l_tot), false, false);
     l_tot = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   }
+  if (split) {
+    // partial result of this key range: unnormalized O^T, reference max m
+    // (log2 domain) and sum l, per head of the workgroup
+    float* w = p.ws + (size_t)(blockIdx.x - p.full_units) * (C::HEADS * (DV + 2));
+    const int hl = wave * C::HPW + l32;                 // head within the workgroup
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) {
+      // a fresh AGPR value per tile, so the reads stay in this branch and
+      // in tile order (hoisted above it they would need 256 VGPRs at once)
+      asm volatile("" : "+a"(o[nt]));
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *(floatx4*)(w + hl * DV + 32 * nt + 8 * r4 + 4 * g2) =
+            (floatx4){o[nt][4 * r4], o[nt][4 * r4 + 1], o[nt][4 * r4 + 2], o[nt][4 * r4 + 3]};
+    }
+    if (g2 == 0) {
+      w[C::HEADS * DV + hl] = m_used;
+      w[C::HEADS * DV + C::HEADS + hl] = l_tot;
+    }
+    return;
+  }
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (hvalid) {
     uint16_t* dst = p.out + ((int64_t)row * p.heads + head) * DV + 4 * g2;
 #pragma unroll
-    for (int nt = 0; nt < C::NT; ++nt)
+    for (int nt = 0; nt < C::NT; ++nt) {
+      asm volatile("" : "+a"(o[nt]));                  // as in the split branch
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4)
         *(u32x2*)(dst + 32 * nt + 8 * r4) = (u32x2){pack_bf16x2(o[nt][4 * r4] * inv, o[nt][4 * r4 + 1] * inv),
                                                     pack_bf16x2(o[nt][4 * r4 + 2] * inv, o[nt][4 * r4 + 3] * inv)};
+    }
     if (p.lse != nullptr && g2 == 0)
       p.lse[(int64_t)head * p.rows + row] = l_tot > 0.f ? (m_used + log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
+// Merge of the split chunks of one workgroup unit, in chunk order (fixed, so
+// the result is deterministic): with M = max_i m_i,
+//   O = sum_i 2^(m_i - M) O_i,  l = sum_i 2^(m_i - M) l_i,
+//   out = O / l (bf16),  lse = ln 2 (M + log2 l),
+// the blockwise merge of eq. (1)(2) (page above, section 进一步探索) with the
+// O update written out.  Workgroup (tail unit, group of HPG heads); one
+// thread per (head, 16-column slice).  Empty chunks carry m = -inf, l = 0.
+template <int DV, int HEADS, int HPG>
+__global__ __launch_bounds__(256) void sparse_merge_kernel(SparseParams p) {
+  const int tu = blockIdx.x;                            // tail unit
+  const int unit = p.full_units + tu;
+  const int row = unit / p.head_blocks;
+  const int hb = unit - row * p.head_blocks;
+  constexpr size_t CF = (size_t)HEADS * (DV + 2);       // floats per chunk
+  constexpr int SLICES = DV / 16;
+  static_assert(HPG * SLICES == 256, "one item per thread");
+  const float* base = p.ws + (size_t)tu * p.nsplit * CF;
+  const int hl = blockIdx.y * HPG + threadIdx.x / SLICES;
+  const int sc = threadIdx.x % SLICES;
+  const int head = hb * HEADS + hl;
+  if (head >= p.heads) return;
+  float mmax = -INFINITY;
+  for (int i = 0; i < p.nsplit; ++i) mmax = fmaxf(mmax, base[i * CF + HEADS * DV + hl]);
+  float acc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+  float l = 0.f;
+  if (mmax != -INFINITY) {
+    for (int i = 0; i < p.nsplit; ++i) {
+      const float* c = base + i * CF;
+      const float mi = c[HEADS * DV + hl];
+      if (mi == -INFINITY) continue;                    // empty chunk
+      const float f = fast_exp2(mi - mmax);
+      l = fmaf(f, c[HEADS * DV + HEADS + hl], l);
+      const floatx4* src = (const floatx4*)(c + hl * DV + 16 * sc);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const floatx4 v = src[q4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[4 * q4 + j] = fmaf(f, v[j], acc[4 * q4 + j]);
+      }
+    }
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  u32x4 w[2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w[j >> 2][j & 3] = pack_bf16x2(acc[2 * j] * inv, acc[2 * j + 1] * inv);
+  uint16_t* dst = p.out + ((int64_t)row * p.heads + head) * DV + 16 * sc;
+  *(u32x4*)dst = w[0];
+  *(u32x4*)(dst + 8) = w[1];
+  if (sc == 0 && p.lse != nullptr)
+    p.lse[(int64_t)head * p.rows + row] = l > 0.f ? (mmax + log2f(l)) * kLn2 : -INFINITY;
+}
+
 }  // namespace
+
+SparseSplit sparse_split_plan(int units, int k, int cus) {
+  // Units are dispatched in order, one workgroup per CU: the last round holds
+  // units % cus of them and would leave the other CUs idle for a whole row's
+  // time.  Each unit of that round is split into as many key ranges as the
+  // idle CUs allow (at most 8, and at most one range per 32-index tile; a
+  // split below 2 is not worth the merge).
+  SparseSplit s{units, 1, 0};
+  if (cus <= 0 || units <= 0) return s;
+  const int tail = units % cus;
+  if (tail == 0) return s;
+  const int nsplit = std::min(std::min(8, cus / tail), (k + 31) / 32);
+  if (nsplit < 2) return s;
+  s.full_units = units - tail;
+  s.nsplit = nsplit;
+  s.chunks = tail * nsplit;
+  return s;
+}
+
+size_t sparse_chunk_bytes(int d_v) { return (size_t)kSparseHeadsPerWG * (d_v + 2) * sizeof(float); }
 
 hipError_t launch_sparse_mqa(const SparseParams& p, int d_qk, int d_v, hipStream_t s) {
   if (d_qk != 576 || d_v != 512) return hipErrorInvalidValue;
   if (p.k > 4096) return hipErrorInvalidValue;
   if (p.rows == 0) return hipSuccess;
-  const dim3 grid(p.rows * p.head_blocks), block(256);
+  const int units = p.rows * p.head_blocks;
+  if (p.nsplit > 1 ? (p.ws == nullptr || p.full_units < 0 || p.full_units >= units) : p.full_units != units)
+    return hipErrorInvalidValue;
+  const int tail = units - p.full_units;
+  const dim3 grid(p.full_units + tail * p.nsplit), block(256);
   if (p.k <= 2048) hipLaunchKernelGGL((sparse_mqa_kernel<576, 512, 2048>), grid, block, 0, s, p);
   else hipLaunchKernelGGL((sparse_mqa_kernel<576, 512, 4096>), grid, block, 0, s, p);
+  if (tail > 0 && p.nsplit > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((sparse_merge_kernel<512, kSparseHeadsPerWG, 8>), dim3(tail, kSparseHeadsPerWG / 8),
+                       dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -56,7 +56,23 @@ struct SparseParams {
   int rows, heads, n_kv, k;
   int head_blocks;           // ceil(heads / heads per workgroup)
   float scale;
+  // Key-range split of the workgroup units of the last, partial round:
+  // units [0, full_units) (unit = row * head_blocks + head block) run whole;
+  // each later unit is split into nsplit workgroups over consecutive ranges
+  // of its sorted tiles, which write partial (O, m, l) to ws, merged after.
+  int full_units;
+  int nsplit;                // 1: no split
+  float* ws;                 // nullable when nsplit == 1
 };
+
+// Split plan of the sparse kernel for `units` workgroup units of k indices
+// each, on a device with `cus` compute units (one workgroup per CU at a time).
+struct SparseSplit {
+  int full_units, nsplit, chunks;   // chunks = (units - full_units) * nsplit, 0 without a split
+};
+SparseSplit sparse_split_plan(int units, int k, int cus);
+// Bytes of workspace per split chunk: HEADS x (d_v + 2) floats.
+size_t sparse_chunk_bytes(int d_v);
 
 struct ProbsParams {
   const void* q;

@@ -111,19 +111,27 @@ class SparseStaged:
     idx: "torch.Tensor"
     out: "torch.Tensor"
     lse: "torch.Tensor"
+    ws: Optional["torch.Tensor"]       # split workspace, None: every row alone
 
 
-def stage_sparse(case: SparseCase, device="cuda", idx: Optional[np.ndarray] = None) -> SparseStaged:
+def stage_sparse(case: SparseCase, device="cuda", idx: Optional[np.ndarray] = None,
+                 split: bool = True) -> SparseStaged:
     torch = _torch()
     q = bits_to_tensor(case.q, device)
     kv = bits_to_tensor(case.kv_latent, device)
     ix = _dev_i32(case.topk_idx if idx is None else idx, device)
     out = torch.empty((case.num_rows, case.num_heads, case.d_v), dtype=torch.bfloat16, device=device)
     lse = torch.empty((case.num_heads, case.num_rows), dtype=torch.float32, device=device)
-    return SparseStaged(case, q, kv, ix, out, lse)
+    ws = None
+    if split:
+        with torch.cuda.device(q.device):
+            n = B.sparse_mqa_workspace_size(case.num_rows, case.num_heads, case.d_qk, case.d_v, ix.shape[1])
+        if n:
+            ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+    return SparseStaged(case, q, kv, ix, out, lse, ws)
 
 
 def run_sparse(st: SparseStaged):
     c = st.case
-    B.sparse_mqa_fwd(st.q, st.kv, st.idx, st.idx.shape[1], c.scale, st.out, st.lse)
+    B.sparse_mqa_fwd(st.q, st.kv, st.idx, st.idx.shape[1], c.scale, st.out, st.lse, workspace=st.ws)
     return st.out, st.lse
