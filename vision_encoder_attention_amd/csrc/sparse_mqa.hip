@@ -207,10 +207,35 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
   const int l32 = lane & 31;
   const int g2 = lane >> 5;                             // which half of the wave
 
+  // ---- loads issued up front, so their latency runs under the sort: this
+  // thread's share of the row's indices (entries tid + THREADS j; entries
+  // past k are excluded where they are used), then the Q^T fragment (B
+  // operand of S^T = K Q^T): head l32 of this wave, dims 16 ks + 8 g2 .. +7.
+  // Addresses are clamped so every load is unconditional (the compiler can
+  // then wait for the index loads alone), and the sort's barriers wait for
+  // LDS only.
+  const int32_t* irow = p.idx + (int64_t)row * p.k;
+  constexpr int IPT = MAXK / C::THREADS;
+  int xi[IPT];
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) xi[j] = irow[min(tid + C::THREADS * j, p.k - 1)];
+  asm volatile("" ::: "memory");                        // index loads first
+  const int head0 = hb * C::HEADS + wave * C::HPW;      // wave-uniform
+  const bool active = head0 < p.heads;                  // wave has at least one head
+  const int head = head0 + l32;
+  const bool hvalid = head < p.heads;
+  u32x4 qf[C::KSTEPS];
+  {
+    const uint16_t* src = p.q + ((int64_t)row * p.heads + (hvalid ? head : 0)) * DQK + 8 * g2;
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) qf[ks] = *(const u32x4*)(src + 16 * ks);
+  }
+  auto lds_barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+  const float c = fmaxf(fabsf(p.scale) * kLog2e, FLT_MIN);   // scale 0: logits ~0, masked ones stay -inf
+
   // ---- canonical order: the row's valid indices in ascending order (with
   // their multiplicity) in sidx[0, nvalid).
   int nvalid;
-  const int32_t* irow = p.idx + (int64_t)row * p.k;
   if (p.n_kv <= C::NSTAGE * C::TILE / 2) {
     // Counting sort in the stage ring (idle until the key loop): a 16-bit
     // count per latent row (two per word; k <= 4096 cannot overflow one),
@@ -220,12 +245,14 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
     uint32_t* cnt = (uint32_t*)ring;
     const int nw = (p.n_kv + 1) >> 1;
     for (int i = tid; i < nw; i += C::THREADS) cnt[i] = 0u;
-    __syncthreads();
-    for (int i = tid; i < p.k; i += C::THREADS) {
-      const int x = irow[i];
-      if (x >= 0 && x < p.n_kv) atomicAdd(&cnt[x >> 1], 1u << (16 * (x & 1)));   // padding / out of range: skipped
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      const int x = xi[j];
+      if (tid + C::THREADS * j < p.k && x >= 0 && x < p.n_kv)   // padding / out of range: skipped
+        atomicAdd(&cnt[x >> 1], 1u << (16 * (x & 1)));
     }
-    __syncthreads();
+    lds_barrier();
     auto count = [&](int v) -> int { return (int)((cnt[v >> 1] >> (16 * (v & 1))) & 0xFFFFu); };
     const int per = (p.n_kv + C::THREADS - 1) / C::THREADS;
     const int v0 = min(tid * per, p.n_kv), v1 = min(v0 + per, p.n_kv);
@@ -238,7 +265,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
       if (lane >= d) incl += y;
     }
     if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
+    lds_barrier();
     int base = incl - tot;
     nvalid = 0;
 #pragma unroll
@@ -248,21 +275,19 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
     }
     for (int v = v0; v < v1; ++v)
       for (int c = count(v); c > 0; --c) sidx[base++] = v;
-    __syncthreads();
+    lds_barrier();
   } else {
     // Bitonic sorting network in LDS; padding and out-of-range entries become
     // INT_MAX and sort to the end.
     int n2 = 1;
     while (n2 < p.k) n2 <<= 1;
-    for (int i = tid; i < n2; i += C::THREADS) {
-      int v = INT_MAX;
-      if (i < p.k) {
-        const int x = irow[i];
-        v = (x >= 0 && x < p.n_kv) ? x : INT_MAX;
-      }
-      sidx[i] = v;
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      const int i = tid + C::THREADS * j;
+      const int x = xi[j];
+      if (i < n2) sidx[i] = (i < p.k && x >= 0 && x < p.n_kv) ? x : INT_MAX;
     }
-    __syncthreads();
+    lds_barrier();
     for (int size = 2; size <= n2; size <<= 1) {
       for (int stride = size >> 1; stride > 0; stride >>= 1) {
         for (int t = tid; t < (n2 >> 1); t += C::THREADS) {
@@ -272,7 +297,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
           const int a = sidx[i], b = sidx[j];
           if ((a > b) == up) { sidx[i] = b; sidx[j] = a; }
         }
-        __syncthreads();
+        lds_barrier();
       }
     }
     // number of valid entries: first position holding INT_MAX (binary search)
@@ -297,32 +322,6 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
   const int* srow = sidx + t0 * C::BN;
   const int slim = MAXK - 1 - t0 * C::BN;               // last entry of sidx, from srow
 
-  // ---- Q^T fragment (B operand of S^T = K Q^T): head l32 of this wave,
-  // dims 16 ks + 8 g2 .. +7
-  const int head0 = hb * C::HEADS + wave * C::HPW;      // wave-uniform
-  const bool active = head0 < p.heads;                  // wave has at least one head
-  const int head = head0 + l32;
-  const bool hvalid = head < p.heads;
-  u32x4 qf[C::KSTEPS];
-  {
-    const uint16_t* src = p.q + ((int64_t)row * p.heads + (hvalid ? head : 0)) * DQK + 8 * g2;
-#pragma unroll
-    for (int ks = 0; ks < C::KSTEPS; ++ks) {
-      const u32x4 v = *(const u32x4*)(src + 16 * ks);
-      qf[ks] = hvalid ? v : (u32x4){0u, 0u, 0u, 0u};
-    }
-  }
-  float c = fabsf(p.scale) * kLog2e;
-  if (p.scale < 0.f) {
-#pragma unroll
-    for (int ks = 0; ks < C::KSTEPS; ++ks) qf[ks] ^= (u32x4){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
-  }
-  c = fmaxf(c, FLT_MIN);
-  // Retire the Q loads here: otherwise the compiler waits for them (vmcnt(0),
-  // which would also drain the in-flight tile DMAs) at their first use inside
-  // the key loop, on every iteration.
-#pragma unroll
-  for (int ks = 0; ks < C::KSTEPS; ++ks) asm volatile("" : "+v"(qf[ks]));
 
   // ---- gather by DMA: 1 KB block bk of a tile is filled by wave bk % WAVES;
   // slot sl of the tile holds row sl / CPR, physical chunk sl % CPR =
@@ -555,9 +554,27 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
   };
   auto stage_ptr = [&](int t) -> const unsigned char* { return ring + (t % C::NSTAGE) * C::TILE; };
 
+  // first tiles in flight before the wait for Q
   if (n_tiles > 0) {
     gather(0);
     if (C::DIST == 2 && 1 < n_tiles) gather(1);
+  }
+  // Q of heads past the count is zero; a negative scale negates Q (exact
+  // sign-bit flip) so the exponent scale is positive.
+#pragma unroll
+  for (int ks = 0; ks < C::KSTEPS; ++ks)
+    if (!hvalid) qf[ks] = (u32x4){0u, 0u, 0u, 0u};
+  if (p.scale < 0.f) {
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) qf[ks] ^= (u32x4){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+  }
+  // Retire the Q loads here: otherwise the compiler waits for them (vmcnt(0),
+  // which would also drain the in-flight tile DMAs) at their first use inside
+  // the key loop, on every iteration.
+#pragma unroll
+  for (int ks = 0; ks < C::KSTEPS; ++ks) asm volatile("" : "+v"(qf[ks]));
+
+  if (n_tiles > 0) {
     u32x4 pb[2];                                        // packed P of the previous tile
     // step 0: QK^T and softmax of tile 0
     wait_tile(0);
@@ -595,40 +612,83 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_tot), __float_as_uint(l_tot), false, false);
     l_tot = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   }
+  // The result goes out through LDS: each wave stages SROWS of its 32 rows
+  // (heads, 1 KB each) at a time in its own part of the ring, 16-byte chunk
+  // c of staged row r at chunk c ^ (r % 16), then writes whole 1 KB rows
+  // with one 16-byte store per lane, rather than 32 scattered 8-byte pieces
+  // per store.  All waves must be done with the ring first.
+  constexpr int SROWS = C::NSTAGE * C::TILE / C::WAVES >= 32 * 1024 ? 32 : 16;
+  static_assert(C::WAVES * SROWS * 1024 <= C::NSTAGE * C::TILE, "staging fits the ring");
+  lds_barrier();
+  // lane values for the epilogue, opaque to the compiler so that nothing
+  // derived from them is computed before the key loop and kept live over it
+  int lane_e = lane;
+  asm volatile("" : "+v"(lane_e));
+  const int l32e = lane_e & 31, g2e = lane_e >> 5;
+  unsigned char* stg = ring + wave * SROWS * 1024;
+  const int sr = l32e % SROWS;                           // this lane's staged row, in its pass
+  const int hsw = sr & 15;
+  const int hl0 = wave * C::HPW;                        // first head of this wave within the workgroup
   if (split) {
-    // partial result of this key range: unnormalized O^T, reference max m
-    // (log2 domain) and sum l, per head of the workgroup
+    // partial result of this key range: unnormalized O^T in fp32 (a row is
+    // two 1 KB halves, staged one half at a time), reference max m (log2
+    // domain) and sum l, per head of the workgroup
     float* w = p.ws + (size_t)(blockIdx.x - p.full_units) * (C::HEADS * (DV + 2));
-    const int hl = wave * C::HPW + l32;                 // head within the workgroup
 #pragma unroll
-    for (int nt = 0; nt < C::NT; ++nt) {
-      // a fresh AGPR value per tile, so the reads stay in this branch and
-      // in tile order (hoisted above it they would need 256 VGPRs at once)
-      asm volatile("" : "+a"(o[nt]));
+    for (int half = 0; half < 2; ++half) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4)
-        *(floatx4*)(w + hl * DV + 32 * nt + 8 * r4 + 4 * g2) =
-            (floatx4){o[nt][4 * r4], o[nt][4 * r4 + 1], o[nt][4 * r4 + 2], o[nt][4 * r4 + 3]};
+      for (int ps = 0; ps < C::HPW / SROWS; ++ps) {
+        if (l32e / SROWS == ps) {
+#pragma unroll
+          for (int nt = 8 * half; nt < 8 * half + 8; ++nt) {
+            // a fresh AGPR value per tile, so the reads stay in this branch
+            // and in tile order (hoisted they would need 256 VGPRs at once)
+            asm volatile("" : "+a"(o[nt]));
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const int ch = 8 * (nt - 8 * half) + 2 * r4 + g2e;   // 16-byte chunk of the half-row
+              *(floatx4*)(stg + sr * 1024 + 16 * (ch ^ hsw)) =
+                  (floatx4){o[nt][4 * r4], o[nt][4 * r4 + 1], o[nt][4 * r4 + 2], o[nt][4 * r4 + 3]};
+            }
+          }
+        }
+#pragma unroll 4
+        for (int h = 0; h < SROWS; ++h) {
+          const floatx4 v = *(const floatx4*)(stg + h * 1024 + 16 * (lane_e ^ (h & 15)));
+          *(floatx4*)(w + (hl0 + ps * SROWS + h) * DV + 256 * half + 4 * lane_e) = v;
+        }
+      }
     }
-    if (g2 == 0) {
-      w[C::HEADS * DV + hl] = m_used;
-      w[C::HEADS * DV + C::HEADS + hl] = l_tot;
+    if (g2e == 0) {
+      w[C::HEADS * DV + hl0 + l32e] = m_used;
+      w[C::HEADS * DV + C::HEADS + hl0 + l32e] = l_tot;
     }
     return;
   }
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (hvalid) {
-    uint16_t* dst = p.out + ((int64_t)row * p.heads + head) * DV + 4 * g2;
+  uint16_t* dst = p.out + ((int64_t)row * p.heads + head0) * DV + 8 * lane_e;
+  const int nrows = min(C::HPW, p.heads - head0);       // rows of this wave that exist
 #pragma unroll
-    for (int nt = 0; nt < C::NT; ++nt) {
-      asm volatile("" : "+a"(o[nt]));                  // as in the split branch
+  for (int ps = 0; ps < C::HPW / SROWS; ++ps) {
+    if (l32e / SROWS == ps) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4)
-        *(u32x2*)(dst + 32 * nt + 8 * r4) = (u32x2){pack_bf16x2(o[nt][4 * r4] * inv, o[nt][4 * r4 + 1] * inv),
-                                                    pack_bf16x2(o[nt][4 * r4 + 2] * inv, o[nt][4 * r4 + 3] * inv)};
+      for (int nt = 0; nt < C::NT; ++nt) {
+        asm volatile("" : "+a"(o[nt]));                // as in the split branch
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *(u32x2*)(stg + sr * 1024 + 16 * ((4 * nt + r4) ^ hsw) + 8 * g2e) =
+              (u32x2){pack_bf16x2(o[nt][4 * r4] * inv, o[nt][4 * r4 + 1] * inv),
+                      pack_bf16x2(o[nt][4 * r4 + 2] * inv, o[nt][4 * r4 + 3] * inv)};
+      }
     }
-    if (p.lse != nullptr && g2 == 0)
-      p.lse[(int64_t)head * p.rows + row] = l_tot > 0.f ? (m_used + log2f(l_tot)) * kLn2 : -INFINITY;
+    const int hn = min(SROWS, nrows - ps * SROWS);
+#pragma unroll 4
+    for (int h = 0; h < hn; ++h)
+      *(u32x4*)(dst + (ps * SROWS + h) * DV) = *(const u32x4*)(stg + h * 1024 + 16 * (lane_e ^ (h & 15)));
+  }
+  if (head0 + l32e < p.heads) {
+    if (p.lse != nullptr && g2e == 0)
+      p.lse[(int64_t)(head0 + l32e) * p.rows + row] = l_tot > 0.f ? (m_used + log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
