@@ -92,9 +92,24 @@ const char* vea_version(void);
  *   scale          finite float (any sign, 0 allowed).
  *   piece_rows     query rows per piece (qb); 0 = one piece per sequence.
  *                  Pieces are [p*qb, (p+1)*qb) within each sequence; no tile
- *                  straddles a piece and the result does not depend on qb.
+ *                  straddles a piece.  Without a workspace the result is
+ *                  bitwise independent of qb; with one, qb changes which rows
+ *                  are split (below) and so their rounding.
  *   out            [total_q, num_heads_q, head_dim] of dtype, stride out_tok_stride.
  *   lse            float [num_heads_q, total_q] or NULL (not written).
+ *   workspace      NULL (workspace_bytes ignored), or device memory of at
+ *                  least vea_attn_fwd_workspace_size bytes for the same sizes
+ *                  on the current device, 16-byte aligned; else
+ *                  VEA_EWORKSPACE.  Contents need no initialisation and are
+ *                  garbage afterwards.  It is used for bf16, batch 1,
+ *                  non-causal calls (one image): the query tiles of the last,
+ *                  partial round of workgroups over the device are split into
+ *                  key ranges that run on otherwise idle CUs and are merged in
+ *                  range order with the same merge.  The rounding of those
+ *                  rows then depends on the sizes and the CU count; without a
+ *                  workspace a row's bits depend only on its sequence.  Both
+ *                  are deterministic.  Calls that share a workspace must be
+ *                  ordered (same stream).
  */
 int vea_attn_fwd(int dtype,
                  const void* q, int64_t q_tok_stride,
@@ -105,7 +120,16 @@ int vea_attn_fwd(int dtype,
                  int num_heads_q, int num_heads_kv, int head_dim,
                  int causal, float scale, int piece_rows,
                  void* out, int64_t out_tok_stride, float* lse,
-                 void* stream);
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * vea_attn_fwd_workspace_size — bytes of workspace vea_attn_fwd uses for these
+ * sizes on the current HIP device (0 when it splits nothing).  Validates the
+ * shape arguments like vea_attn_fwd; VEA_EHIP if the device cannot be queried.
+ */
+int vea_attn_fwd_workspace_size(int dtype, int batch, int total_q, int total_k, int max_seqlen_q,
+                                int max_seqlen_k, int num_heads_q, int num_heads_kv, int head_dim,
+                                int causal, int piece_rows, size_t* bytes);
 
 /*
  * vea_qkv_rope — split a fused QKV projection output and apply rotary position

@@ -31,7 +31,8 @@ def lib():
 
 def test_header_declares_the_operations():
     names = _declared()
-    for n in ("vea_attn_fwd", "vea_qkv_rope", "vea_sparse_mqa_fwd", "vea_sparse_mqa_workspace_size",
+    for n in ("vea_attn_fwd", "vea_attn_fwd_workspace_size", "vea_qkv_rope", "vea_sparse_mqa_fwd",
+              "vea_sparse_mqa_workspace_size",
               "vea_attn_probs_piece", "vea_status_str"):
         assert n in names
 
@@ -56,11 +57,12 @@ FAKE = 0x10000   # 16-byte aligned, never dereferenced: every call below fails v
 
 def _attn(lib, **kw):
     a = dict(dtype=1, q=FAKE, qs=128, k=FAKE, ks=128, v=FAKE, vs=128, cuq=FAKE, cuk=FAKE, batch=1, tq=10, tk=10,
-             mq=10, mk=10, hq=2, hkv=2, d=64, causal=0, scale=0.125, qb=0, out=FAKE, os=128, lse=None)
+             mq=10, mk=10, hq=2, hkv=2, d=64, causal=0, scale=0.125, qb=0, out=FAKE, os=128, lse=None, ws=None,
+             wsb=0)
     a.update(kw)
     return lib.vea_attn_fwd(a["dtype"], a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["cuq"], a["cuk"],
                             a["batch"], a["tq"], a["tk"], a["mq"], a["mk"], a["hq"], a["hkv"], a["d"],
-                            a["causal"], a["scale"], a["qb"], a["out"], a["os"], a["lse"], None)
+                            a["causal"], a["scale"], a["qb"], a["out"], a["os"], a["lse"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -82,9 +84,28 @@ def _attn(lib, **kw):
     (dict(mq=11), VEA_ESHAPE),           # longer than total
     (dict(batch=0), VEA_OK),             # nothing to do, nothing launched
     (dict(tq=0, mq=0), VEA_OK),
+    (dict(ws=FAKE + 8, wsb=1 << 20), VEA_EWORKSPACE),   # misaligned workspace
 ])
 def test_attn_fwd_validation(lib, kw, status):
     assert _attn(lib, **kw) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((7, 1, 10, 10, 10, 10, 2, 2, 64, 0, 0), VEA_EDTYPE),
+    ((1, 1, 10, 10, 10, 10, 3, 2, 64, 0, 0), VEA_ESHAPE),
+    ((1, 1, 10, 10, 10, 10, 2, 2, 96, 0, 0), VEA_EUNSUPPORTED),
+    ((1, 1, 10, 10, 11, 10, 2, 2, 64, 0, 0), VEA_ESHAPE),
+    ((1, 1, 10, 10, 10, 10, 2, 2, 64, 2, 0), VEA_EINVAL),
+    ((1, 0, 0, 0, 0, 0, 2, 2, 64, 0, 0), VEA_OK),
+    ((1, 2, 10, 10, 5, 5, 2, 2, 64, 0, 0), VEA_OK),       # batch > 1: never split, no device query
+    ((1, 1, 10, 10, 10, 10, 2, 2, 64, 1, 0), VEA_OK),     # causal: never split
+    ((0, 1, 10, 10, 10, 10, 2, 2, 64, 0, 0), VEA_OK),     # fp32: never split
+])
+def test_attn_fwd_workspace_size_validation(lib, args, status):
+    n = ctypes.c_size_t(12345)
+    assert lib.vea_attn_fwd_workspace_size(*args, ctypes.byref(n)) == status
+    assert n.value == 0
+    assert lib.vea_attn_fwd_workspace_size(*args, None) == VEA_EINVAL
 
 
 def _rope(lib, **kw):

@@ -118,10 +118,12 @@ def test_edge_cases(torch, i):
 # --------------------------------------------- invariances and determinism
 
 def test_piece_rows_do_not_change_results(torch):
-    """O and lse are bitwise identical for every piece size (the piece is a
-    scheduling unit only)."""
+    """Without a workspace O and lse are bitwise identical for every piece
+    size (the piece is a scheduling unit only).  With one, small pieces make
+    enough workgroups for the last round to be split, and those rows differ
+    only by the merge's rounding."""
     case = W.small_cases()[1]            # 667-token vision case
-    st = R.stage_dense(case)
+    st = R.stage_dense(case, split=False)
     R.run_dense(st, piece_rows=0)
     torch.cuda.synchronize()
     ref_o, ref_l = st.out.clone(), st.lse.clone()
@@ -130,6 +132,14 @@ def test_piece_rows_do_not_change_results(torch):
         torch.cuda.synchronize()
         assert torch.equal(st.out, ref_o), qb
         assert torch.equal(st.lse, ref_l), qb
+    sp = R.stage_dense(case)
+    R.run_rope(sp)
+    for qb in (1, 7):
+        R.run_attn(sp, piece_rows=qb)
+        torch.cuda.synchronize()
+        assert_bf16_close(_f64(sp.out, "bf16"), _f64(ref_o, "bf16"), "split, piece_rows=%d" % qb)
+        assert_bf16_close(sp.lse.cpu().numpy().astype(np.float64), ref_l.cpu().numpy().astype(np.float64),
+                          "lse split, piece_rows=%d" % qb)
 
 
 def test_packing_does_not_change_results(torch):
@@ -247,3 +257,62 @@ def test_full_size_sampled(torch, name):
     torch.cuda.synchronize()
     assert torch.equal(st.out, o0) and torch.equal(st.lse, l0)
     assert bool(torch.isfinite(st.out.float()).all())
+
+
+# ------------------------- split of the last round of workgroups (workspace)
+
+def _round_boundary_case(torch, d, per_cu, seed):
+    """One non-causal image whose 16-head tile count exceeds one round of
+    workgroups (CUs x per_cu) by 16: the last 16 units are split 8 ways."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles = (cus * per_cu) // 16 + 1
+    n = tiles * 128
+    return W.vision(grid_rows=n // 64, grid_cols=64, heads=16, d=d, piece_rows=n, seed=seed)
+
+
+@pytest.mark.parametrize("d,per_cu", [(64, 3), (128, 2)])
+def test_split_at_a_round_boundary(torch, d, per_cu):
+    """The split rows (the first query tile of every head, cut into 8 key
+    ranges and merged) and rows of whole units, against the oracle; repeated
+    runs bitwise equal."""
+    case = _round_boundary_case(torch, d, per_cu, seed=700 + d)
+    rows = np.unique(np.concatenate([np.arange(0, 128, 9), [127, 128, 129, 255, 4000 % case.total_q,
+                                                              case.total_q - 1]]))
+    st = _check_case(torch, case, rows=rows)
+    assert st.ws is not None and st.ws.numel() > 0
+    o0, l0 = st.out.clone(), st.lse.clone()
+    R.run_attn(st)
+    torch.cuda.synchronize()
+    assert torch.equal(st.out, o0) and torch.equal(st.lse, l0)
+
+
+def test_split_matches_unsplit_within_rounding(torch):
+    """On the vision workload the split rows differ from whole rows only by
+    the rounding of the merge; rows of whole units are bitwise equal."""
+    case = W.full_case("vision")
+    a = R.stage_dense(case)
+    b = R.stage_dense(case, split=False)
+    assert a.ws is not None and b.ws is None
+    R.run_dense(a)
+    R.run_dense(b)
+    torch.cuda.synchronize()
+    ao, bo = _f64(a.out, "bf16"), _f64(b.out, "bf16")
+    assert_bf16_close(ao, bo, "split vs unsplit")
+    assert_bf16_close(a.lse.cpu().numpy().astype(np.float64), b.lse.cpu().numpy().astype(np.float64),
+                      "lse split vs unsplit")
+    # the last piece's tiles run whole in both launches
+    last = slice(5 * case.piece_rows, case.total_q)
+    assert torch.equal(a.out[last], b.out[last]) and torch.equal(a.lse[:, last], b.lse[:, last])
+
+
+def test_attn_workspace_too_small_is_rejected(torch):
+    import vision_encoder_attention_amd as vea
+    case = _round_boundary_case(torch, 64, 3, seed=710)
+    st = R.stage_dense(case)
+    R.run_rope(st)
+    need = st.ws.numel()
+    small = torch.empty(need - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(vea.VeaError) as e:
+        vea.attn_fwd(st.q, st.k, st.v, st.cu_q, st.cu_k, False, case.scale, st.out, st.lse,
+                     piece_rows=case.piece_rows, max_seqlen_q=st.max_q, max_seqlen_k=st.max_k, workspace=small)
+    assert e.value.status == -6

@@ -48,8 +48,10 @@ def load_library():
         lib.vea_version.argtypes = []
         lib.vea_version.restype = ctypes.c_char_p
         lib.vea_attn_fwd.argtypes = [i32, vp, i64, vp, i64, vp, i64, vp, vp, i32, i32, i32, i32, i32,
-                                     i32, i32, i32, i32, f32, i32, vp, i64, vp, vp]
+                                     i32, i32, i32, i32, f32, i32, vp, i64, vp, vp, ctypes.c_size_t, vp]
         lib.vea_attn_fwd.restype = i32
+        lib.vea_attn_fwd_workspace_size.argtypes = [i32] * 11 + [ctypes.POINTER(ctypes.c_size_t)]
+        lib.vea_attn_fwd_workspace_size.restype = i32
         lib.vea_qkv_rope.argtypes = [vp, i64, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp]
         lib.vea_qkv_rope.restype = i32
         lib.vea_sparse_mqa_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp,
@@ -117,13 +119,28 @@ def _int32_dev(t, name):
         raise ValueError("%s must be a contiguous int32 GPU tensor" % name)
 
 
+def attn_fwd_workspace_size(dtype_code, batch, total_q, total_k, max_seqlen_q, max_seqlen_k, heads_q, heads_kv,
+                            head_dim, causal, piece_rows=0) -> int:
+    """Workspace bytes vea_attn_fwd uses for these sizes on the current device
+    (0: no split)."""
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    _check(lib.vea_attn_fwd_workspace_size(int(dtype_code), int(batch), int(total_q), int(total_k),
+                                           int(max_seqlen_q), int(max_seqlen_k), int(heads_q), int(heads_kv),
+                                           int(head_dim), 1 if causal else 0, int(piece_rows), ctypes.byref(n)))
+    return int(n.value)
+
+
 def attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, causal, scale, out, lse=None, *, piece_rows=0,
-             max_seqlen_q=None, max_seqlen_k=None):
+             max_seqlen_q=None, max_seqlen_k=None, workspace="auto"):
     """Blockwise attention forward (see vea_attn_fwd in include/vea.h).
 
     q [total_q, Hq, d], k/v [total_k, Hkv, d] (token strides free), out like q,
     lse float32 [Hq, total_q] or None.  max_seqlen_* default to the largest
     sequence length, read from cu_seqlens with one host copy (synchronising).
+    workspace: "auto" allocates what the call asks for (a split of the last
+    round of workgroups for one non-causal bf16 sequence), None never splits,
+    or a contiguous uint8 GPU tensor to use.
     """
     lib = load_library()
     qs, ks, vs, os_ = (_token_major(q, "q"), _token_major(k, "k"), _token_major(v, "v"),
@@ -143,10 +160,22 @@ def attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, causal, scale, out, lse=None, 
         lk = (cu_seqlens_k[1:] - cu_seqlens_k[:-1]).max().item() if batch > 0 else 0
         max_seqlen_q = lq if max_seqlen_q is None else max_seqlen_q
         max_seqlen_k = lk if max_seqlen_k is None else max_seqlen_k
-    st = lib.vea_attn_fwd(dt, _ptr(q), qs, _ptr(k), ks, _ptr(v), vs, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
-                          batch, q.shape[0], k.shape[0], int(max_seqlen_q), int(max_seqlen_k), q.shape[1],
-                          k.shape[1], q.shape[2], 1 if causal else 0, float(scale), int(piece_rows),
-                          _ptr(out), os_, _ptr(lse), _stream(q))
+    torch = _torch()
+    with torch.cuda.device(q.device):
+        if isinstance(workspace, str):
+            if workspace != "auto":
+                raise ValueError('workspace must be "auto", None or a uint8 GPU tensor')
+            nbytes = attn_fwd_workspace_size(dt, batch, q.shape[0], k.shape[0], max_seqlen_q, max_seqlen_k,
+                                             q.shape[1], k.shape[1], q.shape[2], causal, piece_rows)
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
+        if workspace is not None and (workspace.dtype != torch.uint8 or not workspace.is_contiguous()
+                                      or workspace.device != q.device):
+            raise ValueError("workspace must be a contiguous uint8 tensor on q's device")
+        st = lib.vea_attn_fwd(dt, _ptr(q), qs, _ptr(k), ks, _ptr(v), vs, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                              batch, q.shape[0], k.shape[0], int(max_seqlen_q), int(max_seqlen_k), q.shape[1],
+                              k.shape[1], q.shape[2], 1 if causal else 0, float(scale), int(piece_rows),
+                              _ptr(out), os_, _ptr(lse), _ptr(workspace),
+                              0 if workspace is None else workspace.numel(), _stream(q))
     _check(st)
     return out, lse
 

@@ -14,6 +14,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 using namespace vea;
@@ -78,20 +79,88 @@ const char* vea_status_str(int status) {
 
 const char* vea_version(void) { return "vea 0.1.0 gfx950"; }
 
-int vea_attn_fwd(int dtype, const void* q, int64_t q_tok_stride, const void* k, int64_t k_tok_stride,
-                 const void* v, int64_t v_tok_stride, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-                 int batch, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int num_heads_q,
-                 int num_heads_kv, int head_dim, int causal, float scale, int piece_rows, void* out,
-                 int64_t out_tok_stride, float* lse, void* stream) {
-  // ---- validation (host only)
+namespace {
+
+// Validation of the shape arguments shared by vea_attn_fwd and its workspace
+// query.
+int dense_shape_status(int dtype, int batch, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                       int num_heads_q, int num_heads_kv, int head_dim, int causal, int piece_rows) {
   if (dtype != VEA_BF16 && dtype != VEA_F32) return VEA_EDTYPE;
   if (batch < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || piece_rows < 0)
     return VEA_ESHAPE;
   if (num_heads_q <= 0 || num_heads_kv <= 0 || num_heads_q % num_heads_kv != 0) return VEA_ESHAPE;
-  if (!isfinite(scale)) return VEA_EINVAL;
   if (causal != 0 && causal != 1) return VEA_EINVAL;
   if (dtype == VEA_BF16 && head_dim != 64 && head_dim != 128) return VEA_EUNSUPPORTED;
   if (dtype == VEA_F32 && head_dim != 64) return VEA_EUNSUPPORTED;
+  if (max_seqlen_q > total_q || max_seqlen_k > total_k) return VEA_ESHAPE;
+  return VEA_OK;
+}
+
+// Launch shape: (sequence, piece, tile, head) units.
+int dense_layout(int batch, int max_seqlen_q, int num_heads_q, int piece_rows, DenseParams& p) {
+  p.qb = (piece_rows > 0 && piece_rows < max_seqlen_q) ? piece_rows : max_seqlen_q;
+  p.tiles_per_piece = (p.qb + kDenseBM - 1) / kDenseBM;
+  const int64_t pieces = ((int64_t)max_seqlen_q + p.qb - 1) / p.qb;
+  const int64_t tps = pieces * p.tiles_per_piece;
+  const int64_t units = (int64_t)batch * tps * num_heads_q;
+  if (units * 8 > 0x7fffffff) return VEA_EUNSUPPORTED;
+  p.tiles_per_seq = (int)tps;
+  p.units = (int)units;
+  p.full_units = p.units;
+  p.nsplit = 1;
+  p.ws = nullptr;
+  return VEA_OK;
+}
+
+// Split of the last round (bf16, one non-causal sequence: there the host
+// knows which units are empty without reading cu_seqlens).
+int dense_split(int dtype, int batch, int total_q, int total_k, int num_heads_q, int head_dim, int causal,
+                const DenseParams& p, DenseSplit& plan) {
+  plan = DenseSplit{p.units, 1, 0};
+  if (dtype != VEA_BF16 || batch != 1 || causal || total_q == 0) return VEA_OK;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return VEA_EHIP;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return VEA_EHIP;
+  const int per_cu = dense_bf16_blocks_per_cu(head_dim);
+  int64_t real_tiles = 0;                               // tiles with rows, per head
+  for (int64_t r0 = 0; r0 < total_q; r0 += p.qb)
+    real_tiles += (std::min<int64_t>(p.qb, total_q - r0) + kDenseBM - 1) / kDenseBM;
+  const int empty = p.units - (int)(real_tiles * num_heads_q);
+  plan = dense_split_plan(p.units, std::max(empty, 0), cus * per_cu, (total_k + 63) / 64);
+  return VEA_OK;
+}
+
+}  // namespace
+
+int vea_attn_fwd_workspace_size(int dtype, int batch, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                                int num_heads_q, int num_heads_kv, int head_dim, int causal, int piece_rows,
+                                size_t* bytes) {
+  if (bytes == nullptr) return VEA_EINVAL;
+  *bytes = 0;
+  int st = dense_shape_status(dtype, batch, total_q, total_k, max_seqlen_q, max_seqlen_k, num_heads_q,
+                              num_heads_kv, head_dim, causal, piece_rows);
+  if (st != VEA_OK) return st;
+  if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return VEA_OK;
+  DenseParams p;
+  st = dense_layout(batch, max_seqlen_q, num_heads_q, piece_rows, p);
+  if (st != VEA_OK) return st;
+  DenseSplit plan;
+  st = dense_split(dtype, batch, total_q, total_k, num_heads_q, head_dim, causal, p, plan);
+  if (st != VEA_OK) return st;
+  *bytes = (size_t)plan.chunks * dense_chunk_bytes(head_dim);
+  return VEA_OK;
+}
+
+int vea_attn_fwd(int dtype, const void* q, int64_t q_tok_stride, const void* k, int64_t k_tok_stride,
+                 const void* v, int64_t v_tok_stride, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                 int batch, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int num_heads_q,
+                 int num_heads_kv, int head_dim, int causal, float scale, int piece_rows, void* out,
+                 int64_t out_tok_stride, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  // ---- validation (host only)
+  int st = dense_shape_status(dtype, batch, total_q, total_k, max_seqlen_q, max_seqlen_k, num_heads_q,
+                              num_heads_kv, head_dim, causal, piece_rows);
+  if (st != VEA_OK) return st;
+  if (!isfinite(scale)) return VEA_EINVAL;
   if (batch == 0 || total_q == 0) return VEA_OK;                 // nothing to compute
   if (!q || !out || !cu_seqlens_q || !cu_seqlens_k) return VEA_EINVAL;
   if (total_k > 0 && (!k || !v)) return VEA_EINVAL;               // no keys: k/v are never read
@@ -102,33 +171,37 @@ int vea_attn_fwd(int dtype, const void* q, int64_t q_tok_stride, const void* k, 
   if ((q_tok_stride * esz) % 16 || (k_tok_stride * esz) % 16 || (v_tok_stride * esz) % 16 ||
       (out_tok_stride * esz) % 16)
     return VEA_EINVAL;
-  if (max_seqlen_q > total_q || max_seqlen_k > total_k) return VEA_ESHAPE;
+  if (workspace != nullptr && !aligned16(workspace)) return VEA_EWORKSPACE;
   hipStream_t s = (hipStream_t)stream;
 
   if (check_enabled()) {
-    int st = check_cu(cu_seqlens_q, batch, total_q, max_seqlen_q, s);
+    st = check_cu(cu_seqlens_q, batch, total_q, max_seqlen_q, s);
     if (st == VEA_OK) st = check_cu(cu_seqlens_k, batch, total_k, max_seqlen_k, s);
     if (st != VEA_OK) return st;
   }
   if (max_seqlen_q == 0) return finish(VEA_OK, s);
 
-  // ---- launch shape: (sequence, piece, tile, head) units
   DenseParams p;
   p.q = q; p.k = k; p.v = v; p.out = out; p.lse = lse;
   p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k;
   p.q_stride = q_tok_stride; p.k_stride = k_tok_stride; p.v_stride = v_tok_stride; p.o_stride = out_tok_stride;
   p.batch = batch; p.total_q = total_q; p.total_k = total_k;
   p.hq = num_heads_q; p.hkv = num_heads_kv; p.group = num_heads_q / num_heads_kv;
-  p.qb = (piece_rows > 0 && piece_rows < max_seqlen_q) ? piece_rows : max_seqlen_q;
-  p.tiles_per_piece = (p.qb + kDenseBM - 1) / kDenseBM;
-  const int64_t pieces = ((int64_t)max_seqlen_q + p.qb - 1) / p.qb;
-  const int64_t tps = pieces * p.tiles_per_piece;
-  const int64_t units = (int64_t)batch * tps * num_heads_q;
-  if (units > 0x7fffffff) return VEA_EUNSUPPORTED;
-  p.tiles_per_seq = (int)tps;
-  p.units = (int)units;
+  st = dense_layout(batch, max_seqlen_q, num_heads_q, piece_rows, p);
+  if (st != VEA_OK) return st;
   p.xcd_map = (num_heads_kv % 8 == 0) ? 1 : 0;
   p.scale = scale;
+  if (workspace != nullptr) {
+    DenseSplit plan;
+    st = dense_split(dtype, batch, total_q, total_k, num_heads_q, head_dim, causal, p, plan);
+    if (st != VEA_OK) return st;
+    if (plan.nsplit > 1) {
+      if (workspace_bytes < (size_t)plan.chunks * dense_chunk_bytes(head_dim)) return VEA_EWORKSPACE;
+      p.full_units = plan.full_units;
+      p.nsplit = plan.nsplit;
+      p.ws = (float*)workspace;
+    }
+  }
 
   hipError_t e = dtype == VEA_BF16 ? launch_attn_fwd_bf16(p, head_dim, causal != 0, s)
                                    : launch_attn_fwd_f32(p, head_dim, causal != 0, s);

@@ -40,6 +40,7 @@
 #include <float.h>
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 namespace vea {
@@ -188,8 +189,17 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
   __shared__ __attribute__((aligned(1024))) unsigned char vst0[C::TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char vst1[C::TILE];
 
+  // unit, and for a split unit of the last round, its key-range chunk
+  int id = blockIdx.x, chunk = 0;
+  const bool split = id >= p.full_units;
+  if (split) {
+    const int u2 = id - p.full_units;
+    const int tu = u2 / p.nsplit;
+    chunk = u2 - tu * p.nsplit;
+    id = p.full_units + tu;
+  }
   int b, h, t;
-  decode_unit(p, blockIdx.x, b, h, t);
+  decode_unit(p, id, b, h, t);
   TileRange tr;
   if (!tile_range(p, b, t, C::BM, CAUSAL, tr)) return;   // uniform over the workgroup
 
@@ -225,6 +235,15 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
 
   const int kend_i = CAUSAL ? clampi(qi + tr.len_k - tr.len_q + 1, 0, tr.len_k) : tr.len_k;
 
+  // Key tiles [kt0, kt0 + n_tiles) of this workgroup: all of them, or its
+  // chunk's share of a split unit.  Below, kt counts tiles from kt0.
+  const int n_all = (tr.kend + C::BN - 1) / C::BN;
+  int kt0 = 0, n_tiles = n_all;
+  if (split) {
+    kt0 = (n_all * chunk) / p.nsplit;
+    n_tiles = (n_all * (chunk + 1)) / p.nsplit - kt0;
+  }
+
   // ---- DMA of K/V tiles straight into LDS (buffer loads, no register staging).
   // Lane slot sl of the wave's 1 KB destination block holds row sl / CPR,
   // physical chunk sl % CPR = logical chunk ^ swz(row).  Rows past the needed
@@ -242,9 +261,9 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
   const unsigned char* vbase_ptr = (const unsigned char*)p.v + ((int64_t)tr.ks * p.v_stride + (int64_t)kvh * D) * 2;
 
   auto issue_tile = [&](int kt, const unsigned char* base, int64_t sb, const int* voff, unsigned char* stage) {
-    const int rows = min(tr.kend - kt * C::BN, C::BN);
+    const int rows = min(tr.kend - (kt0 + kt) * C::BN, C::BN);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(base + (int64_t)kt * C::BN * sb), (short)0, (int)(rows * sb), 0x00020000);
+        (void*)(base + (int64_t)(kt0 + kt) * C::BN * sb), (short)0, (int)(rows * sb), 0x00020000);
     unsigned char* dst = stage + wave * C::LOADS * 1024;
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i)
@@ -276,8 +295,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
   float l_run = 0.f;         // lane-partial sums of P (two independent chains)
   float l_odd = 0.f;
 
-  const int n_tiles = (tr.kend + C::BN - 1) / C::BN;
-  const int n_full = min(n_tiles, tr.kfull / C::BN);   // tiles no row needs masked
+  const int n_full = min(n_all, tr.kfull / C::BN) - kt0;   // (local) tiles no row needs masked
 
   // S^T = K Q^T for one tile: two independent 32-key accumulators, interleaved.
   auto qk = [&](const unsigned char* ks_, floatx16& s0, floatx16& s1) {
@@ -293,7 +311,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
   };
   // Keys past a row's bound (tail of the sequence, causal diagonal) -> -inf.
   auto mask = [&](int kt, floatx16& s0, floatx16& s1) {
-    const int j0 = kt * C::BN + 4 * g2;
+    const int j0 = (kt0 + kt) * C::BN + 4 * g2;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int j = j0 + 8 * (r >> 2) + (r & 3);
@@ -419,6 +437,23 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
 
   // ---- epilogue: O / l (bf16 RNE), lse = ln 2 * (m + log2 l)
   const float l_tot = lane_swap_add(l_run + l_odd);
+  if (split) {
+    // partial result of this key range, per tile row: unnormalized O
+    // (fp32), reference max m (log2 domain) and sum l
+    float* w = p.ws + (size_t)(blockIdx.x - p.full_units) * (C::BM * (D + 2));
+    const int rl = wave * 32 + l32;                     // row within the tile
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *(floatx4*)(w + rl * D + 32 * nb + 8 * r4 + 4 * g2) =
+            (floatx4){o[nb][4 * r4], o[nb][4 * r4 + 1], o[nb][4 * r4 + 2], o[nb][4 * r4 + 3]};
+    if (g2 == 0) {
+      w[C::BM * D + rl] = m_used;
+      w[C::BM * D + C::BM + rl] = l_tot;
+    }
+    return;
+  }
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qvalid) {
     uint16_t* dst = (uint16_t*)p.out + (int64_t)(tr.qs + qi) * p.o_stride + (int64_t)h * D + 4 * g2;
@@ -434,6 +469,59 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
     if (p.lse != nullptr && g2 == 0)
       p.lse[(int64_t)h * p.total_q + tr.qs + qi] = l_tot > 0.f ? (m_used + log2f(l_tot)) * kLn2 : -INFINITY;
   }
+}
+
+// Merge of the split chunks of one unit, in chunk order (fixed, so the result
+// is deterministic): with M = max_i m_i, O = sum_i 2^(m_i - M) O_i and
+// l = sum_i 2^(m_i - M) l_i, out = O / l (bf16) and lse = ln 2 (M + log2 l):
+// the blockwise merge of [V32] eq. (1)(2) with the O update written out.
+// Workgroup (tail unit, group of 256 (row, 16-column slice) items).  Empty
+// chunks carry m = -inf, l = 0.
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_kernel(DenseParams p) {
+  const int tu = blockIdx.x;
+  int b, h, t;
+  decode_unit(p, p.full_units + tu, b, h, t);
+  TileRange tr;
+  if (!tile_range(p, b, t, kDenseBM, false, tr)) return;
+  constexpr int SL = D / 16;                            // 16-column slices per row
+  const int item = blockIdx.y * 256 + threadIdx.x;
+  const int rl = item / SL, sc = item - rl * SL;        // row within the tile, slice
+  const int qi = tr.row0 + rl;
+  if (rl >= kDenseBM || qi >= tr.row_end) return;
+  constexpr size_t CF = (size_t)kDenseBM * (D + 2);     // floats per chunk
+  const float* base = p.ws + (size_t)tu * p.nsplit * CF;
+  float mmax = -INFINITY;
+  for (int i = 0; i < p.nsplit; ++i) mmax = fmaxf(mmax, base[i * CF + kDenseBM * D + rl]);
+  float acc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+  float l = 0.f;
+  if (mmax != -INFINITY) {
+    for (int i = 0; i < p.nsplit; ++i) {
+      const float* c = base + i * CF;
+      const float mi = c[kDenseBM * D + rl];
+      if (mi == -INFINITY) continue;                    // empty chunk
+      const float f = fast_exp2(mi - mmax);
+      l = fmaf(f, c[kDenseBM * D + kDenseBM + rl], l);
+      const floatx4* src = (const floatx4*)(c + rl * D + 16 * sc);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const floatx4 v = src[q4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[4 * q4 + j] = fmaf(f, v[j], acc[4 * q4 + j]);
+      }
+    }
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  u32x4 w[2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w[j >> 2][j & 3] = pack_bf16x2(acc[2 * j] * inv, acc[2 * j + 1] * inv);
+  uint16_t* dst = (uint16_t*)p.out + (int64_t)(tr.qs + qi) * p.o_stride + (int64_t)h * D + 16 * sc;
+  *(u32x4*)dst = w[0];
+  *(u32x4*)(dst + 8) = w[1];
+  if (sc == 0 && p.lse != nullptr)
+    p.lse[(int64_t)h * p.total_q + tr.qs + qi] = l > 0.f ? (mmax + log2f(l)) * kLn2 : -INFINITY;
 }
 
 // ================================================================ fp32 path
@@ -600,8 +688,42 @@ __global__ __launch_bounds__(256) void attn_probs_kernel(ProbsParams p) {
 
 }  // namespace
 
+DenseSplit dense_split_plan(int units, int empty, int slots, int key_tiles) {
+  // Units go out in grid order, `slots` at a time; the first `empty` have no
+  // rows and end at once.  The last round holds (units - empty) % slots real
+  // units and would leave most slots idle for a whole unit's time, so each of
+  // them is split into as many key ranges as the idle slots allow (at most
+  // 8, at most one per key tile; a split below 2 is not worth the merge).
+  DenseSplit s{units, 1, 0};
+  const int real = units - empty;
+  if (slots <= 0 || real <= slots) return s;
+  const int tail = real % slots;
+  if (tail == 0) return s;
+  const int nsplit = std::min(std::min(8, slots / tail), key_tiles);
+  if (nsplit < 2) return s;
+  s.full_units = units - tail;
+  s.nsplit = nsplit;
+  s.chunks = tail * nsplit;
+  return s;
+}
+
+size_t dense_chunk_bytes(int head_dim) { return (size_t)kDenseBM * (head_dim + 2) * sizeof(float); }
+
+int dense_bf16_blocks_per_cu(int head_dim) {
+  int n = 0;
+  hipError_t e = hipErrorInvalidValue;
+  if (head_dim == 64)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_bf16_kernel<64, false>, 256, 0);
+  else if (head_dim == 128)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_bf16_kernel<128, false>, 256, 0);
+  return e == hipSuccess ? n : 0;
+}
+
 hipError_t launch_attn_fwd_bf16(const DenseParams& p, int head_dim, bool causal, hipStream_t s) {
-  const dim3 grid(p.units), block(256);
+  const bool split = p.nsplit > 1;
+  if (split ? (causal || p.ws == nullptr || p.full_units < 0 || p.full_units >= p.units) : p.full_units != p.units)
+    return hipErrorInvalidValue;
+  const dim3 grid(p.full_units + (p.units - p.full_units) * p.nsplit), block(256);
   if (head_dim == 64) {
     if (causal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, true>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, false>), grid, block, 0, s, p);
@@ -610,6 +732,13 @@ hipError_t launch_attn_fwd_bf16(const DenseParams& p, int head_dim, bool causal,
     else hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, false>), grid, block, 0, s, p);
   } else {
     return hipErrorInvalidValue;
+  }
+  if (split) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 mgrid(p.units - p.full_units, kDenseBM * head_dim / 16 / 256);
+    if (head_dim == 64) hipLaunchKernelGGL((attn_merge_kernel<64>), mgrid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_merge_kernel<128>), mgrid, block, 0, s, p);
   }
   return hipGetLastError();
 }

@@ -35,6 +35,13 @@ struct DenseParams {
   int units;                 // batch * tiles_per_seq * hq
   int xcd_map;               // 1: spread kv heads over the 8 XCDs
   float scale;
+  // Key-range split of the units of the last, partial round (bf16 path):
+  // units [0, full_units) run whole; each later unit is split into nsplit
+  // workgroups over consecutive ranges of its key tiles, which write partial
+  // (O, m, l) to ws (kDenseBM x (d + 2) floats per chunk), merged after.
+  int full_units;
+  int nsplit;                // 1: no split
+  float* ws;                 // nullable when nsplit == 1
 };
 
 struct RopeParams {
@@ -64,6 +71,18 @@ struct SparseParams {
   int nsplit;                // 1: no split
   float* ws;                 // nullable when nsplit == 1
 };
+
+// Split plan of the dense bf16 kernel for one non-causal sequence: `units`
+// grid units of which the first `empty` have no rows, `slots` workgroups
+// resident at once, `key_tiles` key tiles per unit.
+struct DenseSplit {
+  int full_units, nsplit, chunks;
+};
+DenseSplit dense_split_plan(int units, int empty, int slots, int key_tiles);
+// Bytes of workspace per split chunk: kDenseBM x (d + 2) floats.
+size_t dense_chunk_bytes(int head_dim);
+// Workgroups of the dense bf16 kernel resident per CU (0 if unknown).
+int dense_bf16_blocks_per_cu(int head_dim);
 
 // Split plan of the sparse kernel for `units` workgroup units of k indices
 // each, on a device with `cus` compute units (one workgroup per CU at a time).

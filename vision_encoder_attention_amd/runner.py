@@ -52,10 +52,13 @@ class DenseStaged:
     positions: Optional["torch.Tensor"] = None
     max_q: int = 0
     max_k: int = 0
+    split: bool = True                 # let attn_fwd split the last round (workspace)
+    ws: Optional["torch.Tensor"] = None
 
 
-def stage_dense(case: DenseCase, device="cuda") -> DenseStaged:
-    """Copy a dense case to the device and allocate its outputs.
+def stage_dense(case: DenseCase, device="cuda", split: bool = True) -> DenseStaged:
+    """Copy a dense case to the device and allocate its outputs (and the
+    attention workspace, when the call would use one and split is set).
 
     For cases with a fused QKV buffer, q/k are the (not yet computed) outputs
     of qkv_rope and v is a strided view into the fused buffer.
@@ -78,8 +81,16 @@ def stage_dense(case: DenseCase, device="cuda") -> DenseStaged:
     lse = torch.empty((hq, case.total_q), dtype=torch.float32, device=device)
     lq = case.seqlens_q
     lk = case.seqlens_k
-    return DenseStaged(case, q, k, v, _dev_i32(case.cu_seqlens_q, device), _dev_i32(case.cu_seqlens_k, device),
-                       out, lse, x, pos, int(lq.max()) if lq.size else 0, int(lk.max()) if lk.size else 0)
+    st = DenseStaged(case, q, k, v, _dev_i32(case.cu_seqlens_q, device), _dev_i32(case.cu_seqlens_k, device),
+                     out, lse, x, pos, int(lq.max()) if lq.size else 0, int(lk.max()) if lk.size else 0, split)
+    if split:
+        with torch.cuda.device(q.device):
+            n = B.attn_fwd_workspace_size(B.VEA_BF16 if case.dtype == "bf16" else B.VEA_F32, len(lq),
+                                          case.total_q, case.total_k, st.max_q, st.max_k, hq, hkv, d,
+                                          case.causal, case.piece_rows)
+        if n:
+            st.ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+    return st
 
 
 def run_rope(st: DenseStaged):
@@ -91,9 +102,15 @@ def run_rope(st: DenseStaged):
 def run_attn(st: DenseStaged, piece_rows: Optional[int] = None, lse: bool = True):
     """attn_fwd step (writes st.out and st.lse)."""
     c = st.case
+    if not st.split:
+        ws = None
+    elif piece_rows is None or piece_rows == c.piece_rows:
+        ws = st.ws                                          # sized for the case's own pieces
+    else:
+        ws = "auto"
     B.attn_fwd(st.q, st.k, st.v, st.cu_q, st.cu_k, c.causal, c.scale, st.out, st.lse if lse else None,
                piece_rows=c.piece_rows if piece_rows is None else piece_rows,
-               max_seqlen_q=st.max_q, max_seqlen_k=st.max_k)
+               max_seqlen_q=st.max_q, max_seqlen_k=st.max_k, workspace=ws)
 
 
 def run_dense(st: DenseStaged, piece_rows: Optional[int] = None):
