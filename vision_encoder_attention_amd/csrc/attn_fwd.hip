@@ -25,7 +25,11 @@
 //     a single cross-lane exchange and the row sum is lane-local until the end.
 //   * Online softmax in fp32 ([V32] section 进一步探索 eq. (1)(2)): running max
 //     m, rescale alpha = 2^(m_old - m_new), running sum l; exponentials via
-//     v_exp_f32 with log2(e) folded into the scale.
+//     v_exp_f32 with log2(e) folded into the scale.  The reference max moves
+//     lazily and is not recomputed per tile: P is formed with the current
+//     reference and a tile whose P grows too large (or a row still without
+//     a reference) takes a rare path that recomputes its logits, moves the
+//     reference and rescales O and l.
 //   * O^T += V^T P^T with the same MFMA; P is rounded to bf16 (RNE) in
 //     registers, V is stored transposed in LDS so each lane reads 4 keys of one
 //     column as one 8-byte LDS read.  O^T's layout again gives each lane one
@@ -292,8 +296,8 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb) o[nb] = (floatx16){};
   float m_used = -INFINITY;  // max used for exponentiation (times c, log2 domain)
-  float l_run = 0.f;         // lane-partial sums of P (two independent chains)
-  float l_odd = 0.f;
+  float l_run = 0.f;         // lane-partial sum of P
+  float m_use = 0.f;         // m_used, or 0 while the row has none
 
   const int n_full = min(n_all, tr.kfull / C::BN) - kt0;   // (local) tiles no row needs masked
 
@@ -339,33 +343,56 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
 #pragma unroll
       for (int nb = 0; nb < D / 32; ++nb) o[nb] *= alpha;
       l_run *= alpha;
-      l_odd *= alpha;
     }
     return (m_used == -INFINITY) ? 0.f : m_used;
   };
-  // Part 2: P = 2^(s c - m) summed in fp32 for l (so lse is the log-sum-exp of
-  // the logits themselves), rounded to bf16 and packed; then O^T += V^T P^T
-  // with V read transposed from a V stage.  k-slot j of lane half g2 in step
-  // st is key 16 st + 8 (j / 4) + 4 g2 + j % 4 for both operands.
-  auto softmax_pv = [&](const floatx16& s0, const floatx16& s1, float m_use, const unsigned char* vs_) {
-    u32x4 pb[4];
+  // Common part: P = 2^(s c - m) with the current reference, rounded to
+  // bf16 and packed, and this lane's fp32 sum of the tile's P.  A lane sum
+  // above 2^13 (so some P above 2^8) or a row without a reference sends the
+  // wave to the rare part, which recomputes the tile's logits from K in
+  // global memory (they are not kept), moves the reference and recomputes
+  // P.  k-slot j of lane half g2 in step st is key 16 st + 8 (j / 4) + 4 g2 +
+  // j % 4 for both operands.
+  auto softmax_p = [&](const floatx16& s0, const floatx16& s1, float mu, u32x4* pb) -> float {
+    float tq[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const floatx16& sv = kb == 0 ? s0 : s1;
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         uint32_t w[4];
+        float pr[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float e0 = fast_exp2(fmaf(sv[8 * hf + 2 * q], c, -m_use));
-          const float e1 = fast_exp2(fmaf(sv[8 * hf + 2 * q + 1], c, -m_use));
-          if (q & 1) l_odd += e0 + e1;
-          else l_run += e0 + e1;
+          const float e0 = fast_exp2(fmaf(sv[8 * hf + 2 * q], c, -mu));
+          const float e1 = fast_exp2(fmaf(sv[8 * hf + 2 * q + 1], c, -mu));
+          pr[q] = e0 + e1;
           w[q] = pack_bf16x2(e0, e1);
         }
+        tq[2 * kb + hf] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
         pb[2 * kb + hf] = (u32x4){w[0], w[1], w[2], w[3]};
       }
     }
+    return (tq[0] + tq[1]) + (tq[2] + tq[3]);
+  };
+  // S^T of key tile kt from K in global memory (rows past the key bound
+  // clamped to the last one; they are masked).
+  auto qk_global = [&](int kt, floatx16& s0, floatx16& s1) {
+    const int r0 = (kt0 + kt) * C::BN;
+    const unsigned char* pa = kbase_ptr + (int64_t)min(r0 + l32, tr.kend - 1) * ksb + 16 * g2;
+    const unsigned char* pb2 = kbase_ptr + (int64_t)min(r0 + 32 + l32, tr.kend - 1) * ksb + 16 * g2;
+    s0 = (floatx16){};
+    s1 = (floatx16){};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const u32x4 a0 = *(const u32x4*)(pa + 32 * ks);
+      const u32x4 a1 = *(const u32x4*)(pb2 + 32 * ks);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), as_bf16x8(qf[ks]), s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), as_bf16x8(qf[ks]), s1, 0, 0, 0);
+    }
+  };
+  // O^T += V^T P^T with V read transposed from a V stage.
+  auto pv = [&](const u32x4* pb, const unsigned char* vs_) {
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
 #pragma unroll
@@ -400,10 +427,20 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
       if (kt + 1 < n_tiles) issue_k(kt + 1, k_wr);
       issue_v(kt, v_wr);
     }
-    const float m_use = softmax_ref(sp0, sp1);
-    // one branch-free block: QK^T of tile kt, softmax and P V of tile kt-1
+    // QK^T of tile kt under the softmax of tile kt-1, then P V of tile kt-1
     if constexpr (HAS_S) qk(k_rd, sn0, sn1);
-    softmax_pv(sp0, sp1, m_use, v_rd);
+    u32x4 pb[4];
+    float t = softmax_p(sp0, sp1, m_use, pb);
+    if (__any(t > 8192.f || m_used == -INFINITY)) {
+      asm volatile("; rare: recompute the logits, move the reference max, recompute P" ::);
+      floatx16 r0, r1;
+      qk_global(kt - 1, r0, r1);
+      if (kt - 1 >= n_full) mask(kt - 1, r0, r1);
+      m_use = softmax_ref(r0, r1);
+      t = softmax_p(r0, r1, m_use, pb);
+    }
+    l_run += t;
+    pv(pb, v_rd);
     if constexpr (HAS_S) {
       if (kt >= n_full) {
         asm volatile("; masked tile" ::);
@@ -422,6 +459,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
     if (1 < n_tiles) issue_k(1, kst1);
     qk(kst0, sp0, sp1);
     if (0 >= n_full) mask(0, sp0, sp1);
+    m_use = softmax_ref(sp0, sp1);                      // reference from the first tile
     int kt = 1;
     for (; kt + 1 < n_tiles; kt += 2) {                // kt odd here
       iter(kt, std::true_type{}, std::true_type{});
@@ -436,7 +474,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
   }
 
   // ---- epilogue: O / l (bf16 RNE), lse = ln 2 * (m + log2 l)
-  const float l_tot = lane_swap_add(l_run + l_odd);
+  const float l_tot = lane_swap_add(l_run);
   if (split) {
     // partial result of this key range, per tile row: unnormalized O
     // (fp32), reference max m (log2 domain) and sum l
