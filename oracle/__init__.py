@@ -19,6 +19,8 @@ What it computes is the plain definition of each operation, in float64:
 * ``rope_*`` / ``qkv_rope``  rotary position embedding on the Q and K heads
                      of a fused QKV projection output (1D and 2D grid).
 * ``sparse_mqa``     multi-query attention over a per-row set of latent rows.
+* ``topk_indices``   deterministic top-k selection of the sparse indexer
+                     (ties go to the lower position).
 * ``pieces``         query-piece arithmetic of the vision encoder.
 
 Every function says which passage it follows.  Page titles used below:
@@ -35,3 +37,4 @@ from .attention import attention, attn_probs  # noqa: F401
 from .rope import rope_1d, rope_2d, qkv_rope, rope_inv_freq  # noqa: F401
 from .sparse import sparse_mqa  # noqa: F401
 from .pieces import piece_ranges, piece_rows_for_capacity  # noqa: F401
+from .topk import topk_indices  # noqa: F401

@@ -463,6 +463,99 @@ def pin_sparse_reductions(orc):
 SPARSE_PINS = [pin_sparse_permutation, pin_sparse_brute, pin_sparse_reductions]
 
 
+# ====================================================================== top-k
+
+def _ranks_before(x, i, j):
+    """Pairwise rank rule written out: does position i rank before position j?"""
+    xi, xj = float(x[i]), float(x[j])
+    ni, nj = math.isnan(xi), math.isnan(xj)
+    if ni or nj:
+        return (not ni and nj) or (ni and nj and i < j)
+    if xi != xj:                      # -0.0 == +0.0 falls through to the tie rule
+        return xi > xj
+    return i < j
+
+
+def _topk_by_counting(x, k, start, ln):
+    """Brute force without sorting: the rank of position j is the number of
+    valid positions that rank before it; slot t holds the position of rank t."""
+    out = [-1] * k
+    for j in range(start, start + ln):
+        rank = sum(1 for i in range(start, start + ln) if i != j and _ranks_before(x, i, j))
+        if rank < k:
+            out[rank] = j
+    return out
+
+
+def pin_topk_brute_force(orc):
+    """Tiny rows with many ties (values from a 4-level alphabet), spans, k
+    above and below the span length, against the pairwise-count brute force."""
+    rng = _rng(501)
+    for trial in range(40):
+        n = int(rng.integers(1, 13))
+        rows = 3
+        x = rng.choice(np.array([-1.5, 0.0, 0.25, 2.0], np.float32), size=(rows, n))
+        k = int(rng.integers(1, n + 3))
+        starts = rng.integers(0, n, rows)
+        lens = np.array([int(rng.integers(0, n - s + 1)) for s in starts])
+        got = orc.topk_indices(x, k, starts, lens)
+        for r in range(rows):
+            assert got[r].tolist() == _topk_by_counting(x[r], k, int(starts[r]), int(lens[r])), (trial, r)
+
+
+def pin_topk_special_values(orc):
+    """NaN ranks after every number (NaNs by position), +inf first, -inf last
+    among numbers, and -0.0 ties with +0.0 (lower index first)."""
+    x = np.array([[0.0, np.nan, -np.inf, 1.0, -0.0, np.inf, np.nan, 0.0]], np.float32)
+    x[0, 4] = np.float32(-0.0)
+    got = orc.topk_indices(x, 8)[0].tolist()
+    assert got == [5, 3, 0, 4, 7, 2, 1, 6], got
+    assert got == _topk_by_counting(x[0], 8, 0, 8)
+
+
+def pin_topk_closed_forms(orc):
+    """All-equal row: the first k positions in order.  Strictly decreasing:
+    0..k-1.  Strictly increasing: n-1 down to n-k.  A span shorter than k is
+    padded with -1.  k = n returns a permutation of the span."""
+    n, k = 2590, 2048
+    eq = np.full((1, n), 0.5, np.float32)
+    assert orc.topk_indices(eq, k)[0].tolist() == list(range(k))
+    dec = -np.arange(n, dtype=np.float32)[None]
+    assert orc.topk_indices(dec, k)[0].tolist() == list(range(k))
+    inc = np.arange(n, dtype=np.float32)[None]
+    assert orc.topk_indices(inc, k)[0].tolist() == list(range(n - 1, n - 1 - k, -1))
+    short = orc.topk_indices(inc, k, row_starts=[100], row_lens=[1000])[0]
+    assert short[:1000].tolist() == list(range(1099, 99, -1)) and np.all(short[1000:] == -1)
+    rng = _rng(502)
+    x = rng.standard_normal((2, 300)).astype(np.float32)
+    full = orc.topk_indices(x, 300)
+    for r in range(2):
+        assert sorted(full[r].tolist()) == list(range(300))
+        assert np.all(np.diff(x[r, full[r]]) <= 0)
+
+
+def pin_topk_selection_property(orc):
+    """On a full-size row with ties planted at the edge of the selection: every
+    selected value is >= every unselected one, and among values equal to the
+    k-th largest the lowest positions are the ones selected."""
+    rng = _rng(503)
+    n, k = 2590, 2048
+    x = np.round(rng.standard_normal(n) * 8).astype(np.float32)     # many exact ties
+    got = orc.topk_indices(x[None], k)[0]
+    sel = np.zeros(n, bool)
+    sel[got] = True
+    assert sel.sum() == k
+    kth = x[got[-1]]
+    assert x[sel].min() == kth and x[~sel].max() <= kth
+    tied = np.flatnonzero(x == kth)
+    n_in = int(sel[tied].sum())
+    assert 0 < n_in < tied.size                     # the edge does split a tie class
+    assert np.all(sel[tied[:n_in]]) and not np.any(sel[tied[n_in:]])
+
+
+TOPK_PINS = [pin_topk_brute_force, pin_topk_special_values, pin_topk_closed_forms, pin_topk_selection_property]
+
+
 # =================================================================== pieces
 
 def pin_pieces(orc, figures):

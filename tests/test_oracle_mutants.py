@@ -55,9 +55,20 @@ MUTANTS = [
     ("sparse", "sel = idx[r][idx[r] >= 0]", "sel = np.unique(idx[r][idx[r] >= 0])", "repeated indices collapsed"),
     ("sparse", "lse[:, r] = m + np.log(l_sum)", "lse[:, r] = np.log(l_sum)", "lse drops the row max"),
     ("pieces", "return min(n, cap_floats // n)", "return min(n, -(-cap_floats // n))", "piece rows rounded up"),
+    ("topk", "order = np.lexsort((np.arange(ln), key, nan))", "order = np.lexsort((-np.arange(ln), key, nan))",
+     "ties go to the higher position"),
+    ("topk", "order = np.lexsort((np.arange(ln), key, nan))", "order = np.argsort(key)",
+     "unstable sort for ties (and NaN not ranked last)"),
+    ("topk", "key = np.where(nan, 0.0, -seg)", "key = np.where(nan, 0.0, seg)", "lowest values selected"),
+    ("topk", "order = np.lexsort((np.arange(ln), key, nan))", "order = np.lexsort((np.arange(ln), key, ~nan))",
+     "NaN ranked first"),
+    ("topk", "out[r, :m] = (order[:m] + s).astype(np.int32)", "out[r, :m] = order[:m].astype(np.int32)",
+     "positions relative to the span start"),
+    ("topk", "m = min(k, ln)", "m = min(k, ln - 1)", "one selection short"),
 ]
 
-FAMILY = {"attention": P.DENSE_PINS, "rope": P.ROPE_PINS, "sparse": P.SPARSE_PINS, "pieces": ["pieces"]}
+FAMILY = {"attention": P.DENSE_PINS, "rope": P.ROPE_PINS, "sparse": P.SPARSE_PINS, "pieces": ["pieces"],
+          "topk": P.TOPK_PINS}
 
 
 def _mutated_oracle(modname, old, new):
