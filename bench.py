@@ -60,6 +60,13 @@ def sparse_bytes(case) -> float:
     return float(r * k * dqk * 2 + r * h * dqk * 2 + r * h * dv * 2 + r * k * 4 + r * h * 4)
 
 
+def indexer_bytes(case) -> float:
+    """Logits of each row's span read once, the k indices written, the row
+    lengths read."""
+    lens = case.row_lens if case.row_lens is not None else [case.logits.shape[1]] * case.logits.shape[0]
+    return float(sum(int(n) for n in lens) * 4 + case.logits.shape[0] * case.k * 4 + len(lens) * 4)
+
+
 def sparse_flops(case) -> float:
     return 2.0 * case.num_rows * case.num_heads * case.k * (case.d_qk + case.d_v)
 
@@ -154,8 +161,17 @@ def bench_other(torch, steps, warmup, only=None):
         res[case.name] = ent
         del st
         torch.cuda.empty_cache()
-    if only is not None and only != "sparse_mqa":
-        return res
+    if only in (None, "sparse_mqa"):
+        res.update(bench_sparse(torch, steps, warmup))
+    if only in (None, "indexer"):
+        res.update(bench_indexer(torch, steps, warmup))
+    return res
+
+
+def bench_sparse(torch, steps, warmup):
+    from vision_encoder_attention_amd import runner as R
+    from vision_encoder_attention_amd import workloads as W
+    res = {}
     # sparse MQA: evict L2 / MALL between timed launches (untimed fill of 1 GiB)
     case = W.full_case("sparse_mqa")
     st = R.stage_sparse(case)
@@ -179,6 +195,28 @@ def bench_other(torch, steps, warmup, only=None):
                       "hbm_traffic_counter_bytes": committed_traffic("sparse_mqa_hbm_counters.txt")}
     del scratch, st
     torch.cuda.empty_cache()
+    return res
+
+
+def bench_indexer(torch, steps, warmup):
+    """Top-k of the sparse indexer (the step before sparse MQA)."""
+    import vision_encoder_attention_amd as vea
+    from vision_encoder_attention_amd import workloads as W
+    res = {}
+    ic = W.indexer()
+    x = torch.from_numpy(ic.logits).cuda()
+    lens = torch.from_numpy(ic.row_lens).cuda()
+    out = torch.empty((x.shape[0], ic.k), dtype=torch.int32, device="cuda")
+    warm_up(torch, lambda: vea.topk_indices(x, ic.k, out, None, lens), max(1, warmup))
+    tm = Timer(torch)
+    for _ in range(steps):
+        tm.run("topk", lambda: vea.topk_indices(x, ic.k, out, None, lens))
+    torch.cuda.synchronize()
+    t_ms, t_min = tm.ms("topk")
+    by = indexer_bytes(ic)
+    res[ic.name] = {"topk_ms": round(t_ms, 4), "topk_min_ms": round(t_min, 4), "gbs": round(by / t_ms / 1e6, 1),
+                    "frac_hbm": round(by / t_ms / 1e6 / PEAK_HBM_GBS, 4), "bytes": by,
+                    "note": "one workgroup per row sorts the row's keys in LDS; latency-bound, not HBM-bound"}
     return res
 
 
@@ -247,7 +285,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy (reference for HBM byte counters)")
-    ap.add_argument("--only", choices=["varlen_gqa", "long_causal", "sparse_mqa"],
+    ap.add_argument("--only", choices=["varlen_gqa", "long_causal", "sparse_mqa", "indexer"],
                     help="only run one of the other workloads (for profiling one kernel family)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

@@ -207,6 +207,33 @@ int vea_sparse_mqa_fwd(const void* q, const void* kv_latent, const int32_t* topk
 int vea_sparse_mqa_workspace_size(int num_rows, int num_heads, int d_qk, int d_v, int k, size_t* bytes);
 
 /*
+ * vea_topk_indices — deterministic top-k selection of the sparse indexer: for
+ * each row, the positions of its k highest logits in rank order.
+ * Sources: the indexer keeps the 2048 best positions of each [2590] row of
+ * logits, and an unstable top-k let equal scores at the edge of the selection
+ * fall either way, fixed by a stable sort [V32] sections 修改topk结果，输出后排序
+ * and 用 torch.sort 替换 topk，输出对比; ties are resolved by id [MI250]
+ * section 4.2.
+ *
+ * Rank order within a row's span: value descending; equal values by
+ * ascending position; NaN after every number (NaNs by position); -0.0 ties
+ * with +0.0.  The result is unique and independent of timing.
+ *
+ *   logits      fp32 [num_rows, row_stride] (4-byte aligned), columns [0, n).
+ *   row_starts  device int32 [num_rows] or NULL (0); row_lens device int32
+ *               [num_rows] or NULL (n - start).  Row r considers columns
+ *               [start, start + len); spans outside [0, n) are clamped
+ *               (VEA_ERANGE under VEA_CHECK).
+ *   n           1 .. 4096 (VEA_EUNSUPPORTED above).
+ *   k           >= 1.  out int32 [num_rows, k]: absolute column positions
+ *               of ranks 0 .. min(k, len) - 1, then -1 (the padding value
+ *               vea_sparse_mqa_fwd skips).
+ */
+int vea_topk_indices(const float* logits, int64_t row_stride, const int32_t* row_starts,
+                     const int32_t* row_lens, int num_rows, int n, int k, int32_t* out,
+                     void* stream);
+
+/*
  * vea_attn_probs_piece — debug export (not on the timed path) of the
  * probability matrix of one query piece of one head:
  *     P[r][j] = exp(scale * q_{q0+r} . k_j - lse_{q0+r}),  r < rows, j < len_k,

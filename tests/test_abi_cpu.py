@@ -32,7 +32,7 @@ def lib():
 def test_header_declares_the_operations():
     names = _declared()
     for n in ("vea_attn_fwd", "vea_attn_fwd_workspace_size", "vea_qkv_rope", "vea_sparse_mqa_fwd",
-              "vea_sparse_mqa_workspace_size",
+              "vea_sparse_mqa_workspace_size", "vea_topk_indices",
               "vea_attn_probs_piece", "vea_status_str"):
         assert n in names
 
@@ -169,6 +169,26 @@ def test_sparse_workspace_size_validation(lib, args, status):
     assert lib.vea_sparse_mqa_workspace_size(*args, ctypes.byref(n)) == status
     assert n.value == 0
     assert lib.vea_sparse_mqa_workspace_size(*args, None) == VEA_EINVAL
+
+
+def _topk(lib, **kw):
+    a = dict(x=FAKE, rs=2590, st=None, ln=None, r=3, n=2590, k=2048, out=FAKE)
+    a.update(kw)
+    return lib.vea_topk_indices(a["x"], a["rs"], a["st"], a["ln"], a["r"], a["n"], a["k"], a["out"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=4097, rs=4097), VEA_EUNSUPPORTED),
+    (dict(k=0), VEA_ESHAPE),
+    (dict(n=0), VEA_ESHAPE),
+    (dict(r=-1), VEA_ESHAPE),
+    (dict(rs=100), VEA_ESHAPE),              # row stride shorter than n
+    (dict(x=None), VEA_EINVAL),
+    (dict(out=FAKE + 2), VEA_EINVAL),        # not 4-byte aligned
+    (dict(r=0), VEA_OK),
+])
+def test_topk_validation(lib, kw, status):
+    assert _topk(lib, **kw) == status
 
 
 def test_probs_validation(lib):

@@ -7,12 +7,13 @@ in ``include/vea.h``); this package is a thin binding over it:
                       causal or not, GQA, query pieces, fp32 online softmax;
 * ``qkv_rope``        fused QKV output split + 1D / 2D-grid RoPE;
 * ``sparse_mqa_fwd``  top-k sparse MQA over a shared latent KV;
+* ``topk_indices``    deterministic top-k positions per row (the sparse indexer);
 * ``attn_probs_piece`` debug export of one piece's probabilities.
 
 ``workloads`` holds the seeded synthetic inputs; ``build`` compiles the library.
 """
 from ._binding import (VeaError, attn_fwd, attn_fwd_workspace_size, attn_probs_piece, lib_path, load_library,  # noqa: F401
-                       qkv_rope, sparse_mqa_fwd, sparse_mqa_workspace_size, status_str)
+                       qkv_rope, sparse_mqa_fwd, sparse_mqa_workspace_size, status_str, topk_indices)
 
 __all__ = ["attn_fwd", "attn_fwd_workspace_size", "qkv_rope", "sparse_mqa_fwd", "sparse_mqa_workspace_size", "attn_probs_piece",
-           "VeaError", "load_library", "lib_path", "status_str"]
+           "topk_indices", "VeaError", "load_library", "lib_path", "status_str"]

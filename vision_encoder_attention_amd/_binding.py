@@ -59,6 +59,8 @@ def load_library():
         lib.vea_sparse_mqa_fwd.restype = i32
         lib.vea_sparse_mqa_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
         lib.vea_sparse_mqa_workspace_size.restype = i32
+        lib.vea_topk_indices.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp]
+        lib.vea_topk_indices.restype = i32
         lib.vea_attn_probs_piece.argtypes = [i32, vp, i64, vp, i64, vp, i64, i32, i32, i32, i32, i32, i32,
                                              i32, i32, i32, i32, i32, f32, vp, i64, vp]
         lib.vea_attn_probs_piece.restype = i32
@@ -240,6 +242,27 @@ def sparse_mqa_fwd(q, kv_latent, topk_idx, k, scale, out, lse=None, workspace="a
                                     _stream(q))
     _check(st)
     return out, lse
+
+
+def topk_indices(logits, k, out, row_starts=None, row_lens=None):
+    """Deterministic top-k positions per row (see vea_topk_indices): logits
+    float32 [R, n] with contiguous columns, out int32 [R, k] contiguous,
+    row_starts / row_lens int32 [R] or None."""
+    lib = load_library()
+    torch = _torch()
+    if logits.dtype != torch.float32 or logits.dim() != 2 or logits.stride(1) != 1 or not logits.is_cuda:
+        raise ValueError("logits must be a float32 GPU tensor [rows, n] with contiguous columns")
+    if out.dtype != torch.int32 or not out.is_contiguous() or tuple(out.shape) != (logits.shape[0], int(k)):
+        raise ValueError("out must be contiguous int32 [rows, k]")
+    for t, nm in ((row_starts, "row_starts"), (row_lens, "row_lens")):
+        if t is not None:
+            _int32_dev(t, nm)
+            if t.numel() != logits.shape[0]:
+                raise ValueError("%s must have one entry per row" % nm)
+    st = lib.vea_topk_indices(_ptr(logits), logits.stride(0), _ptr(row_starts), _ptr(row_lens), logits.shape[0],
+                              logits.shape[1], int(k), _ptr(out), _stream(logits))
+    _check(st)
+    return out
 
 
 def attn_probs_piece(q, k, lse, head, seq_begin_q, len_q, seq_begin_k, len_k, q0, rows, causal, scale, p_out):

@@ -304,6 +304,33 @@ int vea_sparse_mqa_fwd(const void* q, const void* kv_latent, const int32_t* topk
   return finish(hip_status(launch_sparse_mqa(p, d_qk, d_v, s)), s);
 }
 
+int vea_topk_indices(const float* logits, int64_t row_stride, const int32_t* row_starts, const int32_t* row_lens,
+                     int num_rows, int n, int k, int32_t* out, void* stream) {
+  if (num_rows < 0 || n < 1 || k < 1) return VEA_ESHAPE;
+  if (row_stride < n) return VEA_ESHAPE;
+  if (n > kTopkMaxN) return VEA_EUNSUPPORTED;
+  if (num_rows == 0) return VEA_OK;
+  if (!logits || !out) return VEA_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(logits) & 3u) || (reinterpret_cast<uintptr_t>(out) & 3u)) return VEA_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  if (check_enabled()) {
+    std::vector<int32_t> hs, hl;
+    int st = VEA_OK;
+    if (row_starts) st = fetch_ints(row_starts, (size_t)num_rows, s, hs);
+    if (st == VEA_OK && row_lens) st = fetch_ints(row_lens, (size_t)num_rows, s, hl);
+    if (st != VEA_OK) return st;
+    for (int r = 0; r < num_rows; ++r) {
+      const int64_t b = row_starts ? hs[r] : 0;
+      const int64_t l = row_lens ? hl[r] : n - b;
+      if (b < 0 || l < 0 || b + l > n) return VEA_ERANGE;
+    }
+  }
+  TopkParams p;
+  p.logits = logits; p.row_stride = row_stride; p.starts = row_starts; p.lens = row_lens; p.out = out;
+  p.rows = num_rows; p.n = n; p.k = k;
+  return finish(hip_status(launch_topk(p, s)), s);
+}
+
 int vea_attn_probs_piece(int dtype, const void* q, int64_t q_tok_stride, const void* k, int64_t k_tok_stride,
                          const float* lse, int64_t lse_row_stride, int head, int num_heads_q, int num_heads_kv,
                          int head_dim, int seq_begin_q, int len_q, int seq_begin_k, int len_k, int q0, int rows,

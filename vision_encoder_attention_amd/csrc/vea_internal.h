@@ -111,6 +111,17 @@ hipError_t launch_qkv_rope(const RopeParams& p, hipStream_t s);
 hipError_t launch_sparse_mqa(const SparseParams& p, int d_qk, int d_v, hipStream_t s);
 hipError_t launch_attn_probs(const ProbsParams& p, bool bf16, hipStream_t s);
 
+struct TopkParams {
+  const float* logits;       // [rows, row_stride] fp32
+  int64_t row_stride;        // elements
+  const int32_t* starts;     // nullable: 0
+  const int32_t* lens;       // nullable: n - start
+  int32_t* out;              // [rows, k]
+  int rows, n, k;
+};
+constexpr int kTopkMaxN = 4096;   // positions per row the LDS sort holds
+hipError_t launch_topk(const TopkParams& p, hipStream_t s);
+
 // Tile shape of the dense bf16/f32 kernels (query rows per workgroup); the
 // host uses it to size the launch.
 constexpr int kDenseBM = 128;

@@ -284,6 +284,32 @@ def permute_rows(idx: np.ndarray, seed: int) -> np.ndarray:
 
 # ------------------------------------------------------- named workloads
 
+@dataclasses.dataclass
+class IndexerCase:
+    """Top-k selection over indexer logits."""
+    name: str
+    logits: np.ndarray              # [R, n] float32
+    k: int
+    row_starts: Optional[np.ndarray]  # [R] int32 or None
+    row_lens: Optional[np.ndarray]    # [R] int32 or None
+
+
+def indexer(rows: int = 323, n: int = 2590, k: int = 2048, grid: float = 1.0 / 16, seed: int = 6) -> IndexerCase:
+    """Logits of the sparse indexer's top-k: rows [323, 2590] fp32, the
+    last `rows` of n positions, row r seeing positions [0, n - rows + r + 1)
+    (at least k of them).  Values are N(0,1) rounded to a grid of `grid`, so
+    equal scores are common and fall at the edge of the selection, the case
+    that made an unstable top-k disagree with itself."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, n), dtype=np.float32)
+    if grid:
+        x = (np.round(x / grid) * grid).astype(np.float32)
+    lens = np.minimum(n - rows + 1 + np.arange(rows), n).astype(np.int32)
+    if lens.min() < k:
+        raise ValueError("a row sees fewer than k positions")
+    return IndexerCase("indexer_r%d_n%d_k%d" % (rows, n, k), x, k, None, lens)
+
+
 FULL_CASES = ("single_head_f32", "vision", "varlen_gqa", "long_causal", "sparse_mqa")
 
 
