@@ -13,10 +13,10 @@
 // 64-bit key, its value mapped to an order-preserving 32-bit code in the high
 // half and the bitwise complement of its position in the low half, so that
 // "key descending" is exactly the rank order and no two keys are equal.  One
-// workgroup sorts a row's keys with a bitonic network in LDS (a fixed
-// sequence of compare-exchanges: the result cannot depend on timing) and
-// writes the positions of the first k keys.  Positions past the row's span
-// get key 0, below every valid key, and come out as -1.
+// workgroup sorts a row's keys with a bitonic network (a fixed sequence of
+// compare-exchanges: the result cannot depend on timing) and writes the
+// positions of the first k keys.  Positions past the row's span get key 0,
+// below every valid key, and come out as -1.
 #include "vea_internal.h"
 
 #include <math.h>
@@ -35,49 +35,79 @@ __device__ __forceinline__ uint32_t order_code(float x) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// Bitonic network over CAP = 4096 keys (the row, padded with 0 keys),
+// descending, with the compare-exchanges in registers: each thread holds 16
+// keys whose indices differ only in a window of 4 consecutive index bits
+// [lo, lo + 4), the other 8 bits being its thread id, so the strides 2^lo ..
+// 2^(lo+3) pair keys of the same thread.  The keys pass through LDS only when
+// the window moves (21 times for 4096 keys instead of a barrier for each of
+// the 78 strides).  Every merge width w and stride j pair (i, i + j) with bit
+// j of i clear; blocks with bit w clear go descending, the others ascending,
+// so the last merge leaves the row descending.
 template <int CAP>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
-  __shared__ uint64_t keys[CAP];
+  constexpr int E = CAP / kTopkThreads;
+  constexpr int LOG = 12;
+  static_assert(E == 16 && (1 << LOG) == CAP, "16 keys per thread, 4096 keys");
+  __shared__ uint64_t keys[CAP + CAP / 16];             // one pad slot per 16: few bank conflicts
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
-  int s = 0, len = p.n;
+  int s = 0, len;
   if (p.starts != nullptr) s = min(max(p.starts[r], 0), p.n);
   if (p.lens != nullptr) len = min(max(p.lens[r], 0), p.n - s);
   else len = p.n - s;
-  int size = 2;                                         // sort width: a power of two >= len
-  while (size < len) size <<= 1;
 
+  // index of this thread's key e under window [lo, lo + 4)
+  auto idx = [&](int lo, int e) { return (tid & ((1 << lo) - 1)) | ((tid >> lo) << (lo + 4)) | (e << lo); };
+  auto slot = [](int i) { return i + (i >> 4); };
+
+  uint64_t v[E];
   const float* row = p.logits + (int64_t)r * p.row_stride + s;
-  for (int i = tid; i < size; i += kTopkThreads) {
-    uint64_t key = 0;
-    if (i < len) key = ((uint64_t)order_code(row[i]) << 32) | (uint32_t)~(uint32_t)(s + i);
-    keys[i] = key;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {                         // window [0, 4): index 16 tid + e
+    const int i = E * tid + e;
+    v[e] = i < len ? ((uint64_t)order_code(row[i]) << 32) | (uint32_t)~(uint32_t)(s + i) : 0ull;
   }
-  __syncthreads();
-
-  // Bitonic network, descending: for every merge width w and stride j, pair
-  // (i, i + j) with i's bit j clear; blocks with bit w clear are put in
-  // descending order, the others ascending, so the last merge (w = size)
-  // leaves the whole row descending.
-  for (int w = 2; w <= size; w <<= 1) {
-    for (int j = w >> 1; j > 0; j >>= 1) {
-      for (int t = tid; t < (size >> 1); t += kTopkThreads) {
-        const int i = 2 * t - (t & (j - 1));
-        const uint64_t a = keys[i], b = keys[i + j];
-        const bool desc = (i & w) == 0;
-        if (desc ? (a < b) : (a > b)) {
-          keys[i] = b;
-          keys[i + j] = a;
+  int lo = 0;
+  for (int sb = 1; sb <= LOG; ++sb) {                   // merge width w = 2^sb
+    const int w = 1 << sb;
+    for (int hi = sb - 1; hi >= 0; hi -= 4) {           // strides 2^hi .. 2^max(hi-3, 0)
+      const int nlo = max(hi - 3, 0);
+      if (nlo != lo) {
+        // Each thread writes back exactly the slots it read under the old
+        // window, so one barrier (between the writes and the reads) suffices.
+#pragma unroll
+        for (int e = 0; e < E; ++e) keys[slot(idx(lo, e))] = v[e];
+        __syncthreads();
+        lo = nlo;
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[e] = keys[slot(idx(lo, e))];
+      }
+#pragma unroll
+      for (int m = 3; m >= 0; --m) {
+        if (lo + m > hi) continue;                      // a passenger bit of this window
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if (e & (1 << m)) continue;
+          const int e2 = e | (1 << m);
+          const bool desc = (idx(lo, e) & w) == 0;
+          const uint64_t a = v[e], c = v[e2];
+          const bool sw = desc ? (a < c) : (a > c);
+          v[e] = sw ? c : a;
+          v[e2] = sw ? a : c;
         }
       }
-      __syncthreads();
     }
   }
-
+  // window [0, 4) again: key e of this thread is rank 16 tid + e
   const int m = min(p.k, len);
   int32_t* out = p.out + (int64_t)r * p.k;
-  for (int t = tid; t < p.k; t += kTopkThreads)
-    out[t] = t < m ? (int32_t)~(uint32_t)(keys[t] & 0xFFFFFFFFu) : -1;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int t = E * tid + e;
+    if (t < p.k) out[t] = t < m ? (int32_t)~(uint32_t)(v[e] & 0xFFFFFFFFu) : -1;
+  }
+  for (int t = CAP + tid; t < p.k; t += kTopkThreads) out[t] = -1;
 }
 
 }  // namespace
