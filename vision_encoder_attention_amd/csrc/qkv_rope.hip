@@ -24,10 +24,13 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace vea {
 namespace {
 
 constexpr int kRopeMaxHalf = 128;   // head_dim <= 256
+constexpr int kRopeMaxTokens = 8;   // tokens per workgroup
 
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -37,15 +40,21 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-__global__ __launch_bounds__(256) void qkv_rope_kernel(RopeParams p) {
-  __shared__ float cs[kRopeMaxHalf];
-  __shared__ float sn[kRopeMaxHalf];
-  const int t = blockIdx.x;
+// One workgroup rotates `tpw` consecutive tokens (several when a token's row
+// is short, so that every thread has work): first their angle tables, then
+// their 16-byte chunks.
+__global__ __launch_bounds__(256) void qkv_rope_kernel(RopeParams p, int tpw) {
+  __shared__ float cs[kRopeMaxTokens][kRopeMaxHalf];
+  __shared__ float sn[kRopeMaxTokens][kRopeMaxHalf];
+  const int t0 = blockIdx.x * tpw;
+  const int nt = min(tpw, p.tokens - t0);                    // tokens of this workgroup
   const int half = p.d >> 1;
   const double log2_theta = log2(p.theta);
 
-  // Angle table of this token, indexed by the pair's index inside the head.
-  for (int i = threadIdx.x; i < half; i += blockDim.x) {
+  // Angle tables, indexed by (token, pair index inside the head).
+  for (int idx = threadIdx.x; idx < nt * half; idx += blockDim.x) {
+    const int tk = idx / half, i = idx - tk * half;
+    const int t = t0 + tk;
     double pos, expo;
     if (p.pos_dims == 1) {
       pos = (double)p.pos[t];
@@ -58,28 +67,29 @@ __global__ __launch_bounds__(256) void qkv_rope_kernel(RopeParams p) {
       expo = -2.0 * (double)ii / (double)(p.d >> 1);         // span d/2
     }
     const double ang = pos * exp2(expo * log2_theta);
-    double s, c;
-    sincos(ang, &s, &c);
-    cs[i] = (float)c;
-    sn[i] = (float)s;
+    double sv, cv;
+    sincos(ang, &sv, &cv);
+    cs[tk][i] = (float)cv;
+    sn[tk][i] = (float)sv;
   }
   __syncthreads();
 
   const int cph = p.d >> 3;                                  // 16-byte chunks per head
-  const int nchunks = (p.hq + p.hkv) * cph;
-  const uint16_t* src = p.x + (int64_t)t * p.x_stride;
-  for (int ci = threadIdx.x; ci < nchunks; ci += blockDim.x) {
+  const int nchunks = (p.hq + p.hkv) * cph;                  // per token
+  for (int idx = threadIdx.x; idx < nt * nchunks; idx += blockDim.x) {
+    const int tk = idx / nchunks, ci = idx - tk * nchunks;
+    const int t = t0 + tk;
     const int head = ci / cph;
     const int ch = ci - head * cph;
-    const u32x4 v = *(const u32x4*)(src + 8 * ci);
+    const u32x4 v = *(const u32x4*)(p.x + (int64_t)t * p.x_stride + 8 * ci);
     u32x4 o;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const int pi = 4 * ch + w;                             // pair index inside the head
       const float x0 = bf16lo(v[w]), x1 = bf16hi(v[w]);
-      const float c = cs[pi], s = sn[pi];
-      const float y0 = fmaf(x0, c, -(x1 * s));
-      const float y1 = fmaf(x0, s, x1 * c);
+      const float c = cs[tk][pi], sv = sn[tk][pi];
+      const float y0 = fmaf(x0, c, -(x1 * sv));
+      const float y1 = fmaf(x0, sv, x1 * c);
       o[w] = pack2(y0, y1);
     }
     uint16_t* dst = head < p.hq ? p.q + ((int64_t)t * p.hq + head) * p.d + 8 * ch
@@ -92,7 +102,10 @@ __global__ __launch_bounds__(256) void qkv_rope_kernel(RopeParams p) {
 
 hipError_t launch_qkv_rope(const RopeParams& p, hipStream_t s) {
   if (p.tokens == 0) return hipSuccess;
-  hipLaunchKernelGGL(qkv_rope_kernel, dim3(p.tokens), dim3(256), 0, s, p);
+  // tokens per workgroup: enough 16-byte chunks for about 4 per thread
+  const int nchunks = (p.hq + p.hkv) * (p.d >> 3);
+  const int tpw = std::max(1, std::min(kRopeMaxTokens, 1024 / std::max(1, nchunks)));
+  hipLaunchKernelGGL(qkv_rope_kernel, dim3((p.tokens + tpw - 1) / tpw), dim3(256), 0, s, p, tpw);
   return hipGetLastError();
 }
 
