@@ -18,7 +18,8 @@ What it computes is the plain definition of each operation, in float64:
 * ``attn_probs``     the probability matrix P of one query piece.
 * ``rope_*`` / ``qkv_rope``  rotary position embedding on the Q and K heads
                      of a fused QKV projection output (1D and 2D grid).
-* ``sparse_mqa``     multi-query attention over a per-row set of latent rows.
+* ``sparse_mqa``     multi-query attention over a per-row set of latent rows;
+                     ``sparse_mqa_paged`` the same over a paged cache.
 * ``topk_indices``   deterministic top-k selection of the sparse indexer
                      (ties go to the lower position).
 * ``pieces``         query-piece arithmetic of the vision encoder.
@@ -35,6 +36,6 @@ brute force, independent library implementations and invariants.
 """
 from .attention import attention, attn_probs  # noqa: F401
 from .rope import rope_1d, rope_2d, qkv_rope, rope_inv_freq  # noqa: F401
-from .sparse import sparse_mqa  # noqa: F401
+from .sparse import paged_rows, sparse_mqa, sparse_mqa_paged  # noqa: F401
 from .pieces import piece_ranges, piece_rows_for_capacity  # noqa: F401
 from .topk import topk_indices  # noqa: F401

@@ -460,7 +460,43 @@ def pin_sparse_reductions(orc):
     assert np.allclose(o2[2], ref3.numpy()[0], rtol=0, atol=1e-14)
 
 
-SPARSE_PINS = [pin_sparse_permutation, pin_sparse_brute, pin_sparse_reductions]
+def pin_paged_rows_brute(orc):
+    """Each logical position looked up by hand: page j // ps of the table,
+    offset j % ps inside that physical page."""
+    pt = [5, 0, 3, 7, 1]
+    for ps in (1, 2, 4):
+        n = len(pt) * ps - 1
+        rows = orc.paged_rows(pt, ps, n)
+        for j in range(n):
+            page, off = divmod(j, ps)
+            assert rows[j] == pt[page] * ps + off, (ps, j)
+
+
+def pin_paged_scatter_roundtrip(orc):
+    """A logical cache scattered into shuffled physical pages (plus unused
+    ones) through a table gives the unpaged result bitwise; the identity
+    table gives it too."""
+    rng = _rng(404)
+    rows, heads, n_kv, d_qk, dv, ps = 3, 4, 37, 10, 6, 4
+    q = rng.standard_normal((rows, heads, d_qk))
+    kv = rng.standard_normal((n_kv, d_qk))
+    idx = np.stack([rng.permutation(n_kv)[:11] for _ in range(rows)])
+    want_o, want_l = orc.sparse_mqa(q, kv, idx, dv, 0.3)
+    n_pages = -(-n_kv // ps)
+    phys = rng.permutation(n_pages + 3)[:n_pages]            # 3 physical pages left unused
+    cache = rng.standard_normal(((n_pages + 3) * ps, d_qk))  # garbage everywhere else
+    for j in range(n_kv):
+        cache[phys[j // ps] * ps + j % ps] = kv[j]
+    o, l = orc.sparse_mqa_paged(q, cache, phys, ps, n_kv, idx, dv, 0.3)
+    assert np.array_equal(o, want_o) and np.array_equal(l, want_l)
+    ident = np.zeros(((n_pages) * ps, d_qk))
+    ident[:n_kv] = kv
+    o2, l2 = orc.sparse_mqa_paged(q, ident, np.arange(n_pages), ps, n_kv, idx, dv, 0.3)
+    assert np.array_equal(o2, want_o) and np.array_equal(l2, want_l)
+
+
+SPARSE_PINS = [pin_sparse_permutation, pin_sparse_brute, pin_sparse_reductions, pin_paged_rows_brute,
+               pin_paged_scatter_roundtrip]
 
 
 # ====================================================================== top-k

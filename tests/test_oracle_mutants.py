@@ -54,6 +54,10 @@ MUTANTS = [
     ("sparse", "kr[:, :d_v]", "kr[:, d_qk - d_v:]", "V taken from the last latent columns"),
     ("sparse", "sel = idx[r][idx[r] >= 0]", "sel = np.unique(idx[r][idx[r] >= 0])", "repeated indices collapsed"),
     ("sparse", "lse[:, r] = m + np.log(l_sum)", "lse[:, r] = np.log(l_sum)", "lse drops the row max"),
+    ("sparse", "return pt[j // page_size] * page_size + j % page_size",
+     "return pt[j % page_size] * page_size + j // page_size", "page index and offset swapped"),
+    ("sparse", "return pt[j // page_size] * page_size + j % page_size", "return pt[j // page_size] + j % page_size",
+     "physical page not scaled by the page size"),
     ("pieces", "return min(n, cap_floats // n)", "return min(n, -(-cap_floats // n))", "piece rows rounded up"),
     ("topk", "order = np.lexsort((np.arange(ln), key, nan))", "order = np.lexsort((-np.arange(ln), key, nan))",
      "ties go to the higher position"),
