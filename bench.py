@@ -193,7 +193,38 @@ def bench_sparse(torch, steps, warmup):
                       "gbs": round(by / s_ms / 1e6, 1), "frac_hbm": round(by / s_ms / 1e6 / PEAK_HBM_GBS, 4),
                       "tflops": round(fl / s_ms / 1e9, 2), "bytes": by, "flops": fl,
                       "hbm_traffic_counter_bytes": committed_traffic("sparse_mqa_hbm_counters.txt")}
-    del scratch, st
+    # the same workload over a paged cache: 64-row pages in shuffled places
+    import numpy as np
+    import vision_encoder_attention_amd as vea
+    ps = 64
+    rng = np.random.default_rng(64)
+    n_pages = -(-case.kv_latent.shape[0] // ps)
+    table = rng.permutation(n_pages + 8)[:n_pages].astype(np.int32)
+    cache = np.zeros(((n_pages + 8) * ps, case.kv_latent.shape[1]), np.uint16)
+    j = np.arange(case.kv_latent.shape[0])
+    cache[table[j // ps] * ps + j % ps] = case.kv_latent
+    kvc = R.bits_to_tensor(cache, "cuda")
+    pt = torch.from_numpy(table).cuda()
+
+    def paged():
+        vea.sparse_mqa_paged_fwd(st.q, kvc, pt, ps, case.kv_latent.shape[0], st.idx, case.k, case.scale, st.out,
+                                 st.lse, workspace=st.ws)
+
+    def fill_and_paged():
+        scratch.fill_(1)
+        paged()
+
+    warm_up(torch, fill_and_paged, max(1, warmup))
+    tm = Timer(torch)
+    for _ in range(steps):
+        scratch.fill_(1)
+        tm.run("paged", paged)
+    torch.cuda.synchronize()
+    p_ms, p_min = tm.ms("paged")
+    res[case.name + "_paged64"] = {"sparse_mqa_ms": round(p_ms, 4), "sparse_mqa_min_ms": round(p_min, 4),
+                                   "gbs": round(by / p_ms / 1e6, 1), "frac_hbm": round(by / p_ms / 1e6 / PEAK_HBM_GBS, 4),
+                                   "page_size": ps}
+    del scratch, st, kvc
     torch.cuda.empty_cache()
     return res
 

@@ -199,6 +199,30 @@ int vea_sparse_mqa_fwd(const void* q, const void* kv_latent, const int32_t* topk
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * vea_sparse_mqa_paged_fwd — vea_sparse_mqa_fwd over a paged latent cache.
+ * Sources: the sparse attention fetches its KV rows through a page table
+ * [V32] section 实验方法和结果; the prefill path keeps a paged KV cache
+ * [SGLang] section 2.2.
+ *
+ *   kv_cache    bf16 [num_pages * page_size, d_qk]: num_pages physical pages
+ *               of page_size rows, contiguous.
+ *   page_table  device int32 [ceil(n_kv / page_size)]: logical position j
+ *               (the values in topk_idx, 0 <= j < n_kv) is row
+ *               page_table[j / page_size] * page_size + j % page_size of
+ *               kv_cache.  Entries must lie in [0, num_pages) (VEA_ERANGE
+ *               under VEA_CHECK; otherwise a row past the cache reads as 0).
+ *   page_size   a power of two, 1 .. 65536.
+ * Every other argument as vea_sparse_mqa_fwd (the same workspace size).  The
+ * indices are put in canonical order by their LOGICAL position before the
+ * table is applied, so the output is bitwise independent of both the index
+ * order and the placement of the pages.
+ */
+int vea_sparse_mqa_paged_fwd(const void* q, const void* kv_cache, const int32_t* page_table, int page_size,
+                             int num_pages, const int32_t* topk_idx, int num_rows, int num_heads, int n_kv,
+                             int d_qk, int d_v, int k, float scale, void* out, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * vea_sparse_mqa_workspace_size — bytes of workspace vea_sparse_mqa_fwd uses
  * for these sizes on the current HIP device (0 when no split pays off, e.g.
  * when the units fill whole rounds of the CUs).  Validates like

@@ -32,7 +32,7 @@ def lib():
 def test_header_declares_the_operations():
     names = _declared()
     for n in ("vea_attn_fwd", "vea_attn_fwd_workspace_size", "vea_qkv_rope", "vea_sparse_mqa_fwd",
-              "vea_sparse_mqa_workspace_size", "vea_topk_indices",
+              "vea_sparse_mqa_workspace_size", "vea_topk_indices", "vea_sparse_mqa_paged_fwd",
               "vea_attn_probs_piece", "vea_status_str"):
         assert n in names
 
@@ -169,6 +169,28 @@ def test_sparse_workspace_size_validation(lib, args, status):
     assert lib.vea_sparse_mqa_workspace_size(*args, ctypes.byref(n)) == status
     assert n.value == 0
     assert lib.vea_sparse_mqa_workspace_size(*args, None) == VEA_EINVAL
+
+
+def _paged(lib, **kw):
+    a = dict(q=FAKE, kv=FAKE, pt=FAKE, ps=64, npg=41, idx=FAKE, r=3, h=128, nkv=2590, dqk=576, dv=512, k=64,
+             scale=0.04, out=FAKE, lse=None)
+    a.update(kw)
+    return lib.vea_sparse_mqa_paged_fwd(a["q"], a["kv"], a["pt"], a["ps"], a["npg"], a["idx"], a["r"], a["h"],
+                                        a["nkv"], a["dqk"], a["dv"], a["k"], a["scale"], a["out"], a["lse"], None, 0,
+                                        None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ps=48), VEA_ESHAPE),               # not a power of two
+    (dict(ps=0), VEA_ESHAPE),
+    (dict(npg=-1), VEA_ESHAPE),
+    (dict(pt=None), VEA_EINVAL),
+    (dict(npg=1 << 20), VEA_EUNSUPPORTED),   # rows past 32-bit byte offsets
+    (dict(dqk=512), VEA_EUNSUPPORTED),
+    (dict(r=0), VEA_OK),
+])
+def test_sparse_paged_validation(lib, kw, status):
+    assert _paged(lib, **kw) == status
 
 
 def _topk(lib, **kw):

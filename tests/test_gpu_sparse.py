@@ -207,3 +207,61 @@ def test_workspace_too_small_is_rejected(torch):
     with pytest.raises(vea.VeaError) as e:
         vea.sparse_mqa_fwd(st.q, st.kv, st.idx, 256, case.scale, st.out, st.lse, workspace=small)
     assert e.value.status == -6
+
+
+# ------------------------------------------------------------ paged cache
+
+def _page_out(kv_bits, ps, extra_pages, seed):
+    """Scatter a logical latent cache into shuffled physical pages, with
+    unused garbage pages in between; returns (cache bits, page table)."""
+    rng = np.random.default_rng(seed)
+    n_kv, dqk = kv_bits.shape
+    n_pages = -(-n_kv // ps)
+    table = rng.permutation(n_pages + extra_pages)[:n_pages].astype(np.int32)
+    cache = W.randn_bf16_bits(rng, ((n_pages + extra_pages) * ps, dqk))
+    rows = oracle.paged_rows(table, ps, n_kv)
+    cache[rows] = kv_bits
+    return cache, table
+
+
+def _run_paged(torch, case, cache, table, ps, idx=None):
+    import vision_encoder_attention_amd as vea
+    dev = "cuda"
+    q = R.bits_to_tensor(case.q, dev)
+    kvc = R.bits_to_tensor(cache, dev)
+    pt = torch.from_numpy(table).to(dev)
+    ix = torch.from_numpy(np.ascontiguousarray(case.topk_idx if idx is None else idx, np.int32)).to(dev)
+    out = torch.empty((case.num_rows, case.num_heads, case.d_v), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((case.num_heads, case.num_rows), dtype=torch.float32, device=dev)
+    vea.sparse_mqa_paged_fwd(q, kvc, pt, ps, case.kv_latent.shape[0], ix, ix.shape[1], case.scale, out, lse)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("ps", [1, 16, 64])
+def test_paged_cache_against_the_oracle(torch, ps):
+    """Logical positions resolved through a shuffled page table (garbage in
+    the unused pages), with padding; against the oracle's paged view."""
+    case = W.sparse_mqa(rows=5, heads=128, n_kv=700, k=256, seed=40 + ps)
+    idx = case.topk_idx.copy()
+    idx[1, ::4] = -1
+    cache, table = _page_out(case.kv_latent, ps, extra_pages=5, seed=50 + ps)
+    out, lse = _run_paged(torch, case, cache, table, ps, idx)
+    o_ref, l_ref = oracle.sparse_mqa_paged(W.bf16_bits_to_f64(case.q), W.bf16_bits_to_f64(cache), table, ps,
+                                           case.kv_latent.shape[0], idx, case.d_v, float(np.float32(case.scale)))
+    assert_bf16_close(W.bf16_bits_to_f64(R.tensor_to_bits(out)), o_ref, "paged out")
+    assert_bf16_close(lse.cpu().numpy().astype(np.float64), l_ref, "paged lse")
+
+
+def test_paged_result_is_independent_of_page_placement(torch):
+    """The full workload in two different page layouts (and with each row's
+    indices in another order) gives bitwise the unpaged result: the indices
+    are ordered by logical position before the table is applied."""
+    case = W.full_case("sparse_mqa")
+    st = _run(torch, case)
+    for ps, seed in ((64, 61), (16, 62)):
+        cache, table = _page_out(case.kv_latent, ps, extra_pages=9, seed=seed)
+        out, lse = _run_paged(torch, case, cache, table, ps)
+        assert torch.equal(out, st.out) and torch.equal(lse, st.lse), ps
+    out, lse = _run_paged(torch, case, cache, table, 16, W.permute_rows(case.topk_idx, 111))
+    assert torch.equal(out, st.out) and torch.equal(lse, st.lse)

@@ -57,6 +57,9 @@ def load_library():
         lib.vea_sparse_mqa_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp,
                                            ctypes.c_size_t, vp]
         lib.vea_sparse_mqa_fwd.restype = i32
+        lib.vea_sparse_mqa_paged_fwd.argtypes = [vp, vp, vp, i32, i32, vp, i32, i32, i32, i32, i32, i32, f32, vp, vp,
+                                                 vp, ctypes.c_size_t, vp]
+        lib.vea_sparse_mqa_paged_fwd.restype = i32
         lib.vea_sparse_mqa_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
         lib.vea_sparse_mqa_workspace_size.restype = i32
         lib.vea_topk_indices.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp]
@@ -240,6 +243,43 @@ def sparse_mqa_fwd(q, kv_latent, topk_idx, k, scale, out, lse=None, workspace="a
                                     kv_latent.shape[0], q.shape[2], out.shape[2], int(k), float(scale), _ptr(out),
                                     _ptr(lse), _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                     _stream(q))
+    _check(st)
+    return out, lse
+
+
+def sparse_mqa_paged_fwd(q, kv_cache, page_table, page_size, n_kv, topk_idx, k, scale, out, lse=None,
+                         workspace="auto"):
+    """Top-k sparse MQA over a paged latent cache (see vea_sparse_mqa_paged_fwd):
+    kv_cache [num_pages * page_size, d_qk] bf16, page_table int32
+    [ceil(n_kv / page_size)], topk_idx int32 [R, k] of logical positions."""
+    lib = load_library()
+    torch = _torch()
+    for t, n in ((q, "q"), (kv_cache, "kv_cache"), (out, "out")):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("%s must be a contiguous bfloat16 GPU tensor" % n)
+    _int32_dev(topk_idx, "topk_idx")
+    _int32_dev(page_table, "page_table")
+    page_size = int(page_size)
+    if page_size < 1 or kv_cache.shape[0] % page_size:
+        raise ValueError("kv_cache rows must be a multiple of page_size")
+    if page_table.numel() < -(-int(n_kv) // page_size):
+        raise ValueError("page_table needs ceil(n_kv / page_size) entries")
+    if topk_idx.shape != (q.shape[0], k):
+        raise ValueError("topk_idx must be [rows, k]")
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (q.shape[1], q.shape[0])
+                            or not lse.is_contiguous()):
+        raise ValueError("lse must be contiguous float32 [heads, rows]")
+    with torch.cuda.device(q.device):
+        if isinstance(workspace, str):
+            if workspace != "auto":
+                raise ValueError('workspace must be "auto", None or a uint8 GPU tensor')
+            nbytes = sparse_mqa_workspace_size(q.shape[0], q.shape[1], q.shape[2], out.shape[2], k)
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
+        st = lib.vea_sparse_mqa_paged_fwd(_ptr(q), _ptr(kv_cache), _ptr(page_table), page_size,
+                                          kv_cache.shape[0] // page_size, _ptr(topk_idx), q.shape[0], q.shape[1],
+                                          int(n_kv), q.shape[2], out.shape[2], int(k), float(scale), _ptr(out),
+                                          _ptr(lse), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                          _stream(q))
     _check(st)
     return out, lse
 

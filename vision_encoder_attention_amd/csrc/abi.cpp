@@ -262,25 +262,38 @@ int vea_sparse_mqa_workspace_size(int num_rows, int num_heads, int d_qk, int d_v
   return VEA_OK;
 }
 
-int vea_sparse_mqa_fwd(const void* q, const void* kv_latent, const int32_t* topk_idx, int num_rows, int num_heads,
-                       int n_kv, int d_qk, int d_v, int k, float scale, void* out, float* lse, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+namespace {
+
+int sparse_fwd(const void* q, const void* kv, const int32_t* page_table, int page_size, int num_pages,
+               const int32_t* topk_idx, int num_rows, int num_heads, int n_kv, int d_qk, int d_v, int k, float scale,
+               void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   if (n_kv < 0) return VEA_ESHAPE;
   int st = sparse_shape_status(num_rows, num_heads, d_qk, d_v, k);
   if (st != VEA_OK) return st;
   if (!isfinite(scale)) return VEA_EINVAL;
+  int shift = 0;
+  int64_t n_phys = n_kv;
+  if (page_table != nullptr) {
+    if (page_size < 1 || page_size > (1 << 16) || (page_size & (page_size - 1)) || num_pages < 0) return VEA_ESHAPE;
+    while ((1 << shift) < page_size) ++shift;
+    n_phys = (int64_t)num_pages * page_size;
+  }
+  if (n_phys * 1152 >= ((int64_t)1 << 32) || n_kv >= (1 << 24)) return VEA_EUNSUPPORTED;   // 32-bit row offsets
   if (num_rows == 0) return VEA_OK;
-  if (!q || !topk_idx || !out || (n_kv > 0 && !kv_latent)) return VEA_EINVAL;
-  if (!aligned16(q) || !aligned16(out) || (kv_latent && !aligned16(kv_latent))) return VEA_EINVAL;
+  if (!q || !topk_idx || !out || (n_phys > 0 && !kv)) return VEA_EINVAL;
+  if (!aligned16(q) || !aligned16(out) || (kv && !aligned16(kv))) return VEA_EINVAL;
   if (workspace != nullptr && !aligned16(workspace)) return VEA_EWORKSPACE;
   SparseParams p;
-  p.q = (const uint16_t*)q; p.kv = (const uint16_t*)kv_latent; p.idx = topk_idx; p.out = (uint16_t*)out;
+  p.q = (const uint16_t*)q; p.kv = (const uint16_t*)kv; p.idx = topk_idx; p.out = (uint16_t*)out;
   p.lse = lse; p.rows = num_rows; p.heads = num_heads; p.n_kv = n_kv; p.k = k;
   p.head_blocks = (num_heads + kSparseHeadsPerWG - 1) / kSparseHeadsPerWG;
   p.scale = scale;
   p.full_units = num_rows * p.head_blocks;
   p.nsplit = 1;
   p.ws = nullptr;
+  p.page_table = page_table;
+  p.page_shift = shift;
+  p.n_phys = (int)n_phys;
   if (workspace != nullptr) {
     int cus = 0;
     st = current_cus(&cus);
@@ -300,8 +313,32 @@ int vea_sparse_mqa_fwd(const void* q, const void* kv_latent, const int32_t* topk
     if (st != VEA_OK) return st;
     for (int32_t x : h)
       if (x >= n_kv) return VEA_ERANGE;
+    if (page_table != nullptr) {
+      st = fetch_ints(page_table, (size_t)((n_kv + page_size - 1) / page_size), s, h);
+      if (st != VEA_OK) return st;
+      for (int32_t x : h)
+        if (x < 0 || x >= num_pages) return VEA_ERANGE;
+    }
   }
   return finish(hip_status(launch_sparse_mqa(p, d_qk, d_v, s)), s);
+}
+
+}  // namespace
+
+int vea_sparse_mqa_fwd(const void* q, const void* kv_latent, const int32_t* topk_idx, int num_rows, int num_heads,
+                       int n_kv, int d_qk, int d_v, int k, float scale, void* out, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return sparse_fwd(q, kv_latent, nullptr, 0, 0, topk_idx, num_rows, num_heads, n_kv, d_qk, d_v, k, scale, out, lse,
+                    workspace, workspace_bytes, stream);
+}
+
+int vea_sparse_mqa_paged_fwd(const void* q, const void* kv_cache, const int32_t* page_table, int page_size,
+                             int num_pages, const int32_t* topk_idx, int num_rows, int num_heads, int n_kv, int d_qk,
+                             int d_v, int k, float scale, void* out, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (page_table == nullptr && num_rows > 0) return VEA_EINVAL;
+  return sparse_fwd(q, kv_cache, page_table, page_size, num_pages, topk_idx, num_rows, num_heads, n_kv, d_qk, d_v, k,
+                    scale, out, lse, workspace, workspace_bytes, stream);
 }
 
 int vea_topk_indices(const float* logits, int64_t row_stride, const int32_t* row_starts, const int32_t* row_lens,

@@ -312,6 +312,17 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
   // chunk's share of a split unit.  The key loop sees the list from entry
   // t0 BN on (srow) and the valid count from there (nloc).
   nvalid = __builtin_amdgcn_readfirstlane(nvalid);
+  if (p.page_table != nullptr) {
+    // Paged cache: translate the sorted logical positions to physical rows
+    // in place.  The order stays that of the logical positions, so the
+    // result does not depend on where the pages happen to be.
+    const int pmask = (1 << p.page_shift) - 1;
+    for (int i = tid; i < nvalid; i += C::THREADS) {
+      const int x = sidx[i];
+      sidx[i] = (p.page_table[x >> p.page_shift] << p.page_shift) | (x & pmask);
+    }
+    lds_barrier();
+  }
   const int n_all = (nvalid + C::BN - 1) / C::BN;
   int t0 = 0, n_tiles = n_all;
   if (split) {
@@ -328,7 +339,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
   // logical chunk ^ swz(row).
   const uint64_t kv_addr = (uint64_t)(uintptr_t)p.kv;
   const i32x4 kv_rsrc = (i32x4){(int)(uint32_t)kv_addr, (int)(uint32_t)(kv_addr >> 32) & 0xFFFF,
-                                (int)((int64_t)p.n_kv * C::ROWB), 0x00020000};
+                                (int)((int64_t)p.n_phys * C::ROWB), 0x00020000};
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)ring;
   // Slot (row, byte column) of each of this lane's DMA blocks, packed
   // row << 16 | column; the same for every tile.

@@ -70,6 +70,11 @@ struct SparseParams {
   int full_units;
   int nsplit;                // 1: no split
   float* ws;                 // nullable when nsplit == 1
+  // Paged cache: logical position j is physical row
+  // page_table[j >> page_shift] << page_shift | (j & (page size - 1)).
+  const int32_t* page_table; // nullable: kv holds the logical rows
+  int page_shift;
+  int n_phys;                // rows of kv (the buffer bound); n_kv when not paged
 };
 
 // Split plan of the dense bf16 kernel for one non-causal sequence: `units`
