@@ -169,33 +169,32 @@ def bench_other(torch, steps, warmup, only=None):
 
 
 def bench_sparse(torch, steps, warmup):
+    """Sparse MQA on the full workload, first over a paged copy of the cache
+    (64-row pages in shuffled places), then over the plain cache (the
+    reported figure, timed last).  A 1 GiB fill between launches (untimed)
+    evicts L2 and MALL."""
+    import numpy as np
+    import vision_encoder_attention_amd as vea
     from vision_encoder_attention_amd import runner as R
     from vision_encoder_attention_amd import workloads as W
     res = {}
-    # sparse MQA: evict L2 / MALL between timed launches (untimed fill of 1 GiB)
     case = W.full_case("sparse_mqa")
     st = R.stage_sparse(case)
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-
-    def fill_and_run():
-        scratch.fill_(1)
-        R.run_sparse(st)
-
-    warm_up(torch, fill_and_run, max(1, warmup))
-    tm = Timer(torch)
-    for _ in range(steps):
-        scratch.fill_(1)
-        tm.run("sparse", lambda: R.run_sparse(st))
-    torch.cuda.synchronize()
-    s_ms, s_min = tm.ms("sparse")
     by, fl = sparse_bytes(case), sparse_flops(case)
-    res[case.name] = {"sparse_mqa_ms": round(s_ms, 4), "sparse_mqa_min_ms": round(s_min, 4),
-                      "gbs": round(by / s_ms / 1e6, 1), "frac_hbm": round(by / s_ms / 1e6 / PEAK_HBM_GBS, 4),
-                      "tflops": round(fl / s_ms / 1e9, 2), "bytes": by, "flops": fl,
-                      "hbm_traffic_counter_bytes": committed_traffic("sparse_mqa_hbm_counters.txt")}
-    # the same workload over a paged cache: 64-row pages in shuffled places
-    import numpy as np
-    import vision_encoder_attention_amd as vea
+
+    def timed(name, fn):
+        def fill_and_run():
+            scratch.fill_(1)
+            fn()
+        warm_up(torch, fill_and_run, max(1, warmup))
+        tm = Timer(torch)
+        for _ in range(steps):
+            scratch.fill_(1)
+            tm.run(name, fn)
+        torch.cuda.synchronize()
+        return tm.ms(name)
+
     ps = 64
     rng = np.random.default_rng(64)
     n_pages = -(-case.kv_latent.shape[0] // ps)
@@ -205,22 +204,14 @@ def bench_sparse(torch, steps, warmup):
     cache[table[j // ps] * ps + j % ps] = case.kv_latent
     kvc = R.bits_to_tensor(cache, "cuda")
     pt = torch.from_numpy(table).cuda()
-
-    def paged():
-        vea.sparse_mqa_paged_fwd(st.q, kvc, pt, ps, case.kv_latent.shape[0], st.idx, case.k, case.scale, st.out,
-                                 st.lse, workspace=st.ws)
-
-    def fill_and_paged():
-        scratch.fill_(1)
-        paged()
-
-    warm_up(torch, fill_and_paged, max(1, warmup))
-    tm = Timer(torch)
-    for _ in range(steps):
-        scratch.fill_(1)
-        tm.run("paged", paged)
-    torch.cuda.synchronize()
-    p_ms, p_min = tm.ms("paged")
+    p_ms, p_min = timed("paged", lambda: vea.sparse_mqa_paged_fwd(st.q, kvc, pt, ps, case.kv_latent.shape[0], st.idx,
+                                                                  case.k, case.scale, st.out, st.lse,
+                                                                  workspace=st.ws))
+    s_ms, s_min = timed("sparse", lambda: R.run_sparse(st))
+    res[case.name] = {"sparse_mqa_ms": round(s_ms, 4), "sparse_mqa_min_ms": round(s_min, 4),
+                      "gbs": round(by / s_ms / 1e6, 1), "frac_hbm": round(by / s_ms / 1e6 / PEAK_HBM_GBS, 4),
+                      "tflops": round(fl / s_ms / 1e9, 2), "bytes": by, "flops": fl,
+                      "hbm_traffic_counter_bytes": committed_traffic("sparse_mqa_hbm_counters.txt")}
     res[case.name + "_paged64"] = {"sparse_mqa_ms": round(p_ms, 4), "sparse_mqa_min_ms": round(p_min, 4),
                                    "gbs": round(by / p_ms / 1e6, 1), "frac_hbm": round(by / p_ms / 1e6 / PEAK_HBM_GBS, 4),
                                    "page_size": ps}
