@@ -515,7 +515,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
 // the blockwise merge of [V32] eq. (1)(2) with the O update written out.
 // Workgroup (tail unit, group of 256 (row, 16-column slice) items).  Empty
 // chunks carry m = -inf, l = 0.
-template <int D>
+template <int D, int NS>
 __global__ __launch_bounds__(256) void attn_merge_kernel(DenseParams p) {
   const int tu = blockIdx.x;
   int b, h, t;
@@ -528,27 +528,35 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(DenseParams p) {
   const int qi = tr.row0 + rl;
   if (rl >= kDenseBM || qi >= tr.row_end) return;
   constexpr size_t CF = (size_t)kDenseBM * (D + 2);     // floats per chunk
-  const float* base = p.ws + (size_t)tu * p.nsplit * CF;
+  const float* base = p.ws + (size_t)tu * NS * CF;
+  // every chunk's m, l and 16 values loaded up front (one memory latency)
+  float mi[NS], li[NS];
+  floatx4 vi[NS][4];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const float* c = base + i * CF;
+    mi[i] = c[kDenseBM * D + rl];
+    li[i] = c[kDenseBM * D + kDenseBM + rl];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) vi[i][q4] = ((const floatx4*)(c + rl * D + 16 * sc))[q4];
+  }
   float mmax = -INFINITY;
-  for (int i = 0; i < p.nsplit; ++i) mmax = fmaxf(mmax, base[i * CF + kDenseBM * D + rl]);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) mmax = fmaxf(mmax, mi[i]);
   float acc[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) acc[j] = 0.f;
   float l = 0.f;
   if (mmax != -INFINITY) {
-    for (int i = 0; i < p.nsplit; ++i) {
-      const float* c = base + i * CF;
-      const float mi = c[kDenseBM * D + rl];
-      if (mi == -INFINITY) continue;                    // empty chunk
-      const float f = fast_exp2(mi - mmax);
-      l = fmaf(f, c[kDenseBM * D + kDenseBM + rl], l);
-      const floatx4* src = (const floatx4*)(c + rl * D + 16 * sc);
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const floatx4 v = src[q4];
+    for (int i = 0; i < NS; ++i) {
+      if (mi[i] == -INFINITY) continue;                 // empty chunk
+      const float f = fast_exp2(mi[i] - mmax);
+      l = fmaf(f, li[i], l);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[4 * q4 + j] = fmaf(f, v[j], acc[4 * q4 + j]);
-      }
+      for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[4 * q4 + j] = fmaf(f, vi[i][q4][j], acc[4 * q4 + j]);
     }
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -560,6 +568,21 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(DenseParams p) {
   *(u32x4*)(dst + 8) = w[1];
   if (sc == 0 && p.lse != nullptr)
     p.lse[(int64_t)h * p.total_q + tr.qs + qi] = l > 0.f ? (mmax + log2f(l)) * kLn2 : -INFINITY;
+}
+
+template <int D>
+hipError_t launch_merge(const DenseParams& p, dim3 grid, hipStream_t s) {
+  switch (p.nsplit) {
+    case 2: hipLaunchKernelGGL((attn_merge_kernel<D, 2>), grid, dim3(256), 0, s, p); break;
+    case 3: hipLaunchKernelGGL((attn_merge_kernel<D, 3>), grid, dim3(256), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((attn_merge_kernel<D, 4>), grid, dim3(256), 0, s, p); break;
+    case 5: hipLaunchKernelGGL((attn_merge_kernel<D, 5>), grid, dim3(256), 0, s, p); break;
+    case 6: hipLaunchKernelGGL((attn_merge_kernel<D, 6>), grid, dim3(256), 0, s, p); break;
+    case 7: hipLaunchKernelGGL((attn_merge_kernel<D, 7>), grid, dim3(256), 0, s, p); break;
+    case 8: hipLaunchKernelGGL((attn_merge_kernel<D, 8>), grid, dim3(256), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipSuccess;
 }
 
 // ================================================================ fp32 path
@@ -775,8 +798,8 @@ hipError_t launch_attn_fwd_bf16(const DenseParams& p, int head_dim, bool causal,
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 mgrid(p.units - p.full_units, kDenseBM * head_dim / 16 / 256);
-    if (head_dim == 64) hipLaunchKernelGGL((attn_merge_kernel<64>), mgrid, block, 0, s, p);
-    else hipLaunchKernelGGL((attn_merge_kernel<128>), mgrid, block, 0, s, p);
+    const hipError_t me = head_dim == 64 ? launch_merge<64>(p, mgrid, s) : launch_merge<128>(p, mgrid, s);
+    if (me != hipSuccess) return me;
   }
   return hipGetLastError();
 }

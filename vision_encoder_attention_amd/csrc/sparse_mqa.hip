@@ -710,7 +710,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
 // the blockwise merge of eq. (1)(2) (page above, section 进一步探索) with the
 // O update written out.  Workgroup (tail unit, group of HPG heads); one
 // thread per (head, 16-column slice).  Empty chunks carry m = -inf, l = 0.
-template <int DV, int HEADS, int HPG>
+template <int DV, int HEADS, int HPG, int NS>
 __global__ __launch_bounds__(256) void sparse_merge_kernel(SparseParams p) {
   const int tu = blockIdx.x;                            // tail unit
   const int unit = p.full_units + tu;
@@ -719,31 +719,39 @@ __global__ __launch_bounds__(256) void sparse_merge_kernel(SparseParams p) {
   constexpr size_t CF = (size_t)HEADS * (DV + 2);       // floats per chunk
   constexpr int SLICES = DV / 16;
   static_assert(HPG * SLICES == 256, "one item per thread");
-  const float* base = p.ws + (size_t)tu * p.nsplit * CF;
+  const float* base = p.ws + (size_t)tu * NS * CF;
   const int hl = blockIdx.y * HPG + threadIdx.x / SLICES;
   const int sc = threadIdx.x % SLICES;
   const int head = hb * HEADS + hl;
   if (head >= p.heads) return;
+  // every chunk's m, l and 16 values loaded up front (one memory latency)
+  float mi[NS], li[NS];
+  floatx4 vi[NS][4];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const float* c = base + i * CF;
+    mi[i] = c[HEADS * DV + hl];
+    li[i] = c[HEADS * DV + HEADS + hl];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) vi[i][q4] = ((const floatx4*)(c + hl * DV + 16 * sc))[q4];
+  }
   float mmax = -INFINITY;
-  for (int i = 0; i < p.nsplit; ++i) mmax = fmaxf(mmax, base[i * CF + HEADS * DV + hl]);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) mmax = fmaxf(mmax, mi[i]);
   float acc[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) acc[j] = 0.f;
   float l = 0.f;
   if (mmax != -INFINITY) {
-    for (int i = 0; i < p.nsplit; ++i) {
-      const float* c = base + i * CF;
-      const float mi = c[HEADS * DV + hl];
-      if (mi == -INFINITY) continue;                    // empty chunk
-      const float f = fast_exp2(mi - mmax);
-      l = fmaf(f, c[HEADS * DV + HEADS + hl], l);
-      const floatx4* src = (const floatx4*)(c + hl * DV + 16 * sc);
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const floatx4 v = src[q4];
+    for (int i = 0; i < NS; ++i) {
+      if (mi[i] == -INFINITY) continue;                 // empty chunk
+      const float f = fast_exp2(mi[i] - mmax);
+      l = fmaf(f, li[i], l);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[4 * q4 + j] = fmaf(f, v[j], acc[4 * q4 + j]);
-      }
+      for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[4 * q4 + j] = fmaf(f, vi[i][q4][j], acc[4 * q4 + j]);
     }
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -793,8 +801,17 @@ hipError_t launch_sparse_mqa(const SparseParams& p, int d_qk, int d_v, hipStream
   if (tail > 0 && p.nsplit > 1) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((sparse_merge_kernel<512, kSparseHeadsPerWG, 8>), dim3(tail, kSparseHeadsPerWG / 8),
-                       dim3(256), 0, s, p);
+    const dim3 mgrid(tail, kSparseHeadsPerWG / 8);
+    switch (p.nsplit) {
+      case 2: hipLaunchKernelGGL((sparse_merge_kernel<512, kSparseHeadsPerWG, 8, 2>), mgrid, dim3(256), 0, s, p); break;
+      case 3: hipLaunchKernelGGL((sparse_merge_kernel<512, kSparseHeadsPerWG, 8, 3>), mgrid, dim3(256), 0, s, p); break;
+      case 4: hipLaunchKernelGGL((sparse_merge_kernel<512, kSparseHeadsPerWG, 8, 4>), mgrid, dim3(256), 0, s, p); break;
+      case 5: hipLaunchKernelGGL((sparse_merge_kernel<512, kSparseHeadsPerWG, 8, 5>), mgrid, dim3(256), 0, s, p); break;
+      case 6: hipLaunchKernelGGL((sparse_merge_kernel<512, kSparseHeadsPerWG, 8, 6>), mgrid, dim3(256), 0, s, p); break;
+      case 7: hipLaunchKernelGGL((sparse_merge_kernel<512, kSparseHeadsPerWG, 8, 7>), mgrid, dim3(256), 0, s, p); break;
+      case 8: hipLaunchKernelGGL((sparse_merge_kernel<512, kSparseHeadsPerWG, 8, 8>), mgrid, dim3(256), 0, s, p); break;
+      default: return hipErrorInvalidValue;
+    }
   }
   return hipGetLastError();
 }
