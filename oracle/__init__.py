@@ -15,6 +15,7 @@ What it computes is the plain definition of each operation, in float64:
                      arithmetic (merge identity of
                      「推理引擎的“蝴蝶效应” -- 从V32 模型的输出不一致说起」,
                      section 进一步探索, eq. (1)(2)).
+* ``attention_paged`` the same over paged K/V caches (block tables).
 * ``attn_probs``     the probability matrix P of one query piece.
 * ``rope_*`` / ``qkv_rope``  rotary position embedding on the Q and K heads
                      of a fused QKV projection output (1D and 2D grid).
@@ -22,6 +23,7 @@ What it computes is the plain definition of each operation, in float64:
                      ``sparse_mqa_paged`` the same over a paged cache.
 * ``topk_indices``   deterministic top-k selection of the sparse indexer
                      (ties go to the lower position).
+* ``paged_rows``     logical position -> physical row of a paged cache.
 * ``pieces``         query-piece arithmetic of the vision encoder.
 
 Every function says which passage it follows.  Page titles used below:
@@ -34,8 +36,9 @@ Every function says which passage it follows.  Page titles used below:
 Parity pins (tests/test_oracle_*.py) tie each function to closed forms,
 brute force, independent library implementations and invariants.
 """
-from .attention import attention, attn_probs  # noqa: F401
+from .attention import attention, attention_paged, attn_probs  # noqa: F401
 from .rope import rope_1d, rope_2d, qkv_rope, rope_inv_freq  # noqa: F401
-from .sparse import paged_rows, sparse_mqa, sparse_mqa_paged  # noqa: F401
+from .paging import paged_rows  # noqa: F401
+from .sparse import sparse_mqa, sparse_mqa_paged  # noqa: F401
 from .pieces import piece_ranges, piece_rows_for_capacity  # noqa: F401
 from .topk import topk_indices  # noqa: F401

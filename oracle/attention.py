@@ -31,7 +31,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["attention", "attn_probs", "allowed_key_count", "kv_head"]
+__all__ = ["attention", "attn_probs", "allowed_key_count", "kv_head", "attention_paged"]
 
 
 def kv_head(h: int, num_heads_q: int, num_heads_kv: int) -> int:
@@ -172,3 +172,19 @@ def attn_probs(q, k, cu_seqlens_q, cu_seqlens_k, causal: bool, scale: float, hea
         e, _, l_sum = masked_softmax_stats(logits[has], mask[has])
         p[has] = e / l_sum[:, None]
     return p
+
+
+def attention_paged(q, k_cache, v_cache, block_table, page_size: int, cu_seqlens_q, cu_seqlens_k, causal: bool,
+                    scale: float, rows=None, heads=None):
+    """attention() over paged K/V caches: sequence b's key position j is token
+    row block_table[b, j // page_size] * page_size + j % page_size of
+    k_cache / v_cache ([num_pages * page_size, Hkv, d]); cu_seqlens_k gives
+    the key lengths.  The logical K/V of every sequence are gathered and
+    packed, then the plain definition applies."""
+    from oracle.paging import paged_rows
+    ck = np.asarray(cu_seqlens_k, dtype=np.int64)
+    bt = np.asarray(block_table, dtype=np.int64)
+    idx = [paged_rows(bt[b], page_size, int(ck[b + 1] - ck[b])) for b in range(len(ck) - 1)]
+    idx = np.concatenate(idx) if idx else np.zeros(0, np.int64)
+    kc, vc = np.asarray(k_cache), np.asarray(v_cache)
+    return attention(q, kc[idx], vc[idx], cu_seqlens_q, cu_seqlens_k, causal, scale, rows=rows, heads=heads)

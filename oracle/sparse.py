@@ -20,7 +20,9 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["sparse_mqa", "paged_rows", "sparse_mqa_paged"]
+from oracle.paging import paged_rows
+
+__all__ = ["sparse_mqa", "sparse_mqa_paged"]
 
 
 def sparse_mqa(q, kv_latent, topk_idx, d_v: int, scale: float, rows=None):
@@ -55,21 +57,6 @@ def sparse_mqa(q, kv_latent, topk_idx, d_v: int, scale: float, rows=None):
         out[r] = (e @ kr[:, :d_v]) / l_sum[:, None]
         lse[:, r] = m + np.log(l_sum)
     return out, lse
-
-
-def paged_rows(page_table, page_size: int, n_logical: int):
-    """Physical cache row of each logical position of a paged KV cache.
-
-    Source: the sparse attention fetches its KV rows through a page table
-    ([V32] section 实验方法和结果, pagetable_1); a paged cache of fixed-size
-    pages is also what [SGLang] section 2.2 allocates.  Logical position j
-    lives in page j // page_size at offset j % page_size, and that page is
-    physical page page_table[j // page_size], so its row is
-    page_table[j // page_size] * page_size + j % page_size.
-    """
-    pt = np.asarray(page_table, dtype=np.int64)
-    j = np.arange(n_logical, dtype=np.int64)
-    return pt[j // page_size] * page_size + j % page_size
 
 
 def sparse_mqa_paged(q, kv_cache, page_table, page_size: int, n_logical: int, topk_idx, d_v: int, scale: float,

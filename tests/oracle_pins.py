@@ -297,7 +297,38 @@ def pin_row_subset(orc):
         assert np.array_equal(l2[[1, 3]][:, rows], lse[[1, 3]][:, rows])
 
 
-DENSE_PINS = [pin_zero_query_mean, pin_one_hot_select, pin_brute_force, pin_torch_sdpa, pin_online_merge,
+def pin_attention_paged_roundtrip(orc):
+    """A packed varlen batch (GQA, causal) scattered into shuffled pages of a
+    shared cache, one block table row per sequence, unused pages holding
+    garbage: the paged view gives the unpaged result bitwise."""
+    rng = _rng(230)
+    lens = [5, 17, 1, 12]
+    hq, hkv, d, ps = 4, 2, 6, 4
+    cu = _cu(lens)
+    q = rng.standard_normal((cu[-1], hq, d))
+    k = rng.standard_normal((cu[-1], hkv, d))
+    v = rng.standard_normal((cu[-1], hkv, d))
+    want_o, want_l = orc.attention(q, k, v, cu, cu, True, 0.4)
+    max_pages = max(-(-n // ps) for n in lens)
+    n_pages = sum(-(-n // ps) for n in lens) + 3
+    order = rng.permutation(n_pages)
+    bt = np.full((len(lens), max_pages), -7, np.int64)
+    kc = rng.standard_normal((n_pages * ps, hkv, d))
+    vc = rng.standard_normal((n_pages * ps, hkv, d))
+    nxt = 0
+    for b, n in enumerate(lens):
+        for pg in range(-(-n // ps)):
+            bt[b, pg] = order[nxt]
+            nxt += 1
+        for j in range(n):
+            row = bt[b, j // ps] * ps + j % ps
+            kc[row] = k[cu[b] + j]
+            vc[row] = v[cu[b] + j]
+    o, l = orc.attention_paged(q, kc, vc, bt, ps, cu, cu, True, 0.4)
+    assert np.array_equal(o, want_o) and np.array_equal(l, want_l)
+
+
+DENSE_PINS = [pin_attention_paged_roundtrip, pin_zero_query_mean, pin_one_hot_select, pin_brute_force, pin_torch_sdpa, pin_online_merge,
               pin_single_key_and_causal_edges, pin_packing_and_gqa, pin_probs, pin_row_subset]
 
 

@@ -54,10 +54,13 @@ MUTANTS = [
     ("sparse", "kr[:, :d_v]", "kr[:, d_qk - d_v:]", "V taken from the last latent columns"),
     ("sparse", "sel = idx[r][idx[r] >= 0]", "sel = np.unique(idx[r][idx[r] >= 0])", "repeated indices collapsed"),
     ("sparse", "lse[:, r] = m + np.log(l_sum)", "lse[:, r] = np.log(l_sum)", "lse drops the row max"),
-    ("sparse", "return pt[j // page_size] * page_size + j % page_size",
+    ("paging", "return pt[j // page_size] * page_size + j % page_size",
      "return pt[j % page_size] * page_size + j // page_size", "page index and offset swapped"),
-    ("sparse", "return pt[j // page_size] * page_size + j % page_size", "return pt[j // page_size] + j % page_size",
+    ("paging", "return pt[j // page_size] * page_size + j % page_size", "return pt[j // page_size] + j % page_size",
      "physical page not scaled by the page size"),
+    ("attention", "idx = [paged_rows(bt[b], page_size, int(ck[b + 1] - ck[b])) for b in range(len(ck) - 1)]",
+     "idx = [paged_rows(bt[0], page_size, int(ck[b + 1] - ck[b])) for b in range(len(ck) - 1)]",
+     "every sequence read through the first block table row"),
     ("pieces", "return min(n, cap_floats // n)", "return min(n, -(-cap_floats // n))", "piece rows rounded up"),
     ("topk", "order = np.lexsort((np.arange(ln), key, nan))", "order = np.lexsort((-np.arange(ln), key, nan))",
      "ties go to the higher position"),
@@ -72,7 +75,7 @@ MUTANTS = [
 ]
 
 FAMILY = {"attention": P.DENSE_PINS, "rope": P.ROPE_PINS, "sparse": P.SPARSE_PINS, "pieces": ["pieces"],
-          "topk": P.TOPK_PINS}
+          "topk": P.TOPK_PINS, "paging": P.SPARSE_PINS + P.DENSE_PINS}
 
 
 def _mutated_oracle(modname, old, new):
