@@ -159,6 +159,11 @@ def bench_other(torch, steps, warmup, only=None):
             ent.update({"qkv_rope_ms": round(r_ms, 4), "qkv_rope_gbs": round(rb / r_ms / 1e6, 1),
                         "qkv_rope_frac_hbm": round(rb / r_ms / 1e6 / PEAK_HBM_GBS, 4)})
         res[case.name] = ent
+        if name == "varlen_gqa":
+            p_ms, p_min = bench_dense_paged(torch, st, steps, warmup)
+            res[case.name + "_paged64"] = {"attn_fwd_ms": round(p_ms, 4), "attn_fwd_min_ms": round(p_min, 4),
+                                           "attn_frac_bf16_peak": round(fl / p_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                                           "page_size": 64}
         del st
         torch.cuda.empty_cache()
     if only in (None, "sparse_mqa"):
@@ -166,6 +171,44 @@ def bench_other(torch, steps, warmup, only=None):
     if only in (None, "indexer"):
         res.update(bench_indexer(torch, steps, warmup))
     return res
+
+
+def bench_dense_paged(torch, st, steps, warmup, ps=64):
+    """attn_fwd over the staged case's K/V copied into caches of shuffled
+    64-row pages (one block-table row per sequence)."""
+    import numpy as np
+    import vision_encoder_attention_amd as vea
+    c = st.case
+    lens = np.diff(np.asarray(c.cu_seqlens_k, np.int64))
+    pages = [-(-int(n) // ps) for n in lens]
+    n_pages = sum(pages) + 8
+    order = np.random.default_rng(65).permutation(n_pages)
+    bt = np.zeros((len(lens), max(pages)), np.int32)
+    rows, nxt = [], 0
+    for b, n in enumerate(lens):
+        bt[b, :pages[b]] = order[nxt:nxt + pages[b]]
+        nxt += pages[b]
+        j = np.arange(int(n))
+        rows.append(bt[b, j // ps].astype(np.int64) * ps + j % ps)
+    idx = torch.from_numpy(np.concatenate(rows)).cuda()
+    shape = (n_pages * ps,) + tuple(st.k.shape[1:])
+    kc = torch.zeros(shape, dtype=st.k.dtype, device="cuda")
+    vc = torch.zeros(shape, dtype=st.v.dtype, device="cuda")
+    kc[idx] = st.k
+    vc[idx] = st.v
+    btd = torch.from_numpy(bt).cuda()
+
+    def run():
+        vea.attn_fwd_paged(st.q, kc, vc, btd, ps, st.cu_q, st.cu_k, c.causal, c.scale, st.out, st.lse,
+                           piece_rows=c.piece_rows, max_seqlen_q=st.max_q, max_seqlen_k=st.max_k,
+                           workspace=st.ws)
+
+    warm_up(torch, run, max(1, warmup))
+    tm = Timer(torch)
+    for _ in range(steps):
+        tm.run("paged", run)
+    torch.cuda.synchronize()
+    return tm.ms("paged")
 
 
 def bench_sparse(torch, steps, warmup):

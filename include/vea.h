@@ -123,6 +123,37 @@ int vea_attn_fwd(int dtype,
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * vea_attn_fwd_paged — vea_attn_fwd (bf16) with K and V in paged caches.
+ * Sources: a paged KV cache of fixed-size pages [SGLang] section 2.2; KV rows
+ * fetched through a page table [V32] section 实验方法和结果.
+ *
+ *   k_cache, v_cache  bf16 [num_pages * page_size, num_heads_kv, head_dim],
+ *                     token strides k/v_tok_stride.
+ *   block_table       device int32 [batch, max_pages_per_seq]: key position j
+ *                     of sequence b (0 <= j < its key length, from
+ *                     cu_seqlens_k) is token row
+ *                     block_table[b][j / page_size] * page_size + j % page_size
+ *                     of the caches.  Used entries must lie in [0, num_pages)
+ *                     (VEA_ERANGE under VEA_CHECK).
+ *   page_size         a power of two, 64 .. 65536 (a 64-key tile never spans
+ *                     two pages).  max_pages_per_seq >= ceil(max_seqlen_k /
+ *                     page_size).
+ * Every other argument as vea_attn_fwd (the same workspace size); total_k is
+ * the sum of the key lengths.  The result is bitwise that of vea_attn_fwd on
+ * the same logical K/V, wherever the pages are.
+ */
+int vea_attn_fwd_paged(const void* q, int64_t q_tok_stride,
+                       const void* k_cache, int64_t k_tok_stride,
+                       const void* v_cache, int64_t v_tok_stride,
+                       const int32_t* block_table, int max_pages_per_seq, int page_size, int num_pages,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                       int batch, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                       int num_heads_q, int num_heads_kv, int head_dim,
+                       int causal, float scale, int piece_rows,
+                       void* out, int64_t out_tok_stride, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * vea_attn_fwd_workspace_size — bytes of workspace vea_attn_fwd uses for these
  * sizes on the current HIP device (0 when it splits nothing).  Validates the
  * shape arguments like vea_attn_fwd; VEA_EHIP if the device cannot be queried.

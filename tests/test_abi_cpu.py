@@ -32,7 +32,7 @@ def lib():
 def test_header_declares_the_operations():
     names = _declared()
     for n in ("vea_attn_fwd", "vea_attn_fwd_workspace_size", "vea_qkv_rope", "vea_sparse_mqa_fwd",
-              "vea_sparse_mqa_workspace_size", "vea_topk_indices", "vea_sparse_mqa_paged_fwd",
+              "vea_sparse_mqa_workspace_size", "vea_topk_indices", "vea_sparse_mqa_paged_fwd", "vea_attn_fwd_paged",
               "vea_attn_probs_piece", "vea_status_str"):
         assert n in names
 
@@ -169,6 +169,30 @@ def test_sparse_workspace_size_validation(lib, args, status):
     assert lib.vea_sparse_mqa_workspace_size(*args, ctypes.byref(n)) == status
     assert n.value == 0
     assert lib.vea_sparse_mqa_workspace_size(*args, None) == VEA_EINVAL
+
+
+def _attn_paged(lib, **kw):
+    a = dict(q=FAKE, qs=128, kc=FAKE, ks=128, vc=FAKE, vs=128, bt=FAKE, mp=4, ps=64, npg=10, cuq=FAKE, cuk=FAKE,
+             batch=2, tq=100, tk=100, mq=60, mk=60, hq=2, hkv=2, d=64, causal=1, scale=0.125, qb=0, out=FAKE, os=128,
+             lse=None)
+    a.update(kw)
+    return lib.vea_attn_fwd_paged(a["q"], a["qs"], a["kc"], a["ks"], a["vc"], a["vs"], a["bt"], a["mp"], a["ps"],
+                                  a["npg"], a["cuq"], a["cuk"], a["batch"], a["tq"], a["tk"], a["mq"], a["mk"],
+                                  a["hq"], a["hkv"], a["d"], a["causal"], a["scale"], a["qb"], a["out"], a["os"],
+                                  a["lse"], None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ps=32), VEA_ESHAPE),               # below the 64-key tile
+    (dict(ps=96), VEA_ESHAPE),               # not a power of two
+    (dict(mp=0), VEA_ESHAPE),                # fewer block-table columns than max_seqlen_k needs
+    (dict(npg=-1), VEA_ESHAPE),
+    (dict(bt=None), VEA_EINVAL),
+    (dict(d=96), VEA_EUNSUPPORTED),
+    (dict(batch=0), VEA_OK),
+])
+def test_attn_paged_validation(lib, kw, status):
+    assert _attn_paged(lib, **kw) == status
 
 
 def _paged(lib, **kw):

@@ -316,3 +316,74 @@ def test_attn_workspace_too_small_is_rejected(torch):
         vea.attn_fwd(st.q, st.k, st.v, st.cu_q, st.cu_k, False, case.scale, st.out, st.lse,
                      piece_rows=case.piece_rows, max_seqlen_q=st.max_q, max_seqlen_k=st.max_k, workspace=small)
     assert e.value.status == -6
+
+
+# ------------------------------------------------------- paged K/V caches
+
+def _page_caches(torch, k, v, cu_k, ps, extra_pages, seed):
+    """Scatter packed K/V [total_k, Hkv, d] into caches of shuffled pages (one
+    block-table row per sequence, garbage in unused pages)."""
+    rng = np.random.default_rng(seed)
+    lens = np.diff(np.asarray(cu_k, np.int64))
+    pages = [-(-int(n) // ps) for n in lens]
+    n_pages = sum(pages) + extra_pages
+    order = rng.permutation(n_pages)
+    bt = np.zeros((len(lens), max(1, max(pages) if pages else 1)), np.int32)
+    rows = []
+    nxt = 0
+    for b, n in enumerate(lens):
+        for pg in range(pages[b]):
+            bt[b, pg] = order[nxt]
+            nxt += 1
+        rows.append(oracle.paged_rows(bt[b], ps, int(n)))
+    rows = np.concatenate(rows) if rows else np.zeros(0, np.int64)
+    shape = (n_pages * ps,) + tuple(k.shape[1:])
+    kc = torch.randn(shape, device="cuda").to(torch.bfloat16)
+    vc = torch.randn(shape, device="cuda").to(torch.bfloat16)
+    idx = torch.from_numpy(rows).cuda()
+    kc[idx] = k
+    vc[idx] = v
+    return kc, vc, bt
+
+
+def _run_paged(torch, st, kc, vc, bt, ps):
+    import vision_encoder_attention_amd as vea
+    c = st.case
+    out = torch.empty_like(st.out)
+    lse = torch.empty_like(st.lse)
+    vea.attn_fwd_paged(st.q, kc, vc, torch.from_numpy(bt).cuda(), ps, st.cu_q, st.cu_k, c.causal, c.scale, out, lse,
+                       piece_rows=c.piece_rows, max_seqlen_q=st.max_q, max_seqlen_k=st.max_k,
+                       workspace=st.ws if st.split else None)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("ps", [64, 128])
+def test_paged_kv_against_the_oracle_and_bitwise_unpaged(torch, ps):
+    """Causal GQA varlen batch (an empty and a one-token sequence included)
+    over shuffled pages: against the oracle's paged view, and bitwise equal
+    to the unpaged kernel on the same logical K/V."""
+    case = W.random_dense([130, 1, 257, 0, 700], [130, 1, 257, 0, 700], 8, 2, 128, True, "bf16", seed=620 + ps)
+    st = R.stage_dense(case)
+    R.run_attn(st)
+    kc, vc, bt = _page_caches(torch, st.k, st.v, case.cu_seqlens_k, ps, extra_pages=4, seed=630 + ps)
+    out, lse = _run_paged(torch, st, kc, vc, bt, ps)
+    assert torch.equal(out, st.out) and torch.equal(lse, st.lse)
+    o_ref, l_ref = oracle.attention_paged(W.bf16_bits_to_f64(case.q), W.bf16_bits_to_f64(R.tensor_to_bits(kc)),
+                                          W.bf16_bits_to_f64(R.tensor_to_bits(vc)), bt, ps, case.cu_seqlens_q,
+                                          case.cu_seqlens_k, True, float(np.float32(case.scale)))
+    assert_bf16_close(_f64(out, "bf16"), o_ref, "paged out")
+    assert_bf16_close(lse.cpu().numpy().astype(np.float64), l_ref, "paged lse")
+
+
+@pytest.mark.parametrize("name,ps", [("varlen_gqa", 64), ("split", 64)])
+def test_paged_kv_full_size_is_bitwise_unpaged(torch, name, ps):
+    """The full varlen workload, and an image shape whose last round is split
+    (workspace), give bitwise the unpaged results over shuffled pages."""
+    case = W.full_case("varlen_gqa") if name == "varlen_gqa" else _round_boundary_case(torch, 64, 3, seed=640)
+    st = R.stage_dense(case)
+    R.run_dense(st)
+    torch.cuda.synchronize()
+    kc, vc, bt = _page_caches(torch, st.k, st.v, case.cu_seqlens_k, ps, extra_pages=11, seed=650)
+    out, lse = _run_paged(torch, st, kc, vc, bt, ps)
+    assert torch.equal(out, st.out) and torch.equal(lse, st.lse)

@@ -12,9 +12,9 @@ in ``include/vea.h``); this package is a thin binding over it:
 
 ``workloads`` holds the seeded synthetic inputs; ``build`` compiles the library.
 """
-from ._binding import (VeaError, attn_fwd, attn_fwd_workspace_size, attn_probs_piece, lib_path, load_library,  # noqa: F401
+from ._binding import (VeaError, attn_fwd, attn_fwd_paged, attn_fwd_workspace_size, attn_probs_piece, lib_path, load_library,  # noqa: F401
                        qkv_rope, sparse_mqa_fwd, sparse_mqa_paged_fwd, sparse_mqa_workspace_size, status_str,
                        topk_indices)
 
-__all__ = ["attn_fwd", "attn_fwd_workspace_size", "qkv_rope", "sparse_mqa_fwd", "sparse_mqa_workspace_size", "attn_probs_piece",
+__all__ = ["attn_fwd", "attn_fwd_paged", "attn_fwd_workspace_size", "qkv_rope", "sparse_mqa_fwd", "sparse_mqa_workspace_size", "attn_probs_piece",
            "sparse_mqa_paged_fwd", "topk_indices", "VeaError", "load_library", "lib_path", "status_str"]

@@ -50,6 +50,10 @@ def load_library():
         lib.vea_attn_fwd.argtypes = [i32, vp, i64, vp, i64, vp, i64, vp, vp, i32, i32, i32, i32, i32,
                                      i32, i32, i32, i32, f32, i32, vp, i64, vp, vp, ctypes.c_size_t, vp]
         lib.vea_attn_fwd.restype = i32
+        lib.vea_attn_fwd_paged.argtypes = [vp, i64, vp, i64, vp, i64, vp, i32, i32, i32, vp, vp, i32, i32, i32,
+                                           i32, i32, i32, i32, i32, i32, f32, i32, vp, i64, vp, vp,
+                                           ctypes.c_size_t, vp]
+        lib.vea_attn_fwd_paged.restype = i32
         lib.vea_attn_fwd_workspace_size.argtypes = [i32] * 11 + [ctypes.POINTER(ctypes.c_size_t)]
         lib.vea_attn_fwd_workspace_size.restype = i32
         lib.vea_qkv_rope.argtypes = [vp, i64, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp]
@@ -181,6 +185,55 @@ def attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, causal, scale, out, lse=None, 
                               k.shape[1], q.shape[2], 1 if causal else 0, float(scale), int(piece_rows),
                               _ptr(out), os_, _ptr(lse), _ptr(workspace),
                               0 if workspace is None else workspace.numel(), _stream(q))
+    _check(st)
+    return out, lse
+
+
+def attn_fwd_paged(q, k_cache, v_cache, block_table, page_size, cu_seqlens_q, cu_seqlens_k, causal, scale, out,
+                   lse=None, *, piece_rows=0, max_seqlen_q=None, max_seqlen_k=None, workspace="auto"):
+    """attn_fwd (bf16) over paged K/V caches (see vea_attn_fwd_paged):
+    k_cache / v_cache [num_pages * page_size, Hkv, d] (token strides free),
+    block_table int32 [batch, max_pages_per_seq]; cu_seqlens_k gives the key
+    lengths."""
+    lib = load_library()
+    torch = _torch()
+    qs, ks, vs, os_ = (_token_major(q, "q"), _token_major(k_cache, "k_cache"), _token_major(v_cache, "v_cache"),
+                       _token_major(out, "out"))
+    _int32_dev(cu_seqlens_q, "cu_seqlens_q")
+    _int32_dev(cu_seqlens_k, "cu_seqlens_k")
+    _int32_dev(block_table, "block_table")
+    if q.dtype != torch.bfloat16 or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype or out.dtype != q.dtype:
+        raise TypeError("q, k_cache, v_cache and out must be bfloat16")
+    if block_table.dim() != 2 or not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous int32 [batch, max_pages_per_seq]")
+    page_size = int(page_size)
+    if page_size < 1 or k_cache.shape[0] % page_size or v_cache.shape[0] != k_cache.shape[0]:
+        raise ValueError("cache rows must be a multiple of page_size and equal for k and v")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (q.shape[1], q.shape[0])):
+        raise ValueError("lse must be contiguous float32 [Hq, total_q]")
+    batch = cu_seqlens_q.numel() - 1
+    if block_table.shape[0] != batch:
+        raise ValueError("block_table needs one row per sequence")
+    if max_seqlen_q is None or max_seqlen_k is None:
+        lq = (cu_seqlens_q[1:] - cu_seqlens_q[:-1]).max().item() if batch > 0 else 0
+        lk = (cu_seqlens_k[1:] - cu_seqlens_k[:-1]).max().item() if batch > 0 else 0
+        max_seqlen_q = lq if max_seqlen_q is None else max_seqlen_q
+        max_seqlen_k = lk if max_seqlen_k is None else max_seqlen_k
+    total_k = int(cu_seqlens_k[-1].item()) if batch > 0 else 0
+    with torch.cuda.device(q.device):
+        if isinstance(workspace, str):
+            if workspace != "auto":
+                raise ValueError('workspace must be "auto", None or a uint8 GPU tensor')
+            nbytes = attn_fwd_workspace_size(VEA_BF16, batch, q.shape[0], total_k, max_seqlen_q, max_seqlen_k,
+                                             q.shape[1], k_cache.shape[1], q.shape[2], causal, piece_rows)
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
+        st = lib.vea_attn_fwd_paged(_ptr(q), qs, _ptr(k_cache), ks, _ptr(v_cache), vs, _ptr(block_table),
+                                    block_table.shape[1], page_size, k_cache.shape[0] // page_size,
+                                    _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), batch, q.shape[0], total_k,
+                                    int(max_seqlen_q), int(max_seqlen_k), q.shape[1], k_cache.shape[1], q.shape[2],
+                                    1 if causal else 0, float(scale), int(piece_rows), _ptr(out), os_, _ptr(lse),
+                                    _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(q))
     _check(st)
     return out, lse
 

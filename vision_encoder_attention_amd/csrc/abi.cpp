@@ -109,6 +109,9 @@ int dense_layout(int batch, int max_seqlen_q, int num_heads_q, int piece_rows, D
   p.full_units = p.units;
   p.nsplit = 1;
   p.ws = nullptr;
+  p.block_table = nullptr;
+  p.page_shift = 0;
+  p.max_pages = 0;
   return VEA_OK;
 }
 
@@ -151,19 +154,30 @@ int vea_attn_fwd_workspace_size(int dtype, int batch, int total_q, int total_k, 
   return VEA_OK;
 }
 
-int vea_attn_fwd(int dtype, const void* q, int64_t q_tok_stride, const void* k, int64_t k_tok_stride,
-                 const void* v, int64_t v_tok_stride, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-                 int batch, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int num_heads_q,
-                 int num_heads_kv, int head_dim, int causal, float scale, int piece_rows, void* out,
-                 int64_t out_tok_stride, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+int dense_fwd(int dtype, const void* q, int64_t q_tok_stride, const void* k, int64_t k_tok_stride, const void* v,
+              int64_t v_tok_stride, const int32_t* block_table, int max_pages, int page_size, int num_pages,
+              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch, int total_q, int total_k,
+              int max_seqlen_q, int max_seqlen_k, int num_heads_q, int num_heads_kv, int head_dim, int causal,
+              float scale, int piece_rows, void* out, int64_t out_tok_stride, float* lse, void* workspace,
+              size_t workspace_bytes, void* stream) {
   // ---- validation (host only)
   int st = dense_shape_status(dtype, batch, total_q, total_k, max_seqlen_q, max_seqlen_k, num_heads_q,
                               num_heads_kv, head_dim, causal, piece_rows);
   if (st != VEA_OK) return st;
   if (!isfinite(scale)) return VEA_EINVAL;
+  int shift = 0;
+  if (block_table != nullptr) {
+    if (dtype != VEA_BF16) return VEA_EUNSUPPORTED;
+    if (page_size < 64 || page_size > (1 << 16) || (page_size & (page_size - 1)) || num_pages < 0) return VEA_ESHAPE;
+    while ((1 << shift) < page_size) ++shift;
+    if (max_pages < (max_seqlen_k + page_size - 1) / page_size) return VEA_ESHAPE;
+  }
   if (batch == 0 || total_q == 0) return VEA_OK;                 // nothing to compute
   if (!q || !out || !cu_seqlens_q || !cu_seqlens_k) return VEA_EINVAL;
-  if (total_k > 0 && (!k || !v)) return VEA_EINVAL;               // no keys: k/v are never read
+  const bool has_keys = block_table != nullptr ? num_pages > 0 : total_k > 0;
+  if (has_keys && (!k || !v)) return VEA_EINVAL;                  // no keys: k/v are never read
   const int64_t esz = dtype == VEA_BF16 ? 2 : 4;
   const int64_t qrow = (int64_t)num_heads_q * head_dim, krow = (int64_t)num_heads_kv * head_dim;
   if (q_tok_stride < qrow || out_tok_stride < qrow || k_tok_stride < krow || v_tok_stride < krow) return VEA_ESHAPE;
@@ -178,6 +192,17 @@ int vea_attn_fwd(int dtype, const void* q, int64_t q_tok_stride, const void* k, 
     st = check_cu(cu_seqlens_q, batch, total_q, max_seqlen_q, s);
     if (st == VEA_OK) st = check_cu(cu_seqlens_k, batch, total_k, max_seqlen_k, s);
     if (st != VEA_OK) return st;
+    if (block_table != nullptr) {
+      std::vector<int32_t> cu, bt;
+      st = fetch_ints(cu_seqlens_k, (size_t)batch + 1, s, cu);
+      if (st == VEA_OK) st = fetch_ints(block_table, (size_t)batch * max_pages, s, bt);
+      if (st != VEA_OK) return st;
+      for (int b = 0; b < batch; ++b)
+        for (int pg = 0; pg < (cu[b + 1] - cu[b] + page_size - 1) / page_size; ++pg) {
+          const int32_t x = bt[(size_t)b * max_pages + pg];
+          if (x < 0 || x >= num_pages) return VEA_ERANGE;
+        }
+    }
   }
   if (max_seqlen_q == 0) return finish(VEA_OK, s);
 
@@ -191,6 +216,9 @@ int vea_attn_fwd(int dtype, const void* q, int64_t q_tok_stride, const void* k, 
   if (st != VEA_OK) return st;
   p.xcd_map = (num_heads_kv % 8 == 0) ? 1 : 0;
   p.scale = scale;
+  p.block_table = block_table;
+  p.page_shift = shift;
+  p.max_pages = max_pages;
   if (workspace != nullptr) {
     DenseSplit plan;
     st = dense_split(dtype, batch, total_q, total_k, num_heads_q, head_dim, causal, p, plan);
@@ -206,6 +234,31 @@ int vea_attn_fwd(int dtype, const void* q, int64_t q_tok_stride, const void* k, 
   hipError_t e = dtype == VEA_BF16 ? launch_attn_fwd_bf16(p, head_dim, causal != 0, s)
                                    : launch_attn_fwd_f32(p, head_dim, causal != 0, s);
   return finish(hip_status(e), s);
+}
+
+}  // namespace
+
+int vea_attn_fwd(int dtype, const void* q, int64_t q_tok_stride, const void* k, int64_t k_tok_stride,
+                 const void* v, int64_t v_tok_stride, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                 int batch, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int num_heads_q,
+                 int num_heads_kv, int head_dim, int causal, float scale, int piece_rows, void* out,
+                 int64_t out_tok_stride, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return dense_fwd(dtype, q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, nullptr, 0, 0, 0, cu_seqlens_q,
+                   cu_seqlens_k, batch, total_q, total_k, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv,
+                   head_dim, causal, scale, piece_rows, out, out_tok_stride, lse, workspace, workspace_bytes, stream);
+}
+
+int vea_attn_fwd_paged(const void* q, int64_t q_tok_stride, const void* k_cache, int64_t k_tok_stride,
+                       const void* v_cache, int64_t v_tok_stride, const int32_t* block_table, int max_pages_per_seq,
+                       int page_size, int num_pages, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                       int batch, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int num_heads_q,
+                       int num_heads_kv, int head_dim, int causal, float scale, int piece_rows, void* out,
+                       int64_t out_tok_stride, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (block_table == nullptr && batch > 0 && total_q > 0) return VEA_EINVAL;
+  return dense_fwd(VEA_BF16, q, q_tok_stride, k_cache, k_tok_stride, v_cache, v_tok_stride, block_table,
+                   max_pages_per_seq, page_size, num_pages, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k,
+                   max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim, causal, scale, piece_rows, out,
+                   out_tok_stride, lse, workspace, workspace_bytes, stream);
 }
 
 int vea_qkv_rope(const void* x_qkv, int64_t x_tok_stride, const int32_t* positions, int pos_dims, int num_tokens,

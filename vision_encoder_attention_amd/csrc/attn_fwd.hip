@@ -183,7 +183,7 @@ struct Cfg {
   }
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(DenseParams p) {
   using C = Cfg<D>;
   // Two K stages and two V stages in distinct arrays: the compiler can then see
@@ -261,21 +261,52 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
     voff_k[i] = (int)(r * ksb) + 16 * ch;
     voff_v[i] = (int)(r * vsb) + 16 * ch;
   }
-  const unsigned char* kbase_ptr = (const unsigned char*)p.k + ((int64_t)tr.ks * p.k_stride + (int64_t)kvh * D) * 2;
-  const unsigned char* vbase_ptr = (const unsigned char*)p.v + ((int64_t)tr.ks * p.v_stride + (int64_t)kvh * D) * 2;
-
-  auto issue_tile = [&](int kt, const unsigned char* base, int64_t sb, const int* voff, unsigned char* stage) {
+  // Key row j of this sequence: row tr.ks + j of the packed K/V, or, for a
+  // paged cache, row j's page looked up in the sequence's block-table row.
+  const unsigned char* kbase_ptr =
+      (const unsigned char*)p.k + ((PAGED ? 0 : (int64_t)tr.ks * p.k_stride) + (int64_t)kvh * D) * 2;
+  const unsigned char* vbase_ptr =
+      (const unsigned char*)p.v + ((PAGED ? 0 : (int64_t)tr.ks * p.v_stride) + (int64_t)kvh * D) * 2;
+  // Physical row of the sequence's key j.  A tile never spans two pages (page
+  // sizes are multiples of the tile height).
+  auto phys_row = [&](int j) -> int64_t {
+    if constexpr (!PAGED) return j;
+    const int64_t page = p.block_table[(int64_t)b * p.max_pages + (j >> p.page_shift)];
+    return (page << p.page_shift) | (j & ((1 << p.page_shift) - 1));
+  };
+  auto row_ptr = [&](const unsigned char* base, int64_t sb, int j) -> const unsigned char* {
+    return base + phys_row(j) * sb;
+  };
+  // First physical row of tile kt, 0 past the key range (such a tile is never
+  // loaded).  The paged pipeline below reads these block-table entries two
+  // tiles ahead of their DMA, so the lookup's latency stays off the issue.
+  auto tile_row = [&](int kt) -> int64_t {
+    const int j = (kt0 + kt) * C::BN;
+    return j < tr.kend ? phys_row(j) : 0;
+  };
+  auto issue_tile = [&](int kt, int64_t row0, const unsigned char* base, int64_t sb, const int* voff,
+                        unsigned char* stage) {
     const int rows = min(tr.kend - (kt0 + kt) * C::BN, C::BN);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(base + (int64_t)(kt0 + kt) * C::BN * sb), (short)0, (int)(rows * sb), 0x00020000);
+        (void*)(base + row0 * sb), (short)0, (int)(rows * sb), 0x00020000);
     unsigned char* dst = stage + wave * C::LOADS * 1024;
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16,
                                                (unsigned)voff[i], 0, 0, 0);
   };
-  auto issue_k = [&](int kt, unsigned char* stage) { issue_tile(kt, kbase_ptr, ksb, voff_k, stage); };
-  auto issue_v = [&](int kt, unsigned char* stage) { issue_tile(kt, vbase_ptr, vsb, voff_v, stage); };
+  // rows of tiles kt, kt + 1, kt + 2 at the top of iteration kt (paged only)
+  int64_t rv = 0, rk = 0, rn = 0;
+  auto row_of = [&](int kt, int64_t pre) -> int64_t {
+    if constexpr (PAGED) return pre;
+    else return (int64_t)(kt0 + kt) * C::BN;
+  };
+  auto issue_k = [&](int kt, int64_t pre, unsigned char* stage) {
+    issue_tile(kt, row_of(kt, pre), kbase_ptr, ksb, voff_k, stage);
+  };
+  auto issue_v = [&](int kt, int64_t pre, unsigned char* stage) {
+    issue_tile(kt, row_of(kt, pre), vbase_ptr, vsb, voff_v, stage);
+  };
 
   // ---- per-lane LDS read offsets (loop invariant)
   const int sw = C::swz(l32);                         // same for rows l32 and 32 + l32
@@ -379,8 +410,8 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
   // clamped to the last one; they are masked).
   auto qk_global = [&](int kt, floatx16& s0, floatx16& s1) {
     const int r0 = (kt0 + kt) * C::BN;
-    const unsigned char* pa = kbase_ptr + (int64_t)min(r0 + l32, tr.kend - 1) * ksb + 16 * g2;
-    const unsigned char* pb2 = kbase_ptr + (int64_t)min(r0 + 32 + l32, tr.kend - 1) * ksb + 16 * g2;
+    const unsigned char* pa = row_ptr(kbase_ptr, ksb, min(r0 + l32, tr.kend - 1)) + 16 * g2;
+    const unsigned char* pb2 = row_ptr(kbase_ptr, ksb, min(r0 + 32 + l32, tr.kend - 1)) + 16 * g2;
     s0 = (floatx16){};
     s1 = (floatx16){};
 #pragma unroll
@@ -424,8 +455,13 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
     __syncthreads();                                  // everyone's landed; the stages refilled below are consumed
     floatx16 sn0, sn1;
     if constexpr (HAS_S) {
-      if (kt + 1 < n_tiles) issue_k(kt + 1, k_wr);
-      issue_v(kt, v_wr);
+      if (kt + 1 < n_tiles) issue_k(kt + 1, rk, k_wr);
+      issue_v(kt, rv, v_wr);
+      if constexpr (PAGED) {
+        rv = rk;
+        rk = rn;
+        rn = tile_row(kt + 3);
+      }
     }
     // QK^T of tile kt under the softmax of tile kt-1, then P V of tile kt-1
     if constexpr (HAS_S) qk(k_rd, sn0, sn1);
@@ -452,11 +488,17 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
   };
 
   if (n_tiles > 0) {
-    issue_k(0, kst0);
-    issue_v(0, vst0);
+    if constexpr (PAGED) rv = tile_row(0);
+    issue_k(0, rv, kst0);
+    issue_v(0, rv, vst0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (1 < n_tiles) issue_k(1, kst1);
+    if constexpr (PAGED) {
+      rv = tile_row(1);
+      rk = tile_row(2);
+      rn = tile_row(3);
+    }
+    if (1 < n_tiles) issue_k(1, rv, kst1);
     qk(kst0, sp0, sp1);
     if (0 >= n_full) mask(0, sp0, sp1);
     m_use = softmax_ref(sp0, sp1);                      // reference from the first tile
@@ -774,10 +816,21 @@ int dense_bf16_blocks_per_cu(int head_dim) {
   int n = 0;
   hipError_t e = hipErrorInvalidValue;
   if (head_dim == 64)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_bf16_kernel<64, false>, 256, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_bf16_kernel<64, false, false>, 256, 0);
   else if (head_dim == 128)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_bf16_kernel<128, false>, 256, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_bf16_kernel<128, false, false>, 256, 0);
   return e == hipSuccess ? n : 0;
+}
+
+template <int D>
+void launch_dense(const DenseParams& p, bool causal, bool paged, dim3 grid, dim3 block, hipStream_t s) {
+  if (paged) {
+    if (causal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, true>), grid, block, 0, s, p);
+  } else {
+    if (causal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, false>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, false>), grid, block, 0, s, p);
+  }
 }
 
 hipError_t launch_attn_fwd_bf16(const DenseParams& p, int head_dim, bool causal, hipStream_t s) {
@@ -785,12 +838,11 @@ hipError_t launch_attn_fwd_bf16(const DenseParams& p, int head_dim, bool causal,
   if (split ? (causal || p.ws == nullptr || p.full_units < 0 || p.full_units >= p.units) : p.full_units != p.units)
     return hipErrorInvalidValue;
   const dim3 grid(p.full_units + (p.units - p.full_units) * p.nsplit), block(256);
+  const bool paged = p.block_table != nullptr;
   if (head_dim == 64) {
-    if (causal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, false>), grid, block, 0, s, p);
+    launch_dense<64>(p, causal, paged, grid, block, s);
   } else if (head_dim == 128) {
-    if (causal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, false>), grid, block, 0, s, p);
+    launch_dense<128>(p, causal, paged, grid, block, s);
   } else {
     return hipErrorInvalidValue;
   }

@@ -42,6 +42,13 @@ struct DenseParams {
   int full_units;
   int nsplit;                // 1: no split
   float* ws;                 // nullable when nsplit == 1
+  // Paged K/V (bf16 path): k and v are caches of pages of 2^page_shift token
+  // rows (>= the 64-key tile, so a tile never straddles a page); key row j
+  // of sequence b is token row block_table[b * max_pages + (j >> page_shift)]
+  // << page_shift | (j & (page size - 1)).  cu_k then only gives lengths.
+  const int32_t* block_table;   // nullable: K/V packed by cu_k
+  int page_shift;
+  int max_pages;
 };
 
 struct RopeParams {
