@@ -411,7 +411,7 @@ def main():
         "kernels": {"attn_fwd_ms": round(a_ms, 5), "attn_fwd_min_ms": round(a_min, 5),
                     "qkv_rope_ms": round(r_ms, 5), "qkv_rope_gbs": round(rb / r_ms / 1e6, 1),
                     "qkv_rope_frac_hbm": round(rb / r_ms / 1e6 / PEAK_HBM_GBS, 4)},
-        "roofline": {"bound": "mfma", "kernel": "attn_fwd_bf16_kernel<64,false>", "achieved": round(achieved, 2),
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_bf16_kernel<64,false,false>", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": committed_traffic("attn_fwd_vision_hbm_counters.txt"),
                      "traffic_unit": "bytes per launch (HBM, counter-measured)",

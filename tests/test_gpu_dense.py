@@ -358,7 +358,7 @@ def _run_paged(torch, st, kc, vc, bt, ps):
     return out, lse
 
 
-@pytest.mark.parametrize("ps", [64, 128])
+@pytest.mark.parametrize("ps", [64, 128, 1024])
 def test_paged_kv_against_the_oracle_and_bitwise_unpaged(torch, ps):
     """Causal GQA varlen batch (an empty and a one-token sequence included)
     over shuffled pages: against the oracle's paged view, and bitwise equal
