@@ -19,6 +19,9 @@ What it computes is the plain definition of each operation, in float64:
 * ``attn_probs``     the probability matrix P of one query piece.
 * ``rope_*`` / ``qkv_rope``  rotary position embedding on the Q and K heads
                      of a fused QKV projection output (1D and 2D grid).
+* ``qkv_proj`` / ``qkv_proj_rope``  the fused QKV projection (x w + b) and
+                     its split into Q, K (rotated) and V; ``rope_cos_sin``
+                     the per-token rotation table.
 * ``sparse_mqa``     multi-query attention over a per-row set of latent rows;
                      ``sparse_mqa_paged`` the same over a paged cache.
 * ``topk_indices``   deterministic top-k selection of the sparse indexer
@@ -42,3 +45,4 @@ from .paging import paged_rows  # noqa: F401
 from .sparse import sparse_mqa, sparse_mqa_paged  # noqa: F401
 from .pieces import piece_ranges, piece_rows_for_capacity  # noqa: F401
 from .topk import topk_indices  # noqa: F401
+from .qkv_proj import qkv_proj, qkv_proj_rope, rope_cos_sin  # noqa: F401

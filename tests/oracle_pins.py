@@ -422,6 +422,110 @@ def pin_qkv_split(orc):
 ROPE_PINS = [pin_rope_identity_and_norm, pin_rope_complex, pin_rope_relative, pin_rope_2d_halves, pin_qkv_split]
 
 
+# ============================================== fused QKV projection + RoPE
+
+def pin_qkv_proj_brute(orc):
+    """Each output is the exactly rounded dot product of a row of x with a
+    column of w, plus the bias (math.fsum over the terms, tiny sizes)."""
+    rng = _rng(311)
+    x = rng.standard_normal((5, 7))
+    w = rng.standard_normal((7, 9))
+    b = rng.standard_normal(9)
+    y = orc.qkv_proj(x, w, b)
+    y0 = orc.qkv_proj(x, w)
+    for t in range(5):
+        for n in range(9):
+            terms = [x[t, i] * w[i, n] for i in range(7)]
+            assert abs(y[t, n] - math.fsum(terms + [b[n]])) < 1e-13
+            assert abs(y0[t, n] - math.fsum(terms)) < 1e-13
+
+
+def pin_qkv_proj_rope_identity_weight(orc):
+    """With the identity as weight (hidden = N) the fused step is the
+    already-pinned qkv_rope of x, and V is x's last Hkv heads unrotated."""
+    rng = _rng(312)
+    hq, hkv, d, t = 3, 1, 8, 6
+    n = (hq + 2 * hkv) * d
+    x = rng.standard_normal((t, n))
+    for pos in (rng.integers(0, 3000, t), rng.integers(0, 90, (t, 2))):
+        q, k, v = orc.qkv_proj_rope(x, np.eye(n), None, pos, 1e4, hq, hkv, d)
+        q0, k0 = orc.qkv_rope(x, pos, 1e4, hq, hkv, d)
+        assert np.array_equal(q, q0) and np.array_equal(k, k0)
+        assert np.array_equal(v, x[:, (hq + hkv) * d:].reshape(t, hkv, d))
+
+
+def pin_qkv_proj_rope_structure(orc):
+    """Position 0 (or rotate=False) gives the plain column split of x w + b,
+    column by column; the rotation keeps each pair's length; a token's output
+    depends only on its own row and position; the map is linear in (x, b)."""
+    rng = _rng(313)
+    hq, hkv, d, t, hid = 2, 2, 8, 5, 11
+    n = (hq + 2 * hkv) * d
+    x = rng.standard_normal((t, hid))
+    w = rng.standard_normal((hid, n))
+    b = rng.standard_normal(n)
+    q, k, v = orc.qkv_proj_rope(x, w, b, np.zeros(t, np.int64), 1e4, hq, hkv, d)
+    pos = rng.integers(1, 5000, t)
+    qa, ka, va = orc.qkv_proj_rope(x, w, b, pos, 1e4, hq, hkv, d, rotate=False)
+    for tt in range(t):
+        for c in range(n):
+            ref = math.fsum([x[tt, i] * w[i, c] for i in range(hid)] + [b[c]])
+            h, e = divmod(c, d)
+            if h < hq:
+                got = (q[tt, h, e], qa[tt, h, e])
+            elif h < hq + hkv:
+                got = (k[tt, h - hq, e], ka[tt, h - hq, e])
+            else:
+                got = (v[tt, h - hq - hkv, e], va[tt, h - hq - hkv, e])
+            assert abs(got[0] - ref) < 1e-12 and abs(got[1] - ref) < 1e-12
+    qr, kr, vr = orc.qkv_proj_rope(x, w, b, pos, 1e4, hq, hkv, d)
+    assert np.array_equal(vr, v)
+    assert np.allclose(np.hypot(qr[..., 0::2], qr[..., 1::2]), np.hypot(q[..., 0::2], q[..., 1::2]), rtol=1e-13, atol=0)
+    assert np.allclose(np.hypot(kr[..., 0::2], kr[..., 1::2]), np.hypot(k[..., 0::2], k[..., 1::2]), rtol=1e-13, atol=0)
+    qs, ks_, _ = orc.qkv_proj_rope(x[2:3], w, b, pos[2:3], 1e4, hq, hkv, d)
+    assert np.allclose(qs[0], qr[2], rtol=0, atol=1e-12) and np.allclose(ks_[0], kr[2], rtol=0, atol=1e-12)
+    x2 = rng.standard_normal((t, hid))
+    b2 = rng.standard_normal(n)
+    s1 = orc.qkv_proj_rope(x, w, b, pos, 1e4, hq, hkv, d)
+    s2 = orc.qkv_proj_rope(x2, w, b2, pos, 1e4, hq, hkv, d)
+    s12 = orc.qkv_proj_rope(x + x2, w, b + b2, pos, 1e4, hq, hkv, d)
+    for a1, a2, a12 in zip(s1, s2, s12):
+        assert np.allclose(a1 + a2, a12, rtol=0, atol=1e-11)
+
+
+def pin_rope_cos_sin(orc):
+    """Table entry e of a token is (cos, sin) of pair e's angle: 1D pos *
+    theta^(-2e/d); 2D the first d/4 pairs by the grid row with span d/2, the
+    rest by the column.  Turning pairs by the table (as complex numbers)
+    reproduces the pinned rope_1d / rope_2d."""
+    rng = _rng(314)
+    d, theta, t = 16, 777.0, 7
+    p1 = rng.integers(0, 9000, t)
+    cs = orc.rope_cos_sin(p1, theta, d)
+    assert cs.shape == (t, d // 2, 2)
+    for tt in range(t):
+        for e in range(d // 2):
+            phi = p1[tt] * theta ** (-2.0 * e / d)
+            assert abs(cs[tt, e, 0] - math.cos(phi)) < 1e-12 and abs(cs[tt, e, 1] - math.sin(phi)) < 1e-12
+    p2 = rng.integers(0, 120, (t, 2))
+    cs2 = orc.rope_cos_sin(p2, theta, d)
+    for tt in range(t):
+        for e in range(d // 2):
+            axis, i = divmod(e, d // 4)
+            phi = p2[tt, axis] * theta ** (-2.0 * i / (d // 2))
+            assert abs(cs2[tt, e, 0] - math.cos(phi)) < 1e-12 and abs(cs2[tt, e, 1] - math.sin(phi)) < 1e-12
+    assert np.array_equal(orc.rope_cos_sin(np.zeros(3, np.int64), theta, d)[..., 0], np.ones((3, d // 2)))
+    x = rng.standard_normal((t, 3, d))
+    for pos, table, rot in ((p1, cs, orc.rope_1d), (p2, cs2, orc.rope_2d)):
+        z = (x[..., 0::2] + 1j * x[..., 1::2]) * (table[:, None, :, 0] + 1j * table[:, None, :, 1])
+        y = rot(x, pos, theta)
+        assert np.allclose(y[..., 0::2], z.real, rtol=0, atol=1e-12)
+        assert np.allclose(y[..., 1::2], z.imag, rtol=0, atol=1e-12)
+
+
+PROJ_PINS = [pin_qkv_proj_brute, pin_qkv_proj_rope_identity_weight, pin_qkv_proj_rope_structure, pin_rope_cos_sin]
+
+
 # ================================================================ sparse MQA
 
 def _sparse_small(seed, rows=4, heads=5, n_kv=30, d_qk=12, k=9):

@@ -72,10 +72,29 @@ MUTANTS = [
     ("topk", "out[r, :m] = (order[:m] + s).astype(np.int32)", "out[r, :m] = order[:m].astype(np.int32)",
      "positions relative to the span start"),
     ("topk", "m = min(k, ln)", "m = min(k, ln - 1)", "one selection short"),
+    ("qkv_proj", "y = y + np.asarray(bias, dtype=np.float64)[None, :]", "y = y", "bias dropped"),
+    ("qkv_proj", "y = x @ w\n    if bias", "y = x @ w[::-1]\n    if bias", "weight rows reversed (input features misaligned)"),
+    ("qkv_proj", "v = y[:, (hq + hkv) * d:].reshape(t, hkv, d)", "v = y[:, hq * d:(hq + hkv) * d].reshape(t, hkv, d)",
+     "V taken from the K columns"),
+    ("qkv_proj", "q, k = qkv_rope(y, positions, theta, hq, hkv, d)\n    return q, k, v",
+     "q, k = qkv_rope(y, positions, theta, hq, hkv, d)\n    return k, q, v", "Q and K swapped"),
+    ("qkv_proj", "return y[:, :hq * d].reshape(t, hq, d), y[:, hq * d:(hq + hkv) * d].reshape(t, hkv, d), v",
+     "return y[:, :hq * d].reshape(t, hq, d), y[:, (hq + hkv) * d:].reshape(t, hkv, d), v",
+     "unrotated K taken from the V columns"),
+    ("qkv_proj", "phi = np.concatenate([positions[:, 0].astype(np.float64)[:, None] * f,\n"
+                 "                              positions[:, 1].astype(np.float64)[:, None] * f], axis=1)",
+     "phi = np.concatenate([positions[:, 1].astype(np.float64)[:, None] * f,\n"
+     "                              positions[:, 0].astype(np.float64)[:, None] * f], axis=1)",
+     "2D table halves swapped"),
+    ("qkv_proj", "return np.stack([np.cos(phi), np.sin(phi)], axis=-1)",
+     "return np.stack([np.cos(phi), -np.sin(phi)], axis=-1)", "table turns clockwise"),
+    ("qkv_proj", "phi = positions.astype(np.float64)[:, None] * rope_inv_freq(d, theta)[None, :]",
+     "phi = positions.astype(np.float64)[:, None] * rope_inv_freq(d // 2, theta)[None, :].repeat(2, 1)",
+     "1D table built with half-span frequencies"),
 ]
 
 FAMILY = {"attention": P.DENSE_PINS, "rope": P.ROPE_PINS, "sparse": P.SPARSE_PINS, "pieces": ["pieces"],
-          "topk": P.TOPK_PINS, "paging": P.SPARSE_PINS + P.DENSE_PINS}
+          "topk": P.TOPK_PINS, "paging": P.SPARSE_PINS + P.DENSE_PINS, "qkv_proj": P.PROJ_PINS}
 
 
 def _mutated_oracle(modname, old, new):

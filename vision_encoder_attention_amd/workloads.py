@@ -310,6 +310,56 @@ def indexer(rows: int = 323, n: int = 2590, k: int = 2048, grid: float = 1.0 / 1
     return IndexerCase("indexer_r%d_n%d_k%d" % (rows, n, k), x, k, None, lens)
 
 
+@dataclasses.dataclass
+class ProjCase:
+    """Fused QKV projection + RoPE: x [T, hidden] and the fused weight
+    [hidden, (Hq + 2 Hkv) d] as bf16 bits, optional bias [N] bf16 bits."""
+    name: str
+    x: np.ndarray                   # uint16 [T, hidden]
+    w: np.ndarray                   # uint16 [hidden, N]
+    bias: Optional[np.ndarray]      # uint16 [N] or None
+    positions: np.ndarray           # int32 [T] or [T, 2]
+    hq: int
+    hkv: int
+    d: int
+    theta: float
+
+
+def qkv_proj(tokens: int = 0, hidden: int = 1024, hq: int = 16, hkv: int = 16, d: int = 64, grid=(77, 111),
+             lengths=None, bias: bool = False, seed: int = 7, theta: float = 10000.0) -> ProjCase:
+    """x ~ N(0, 1), w ~ N(0, 1) / sqrt(hidden) (outputs ~ N(0, 1)), bias ~
+    N(0, 1) when asked.  Positions: the patch grid `grid` (2D) when given,
+    else per-sequence positions of `lengths` (1D), else 0 .. tokens - 1."""
+    rng = np.random.default_rng(seed)
+    if grid is not None:
+        positions = grid_positions(*grid)
+    elif lengths is not None:
+        positions = seq_positions(lengths)
+    else:
+        positions = np.arange(tokens, dtype=np.int32)
+    t = positions.shape[0]
+    n = (hq + 2 * hkv) * d
+    x = randn_bf16_bits(rng, (t, hidden))
+    w = randn_bf16_bits(rng, (hidden, n), mul=1.0 / math.sqrt(hidden))
+    b = randn_bf16_bits(rng, (n,)) if bias else None
+    return ProjCase("qkv_proj_tok%d_hid%d_h%d-%d_d%d" % (t, hidden, hq, hkv, d), x, w, b, positions, hq, hkv, d,
+                    theta)
+
+
+def vision_proj(seed: int = 7) -> ProjCase:
+    """The vision encoder's projection before qkv_rope: 8547 grid tokens,
+    hidden 1024 = 16 heads x 64, 2D positions."""
+    return qkv_proj(hidden=1024, hq=16, hkv=16, d=64, grid=(77, 111), seed=seed)
+
+
+def varlen_proj(seed: int = 8) -> ProjCase:
+    """The varlen prefill batch's projection: the same 8 sequence lengths as
+    varlen_gqa (32876 tokens), hidden 4096 = 32 heads x 128, GQA 32/8, 1D."""
+    rng = np.random.default_rng(3)
+    lengths = [int(n) for n in rng.integers(512, 8192, size=8, endpoint=True)]
+    return qkv_proj(hidden=4096, hq=32, hkv=8, d=128, grid=None, lengths=lengths, seed=seed)
+
+
 FULL_CASES = ("single_head_f32", "vision", "varlen_gqa", "long_causal", "sparse_mqa")
 
 
