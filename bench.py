@@ -170,6 +170,8 @@ def bench_other(torch, steps, warmup, only=None):
         res.update(bench_sparse(torch, steps, warmup))
     if only in (None, "indexer"):
         res.update(bench_indexer(torch, steps, warmup))
+    if only in (None, "qkv_proj"):
+        res.update(bench_proj(torch, steps, warmup))
     return res
 
 
@@ -285,6 +287,48 @@ def bench_indexer(torch, steps, warmup):
     return res
 
 
+def bench_proj(torch, steps, warmup):
+    """Fused QKV projection + RoPE epilogue (the step before qkv_rope), on the
+    vision image and the varlen batch; beside it the unfused form of the same
+    step: the library GEMM (torch.matmul, hipBLASLt) followed by qkv_rope."""
+    import vision_encoder_attention_amd as vea
+    from vision_encoder_attention_amd import runner as R
+    from vision_encoder_attention_amd import workloads as W
+    res = {}
+    for case in (W.vision_proj(), W.varlen_proj()):
+        st = R.stage_proj(case)
+        R.run_rope_table(st)
+        t, hid = case.x.shape
+        n = (case.hq + 2 * case.hkv) * case.d
+        y = torch.empty((t, n), dtype=torch.bfloat16, device="cuda")
+        qr = torch.empty_like(st.q)
+        kr = torch.empty_like(st.k)
+
+        def unfused():
+            torch.matmul(st.x, st.w, out=y)
+            vea.qkv_rope(y, st.positions, case.theta, qr, kr)
+
+        warm_up(torch, lambda: R.run_proj(st), max(1, warmup))
+        warm_up(torch, unfused, 2)
+        tm = Timer(torch)
+        for _ in range(steps):
+            tm.run("proj", lambda: R.run_proj(st))
+            tm.run("table", lambda: R.run_rope_table(st))
+            tm.run("unfused", unfused)
+        torch.cuda.synchronize()
+        fl = 2.0 * t * hid * n
+        p_ms, p_min = tm.ms("proj")
+        u_ms, _ = tm.ms("unfused")
+        tb_ms, _ = tm.ms("table")
+        res[case.name] = {"qkv_proj_rope_ms": round(p_ms, 4), "qkv_proj_rope_min_ms": round(p_min, 4),
+                          "tflops": round(fl / p_ms / 1e9, 2), "frac_bf16_peak": round(fl / p_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                          "flops": fl, "rope_table_ms": round(tb_ms, 4),
+                          "unfused_matmul_plus_qkv_rope_ms": round(u_ms, 4)}
+        del st, y, qr, kr
+        torch.cuda.empty_cache()
+    return res
+
+
 def source_digest(paths) -> str:
     """sha256 over the given source files (identifies the kernel build a
     committed counter summary belongs to)."""
@@ -350,7 +394,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy (reference for HBM byte counters)")
-    ap.add_argument("--only", choices=["varlen_gqa", "long_causal", "sparse_mqa", "indexer"],
+    ap.add_argument("--only", choices=["varlen_gqa", "long_causal", "sparse_mqa", "indexer", "qkv_proj"],
                     help="only run one of the other workloads (for profiling one kernel family)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

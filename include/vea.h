@@ -289,6 +289,53 @@ int vea_topk_indices(const float* logits, int64_t row_stride, const int32_t* row
                      void* stream);
 
 /*
+ * vea_rope_cos_sin — per-token rotation table for vea_qkv_proj_rope: entry
+ * [t][e] = (cos phi, sin phi) of pair e (features 2e, 2e + 1 of a head) of
+ * token t, with the angle vea_qkv_rope uses for that pair (pos_dims 1: phi =
+ * positions[t] * theta^(-2e/d); pos_dims 2: pairs e < d/4 turn with
+ * positions[t][0] by theta^(-2e/(d/2)), the others with positions[t][1] by
+ * theta^(-2(e - d/4)/(d/2))).  Angle, sine and cosine in fp64, stored as
+ * fp32 (trigonometry in at least fp32 [MI250] section 4.1).  The positions of
+ * an encoder's tokens are the same in every layer, so one table serves all
+ * of its projections.
+ *
+ *   positions   device int32 [num_tokens] or [num_tokens, 2].
+ *   head_dim    even (pos_dims 1) or a multiple of 4 (pos_dims 2), <= 256.
+ *   theta       finite, > 0.
+ *   cos_sin     float [num_tokens, head_dim / 2, 2], 8-byte aligned.
+ */
+int vea_rope_cos_sin(const int32_t* positions, int pos_dims, int num_tokens, int head_dim, float theta,
+                     float* cos_sin, void* stream);
+
+/*
+ * vea_qkv_proj_rope — the fused QKV projection with the rotary embedding
+ * applied in its epilogue: y = x w (+ bias), then q = rotate(y[:, Q]),
+ * k = rotate(y[:, K]), v = y[:, V].
+ * Sources: one fused weight holds Wq | Wk | Wv ([hidden, 3 * hidden] in
+ * [SGLang] section 3.1); fusing the memory-bound work next to a projection
+ * into it [MI250] section 5.2 (fourth point); the rotation as vea_qkv_rope.
+ * The product runs on bf16 MFMA with fp32 accumulation; bias and rotation
+ * are applied to the fp32 values, which are rounded to bf16 (nearest even)
+ * once, when stored.
+ *
+ *   x           bf16 [num_tokens, x_tok_stride], columns [0, hidden).
+ *   w           bf16 [hidden, w_row_stride], columns [Q heads | K heads |
+ *               V heads] = (Hq + 2 Hkv) * head_dim, each head contiguous.
+ *   bias        bf16 [(Hq + 2 Hkv) * head_dim] or NULL (no bias).
+ *   cos_sin     the table of vea_rope_cos_sin for these tokens and head_dim,
+ *               or NULL: no rotation (a plain projection and split).
+ *   hidden      a multiple of 32.  head_dim: a multiple of 32, <= 256.
+ *   q, k, v     bf16 outputs [num_tokens, Hq, head_dim], [num_tokens, Hkv,
+ *               head_dim] (both) contiguous; they must not overlap the inputs.
+ * All pointers 16-byte aligned, strides multiples of 8 elements
+ * (VEA_EINVAL).  num_tokens * x_tok_stride and hidden * w_row_stride must stay
+ * below 2^30 elements (VEA_EUNSUPPORTED): buffer ranges are 32-bit.
+ */
+int vea_qkv_proj_rope(const void* x, int64_t x_tok_stride, const void* w, int64_t w_row_stride, const void* bias,
+                      const float* cos_sin, int num_tokens, int hidden, int num_heads_q, int num_heads_kv,
+                      int head_dim, void* q, void* k, void* v, void* stream);
+
+/*
  * vea_attn_probs_piece — debug export (not on the timed path) of the
  * probability matrix of one query piece of one head:
  *     P[r][j] = exp(scale * q_{q0+r} . k_j - lse_{q0+r}),  r < rows, j < len_k,

@@ -33,7 +33,7 @@ def test_header_declares_the_operations():
     names = _declared()
     for n in ("vea_attn_fwd", "vea_attn_fwd_workspace_size", "vea_qkv_rope", "vea_sparse_mqa_fwd",
               "vea_sparse_mqa_workspace_size", "vea_topk_indices", "vea_sparse_mqa_paged_fwd", "vea_attn_fwd_paged",
-              "vea_attn_probs_piece", "vea_status_str"):
+              "vea_attn_probs_piece", "vea_status_str", "vea_rope_cos_sin", "vea_qkv_proj_rope"):
         assert n in names
 
 
@@ -235,6 +235,50 @@ def _topk(lib, **kw):
 ])
 def test_topk_validation(lib, kw, status):
     assert _topk(lib, **kw) == status
+
+
+def _proj(lib, **kw):
+    a = dict(x=FAKE, xs=1024, w=FAKE, ws=3072, b=None, cs=None, t=100, hid=1024, hq=16, hkv=16, d=64,
+             q=FAKE, k=FAKE, v=FAKE)
+    a.update(kw)
+    return lib.vea_qkv_proj_rope(a["x"], a["xs"], a["w"], a["ws"], a["b"], a["cs"], a["t"], a["hid"], a["hq"],
+                                 a["hkv"], a["d"], a["q"], a["k"], a["v"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hid=1000, xs=1000), VEA_EUNSUPPORTED),   # hidden not a multiple of 32
+    (dict(d=48, ws=2304), VEA_EUNSUPPORTED),       # head_dim not a multiple of 32
+    (dict(d=288, ws=288 * 48), VEA_EUNSUPPORTED),
+    (dict(xs=512), VEA_ESHAPE),                    # x stride shorter than hidden
+    (dict(ws=3000), VEA_ESHAPE),                   # w stride shorter than (Hq + 2 Hkv) d
+    (dict(t=-1), VEA_ESHAPE),
+    (dict(hkv=0), VEA_ESHAPE),
+    (dict(x=None), VEA_EINVAL),
+    (dict(v=None), VEA_EINVAL),
+    (dict(w=FAKE + 8), VEA_EINVAL),                # misaligned
+    (dict(b=FAKE + 4), VEA_EINVAL),
+    (dict(cs=FAKE + 8), VEA_EINVAL),
+    (dict(xs=1028), VEA_EINVAL),                   # stride not 16 bytes
+    (dict(t=1 << 20), VEA_EUNSUPPORTED),           # x beyond 32-bit byte ranges
+    (dict(hid=1 << 19, xs=1 << 19, t=1), VEA_EUNSUPPORTED),
+    (dict(t=0), VEA_OK),
+])
+def test_qkv_proj_validation(lib, kw, status):
+    assert _proj(lib, **kw) == status
+
+
+def test_rope_table_validation(lib):
+    f = lib.vea_rope_cos_sin
+    assert f(FAKE, 3, 10, 64, 1e4, FAKE, None) == VEA_EINVAL          # pos_dims
+    assert f(FAKE, 1, 10, 64, -1.0, FAKE, None) == VEA_EINVAL         # theta
+    assert f(FAKE, 1, 10, 64, float("inf"), FAKE, None) == VEA_EINVAL
+    assert f(FAKE, 1, 10, 63, 1e4, FAKE, None) == VEA_EUNSUPPORTED    # odd head_dim
+    assert f(FAKE, 2, 10, 66, 1e4, FAKE, None) == VEA_EUNSUPPORTED    # 2D needs a multiple of 4
+    assert f(FAKE, 1, 10, 512, 1e4, FAKE, None) == VEA_EUNSUPPORTED
+    assert f(FAKE, 1, -1, 64, 1e4, FAKE, None) == VEA_ESHAPE
+    assert f(None, 1, 10, 64, 1e4, FAKE, None) == VEA_EINVAL
+    assert f(FAKE, 1, 10, 64, 1e4, FAKE + 4, None) == VEA_EINVAL      # table not 8-byte aligned
+    assert f(FAKE, 1, 0, 64, 1e4, FAKE, None) == VEA_OK
 
 
 def test_probs_validation(lib):

@@ -68,6 +68,10 @@ def load_library():
         lib.vea_sparse_mqa_workspace_size.restype = i32
         lib.vea_topk_indices.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp]
         lib.vea_topk_indices.restype = i32
+        lib.vea_rope_cos_sin.argtypes = [vp, i32, i32, i32, f32, vp, vp]
+        lib.vea_rope_cos_sin.restype = i32
+        lib.vea_qkv_proj_rope.argtypes = [vp, i64, vp, i64, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
+        lib.vea_qkv_proj_rope.restype = i32
         lib.vea_attn_probs_piece.argtypes = [i32, vp, i64, vp, i64, vp, i64, i32, i32, i32, i32, i32, i32,
                                              i32, i32, i32, i32, i32, f32, vp, i64, vp]
         lib.vea_attn_probs_piece.restype = i32
@@ -254,6 +258,46 @@ def qkv_rope(x_qkv, positions, theta, q, k):
                           q.shape[1], k.shape[1], q.shape[2], float(theta), _ptr(q), _ptr(k), _stream(x_qkv))
     _check(st)
     return q, k
+
+
+def rope_cos_sin(positions, head_dim, theta, out=None):
+    """Per-token rotation table float32 [T, head_dim/2, 2] of (cos, sin) for
+    qkv_proj_rope (see vea_rope_cos_sin); positions int32 [T] or [T, 2]."""
+    lib = load_library()
+    torch = _torch()
+    _int32_dev(positions, "positions")
+    t = positions.shape[0]
+    if out is None:
+        out = torch.empty((t, head_dim // 2, 2), dtype=torch.float32, device=positions.device)
+    if out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != (t, head_dim // 2, 2):
+        raise ValueError("out must be a contiguous float32 [T, head_dim/2, 2] tensor")
+    _check(lib.vea_rope_cos_sin(_ptr(positions), positions.dim(), t, int(head_dim), float(theta), _ptr(out),
+                                _stream(positions)))
+    return out
+
+
+def qkv_proj_rope(x, w, bias, cos_sin, q, k, v):
+    """q, k, v = split(x @ w (+ bias)) with Q and K rotated by the table
+    cos_sin (None: not rotated); see vea_qkv_proj_rope.  x [T, hidden] and
+    w [hidden, (Hq + 2 Hkv) d] bf16 with contiguous rows; q [T, Hq, d],
+    k and v [T, Hkv, d] contiguous bf16 outputs."""
+    lib = load_library()
+    torch = _torch()
+    for t, n in ((x, "x"), (w, "w"), (q, "q"), (k, "k"), (v, "v")) + (((bias, "bias"),) if bias is not None else ()):
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise TypeError("%s must be a bfloat16 GPU tensor" % n)
+    if x.dim() != 2 or x.stride(1) != 1 or w.dim() != 2 or w.stride(1) != 1:
+        raise ValueError("x and w must be 2-D with contiguous rows")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k and v outputs must be contiguous")
+    if bias is not None and not bias.is_contiguous():
+        raise ValueError("bias must be contiguous")
+    if cos_sin is not None and (cos_sin.dtype != torch.float32 or not cos_sin.is_contiguous()):
+        raise ValueError("cos_sin must be a contiguous float32 table")
+    st = lib.vea_qkv_proj_rope(_ptr(x), x.stride(0), _ptr(w), w.stride(0), _ptr(bias), _ptr(cos_sin), x.shape[0],
+                               x.shape[1], q.shape[1], k.shape[1], q.shape[2], _ptr(q), _ptr(k), _ptr(v), _stream(x))
+    _check(st)
+    return q, k, v
 
 
 def sparse_mqa_workspace_size(rows, heads, d_qk, d_v, k) -> int:

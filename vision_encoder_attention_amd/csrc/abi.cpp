@@ -421,6 +421,50 @@ int vea_topk_indices(const float* logits, int64_t row_stride, const int32_t* row
   return finish(hip_status(launch_topk(p, s)), s);
 }
 
+int vea_rope_cos_sin(const int32_t* positions, int pos_dims, int num_tokens, int head_dim, float theta,
+                     float* cos_sin, void* stream) {
+  if (num_tokens < 0 || head_dim <= 0) return VEA_ESHAPE;
+  if (pos_dims != 1 && pos_dims != 2) return VEA_EINVAL;
+  if (!isfinite(theta) || !(theta > 0.f)) return VEA_EINVAL;
+  if (head_dim % 2 != 0 || head_dim > 256 || (pos_dims == 2 && head_dim % 4 != 0)) return VEA_EUNSUPPORTED;
+  if (num_tokens == 0) return VEA_OK;
+  if (!positions || !cos_sin) return VEA_EINVAL;
+  if (reinterpret_cast<uintptr_t>(cos_sin) & 7u) return VEA_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  RopeTableParams p;
+  p.pos = positions; p.out = cos_sin; p.tokens = num_tokens; p.d = head_dim; p.pos_dims = pos_dims;
+  p.theta = (double)theta;
+  return finish(hip_status(launch_rope_cos_sin(p, s)), s);
+}
+
+int vea_qkv_proj_rope(const void* x, int64_t x_tok_stride, const void* w, int64_t w_row_stride, const void* bias,
+                      const float* cos_sin, int num_tokens, int hidden, int num_heads_q, int num_heads_kv,
+                      int head_dim, void* q, void* k, void* v, void* stream) {
+  if (num_tokens < 0 || hidden <= 0 || num_heads_q <= 0 || num_heads_kv <= 0 || head_dim <= 0) return VEA_ESHAPE;
+  const int64_t n = (int64_t)(num_heads_q + 2 * (int64_t)num_heads_kv) * head_dim;
+  if (x_tok_stride < hidden || w_row_stride < n) return VEA_ESHAPE;
+  if (hidden % kProjStepK != 0 || head_dim % 32 != 0 || head_dim > 256) return VEA_EUNSUPPORTED;
+  // Buffer ranges and per-lane offsets are 32-bit.
+  if (n > 0x7fffffff / 2 || (int64_t)num_tokens * x_tok_stride * 2 > 0x7fffffff ||
+      (int64_t)kProjTileT * x_tok_stride * 2 > 0x7fffffff || (int64_t)hidden * w_row_stride * 2 > 0x7fffffff)
+    return VEA_EUNSUPPORTED;
+  const int64_t ftiles = (n + kProjTileF - 1) / kProjTileF;
+  if (ftiles * ((num_tokens + kProjTileT - 1) / kProjTileT) > 0x7fffffff) return VEA_EUNSUPPORTED;
+  if (num_tokens == 0) return VEA_OK;
+  if (!x || !w || !q || !k || !v) return VEA_EINVAL;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(q) || !aligned16(k) || !aligned16(v)) return VEA_EINVAL;
+  if ((bias && !aligned16(bias)) || (cos_sin && !aligned16(cos_sin))) return VEA_EINVAL;
+  if ((x_tok_stride * 2) % 16 || (w_row_stride * 2) % 16) return VEA_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  ProjParams p;
+  p.x = (const uint16_t*)x; p.w = (const uint16_t*)w; p.bias = (const uint16_t*)bias; p.cs = cos_sin;
+  p.q = (uint16_t*)q; p.k = (uint16_t*)k; p.v = (uint16_t*)v;
+  p.x_stride = x_tok_stride; p.w_stride = w_row_stride;
+  p.tokens = num_tokens; p.hidden = hidden; p.hq = num_heads_q; p.hkv = num_heads_kv; p.d = head_dim;
+  p.n_feat = (int)n; p.ftiles = (int)ftiles;
+  return finish(hip_status(launch_qkv_proj(p, s)), s);
+}
+
 int vea_attn_probs_piece(int dtype, const void* q, int64_t q_tok_stride, const void* k, int64_t k_tok_stride,
                          const float* lse, int64_t lse_row_stride, int head, int num_heads_q, int num_heads_kv,
                          int head_dim, int seq_begin_q, int len_q, int seq_begin_k, int len_k, int q0, int rows,

@@ -134,6 +134,34 @@ struct TopkParams {
 constexpr int kTopkMaxN = 4096;   // positions per row the LDS sort holds
 hipError_t launch_topk(const TopkParams& p, hipStream_t s);
 
+// Fused QKV projection: out = x w (+ bias), Q and K rotated by the per-token
+// (cos, sin) table cs [tokens, d/2, 2] (nullable: no rotation).
+struct ProjParams {
+  const uint16_t* x;         // bf16 [tokens, x_stride]
+  const uint16_t* w;         // bf16 [hidden, w_stride], columns [Q | K | V]
+  const uint16_t* bias;      // bf16 [n_feat] or null
+  const float* cs;           // [tokens, d/2, 2] or null
+  uint16_t* q;               // bf16 [tokens, hq, d]
+  uint16_t* k;               // bf16 [tokens, hkv, d]
+  uint16_t* v;               // bf16 [tokens, hkv, d]
+  int64_t x_stride, w_stride;   // elements
+  int tokens, hidden, hq, hkv, d;
+  int n_feat;                // (hq + 2 hkv) d
+  int ftiles;                // ceil(n_feat / kProjTileF)
+};
+constexpr int kProjTileF = 256;   // features per workgroup tile
+constexpr int kProjTileT = 256;   // tokens per workgroup tile
+constexpr int kProjStepK = 32;    // hidden is a multiple of this
+hipError_t launch_qkv_proj(const ProjParams& p, hipStream_t s);
+
+struct RopeTableParams {
+  const int32_t* pos;        // [tokens] or [tokens, 2]
+  float* out;                // [tokens, d/2, 2]
+  int tokens, d, pos_dims;
+  double theta;
+};
+hipError_t launch_rope_cos_sin(const RopeTableParams& p, hipStream_t s);
+
 // Tile shape of the dense bf16/f32 kernels (query rows per workgroup); the
 // host uses it to size the launch.
 constexpr int kDenseBM = 128;

@@ -12,7 +12,7 @@ from typing import Optional
 import numpy as np
 
 from . import _binding as B
-from .workloads import DenseCase, SparseCase
+from .workloads import DenseCase, ProjCase, SparseCase
 
 
 def _torch():
@@ -152,3 +152,41 @@ def run_sparse(st: SparseStaged):
     c = st.case
     B.sparse_mqa_fwd(st.q, st.kv, st.idx, st.idx.shape[1], c.scale, st.out, st.lse, workspace=st.ws)
     return st.out, st.lse
+
+
+@dataclasses.dataclass
+class ProjStaged:
+    case: ProjCase
+    x: "torch.Tensor"
+    w: "torch.Tensor"
+    bias: Optional["torch.Tensor"]
+    positions: "torch.Tensor"
+    cs: Optional["torch.Tensor"]       # rotation table, None: no rotation
+    q: "torch.Tensor"
+    k: "torch.Tensor"
+    v: "torch.Tensor"
+
+
+def stage_proj(case: ProjCase, device="cuda", rotate: bool = True) -> ProjStaged:
+    torch = _torch()
+    x = bits_to_tensor(case.x, device)
+    w = bits_to_tensor(case.w, device)
+    bias = None if case.bias is None else bits_to_tensor(case.bias, device)
+    pos = _dev_i32(case.positions, device)
+    t = x.shape[0]
+    cs = torch.empty((t, case.d // 2, 2), dtype=torch.float32, device=device) if rotate else None
+    q = torch.empty((t, case.hq, case.d), dtype=torch.bfloat16, device=device)
+    k = torch.empty((t, case.hkv, case.d), dtype=torch.bfloat16, device=device)
+    v = torch.empty((t, case.hkv, case.d), dtype=torch.bfloat16, device=device)
+    return ProjStaged(case, x, w, bias, pos, cs, q, k, v)
+
+
+def run_rope_table(st: ProjStaged):
+    if st.cs is not None:
+        B.rope_cos_sin(st.positions, st.case.d, st.case.theta, st.cs)
+    return st.cs
+
+
+def run_proj(st: ProjStaged):
+    B.qkv_proj_rope(st.x, st.w, st.bias, st.cs, st.q, st.k, st.v)
+    return st.q, st.k, st.v

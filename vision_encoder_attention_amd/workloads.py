@@ -327,7 +327,8 @@ class ProjCase:
 
 def qkv_proj(tokens: int = 0, hidden: int = 1024, hq: int = 16, hkv: int = 16, d: int = 64, grid=(77, 111),
              lengths=None, bias: bool = False, seed: int = 7, theta: float = 10000.0) -> ProjCase:
-    """x ~ N(0, 1), w ~ N(0, 1) / sqrt(hidden) (outputs ~ N(0, 1)), bias ~
+    """x ~ N(0, 1), w ~ N(0, 1) / sqrt(hidden) (rounded to a power of two;
+    outputs ~ N(0, 1)), bias ~
     N(0, 1) when asked.  Positions: the patch grid `grid` (2D) when given,
     else per-sequence positions of `lengths` (1D), else 0 .. tokens - 1."""
     rng = np.random.default_rng(seed)
@@ -340,7 +341,7 @@ def qkv_proj(tokens: int = 0, hidden: int = 1024, hq: int = 16, hkv: int = 16, d
     t = positions.shape[0]
     n = (hq + 2 * hkv) * d
     x = randn_bf16_bits(rng, (t, hidden))
-    w = randn_bf16_bits(rng, (hidden, n), mul=1.0 / math.sqrt(hidden))
+    w = randn_bf16_bits(rng, (hidden, n), mul=2.0 ** -round(math.log2(math.sqrt(hidden))))
     b = randn_bf16_bits(rng, (n,)) if bias else None
     return ProjCase("qkv_proj_tok%d_hid%d_h%d-%d_d%d" % (t, hidden, hq, hkv, d), x, w, b, positions, hq, hkv, d,
                     theta)
