@@ -79,7 +79,14 @@ constexpr int kXLoads = kXTile / (kThreads * 16);
 static_assert(kWLoads == 2 && kXLoads == 2, "the step's vmcnt below counts 4 loads per lane");
 constexpr unsigned kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit format
 
-__global__ __launch_bounds__(kThreads, 1) void qkv_proj_kernel(ProjParams p) {
+// The table, bias and outputs also come as separate restrict-qualified
+// arguments: the compiler may then issue the epilogue's table and bias loads
+// ahead of its stores instead of one load-use round trip per block.
+__global__ __launch_bounds__(kThreads, 1) void qkv_proj_kernel(ProjParams p, const float* __restrict__ cs_tab,
+                                                               const uint16_t* __restrict__ bias,
+                                                               uint16_t* __restrict__ out_q,
+                                                               uint16_t* __restrict__ out_k,
+                                                               uint16_t* __restrict__ out_v) {
   __shared__ __attribute__((aligned(1024))) unsigned char w0[kWTile];
   __shared__ __attribute__((aligned(1024))) unsigned char w1[kWTile];
   __shared__ __attribute__((aligned(1024))) unsigned char w2[kWTile];
@@ -223,75 +230,107 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_proj_kernel(ProjParams p) {
   }
   __builtin_amdgcn_s_waitcnt(0x0070);                     // the last (zero) loads: vmcnt(0)
 
-  // ---- epilogue
+  // ---- epilogue, block by block (8 blocks of 32 features x 32 tokens per
+  // lane set).  The table entries and bias of block i + 1 are loaded while
+  // block i is finished, so each round trip to memory is paid about once.
   const int qn = p.hq * p.d, kn = (p.hq + p.hkv) * p.d;
   const int half = p.d >> 1;
+  struct Blk {
+    bool live, rot;
+    int t, base, heads, f0, dd0;
+    uint16_t* out;
+  };
+  auto blk = [&](int i) {
+    const int tb = i >> 2, fb = i & 3;
+    Blk b;
+    const int nb = n0 + 128 * wf + 32 * fb;               // first feature of the block (uniform)
+    b.t = t0 + 64 * wt + 32 * tb + l32;
+    b.live = nb < p.n_feat;
+    if (nb < qn) {
+      b.out = out_q; b.base = 0; b.heads = p.hq;
+    } else if (nb < kn) {
+      b.out = out_k; b.base = qn; b.heads = p.hkv;
+    } else {
+      b.out = out_v; b.base = kn; b.heads = p.hkv;
+    }
+    b.rot = cs_tab != nullptr && nb < kn;
+    b.f0 = nb - b.base;                                   // feature inside the region
+    b.dd0 = b.f0 % p.d;                                   // inside the head (multiple of 32)
+    return b;
+  };
+  // Operands of one block: (cos, sin) of pair entries e, e + 1 of each run a
+  // (e = (dd0 + 8a + 4 g2) / 2) and the bias of the run's 4 features.
+  struct Ops {
+    floatx4 cs[4];
+    u32x2 bb[4];
+  };
+  auto load_ops = [&](const Blk& b, Ops& o) {
+    if (!b.live) return;
+    const int tc = b.t < p.tokens ? b.t : p.tokens - 1;
+    if (b.rot) {
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
-    const int t = t0 + 64 * wt + 32 * tb + l32;
-    const bool tv = t < p.tokens;
-    const int tc = tv ? t : p.tokens - 1;
+      for (int a = 0; a < 4; ++a)
+        o.cs[a] = *(const floatx4*)(cs_tab + ((int64_t)tc * half + ((b.dd0 + 8 * a + 4 * g2) >> 1)) * 2);
+    }
+    if (bias != nullptr) {
 #pragma unroll
-    for (int fb = 0; fb < 4; ++fb) {
-      const int nb = n0 + 128 * wf + 32 * fb;             // first feature of the block
-      if (nb >= p.n_feat) continue;                       // uniform
-      uint16_t* out;
-      int base, heads;
-      if (nb < qn) {
-        out = p.q; base = 0; heads = p.hq;
-      } else if (nb < kn) {
-        out = p.k; base = qn; heads = p.hkv;
-      } else {
-        out = p.v; base = kn; heads = p.hkv;
+      for (int a = 0; a < 4; ++a) o.bb[a] = *(const u32x2*)(bias + b.base + b.f0 + 8 * a + 4 * g2);
+    }
+  };
+  auto finish = [&](const Blk& b, const Ops& o, const floatx16& c) {
+    if (!b.live) return;
+    uint32_t pk[4][2];                                    // bf16 of run a: 4 features 8a + 4 g2 + (0..3)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      float y0 = c[4 * a], y1 = c[4 * a + 1], y2 = c[4 * a + 2], y3 = c[4 * a + 3];
+      if (bias != nullptr) {
+        y0 += bf16_lo(o.bb[a][0]);
+        y1 += bf16_hi(o.bb[a][0]);
+        y2 += bf16_lo(o.bb[a][1]);
+        y3 += bf16_hi(o.bb[a][1]);
       }
-      const bool rot = p.cs != nullptr && nb < kn;
-      const int f0 = nb - base;                           // feature inside the region
-      const int dd0 = f0 % p.d;                           // inside the head (multiple of 32)
-      const floatx16 c = acc[fb][tb];
-      uint32_t pk[4][2];                                  // bf16 of run a: 4 features 8a + 4 g2 + (0..3)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        float y0 = c[4 * a], y1 = c[4 * a + 1], y2 = c[4 * a + 2], y3 = c[4 * a + 3];
-        const int fo = f0 + 8 * a + 4 * g2;               // this lane's first feature of the run
-        if (p.bias != nullptr) {
-          const u32x2 bb = *(const u32x2*)(p.bias + base + fo);
-          y0 += bf16_lo(bb[0]);
-          y1 += bf16_hi(bb[0]);
-          y2 += bf16_lo(bb[1]);
-          y3 += bf16_hi(bb[1]);
-        }
-        if (rot) {
-          const int e = (dd0 + 8 * a + 4 * g2) >> 1;       // pair entry of (y0, y1); (y2, y3) is e + 1
-          const floatx4 cs = *(const floatx4*)(p.cs + ((int64_t)tc * half + e) * 2);
-          const float r0 = y0 * cs[0] - y1 * cs[1], r1 = y0 * cs[1] + y1 * cs[0];
-          const float r2 = y2 * cs[2] - y3 * cs[3], r3 = y2 * cs[3] + y3 * cs[2];
-          y0 = r0; y1 = r1; y2 = r2; y3 = r3;
-        }
-        pk[a][0] = pack_bf16x2(y0, y1);
-        pk[a][1] = pack_bf16x2(y2, y3);
+      if (b.rot) {
+        const floatx4 cs = o.cs[a];
+        const float r0 = y0 * cs[0] - y1 * cs[1], r1 = y0 * cs[1] + y1 * cs[0];
+        const float r2 = y2 * cs[2] - y3 * cs[3], r3 = y2 * cs[3] + y3 * cs[2];
+        y0 = r0; y1 = r1; y2 = r2; y3 = r3;
       }
-      // Lanes l and l + 32 hold the two halves of every 8-feature run.  Swap
-      // so that the low lane gets runs 1 and 3 whole and the high lane runs 0
-      // and 2 (permlane32_swap(x, y): lanes 32..63 of x trade with lanes
-      // 0..31 of y).
-      uint32_t run[2][4];
+      pk[a][0] = pack_bf16x2(y0, y1);
+      pk[a][1] = pack_bf16x2(y2, y3);
+    }
+    // Lanes l and l + 32 hold the two halves of every 8-feature run.  Swap so
+    // that the low lane gets runs 1 and 3 whole and the high lane runs 0 and 2
+    // (permlane32_swap(x, y): lanes 32..63 of x trade with lanes 0..31 of y).
+    uint32_t run[2][4];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {                       // run pair (2h, 2h + 1)
+    for (int h = 0; h < 2; ++h) {                         // run pair (2h, 2h + 1)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const auto r = __builtin_amdgcn_permlane32_swap(pk[2 * h + 1][j], pk[2 * h][j], false, false);
-          run[h][j] = r[0];                               // low: run 2h+1 features 0..3; high: run 2h 0..3
-          run[h][2 + j] = r[1];                           // low: run 2h+1 features 4..7; high: run 2h 4..7
-        }
-      }
-      if (tv) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int fo = f0 + 8 * (2 * h + 1 - g2);
-          *(u32x4*)(out + (int64_t)t * heads * p.d + fo) = (u32x4){run[h][0], run[h][1], run[h][2], run[h][3]};
-        }
+      for (int j = 0; j < 2; ++j) {
+        const auto r = __builtin_amdgcn_permlane32_swap(pk[2 * h + 1][j], pk[2 * h][j], false, false);
+        run[h][j] = r[0];                                 // low: run 2h+1 features 0..3; high: run 2h 0..3
+        run[h][2 + j] = r[1];                             // low: run 2h+1 features 4..7; high: run 2h 4..7
       }
     }
+    if (b.t < p.tokens) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int fo = b.f0 + 8 * (2 * h + 1 - g2);
+        *(u32x4*)(b.out + (int64_t)b.t * b.heads * p.d + fo) = (u32x4){run[h][0], run[h][1], run[h][2], run[h][3]};
+      }
+    }
+  };
+  Ops ops[2];
+  Blk cur = blk(0);
+  load_ops(cur, ops[0]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    Blk nxt;
+    if (i + 1 < 8) {
+      nxt = blk(i + 1);
+      load_ops(nxt, ops[(i + 1) & 1]);
+    }
+    finish(cur, ops[i & 1], acc[i & 3][i >> 2]);
+    cur = nxt;
   }
 }
 
@@ -328,7 +367,7 @@ hipError_t launch_qkv_proj(const ProjParams& p, hipStream_t s) {
     return hipErrorInvalidValue;
   const int64_t tiles = (int64_t)p.ftiles * ((p.tokens + kPT - 1) / kPT);
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(qkv_proj_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(qkv_proj_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, p, p.cs, p.bias, p.q, p.k, p.v);
   return hipGetLastError();
 }
 
