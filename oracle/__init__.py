@@ -22,6 +22,8 @@ What it computes is the plain definition of each operation, in float64:
 * ``qkv_proj`` / ``qkv_proj_rope``  the fused QKV projection (x w + b) and
                      its split into Q, K (rotated) and V; ``rope_cos_sin``
                      the per-token rotation table.
+* ``e4m3_*`` / ``quantize_fp8`` / ``attention_fp8``  OCP FP8 E4M3 coding,
+                     block quantisation and attention on quantised inputs.
 * ``sparse_mqa``     multi-query attention over a per-row set of latent rows;
                      ``sparse_mqa_paged`` the same over a paged cache.
 * ``topk_indices``   deterministic top-k selection of the sparse indexer
@@ -46,3 +48,4 @@ from .sparse import sparse_mqa, sparse_mqa_paged  # noqa: F401
 from .pieces import piece_ranges, piece_rows_for_capacity  # noqa: F401
 from .topk import topk_indices  # noqa: F401
 from .qkv_proj import qkv_proj, qkv_proj_rope, rope_cos_sin  # noqa: F401
+from .fp8 import attention_fp8, e4m3_decode, e4m3_encode, e4m3_values, quantize_fp8  # noqa: F401

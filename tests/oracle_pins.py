@@ -526,6 +526,133 @@ def pin_rope_cos_sin(orc):
 PROJ_PINS = [pin_qkv_proj_brute, pin_qkv_proj_rope_identity_weight, pin_qkv_proj_rope_structure, pin_rope_cos_sin]
 
 
+# ========================================================== FP8 (OCP e4m3)
+
+def _e4m3_by_fields(c):
+    """Value of code c from its bit fields, written out: (-1)^s 2^(e-7) (1 + m/8),
+    subnormals (e = 0) m 2^-9, S.1111.111 NaN."""
+    c = int(c)
+    s, e, m = c >> 7, (c >> 3) & 15, c & 7
+    if e == 15 and m == 7:
+        return math.nan
+    mag = m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+    return -mag if s else mag
+
+
+def pin_e4m3_table(orc):
+    """Every code decodes as its bit fields say; 254 non-NaN codes; 1.0 is
+    0x38, the largest value 448 is 0x7e, the smallest normal 2^-6 is 0x08,
+    the smallest subnormal 2^-9 is 0x01; codes 0x00..0x7e increase."""
+    v = orc.e4m3_values()
+    for c in range(256):
+        f = _e4m3_by_fields(c)
+        assert (math.isnan(f) and math.isnan(v[c])) or v[c] == f, c
+    assert int(np.sum(~np.isnan(v))) == 254
+    assert v[0x38] == 1.0 and v[0x7E] == 448.0 and v[0x08] == 2.0 ** -6 and v[0x01] == 2.0 ** -9
+    assert np.all(np.diff(v[:0x7F]) > 0) and np.array_equal(v[0x80:0xFF], -v[:0x7F])
+
+
+def pin_e4m3_rounding(orc):
+    """Encoding returns every finite value's own code; a value strictly
+    between two neighbours goes to the nearer; a midpoint goes to the even
+    code (the even mantissa); the sign survives rounding to zero.  Worked
+    cases: 1.0625 (midpoint of 1 and 1.125) -> 0x38, 1.1875 -> 0x3a (1.25),
+    2^-10 (midpoint of 0 and 2^-9) -> 0x00, 1.5 * 2^-10 -> 0x01, 240 -> 0x77,
+    3 -> 0x44, -0.0 -> 0x80."""
+    v = orc.e4m3_values()
+    fin = [c for c in range(256) if not math.isnan(v[c])]
+    got = orc.e4m3_encode(v[fin])
+    for c, g in zip(fin, got):
+        assert int(g) == c or (v[c] == 0 and v[int(g)] == 0 and (c >> 7) == (int(g) >> 7)), (c, int(g))
+    pos = v[:0x7F]
+    mid = (pos[:-1] + pos[1:]) / 2
+    enc = orc.e4m3_encode(mid)
+    even = np.where(np.arange(0x7E) % 2 == 0, np.arange(0x7E), np.arange(1, 0x7F))
+    assert np.array_equal(enc, even.astype(np.uint8))
+    eps = (pos[1:] - pos[:-1]) * 1e-3
+    assert np.array_equal(orc.e4m3_encode(mid - eps), np.arange(0x7E, dtype=np.uint8))
+    assert np.array_equal(orc.e4m3_encode(mid + eps), np.arange(1, 0x7F, dtype=np.uint8))
+    cases = [(1.0625, 0x38), (1.1875, 0x3A), (2.0 ** -10, 0x00), (1.5 * 2.0 ** -10, 0x01), (240.0, 0x77),
+             (3.0, 0x44), (-0.0, 0x80), (-2.0 ** -11, 0x80), (-448.0, 0xFE)]
+    got = orc.e4m3_encode(np.array([a for a, _ in cases]))
+    assert [int(g) for g in got] == [b for _, b in cases]
+
+
+def pin_quantize_fp8(orc):
+    """Each block's largest magnitude becomes +-448 exactly (code 0x7e /
+    0xfe) and its scale is amax / 448; the dequantised values are within half
+    an e4m3 step of the inputs; an all-zero block gets scale 1 and zero
+    codes; the block axes are (token, head), head, (head, channel) -- checked
+    by brute force over each block."""
+    rng = _rng(321)
+    x = (rng.standard_normal((7, 3, 16)) * np.array([1.0, 30.0, 0.01])[None, :, None]).astype(np.float32)
+    x[2, 1, :] = 0.0
+    v = orc.e4m3_values()
+    for g in (0, 1, 2):
+        codes, sc = orc.quantize_fp8(x, g)
+        blocks = {0: [(t, h, slice(None)) for t in range(7) for h in range(3)],
+                  1: [(slice(None), h, slice(None)) for h in range(3)],
+                  2: [(slice(None), h, c) for h in range(3) for c in range(16)]}[g]
+        for blk in blocks:
+            xb = x[blk].astype(np.float64)
+            cb = codes[blk]
+            s = float({0: sc[blk[0], blk[1]] if g == 0 else 0, 1: sc[blk[1]] if g == 1 else 0,
+                       2: sc[blk[1], blk[2]] if g == 2 else 0}[g])
+            amax = float(np.abs(xb).max())
+            if amax == 0:
+                assert s == 1.0 and not np.any(v[cb]) 
+                continue
+            assert s == float(np.float32(np.float32(amax) / np.float32(448.0)))
+            i = np.unravel_index(np.argmax(np.abs(xb)), xb.shape)
+            assert abs(v[cb[i]]) == 448.0
+            deq = v[cb] * s
+            step = np.maximum(2.0 ** (np.floor(np.log2(np.maximum(np.abs(v[cb]), 2.0 ** -6))) - 3), 2.0 ** -9)
+            assert np.all(np.abs(deq - xb) <= step * s * 0.5 * (1 + 1e-6) + 448 * s * 2.0 ** -24)
+
+
+def pin_attention_fp8(orc):
+    """Attention on fp8 inputs is attention on the inputs decoded from their
+    bit fields and scaled (per (token, head), head, (head, channel)); and for
+    inputs that are exact e4m3 values with power-of-two block maxima the whole
+    quantise -> attention_fp8 chain returns attention on the inputs."""
+    rng = _rng(322)
+    cu = _cu([5, 0, 9])
+    tq, hq, hkv, d = 14, 4, 2, 8
+    q8 = rng.integers(0, 256, (tq, hq, d)).astype(np.uint8)
+    k8 = rng.integers(0, 256, (tq, hkv, d)).astype(np.uint8)
+    v8 = rng.integers(0, 256, (tq, hkv, d)).astype(np.uint8)
+    for a in (q8, k8, v8):
+        a[(a & 0x7F) == 0x7F] = 0x38                     # no NaN codes
+    qs = rng.uniform(0.01, 0.1, (tq, hq)).astype(np.float32)
+    ks = rng.uniform(0.01, 0.1, hkv).astype(np.float32)
+    vs = rng.uniform(0.5, 2.0, (hkv, d)).astype(np.float32)
+    dec = np.vectorize(_e4m3_by_fields)
+    q = dec(q8) * qs[:, :, None]
+    k = dec(k8) * ks[None, :, None]
+    v = dec(v8) * vs[None, :, :]
+    for causal in (False, True):
+        o1, l1 = orc.attention_fp8(q8, qs, k8, ks, v8, vs, cu, cu, causal, 0.3)
+        o2, l2 = orc.attention(q, k, v, cu, cu, causal, 0.3)
+        assert np.allclose(o1, o2, rtol=0, atol=1e-13) and np.allclose(l1, l2, rtol=0, atol=1e-13)
+    vals = orc.e4m3_values()[[0x30, 0x38, 0x3C, 0x44, 0x7E, 0xB8, 0xC4, 0x00]]
+    xq = rng.choice(vals, (tq, hq, d))
+    xq[:, :, 0] = 448.0                                  # every block's max is 448: scale 1
+    xk = rng.choice(vals, (tq, hkv, d))
+    xk[0, :, 0] = 448.0
+    xv = rng.choice(vals, (tq, hkv, d))
+    xv[0, :, :] = 448.0
+    cq, sq = orc.quantize_fp8(xq, 0)
+    ck, sk = orc.quantize_fp8(xk, 1)
+    cv, sv = orc.quantize_fp8(xv, 2)
+    assert np.all(sq == 1) and np.all(sk == 1) and np.all(sv == 1)
+    o1, l1 = orc.attention_fp8(cq, sq, ck, sk, cv, sv, cu, cu, True, 0.01)
+    o2, l2 = orc.attention(xq, xk, xv, cu, cu, True, 0.01)
+    assert np.allclose(o1, o2, rtol=0, atol=1e-12) and np.allclose(l1, l2, rtol=0, atol=1e-12)
+
+
+FP8_PINS = [pin_e4m3_table, pin_e4m3_rounding, pin_quantize_fp8, pin_attention_fp8]
+
+
 # ================================================================ sparse MQA
 
 def _sparse_small(seed, rows=4, heads=5, n_kv=30, d_qk=12, k=9):

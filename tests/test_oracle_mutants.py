@@ -91,10 +91,26 @@ MUTANTS = [
     ("qkv_proj", "phi = positions.astype(np.float64)[:, None] * rope_inv_freq(d, theta)[None, :]",
      "phi = positions.astype(np.float64)[:, None] * rope_inv_freq(d // 2, theta)[None, :].repeat(2, 1)",
      "1D table built with half-span frequencies"),
+    ("fp8", "v[c] = s * (1.0 + m / 8.0) * 2.0 ** (e - 7)", "v[c] = s * (1.0 + m / 8.0) * 2.0 ** (e - 8)",
+     "e4m3 exponent bias 8 (the FNUZ variant)"),
+    ("fp8", "v[c] = s * m * 2.0 ** -9", "v[c] = s * m * 2.0 ** -10", "subnormal step halved"),
+    ("fp8", "pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))", "pick_hi = (dhi <= dlo)",
+     "ties rounded up instead of to even"),
+    ("fp8", "return np.where(neg, code | 0x80, code).astype(np.uint8)", "return code.astype(np.uint8)",
+     "sign dropped"),
+    ("fp8", "ax = {0: (2,), 1: (0, 2), 2: (0,)}[granularity]", "ax = {0: (1,), 1: (0, 2), 2: (0,)}[granularity]",
+     "per-token blocks taken over heads instead of channels"),
+    ("fp8", "ax = {0: (2,), 1: (0, 2), 2: (0,)}[granularity]", "ax = {0: (2,), 1: (0, 2), 2: (2,)}[granularity]",
+     "per-channel scales taken over channels"),
+    ("fp8", "scale = np.where(zero, np.float32(1), safe / np.float32(E4M3_MAX)).astype(np.float32)",
+     "scale = np.where(zero, np.float32(1), safe / np.float32(240.0)).astype(np.float32)",
+     "dequantisation scale for a 240 maximum"),
+    ("fp8", "return v * s[None, :, :]", "return v * s[None, :, 0:1]", "v scaled by its first channel's scale"),
+    ("fp8", "k = dequantize(k8, k_scale, 1)", "k = e4m3_decode(k8)", "k scale ignored"),
 ]
 
 FAMILY = {"attention": P.DENSE_PINS, "rope": P.ROPE_PINS, "sparse": P.SPARSE_PINS, "pieces": ["pieces"],
-          "topk": P.TOPK_PINS, "paging": P.SPARSE_PINS + P.DENSE_PINS, "qkv_proj": P.PROJ_PINS}
+          "topk": P.TOPK_PINS, "paging": P.SPARSE_PINS + P.DENSE_PINS, "qkv_proj": P.PROJ_PINS, "fp8": P.FP8_PINS}
 
 
 def _mutated_oracle(modname, old, new):

@@ -10,7 +10,7 @@ from tests import oracle_pins as P
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_figures.json")
 
 
-@pytest.mark.parametrize("pin", P.DENSE_PINS + P.ROPE_PINS + P.SPARSE_PINS + P.TOPK_PINS + P.PROJ_PINS, ids=lambda f: f.__name__)
+@pytest.mark.parametrize("pin", P.DENSE_PINS + P.ROPE_PINS + P.SPARSE_PINS + P.TOPK_PINS + P.PROJ_PINS + P.FP8_PINS, ids=lambda f: f.__name__)
 def test_pin(pin):
     pin(oracle)
 
