@@ -14,12 +14,15 @@ Quantisation of a block B of real values (a block is one (token, head) row,
 one head, or one (head, channel) column, depending on the granularity):
 
     amax  = max |x| over B                    (exact: the inputs are bf16)
-    scale = amax / 448,  inv = 448 / amax     (fp32 divisions; both 1 when
-                                               amax = 0)
+    scale = fp32(amax / 448),  inv = fp32(1 / scale)
+                                              (both 1 when amax < 2^-64,
+                                               which counts as an empty block)
     code  = e4m3 nearest-even of clamp(fp32(x * inv), -448, 448)
 
-The product x * inv is rounded to fp32 before the rounding to e4m3, so that
-the integer code is decided in the precision of the kernel that produces it.
+inv is derived from the stored scale, and the product x * inv is rounded to
+fp32 before the rounding to e4m3: the integer code is decided from the same
+fp32 values a kernel has, also when the scales are computed by one pass and
+the codes by another.
 The dequantised value is decode(code) * scale.
 
 ``attention_fp8`` is attention (oracle.attention) on the dequantised q, k and
@@ -88,10 +91,10 @@ def quantize_fp8(x, granularity: int):
         raise ValueError("x must be [tokens, heads, head_dim]")
     ax = {0: (2,), 1: (0, 2), 2: (0,)}[granularity]
     amax = np.abs(x).max(axis=ax, keepdims=True) if x.size else np.zeros((1, 1, 1), np.float32)
-    zero = amax == 0
+    zero = amax < np.float32(2.0 ** -64)
     safe = np.where(zero, np.float32(1), amax).astype(np.float32)
-    inv = np.where(zero, np.float32(1), np.float32(E4M3_MAX) / safe).astype(np.float32)
     scale = np.where(zero, np.float32(1), safe / np.float32(E4M3_MAX)).astype(np.float32)
+    inv = (np.float32(1) / scale).astype(np.float32)
     y = np.clip((x * inv).astype(np.float32), -E4M3_MAX, E4M3_MAX)
     codes = e4m3_encode(y)
     return codes, np.squeeze(scale, axis=ax).astype(np.float32)
