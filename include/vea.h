@@ -289,6 +289,46 @@ int vea_topk_indices(const float* logits, int64_t row_stride, const int32_t* row
                      void* stream);
 
 /*
+ * vea_quantize_fp8 — block quantisation of a bf16 tensor to OCP FP8 E4M3.
+ * Sources: FP8 for matrix products, statistics kept in fp32 [MI250] section
+ * 4.1; block-wise quantisation [MI250] section 5.3.
+ *
+ * x bf16 [num_tokens, num_heads, head_dim] (token stride x_tok_stride) is cut
+ * into blocks: granularity 0 one per (token, head), scales float
+ * [num_tokens, num_heads]; 1 one per head, scales [num_heads]; 2 one per
+ * (head, channel), scales [num_heads, head_dim].  Per block:
+ *     scale = fp32(amax / 448)   (1 when amax < 2^-64), inv = fp32(1 / scale)
+ *     code  = nearest-even E4M3 of clamp(fp32(x * inv), -448, 448)
+ * and x ~ code * scale.  out: uint8 codes [num_tokens, num_heads, head_dim],
+ * contiguous.  head_dim 64 or 128.  Granularities 1 and 2 run two kernels (the
+ * block maxima over all tokens, then the codes); there are no atomics and the
+ * result is bitwise reproducible.  Non-finite inputs are not supported.
+ */
+int vea_quantize_fp8(const void* x, int64_t x_tok_stride, int num_tokens, int num_heads, int head_dim,
+                     int granularity, void* out, float* scales, void* stream);
+
+/*
+ * vea_attn_fwd_fp8 — vea_attn_fwd with q, k and v as E4M3 codes
+ * (vea_quantize_fp8): the attention of the dequantised
+ *     q[t][h][:] * q_scale[t][h],  k[t][g][:] * k_scale[g],
+ *     v[t][g][c] * v_scale[g][c]
+ * (granularities 0, 1 and 2 of vea_quantize_fp8), written in bf16.
+ * Sources: FP8 for the Q K^T and P V products with fp32 softmax statistics
+ * and accumulation [MI250] section 4.1, block scales [MI250] section 5.3,
+ * FP8 in the prefill attention kernel [SGLang] section 3.2.
+ * The products run on the FP8 MFMA with fp32 accumulation; P is rounded to
+ * E4M3 (nearest even) for the P V product, while l and lse use the fp32 P.
+ * Every other argument as vea_attn_fwd (bf16 rules: head_dim 64 or 128;
+ * strides of q, k, v in bytes = elements, multiples of 16; out bf16).  No
+ * workspace, no paging.  k_tok_stride, v_tok_stride <= 2^24.
+ */
+int vea_attn_fwd_fp8(const void* q, int64_t q_tok_stride, const void* k, int64_t k_tok_stride, const void* v,
+                     int64_t v_tok_stride, const float* q_scale, const float* k_scale, const float* v_scale,
+                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch, int total_q, int total_k,
+                     int max_seqlen_q, int max_seqlen_k, int num_heads_q, int num_heads_kv, int head_dim, int causal,
+                     float scale, int piece_rows, void* out, int64_t out_tok_stride, float* lse, void* stream);
+
+/*
  * vea_rope_cos_sin — per-token rotation table for vea_qkv_proj_rope: entry
  * [t][e] = (cos phi, sin phi) of pair e (features 2e, 2e + 1 of a head) of
  * token t, with the angle vea_qkv_rope uses for that pair (pos_dims 1: phi =

@@ -33,7 +33,8 @@ def test_header_declares_the_operations():
     names = _declared()
     for n in ("vea_attn_fwd", "vea_attn_fwd_workspace_size", "vea_qkv_rope", "vea_sparse_mqa_fwd",
               "vea_sparse_mqa_workspace_size", "vea_topk_indices", "vea_sparse_mqa_paged_fwd", "vea_attn_fwd_paged",
-              "vea_attn_probs_piece", "vea_status_str", "vea_rope_cos_sin", "vea_qkv_proj_rope"):
+              "vea_attn_probs_piece", "vea_status_str", "vea_rope_cos_sin", "vea_qkv_proj_rope",
+              "vea_quantize_fp8", "vea_attn_fwd_fp8"):
         assert n in names
 
 
@@ -265,6 +266,46 @@ def _proj(lib, **kw):
 ])
 def test_qkv_proj_validation(lib, kw, status):
     assert _proj(lib, **kw) == status
+
+
+def _fp8(lib, **kw):
+    a = dict(q=FAKE, qs=128, k=FAKE, ks=128, v=FAKE, vs=128, qsc=FAKE, ksc=FAKE, vsc=FAKE, cuq=FAKE, cuk=FAKE,
+             batch=1, tq=10, tk=10, mq=10, mk=10, hq=2, hkv=2, d=64, causal=0, scale=0.125, qb=0, out=FAKE, os=128,
+             lse=None)
+    a.update(kw)
+    return lib.vea_attn_fwd_fp8(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["qsc"], a["ksc"], a["vsc"],
+                                a["cuq"], a["cuk"], a["batch"], a["tq"], a["tk"], a["mq"], a["mk"], a["hq"],
+                                a["hkv"], a["d"], a["causal"], a["scale"], a["qb"], a["out"], a["os"], a["lse"],
+                                None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96, qs=192, ks=192, vs=192, os=192), VEA_EUNSUPPORTED),
+    (dict(hq=3), VEA_ESHAPE),                       # Hq % Hkv
+    (dict(qs=64), VEA_ESHAPE),                      # q stride shorter than a row
+    (dict(qs=136), VEA_EINVAL),                     # stride not a multiple of 16 bytes
+    (dict(qsc=None), VEA_EINVAL),
+    (dict(vsc=None), VEA_EINVAL),
+    (dict(vsc=FAKE + 4), VEA_EINVAL),               # v scales read 16 bytes at a time
+    (dict(scale=float("nan")), VEA_EINVAL),
+    (dict(causal=2), VEA_EINVAL),
+    (dict(ks=1 << 25, vs=1 << 25), VEA_EUNSUPPORTED),
+    (dict(tq=0, mq=0), VEA_OK),
+])
+def test_fp8_attention_validation(lib, kw, status):
+    assert _fp8(lib, **kw) == status
+
+
+def test_quantiser_validation(lib):
+    f = lib.vea_quantize_fp8
+    assert f(FAKE, 128, 10, 2, 64, 3, FAKE, FAKE, None) == VEA_EINVAL      # granularity
+    assert f(FAKE, 128, 10, 2, 96, 0, FAKE, FAKE, None) == VEA_EUNSUPPORTED
+    assert f(FAKE, 64, 10, 2, 64, 0, FAKE, FAKE, None) == VEA_ESHAPE       # stride shorter than a row
+    assert f(FAKE, 128, -1, 2, 64, 0, FAKE, FAKE, None) == VEA_ESHAPE
+    assert f(FAKE, 128, 10, 2, 64, 1, FAKE, None, None) == VEA_EINVAL
+    assert f(FAKE + 8, 128, 10, 2, 64, 1, FAKE, FAKE, None) == VEA_EINVAL
+    assert f(FAKE, 132, 10, 2, 64, 1, FAKE, FAKE, None) == VEA_EINVAL      # stride not 16 bytes
+    assert f(FAKE, 128, 0, 2, 64, 0, FAKE, FAKE, None) == VEA_OK
 
 
 def test_rope_table_validation(lib):

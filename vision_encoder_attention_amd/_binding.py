@@ -68,6 +68,11 @@ def load_library():
         lib.vea_sparse_mqa_workspace_size.restype = i32
         lib.vea_topk_indices.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp]
         lib.vea_topk_indices.restype = i32
+        lib.vea_quantize_fp8.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp]
+        lib.vea_quantize_fp8.restype = i32
+        lib.vea_attn_fwd_fp8.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                         i32, i32, i32, i32, f32, i32, vp, i64, vp, vp]
+        lib.vea_attn_fwd_fp8.restype = i32
         lib.vea_rope_cos_sin.argtypes = [vp, i32, i32, i32, f32, vp, vp]
         lib.vea_rope_cos_sin.restype = i32
         lib.vea_qkv_proj_rope.argtypes = [vp, i64, vp, i64, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
@@ -258,6 +263,59 @@ def qkv_rope(x_qkv, positions, theta, q, k):
                           q.shape[1], k.shape[1], q.shape[2], float(theta), _ptr(q), _ptr(k), _stream(x_qkv))
     _check(st)
     return q, k
+
+
+def quantize_fp8(x, granularity, out=None, scales=None):
+    """Block quantisation of bf16 x [T, H, d] to E4M3 codes (see
+    vea_quantize_fp8).  granularity 0: scales [T, H]; 1: [H]; 2: [H, d].
+    Returns (codes uint8 [T, H, d], scales float32)."""
+    lib = load_library()
+    torch = _torch()
+    if x.dtype != torch.bfloat16 or not x.is_cuda or x.dim() != 3 or x.stride(2) != 1 or x.stride(1) != x.shape[2]:
+        raise ValueError("x must be a bfloat16 GPU tensor [T, H, d] with contiguous heads")
+    t, hh, d = x.shape
+    shape = {0: (t, hh), 1: (hh,), 2: (hh, d)}[int(granularity)]
+    if out is None:
+        out = torch.empty((t, hh, d), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(shape, dtype=torch.float32, device=x.device)
+    if out.dtype != torch.uint8 or not out.is_contiguous() or tuple(out.shape) != (t, hh, d):
+        raise ValueError("out must be a contiguous uint8 [T, H, d] tensor")
+    if scales.dtype != torch.float32 or not scales.is_contiguous() or tuple(scales.shape) != shape:
+        raise ValueError("scales must be a contiguous float32 tensor of shape %s" % (shape,))
+    _check(lib.vea_quantize_fp8(_ptr(x), x.stride(0), t, hh, d, int(granularity), _ptr(out), _ptr(scales), _stream(x)))
+    return out, scales
+
+
+def attn_fwd_fp8(q, q_scale, k, k_scale, v, v_scale, cu_seqlens_q, cu_seqlens_k, causal, scale, out, lse=None, *,
+                 piece_rows=0, max_seqlen_q=None, max_seqlen_k=None):
+    """Attention on E4M3 codes (see vea_attn_fwd_fp8): q [Tq, Hq, d] uint8 with
+    q_scale [Tq, Hq], k / v [Tk, Hkv, d] uint8 with k_scale [Hkv] and v_scale
+    [Hkv, d]; out bf16 [Tq, Hq, d], lse float32 [Hq, Tq] or None."""
+    lib = load_library()
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dtype != torch.uint8 or not t.is_cuda or t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+            raise ValueError("%s must be a uint8 GPU tensor [T, H, d] with contiguous heads" % n)
+    for t, n in ((q_scale, "q_scale"), (k_scale, "k_scale"), (v_scale, "v_scale")):
+        if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("%s must be a contiguous float32 GPU tensor" % n)
+    if out.dtype != torch.bfloat16 or out.stride(2) != 1:
+        raise ValueError("out must be bfloat16 with contiguous head_dim")
+    _int32_dev(cu_seqlens_q, "cu_seqlens_q")
+    _int32_dev(cu_seqlens_k, "cu_seqlens_k")
+    if max_seqlen_q is None or max_seqlen_k is None:
+        cq = cu_seqlens_q.cpu()
+        ck = cu_seqlens_k.cpu()
+        max_seqlen_q = int((cq[1:] - cq[:-1]).max()) if cq.numel() > 1 else 0
+        max_seqlen_k = int((ck[1:] - ck[:-1]).max()) if ck.numel() > 1 else 0
+    st = lib.vea_attn_fwd_fp8(_ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0), _ptr(q_scale),
+                              _ptr(k_scale), _ptr(v_scale), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                              cu_seqlens_q.numel() - 1, q.shape[0], k.shape[0], int(max_seqlen_q),
+                              int(max_seqlen_k), q.shape[1], k.shape[1], q.shape[2], int(bool(causal)), float(scale),
+                              int(piece_rows), _ptr(out), out.stride(0), _ptr(lse), _stream(q))
+    _check(st)
+    return out, lse
 
 
 def rope_cos_sin(positions, head_dim, theta, out=None):

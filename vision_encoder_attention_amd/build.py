@@ -31,7 +31,7 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
-SOURCES = ["attn_fwd.hip", "qkv_rope.hip", "qkv_proj.hip", "sparse_mqa.hip", "topk.hip", "abi.cpp"]
+SOURCES = ["attn_fwd.hip", "qkv_rope.hip", "qkv_proj.hip", "quant_fp8.hip", "sparse_mqa.hip", "topk.hip", "abi.cpp"]
 
 
 def _hipcc() -> str:

@@ -112,6 +112,7 @@ int dense_layout(int batch, int max_seqlen_q, int num_heads_q, int piece_rows, D
   p.block_table = nullptr;
   p.page_shift = 0;
   p.max_pages = 0;
+  p.q_scale = p.k_scale = p.v_scale = nullptr;
   return VEA_OK;
 }
 
@@ -259,6 +260,64 @@ int vea_attn_fwd_paged(const void* q, int64_t q_tok_stride, const void* k_cache,
                    max_pages_per_seq, page_size, num_pages, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k,
                    max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim, causal, scale, piece_rows, out,
                    out_tok_stride, lse, workspace, workspace_bytes, stream);
+}
+
+int vea_attn_fwd_fp8(const void* q, int64_t q_tok_stride, const void* k, int64_t k_tok_stride, const void* v,
+                     int64_t v_tok_stride, const float* q_scale, const float* k_scale, const float* v_scale,
+                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch, int total_q, int total_k,
+                     int max_seqlen_q, int max_seqlen_k, int num_heads_q, int num_heads_kv, int head_dim, int causal,
+                     float scale, int piece_rows, void* out, int64_t out_tok_stride, float* lse, void* stream) {
+  // same shape rules as the bf16 path
+  int st = dense_shape_status(VEA_BF16, batch, total_q, total_k, max_seqlen_q, max_seqlen_k, num_heads_q,
+                              num_heads_kv, head_dim, causal, piece_rows);
+  if (st != VEA_OK) return st;
+  if (!isfinite(scale)) return VEA_EINVAL;
+  if (batch == 0 || total_q == 0) return VEA_OK;
+  if (!q || !out || !cu_seqlens_q || !cu_seqlens_k || !q_scale) return VEA_EINVAL;
+  if (total_k > 0 && (!k || !v || !k_scale || !v_scale)) return VEA_EINVAL;
+  const int64_t qrow = (int64_t)num_heads_q * head_dim, krow = (int64_t)num_heads_kv * head_dim;
+  if (q_tok_stride < qrow || out_tok_stride < qrow || k_tok_stride < krow || v_tok_stride < krow) return VEA_ESHAPE;
+  // 16-byte loads; per-lane DMA offsets are 32-bit (64 rows of a tile)
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (v_scale && !aligned16(v_scale)))
+    return VEA_EINVAL;
+  if (q_tok_stride % 16 || k_tok_stride % 16 || v_tok_stride % 16 || (out_tok_stride * 2) % 16) return VEA_EINVAL;
+  if (k_tok_stride > (1 << 24) || v_tok_stride > (1 << 24)) return VEA_EUNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  if (check_enabled()) {
+    st = check_cu(cu_seqlens_q, batch, total_q, max_seqlen_q, s);
+    if (st == VEA_OK) st = check_cu(cu_seqlens_k, batch, total_k, max_seqlen_k, s);
+    if (st != VEA_OK) return st;
+  }
+  if (max_seqlen_q == 0) return finish(VEA_OK, s);
+  DenseParams p;
+  p.q = q; p.k = k; p.v = v; p.out = out; p.lse = lse;
+  p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k;
+  p.q_stride = q_tok_stride; p.k_stride = k_tok_stride; p.v_stride = v_tok_stride; p.o_stride = out_tok_stride;
+  p.batch = batch; p.total_q = total_q; p.total_k = total_k;
+  p.hq = num_heads_q; p.hkv = num_heads_kv; p.group = num_heads_q / num_heads_kv;
+  st = dense_layout(batch, max_seqlen_q, num_heads_q, piece_rows, p);
+  if (st != VEA_OK) return st;
+  p.xcd_map = (num_heads_kv % 8 == 0) ? 1 : 0;
+  p.scale = scale;
+  p.q_scale = q_scale; p.k_scale = k_scale; p.v_scale = v_scale;
+  return finish(hip_status(launch_attn_fwd_fp8(p, head_dim, causal != 0, s)), s);
+}
+
+int vea_quantize_fp8(const void* x, int64_t x_tok_stride, int num_tokens, int num_heads, int head_dim,
+                     int granularity, void* out, float* scales, void* stream) {
+  if (num_tokens < 0 || num_heads <= 0) return VEA_ESHAPE;
+  if (granularity < 0 || granularity > 2) return VEA_EINVAL;
+  if (head_dim != 64 && head_dim != 128) return VEA_EUNSUPPORTED;
+  if (x_tok_stride < (int64_t)num_heads * head_dim) return VEA_ESHAPE;
+  if (num_tokens == 0 && granularity == 0) return VEA_OK;
+  if (!scales || (num_tokens > 0 && (!x || !out))) return VEA_EINVAL;
+  if ((x && !aligned16(x)) || (out && !aligned16(out)) || !aligned16(scales) || (x_tok_stride * 2) % 16)
+    return VEA_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  QuantParams p;
+  p.x = (const uint16_t*)x; p.x_stride = x_tok_stride; p.out = (uint8_t*)out; p.scales = scales;
+  p.tokens = num_tokens; p.heads = num_heads; p.d = head_dim; p.granularity = granularity;
+  return finish(hip_status(launch_quant_fp8(p, s)), s);
 }
 
 int vea_qkv_rope(const void* x_qkv, int64_t x_tok_stride, const int32_t* positions, int pos_dims, int num_tokens,

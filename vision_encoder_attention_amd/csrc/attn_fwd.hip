@@ -551,6 +551,340 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
   }
 }
 
+// =============================================================== fp8 path
+// Attention on OCP FP8 E4M3 inputs (v_mfma_scale_f32_32x32x64_f8f6f4, unit
+// scales).  FP8 is allowed for the matrix products, the softmax statistics
+// and accumulation stay fp32 (「AMD MI250部署DeepSeek-V4-Flash：先修正确性再谈
+// 性能」 section 4.1); q carries one dequantisation scale per (token, head),
+// k one per head and v one per (head, channel) (the block scales of that
+// page's section 5.3).  The q and k scales fold into the per-lane exponent
+// factor c, the v scales into the epilogue, so the key loop is the bf16
+// kernel's with one MFMA per 64 channels of Q K^T and one per 64 keys of P V.
+// P is rounded to E4M3 for the P V product; its fp32 values form l.  The
+// max-free softmax of the bf16 kernel is kept, with the rare path taken when
+// a lane's tile sum exceeds 448 (the largest E4M3 value; above it the
+// conversion gives NaN), which bounds every P below 448.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+template <int D>
+struct CfgF8 {
+  static constexpr int BM = kDenseBM;                   // 4 waves x 32 query rows
+  static constexpr int BN = 64;                         // keys per step
+  static constexpr int THREADS = 256;
+  static constexpr int CPR = D / 16;                    // 16-byte chunks per K/V row
+  static constexpr int TILE = BN * D;                   // bytes of one K (or V) tile
+  static constexpr int LOADS = TILE / (THREADS * 16);   // 16-byte DMA loads per lane per tile
+  static_assert(LOADS == 1 || LOADS == 2, "tile split");
+  // XOR swizzles of the 16-byte chunks of a row (64 four-byte banks: 16
+  // chunk slots per 256 bytes).
+  //  * K reads (ds_read_b128): 16 lanes read one logical chunk of 16
+  //    consecutive rows; rows fill 4 (d 64) or 2 (d 128) chunk slots each.
+  //  * V^T reads (ds_read_b64_tr_b8): 32 lanes read two adjacent logical
+  //    chunks of 8 rows {r, r + 1, r + 2, r + 3, r + 8, .., r + 11} (r a
+  //    multiple of 4); rows r and r + 8 (and for d 128 rows r and r + 2)
+  //    otherwise fall on the same slots.
+  static __device__ __forceinline__ int swk(int r) { return D == 64 ? ((r >> 2) & 3) : ((r >> 1) & 7); }
+  static __device__ __forceinline__ int swv(int r) {
+    return D == 64 ? (((r >> 3) & 1) << 1) : ((((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2));
+  }
+};
+
+// ds_read_b64_tr_b8: each lane of a 16-lane group reads 8 bytes (row i/2,
+// bytes 8(i%2)..+7 of an 8 x 16 byte block, one row address per lane pair)
+// and receives column i of the block (its 8 rows, in row order).
+__device__ __forceinline__ u32x2 lds_read_tr8(const void* p) {
+  i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ floatx16 mfma_f8(const i32x8& a, const i32x8& b, const floatx16& c) {
+  // formats 0/0: E4M3 x E4M3; scale bytes 127: 2^0
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt_f8x2(float a, float b, uint32_t w) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)w, HI);
+}
+
+__device__ __forceinline__ i32x8 cat8(u32x4 lo, u32x4 hi) {
+  return (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_fp8_kernel(DenseParams p) {
+  using C = CfgF8<D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char kst0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char kst1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char vst0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char vst1[C::TILE];
+
+  int b, h, t;
+  decode_unit(p, blockIdx.x, b, h, t);
+  TileRange tr;
+  if (!tile_range(p, b, t, C::BM, CAUSAL, tr)) return;   // uniform over the workgroup
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int g2 = lane >> 5;
+  const int kvh = h / p.group;
+  const int qi = tr.row0 + wave * 32 + l32;
+  const bool qvalid = qi < tr.row_end;
+  const int64_t qrow = tr.qs + (qvalid ? qi : tr.row0);
+
+  // ---- Q fragment (B operand of S^T = K Q^T): Q[qi][64 ks + 32 g2 .. + 31].
+  // A negative scale flips the sign bits (exact).
+  i32x8 qf[D / 64];
+  {
+    const unsigned char* src = (const unsigned char*)p.q + qrow * p.q_stride + (int64_t)h * D + 32 * g2;
+    const uint32_t flip = p.scale < 0.f ? 0x80808080u : 0u;
+#pragma unroll
+    for (int ks = 0; ks < D / 64; ++ks) {
+      u32x4 lo = *(const u32x4*)(src + 64 * ks);
+      u32x4 hi = *(const u32x4*)(src + 64 * ks + 16);
+      lo ^= flip;
+      hi ^= flip;
+      if (!qvalid) lo = hi = (u32x4){0u, 0u, 0u, 0u};
+      qf[ks] = cat8(lo, hi);
+    }
+  }
+  float c = fabsf(p.scale) * kLog2e * p.q_scale[qrow * p.hq + h] * p.k_scale[kvh];
+  c = fmaxf(c, FLT_MIN);   // a zero factor: every logit becomes ~0, masked ones stay -inf
+
+  const int kend_i = CAUSAL ? clampi(qi + tr.len_k - tr.len_q + 1, 0, tr.len_k) : tr.len_k;
+  const int n_tiles = (tr.kend + C::BN - 1) / C::BN;
+
+  // ---- DMA of K/V tiles straight into LDS.  Lane slot sl of the wave's 1 KB
+  // destination block holds row sl / CPR, physical chunk sl % CPR = logical
+  // chunk ^ swizzle(row).  Rows past the key range read as zeros.
+  const int64_t ksb = p.k_stride, vsb = p.v_stride;     // bytes per token
+  int voff_k[C::LOADS], voff_v[C::LOADS];
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i) {
+    const int sl = (wave * C::LOADS + i) * 64 + lane;
+    const int r = sl / C::CPR, ph = sl % C::CPR;
+    voff_k[i] = (int)(r * ksb) + 16 * (ph ^ C::swk(r));
+    voff_v[i] = (int)(r * vsb) + 16 * (ph ^ C::swv(r));
+  }
+  const unsigned char* kbase = (const unsigned char*)p.k + (int64_t)tr.ks * ksb + (int64_t)kvh * D;
+  const unsigned char* vbase = (const unsigned char*)p.v + (int64_t)tr.ks * vsb + (int64_t)kvh * D;
+  auto issue_tile = [&](int kt, const unsigned char* base, int64_t sb, const int* voff, unsigned char* stage) {
+    const int rows = min(tr.kend - kt * C::BN, C::BN);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(base + (int64_t)kt * C::BN * sb), (short)0, (int)(rows * sb), 0x00020000);
+    unsigned char* dst = stage + wave * C::LOADS * 1024;
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16,
+                                               (unsigned)voff[i], 0, 0, 0);
+  };
+  auto issue_k = [&](int kt, unsigned char* stage) { issue_tile(kt, kbase, ksb, voff_k, stage); };
+  auto issue_v = [&](int kt, unsigned char* stage) { issue_tile(kt, vbase, vsb, voff_v, stage); };
+
+  // ---- per-lane LDS read offsets (loop invariant)
+  // K rows l32 (+ 32), logical chunks 4 ks + 2 g2 and + 1 (channels 64 ks +
+  // 32 g2 .. + 31, as in the Q fragment).  Rows l32 and l32 + 32 share a swizzle.
+  int koff[D / 64][2];
+#pragma unroll
+  for (int ks = 0; ks < D / 64; ++ks)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) koff[ks][u] = l32 * D + 16 * ((4 * ks + 2 * g2 + u) ^ C::swk(l32));
+  // V^T operand of channel block nb: k-slot s of lane half g2 is key
+  // kslot(s) = 8 (s / 4) + 4 g2 + s % 4 for s < 16 and 32 + that of s - 16
+  // above, the order in which the lane holds P (its S registers of key
+  // blocks 0 and 1).  Read m returns slots 8m .. 8m + 7: lane pair (2q,
+  // 2q + 1) of a 16-lane group addresses the row of slot 8m + q, both halves
+  // of the group's 16-channel chunk (2 nb + nhalf).
+  const int i16 = lane & 15, nhalf = (lane >> 4) & 1;
+  int voffr[4][D / 32];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int sl = 8 * m + (i16 >> 1);
+    const int key = sl < 16 ? 8 * (sl >> 2) + 4 * g2 + (sl & 3) : 32 + 8 * ((sl - 16) >> 2) + 4 * g2 + (sl & 3);
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb)
+      voffr[m][nb] = key * D + 16 * ((2 * nb + nhalf) ^ C::swv(key)) + 8 * (i16 & 1);
+  }
+
+  floatx16 o[D / 32];
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb) o[nb] = (floatx16){};
+  float m_used = -INFINITY;  // max used for exponentiation (times c, log2 domain)
+  float l_run = 0.f;         // lane-partial sum of P
+  float m_use = 0.f;         // m_used, or 0 while the row has none
+  const int n_full = min(n_tiles, tr.kfull / C::BN);   // tiles no row needs masked
+
+  auto qk = [&](const unsigned char* ks_, floatx16& s0, floatx16& s1) {
+    s0 = (floatx16){};
+    s1 = (floatx16){};
+#pragma unroll
+    for (int ks = 0; ks < D / 64; ++ks) {
+      const i32x8 a0 = cat8(*(const u32x4*)(ks_ + koff[ks][0]), *(const u32x4*)(ks_ + koff[ks][1]));
+      const i32x8 a1 = cat8(*(const u32x4*)(ks_ + 32 * D + koff[ks][0]), *(const u32x4*)(ks_ + 32 * D + koff[ks][1]));
+      s0 = mfma_f8(a0, qf[ks], s0);
+      s1 = mfma_f8(a1, qf[ks], s1);
+    }
+  };
+  auto mask = [&](int kt, floatx16& s0, floatx16& s1) {
+    const int j0 = kt * C::BN + 4 * g2;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = j0 + 8 * (r >> 2) + (r & 3);
+      if (j >= kend_i) s0[r] = -INFINITY;
+      if (j + 32 >= kend_i) s1[r] = -INFINITY;
+    }
+  };
+  // Reference max (moved lazily, as in the bf16 kernel: only when a tile max
+  // exceeds it by more than 8 in log2 units, so P stays below 2^8).
+  auto softmax_ref = [&](const floatx16& s0, const floatx16& s1) -> float {
+    float mx = vmax(s0[0], s1[0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = vmax(vmax(mx, s0[r]), s1[r]);
+    mx = lane_swap_max(mx);
+    const float mx_sc = (mx == -INFINITY) ? -INFINITY : mx * c;
+    const bool upd = mx_sc > m_used + 8.0f;
+    if (__any(upd)) {
+      asm volatile("; rare: move the reference max, rescale O and l" ::);
+      const float m_new = upd ? mx_sc : m_used;
+      const float alpha = upd ? fast_exp2(m_used - m_new) : 1.0f;
+      m_used = m_new;
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb) o[nb] *= alpha;
+      l_run *= alpha;
+    }
+    return (m_used == -INFINITY) ? 0.f : m_used;
+  };
+  // P = 2^(s c - m) with the current reference, rounded to E4M3 in k-slot
+  // order (byte s of the operand = slot s), and the lane's fp32 sum of P.
+  auto softmax_p = [&](const floatx16& s0, const floatx16& s1, float mu, i32x8& pb) -> float {
+    float tq[8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const floatx16& sv = w < 4 ? s0 : s1;
+      const int r = 4 * (w & 3);
+      const float e0 = fast_exp2(fmaf(sv[r], c, -mu));
+      const float e1 = fast_exp2(fmaf(sv[r + 1], c, -mu));
+      const float e2 = fast_exp2(fmaf(sv[r + 2], c, -mu));
+      const float e3 = fast_exp2(fmaf(sv[r + 3], c, -mu));
+      tq[w] = (e0 + e1) + (e2 + e3);
+      pb[w] = (int)cvt_f8x2<true>(e2, e3, cvt_f8x2<false>(e0, e1, 0u));
+    }
+    return ((tq[0] + tq[1]) + (tq[2] + tq[3])) + ((tq[4] + tq[5]) + (tq[6] + tq[7]));
+  };
+  // S^T of key tile kt from K in global memory (rows past the key bound
+  // clamped to the last one; they are masked): bitwise the LDS path's logits.
+  auto qk_global = [&](int kt, floatx16& s0, floatx16& s1) {
+    const int r0 = kt * C::BN;
+    const unsigned char* pa = kbase + (int64_t)min(r0 + l32, tr.kend - 1) * ksb + 32 * g2;
+    const unsigned char* pb2 = kbase + (int64_t)min(r0 + 32 + l32, tr.kend - 1) * ksb + 32 * g2;
+    s0 = (floatx16){};
+    s1 = (floatx16){};
+#pragma unroll
+    for (int ks = 0; ks < D / 64; ++ks) {
+      const i32x8 a0 = cat8(*(const u32x4*)(pa + 64 * ks), *(const u32x4*)(pa + 64 * ks + 16));
+      const i32x8 a1 = cat8(*(const u32x4*)(pb2 + 64 * ks), *(const u32x4*)(pb2 + 64 * ks + 16));
+      s0 = mfma_f8(a0, qf[ks], s0);
+      s1 = mfma_f8(a1, qf[ks], s1);
+    }
+  };
+  // O^T += V^T P^T over the tile's 64 keys, one MFMA per 32 channels.
+  auto pv = [&](const i32x8& pb, const unsigned char* vs_) {
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) {
+      const u32x2 r0 = lds_read_tr8(vs_ + voffr[0][nb]);
+      const u32x2 r1 = lds_read_tr8(vs_ + voffr[1][nb]);
+      const u32x2 r2 = lds_read_tr8(vs_ + voffr[2][nb]);
+      const u32x2 r3 = lds_read_tr8(vs_ + voffr[3][nb]);
+      const i32x8 a = (i32x8){(int)r0[0], (int)r0[1], (int)r1[0], (int)r1[1],
+                              (int)r2[0], (int)r2[1], (int)r3[0], (int)r3[1]};
+      o[nb] = mfma_f8(a, pb, o[nb]);
+    }
+  };
+
+  // ---- software pipeline over key tiles, as in the bf16 kernel: iteration
+  // kt computes S of tile kt and finishes tile kt - 1; K is staged one tile
+  // ahead of V; stage parity is static per iteration.
+  floatx16 sp0, sp1;
+  auto iter = [&](int kt, auto odd_tag, auto has_s_tag) {
+    constexpr bool ODD = decltype(odd_tag)::value;
+    constexpr bool HAS_S = decltype(has_s_tag)::value;
+    unsigned char* k_rd = ODD ? kst1 : kst0;
+    unsigned char* k_wr = ODD ? kst0 : kst1;
+    unsigned char* v_rd = ODD ? vst0 : vst1;
+    unsigned char* v_wr = ODD ? vst1 : vst0;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    floatx16 sn0, sn1;
+    if constexpr (HAS_S) {
+      if (kt + 1 < n_tiles) issue_k(kt + 1, k_wr);
+      issue_v(kt, v_wr);
+      qk(k_rd, sn0, sn1);
+    }
+    i32x8 pb;
+    float tsum = softmax_p(sp0, sp1, m_use, pb);
+    if (__any(tsum > 448.f || m_used == -INFINITY)) {
+      asm volatile("; rare: recompute the logits, move the reference max, recompute P" ::);
+      floatx16 r0, r1;
+      qk_global(kt - 1, r0, r1);
+      if (kt - 1 >= n_full) mask(kt - 1, r0, r1);
+      m_use = softmax_ref(r0, r1);
+      tsum = softmax_p(r0, r1, m_use, pb);
+    }
+    l_run += tsum;
+    pv(pb, v_rd);
+    if constexpr (HAS_S) {
+      if (kt >= n_full) mask(kt, sn0, sn1);
+      sp0 = sn0;
+      sp1 = sn1;
+    }
+  };
+
+  if (n_tiles > 0) {
+    issue_k(0, kst0);
+    issue_v(0, vst0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (1 < n_tiles) issue_k(1, kst1);
+    qk(kst0, sp0, sp1);
+    if (0 >= n_full) mask(0, sp0, sp1);
+    m_use = softmax_ref(sp0, sp1);
+    int kt = 1;
+    for (; kt + 1 < n_tiles; kt += 2) {
+      iter(kt, std::true_type{}, std::true_type{});
+      iter(kt + 1, std::false_type{}, std::true_type{});
+    }
+    if (kt < n_tiles) {
+      iter(kt, std::true_type{}, std::true_type{});
+      iter(kt + 1, std::false_type{}, std::false_type{});
+    } else {
+      iter(kt, std::true_type{}, std::false_type{});
+    }
+  }
+
+  // ---- epilogue: out = O v_scale / l (bf16 RNE), lse = ln 2 (m + log2 l)
+  const float l_tot = lane_swap_add(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qvalid) {
+    uint16_t* dst = (uint16_t*)p.out + (int64_t)(tr.qs + qi) * p.o_stride + (int64_t)h * D + 4 * g2;
+    const float* vsc = p.v_scale + (int64_t)kvh * D + 4 * g2;
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const floatx4 sv = *(const floatx4*)(vsc + 32 * nb + 8 * r4);
+        const floatx16& ov = o[nb];
+        const u32x2 w = (u32x2){pack_bf16x2(ov[4 * r4 + 0] * sv[0] * inv, ov[4 * r4 + 1] * sv[1] * inv),
+                                pack_bf16x2(ov[4 * r4 + 2] * sv[2] * inv, ov[4 * r4 + 3] * sv[3] * inv)};
+        *(u32x2*)(dst + 32 * nb + 8 * r4) = w;
+      }
+    if (p.lse != nullptr && g2 == 0)
+      p.lse[(int64_t)h * p.total_q + tr.qs + qi] = l_tot > 0.f ? (m_used + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
 // Merge of the split chunks of one unit, in chunk order (fixed, so the result
 // is deterministic): with M = max_i m_i, O = sum_i 2^(m_i - M) O_i and
 // l = sum_i 2^(m_i - M) l_i, out = O / l (bf16) and lse = ln 2 (M + log2 l):
@@ -831,6 +1165,21 @@ void launch_dense(const DenseParams& p, bool causal, bool paged, dim3 grid, dim3
     if (causal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, false>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, false>), grid, block, 0, s, p);
   }
+}
+
+hipError_t launch_attn_fwd_fp8(const DenseParams& p, int head_dim, bool causal, hipStream_t s) {
+  if (p.nsplit != 1 || p.full_units != p.units || p.block_table != nullptr) return hipErrorInvalidValue;
+  const dim3 grid(p.units), block(256);
+  if (head_dim == 64) {
+    if (causal) hipLaunchKernelGGL((attn_fwd_fp8_kernel<64, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_fwd_fp8_kernel<64, false>), grid, block, 0, s, p);
+  } else if (head_dim == 128) {
+    if (causal) hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, false>), grid, block, 0, s, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_fwd_bf16(const DenseParams& p, int head_dim, bool causal, hipStream_t s) {

@@ -49,6 +49,12 @@ struct DenseParams {
   const int32_t* block_table;   // nullable: K/V packed by cu_k
   int page_shift;
   int max_pages;
+  // FP8 path: q, k, v hold e4m3 codes; dequantisation scales per (query
+  // token, head) [total_q, hq], per key/value head [hkv] and per (key/value
+  // head, channel) [hkv, d].
+  const float* q_scale;
+  const float* k_scale;
+  const float* v_scale;
 };
 
 struct RopeParams {
@@ -119,6 +125,7 @@ struct ProbsParams {
 // Launchers (one per kernel family).  Each returns the hipError_t of the launch.
 hipError_t launch_attn_fwd_bf16(const DenseParams& p, int head_dim, bool causal, hipStream_t s);
 hipError_t launch_attn_fwd_f32(const DenseParams& p, int head_dim, bool causal, hipStream_t s);
+hipError_t launch_attn_fwd_fp8(const DenseParams& p, int head_dim, bool causal, hipStream_t s);
 hipError_t launch_qkv_rope(const RopeParams& p, hipStream_t s);
 hipError_t launch_sparse_mqa(const SparseParams& p, int d_qk, int d_v, hipStream_t s);
 hipError_t launch_attn_probs(const ProbsParams& p, bool bf16, hipStream_t s);
@@ -161,6 +168,17 @@ struct RopeTableParams {
   double theta;
 };
 hipError_t launch_rope_cos_sin(const RopeTableParams& p, hipStream_t s);
+
+// Block quantisation to OCP FP8 E4M3: granularity 0 one scale per (token,
+// head) [tokens, heads]; 1 per head [heads]; 2 per (head, channel) [heads, d].
+struct QuantParams {
+  const uint16_t* x;         // bf16 [tokens, x_stride], heads x d per token
+  int64_t x_stride;          // elements
+  uint8_t* out;              // e4m3 [tokens, heads, d], contiguous
+  float* scales;
+  int tokens, heads, d, granularity;
+};
+hipError_t launch_quant_fp8(const QuantParams& p, hipStream_t s);
 
 // Tile shape of the dense bf16/f32 kernels (query rows per workgroup); the
 // host uses it to size the launch.
