@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 MFMA (twice the bf16 rate)
 
 
 def err(*a):
@@ -172,6 +173,8 @@ def bench_other(torch, steps, warmup, only=None):
         res.update(bench_indexer(torch, steps, warmup))
     if only in (None, "qkv_proj"):
         res.update(bench_proj(torch, steps, warmup))
+    if only in (None, "fp8"):
+        res.update(bench_fp8(torch, steps, warmup))
     return res
 
 
@@ -287,6 +290,55 @@ def bench_indexer(torch, steps, warmup):
     return res
 
 
+def bench_fp8(torch, steps, warmup):
+    """FP8 (E4M3) attention on the vision image, the varlen batch and the 32K
+    causal prefill: q, k, v quantised on the GPU (per (token, head), per head,
+    per (head, channel)), then vea_attn_fwd_fp8; TFLOP/s against the dense
+    FP8 MFMA peak, the bf16 kernel's time on the same shape beside it."""
+    import vision_encoder_attention_amd as vea
+    from vision_encoder_attention_amd import runner as R
+    from vision_encoder_attention_amd import workloads as W
+    res = {}
+    for name in ("vision", "varlen_gqa", "long_causal"):
+        case = W.full_case(name)
+        st = R.stage_dense(case)
+        if case.x_qkv is not None:
+            R.run_rope(st)
+        torch.cuda.synchronize()
+        q = st.q if st.q.is_contiguous() else st.q.contiguous()
+        k = st.k.contiguous()
+        v = st.v.contiguous()
+
+        def quant():
+            return vea.quantize_fp8(q, 0), vea.quantize_fp8(k, 1), vea.quantize_fp8(v, 2)
+        (q8, qs), (k8, ks), (v8, vs) = quant()
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((case.num_heads_q, case.total_q), dtype=torch.float32, device="cuda")
+
+        def run():
+            vea.attn_fwd_fp8(q8, qs, k8, ks, v8, vs, st.cu_q, st.cu_k, case.causal, case.scale, out, lse,
+                             piece_rows=case.piece_rows, max_seqlen_q=st.max_q, max_seqlen_k=st.max_k)
+        warm_up(torch, run, max(1, warmup))
+        tm = Timer(torch)
+        for _ in range(steps):
+            tm.run("fp8", run)
+            tm.run("quant", quant)
+            tm.run("bf16", lambda: R.run_attn(st))
+        torch.cuda.synchronize()
+        fl = dense_flops(case)
+        f_ms, f_min = tm.ms("fp8")
+        b_ms, _ = tm.ms("bf16")
+        qn_ms, _ = tm.ms("quant")
+        res[case.name + "_fp8"] = {"attn_fwd_fp8_ms": round(f_ms, 4), "attn_fwd_fp8_min_ms": round(f_min, 4),
+                                   "tflops": round(fl / f_ms / 1e9, 2),
+                                   "frac_fp8_peak": round(fl / f_ms / 1e9 / PEAK_FP8_TFLOPS, 4),
+                                   "bf16_attn_fwd_ms": round(b_ms, 4), "quantize_qkv_ms": round(qn_ms, 4),
+                                   "flops": fl}
+        del st, q, k, v, q8, k8, v8, out, lse
+        torch.cuda.empty_cache()
+    return res
+
+
 def bench_proj(torch, steps, warmup):
     """Fused QKV projection + RoPE epilogue (the step before qkv_rope), on the
     vision image and the varlen batch; beside it the unfused form of the same
@@ -394,7 +446,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy (reference for HBM byte counters)")
-    ap.add_argument("--only", choices=["varlen_gqa", "long_causal", "sparse_mqa", "indexer", "qkv_proj"],
+    ap.add_argument("--only", choices=["varlen_gqa", "long_causal", "sparse_mqa", "indexer", "qkv_proj", "fp8"],
                     help="only run one of the other workloads (for profiling one kernel family)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
