@@ -51,11 +51,13 @@ def _bf16(torch, bits):
 
 # ----------------------------------------------------------------- quantiser
 
-@pytest.mark.parametrize("d", [64, 128])
-def test_quantiser_bit_exact(torch, d):
+@pytest.mark.parametrize("d,t", [(64, 333), (128, 333), (64, 2500), (128, 2500)])
+def test_quantiser_bit_exact(torch, d, t):
+    """333 tokens: one pass per head; 2500: the chunked maximum (ragged last
+    chunk) staged in the code buffer."""
     import vision_encoder_attention_amd as vea
-    rng = np.random.default_rng(900 + d)
-    t, h = 333, 3
+    rng = np.random.default_rng(900 + d + t)
+    h = 3
     x = W.randn_bf16_bits(rng, (t, h, d))
     xf = W.bf16_bits_to_f32(x)
     # magnitudes spread over heads, a zero row, negative zeros, a tiny row

@@ -9,9 +9,14 @@
 //   code  = e4m3 nearest-even of clamp(fp32(x * inv), -448, 448)
 // The conversion is v_cvt_pk_fp8_f32 (OCP E4M3, nearest-even), after the
 // clamp: above 448 the instruction would produce NaN rather than saturate.
-// Per-head and per-channel scales need the whole tensor: fp8_amax_kernel
-// (one workgroup per head, a fixed reduction order, no atomics) writes them
-// first, and fp8_quant_kernel reads them.
+// Per-head and per-channel scales need the whole tensor.  From 1024 tokens
+// on, fp8_amax_partial_kernel takes channel maxima over chunks of 256 tokens
+// (one workgroup per (chunk, head)) and fp8_amax_final_kernel combines the
+// chunks of a head in chunk order; the partial maxima are staged in the
+// output code buffer, which holds at least four times their size and is
+// overwritten with the codes afterwards.  Below 1024 tokens fp8_amax_kernel
+// scans a head in one workgroup.  Maxima are exact and combined in a fixed
+// order: no atomics, bitwise reproducible.  fp8_quant_kernel then codes.
 #include "vea_internal.h"
 
 #include <math.h>
@@ -72,6 +77,54 @@ __global__ __launch_bounds__(256) void fp8_amax_kernel(QuantParams p) {
   }
 }
 
+constexpr int kAmaxChunk = 256;                        // tokens per partial maximum
+
+// Channel maxima of one (chunk, head): partial[chunk][h][c].
+__global__ __launch_bounds__(256) void fp8_amax_partial_kernel(QuantParams p, float* partial) {
+  __shared__ float part[256][9];
+  const int ch = blockIdx.x, h = blockIdx.y;
+  const int cpr = p.d >> 3;
+  const int c8 = threadIdx.x % cpr, tl = threadIdx.x / cpr, tpp = 256 / cpr;
+  const int t0 = ch * kAmaxChunk, t1 = min(t0 + kAmaxChunk, p.tokens);
+  float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const uint16_t* base = p.x + (int64_t)h * p.d + 8 * c8;
+  for (int t = t0 + tl; t < t1; t += tpp) {
+    const u32x4 w = *(const u32x4*)(base + (int64_t)t * p.x_stride);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      m[2 * j] = fmaxf(m[2 * j], fabsf(bf16_lo(w[j])));
+      m[2 * j + 1] = fmaxf(m[2 * j + 1], fabsf(bf16_hi(w[j])));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) part[threadIdx.x][j] = m[j];
+  __syncthreads();
+  if (threadIdx.x < p.d) {
+    const int c = threadIdx.x, cc = c >> 3, j = c & 7;
+    float a = 0.f;
+    for (int l = 0; l < tpp; ++l) a = fmaxf(a, part[l * cpr + cc][j]);
+    partial[((int64_t)ch * p.heads + h) * p.d + c] = a;
+  }
+}
+
+// Maximum over the chunks of head h (chunk order), then the scales.
+__global__ __launch_bounds__(256) void fp8_amax_final_kernel(QuantParams p, const float* partial, int chunks) {
+  __shared__ float cm[256];
+  const int h = blockIdx.x, c = threadIdx.x;
+  float a = 0.f;
+  if (c < p.d)
+    for (int k = 0; k < chunks; ++k) a = fmaxf(a, partial[((int64_t)k * p.heads + h) * p.d + c]);
+  cm[c] = a;
+  __syncthreads();
+  if (p.granularity == 2) {
+    if (c < p.d) p.scales[(int64_t)h * p.d + c] = scale_of(a);
+  } else if (c == 0) {
+    float b = 0.f;
+    for (int j = 0; j < p.d; ++j) b = fmaxf(b, cm[j]);
+    p.scales[h] = scale_of(b);
+  }
+}
+
 // One thread per 8 consecutive values of a (token, head) row; the cpr threads
 // of a row are adjacent lanes of one wave.  Granularity 0 reduces the row's
 // amax across them and writes the row's scale.
@@ -128,7 +181,18 @@ hipError_t launch_quant_fp8(const QuantParams& p, hipStream_t s) {
   const int64_t n = (int64_t)p.tokens * p.heads * (p.d >> 3);
   if (p.heads == 0) return hipSuccess;
   if (p.granularity != 0) {
-    hipLaunchKernelGGL(fp8_amax_kernel, dim3(p.heads), dim3(256), 0, s, p);
+    if (p.tokens >= 1024) {
+      // partial maxima [chunks][heads][d] floats in the code buffer
+      // ([tokens][heads][d] bytes >= 4 x that size from 1024 tokens on)
+      const int chunks = (p.tokens + kAmaxChunk - 1) / kAmaxChunk;
+      float* partial = (float*)p.out;
+      hipLaunchKernelGGL(fp8_amax_partial_kernel, dim3(chunks, p.heads), dim3(256), 0, s, p, partial);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(fp8_amax_final_kernel, dim3(p.heads), dim3(256), 0, s, p, (const float*)partial, chunks);
+    } else {
+      hipLaunchKernelGGL(fp8_amax_kernel, dim3(p.heads), dim3(256), 0, s, p);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
