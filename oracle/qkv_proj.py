@@ -40,7 +40,7 @@ def qkv_proj(x, w, bias=None) -> np.ndarray:
 
 
 def qkv_proj_rope(x, w, bias, positions, theta: float, num_heads_q: int, num_heads_kv: int, head_dim: int,
-                  rotate: bool = True):
+                  rotate: bool = True, rotate_half: bool = False):
     """Project and split; rotate Q and K unless rotate is False.
 
     Returns (q [T, Hq, d], k [T, Hkv, d], v [T, Hkv, d]) in float64.
@@ -55,7 +55,7 @@ def qkv_proj_rope(x, w, bias, positions, theta: float, num_heads_q: int, num_hea
     v = y[:, (hq + hkv) * d:].reshape(t, hkv, d)
     if not rotate:
         return y[:, :hq * d].reshape(t, hq, d), y[:, hq * d:(hq + hkv) * d].reshape(t, hkv, d), v
-    q, k = qkv_rope(y, positions, theta, hq, hkv, d)
+    q, k = qkv_rope(y, positions, theta, hq, hkv, d, rotate_half)
     return q, k, v
 
 

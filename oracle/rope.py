@@ -16,6 +16,11 @@ define the rotation itself, so the oracle uses the standard rotary form:
 * 2D (patch grid): dims [0, d/2) rotate with the grid row, dims [d/2, d) with
   the grid column, each as a span of width d/2.
 
+``rotate_half`` pairs x[i] with x[i + d_r/2] instead (i < d_r/2, same angles):
+        x[i]'        = x[i] cos(phi_i) - x[i + d_r/2] sin(phi_i)
+        x[i + d_r/2]' = x[i] sin(phi_i) + x[i + d_r/2] cos(phi_i)
+the other common convention of the rotary form, offered as a flag.
+
 Trigonometry is float64 here; the pages require at least float32 for it
 ([MI250] section 4.1, precision table).  V is not rotated.
 
@@ -37,7 +42,7 @@ def rope_inv_freq(span: int, theta: float) -> np.ndarray:
     return np.power(np.float64(theta), -2.0 * i / span)
 
 
-def _rotate_span(x: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
+def _rotate_span(x: np.ndarray, pos: np.ndarray, theta: float, rotate_half: bool = False) -> np.ndarray:
     """Rotate the last axis of x (width d_r) pairwise; pos broadcasts over the
     leading token axis.  x: [T, ..., d_r], pos: [T]."""
     d_r = x.shape[-1]
@@ -45,21 +50,23 @@ def _rotate_span(x: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
     shape = (x.shape[0],) + (1,) * (x.ndim - 2) + (d_r // 2,)
     c = np.cos(phi).reshape(shape)
     s = np.sin(phi).reshape(shape)
-    x0 = x[..., 0::2]
-    x1 = x[..., 1::2]
+    first, second = (np.s_[..., :d_r // 2], np.s_[..., d_r // 2:]) if rotate_half else \
+        (np.s_[..., 0::2], np.s_[..., 1::2])
+    x0 = x[first]
+    x1 = x[second]
     out = np.empty_like(x)
-    out[..., 0::2] = x0 * c - x1 * s
-    out[..., 1::2] = x0 * s + x1 * c
+    out[first] = x0 * c - x1 * s
+    out[second] = x0 * s + x1 * c
     return out
 
 
-def rope_1d(x, positions, theta: float) -> np.ndarray:
+def rope_1d(x, positions, theta: float, rotate_half: bool = False) -> np.ndarray:
     """x: [T, H, d] real; positions: int [T].  Returns float64 [T, H, d]."""
     x = np.asarray(x, dtype=np.float64)
-    return _rotate_span(x, np.asarray(positions), theta)
+    return _rotate_span(x, np.asarray(positions), theta, rotate_half)
 
 
-def rope_2d(x, positions, theta: float) -> np.ndarray:
+def rope_2d(x, positions, theta: float, rotate_half: bool = False) -> np.ndarray:
     """x: [T, H, d]; positions: int [T, 2] = (grid row, grid column).
 
     First half of each head rotates with the row, second half with the column.
@@ -70,12 +77,13 @@ def rope_2d(x, positions, theta: float) -> np.ndarray:
     if d % 4:
         raise ValueError("2D RoPE needs head_dim divisible by 4")
     out = np.empty_like(x)
-    out[..., : d // 2] = _rotate_span(x[..., : d // 2], positions[:, 0], theta)
-    out[..., d // 2:] = _rotate_span(x[..., d // 2:], positions[:, 1], theta)
+    out[..., : d // 2] = _rotate_span(x[..., : d // 2], positions[:, 0], theta, rotate_half)
+    out[..., d // 2:] = _rotate_span(x[..., d // 2:], positions[:, 1], theta, rotate_half)
     return out
 
 
-def qkv_rope(x_qkv, positions, theta: float, num_heads_q: int, num_heads_kv: int, head_dim: int):
+def qkv_rope(x_qkv, positions, theta: float, num_heads_q: int, num_heads_kv: int, head_dim: int,
+             rotate_half: bool = False):
     """Split a fused [T, (Hq + 2 Hkv) d] projection output and rotate Q and K.
 
     positions: int [T] (1D) or [T, 2] (2D grid).  Returns (q [T, Hq, d],
@@ -90,4 +98,4 @@ def qkv_rope(x_qkv, positions, theta: float, num_heads_q: int, num_heads_kv: int
     k = x[:, hq * d:(hq + hkv) * d].reshape(t, hkv, d)
     positions = np.asarray(positions)
     rot = rope_1d if positions.ndim == 1 else rope_2d
-    return rot(q, positions, theta), rot(k, positions, theta)
+    return rot(q, positions, theta, rotate_half), rot(k, positions, theta, rotate_half)

@@ -419,7 +419,42 @@ def pin_qkv_split(orc):
     assert np.allclose(q1, orc.rope_1d(x[:, :hq * d].reshape(t, hq, d), p1, 1e4), rtol=0, atol=0)
 
 
-ROPE_PINS = [pin_rope_identity_and_norm, pin_rope_complex, pin_rope_relative, pin_rope_2d_halves, pin_qkv_split]
+def pin_rope_rotate_half(orc):
+    """Rotate-half pairing is the adjacent-pair rotation of the same vector
+    with its features reordered (halves interleaved): R_half(x) = P^T
+    R_adj(P x) with (P x)[2i] = x[i], (P x)[2i+1] = x[i + d_r/2], per span;
+    and pair i of the halves keeps its length."""
+    rng = _rng(306)
+    d, t = 16, 7
+    x = rng.standard_normal((t, 3, d))
+    pos = rng.integers(0, 4000, t)
+    perm = np.empty(d, np.int64)
+    perm[0::2] = np.arange(d // 2)
+    perm[1::2] = np.arange(d // 2) + d // 2
+    y = orc.rope_1d(x, pos, 1e4, rotate_half=True)
+    ref = np.empty_like(x)
+    ref[..., perm] = orc.rope_1d(x[..., perm], pos, 1e4)
+    assert np.allclose(y, ref, rtol=0, atol=1e-13)
+    assert np.allclose(np.hypot(y[..., :d // 2], y[..., d // 2:]), np.hypot(x[..., :d // 2], x[..., d // 2:]),
+                       rtol=1e-13, atol=0)
+    pos2 = rng.integers(0, 90, (t, 2))
+    y2 = orc.rope_2d(x, pos2, 1e4, rotate_half=True)
+    q = d // 2
+    perm2 = np.empty(q, np.int64)
+    perm2[0::2] = np.arange(q // 2)
+    perm2[1::2] = np.arange(q // 2) + q // 2
+    for sp in range(2):
+        seg = x[..., sp * q:(sp + 1) * q]
+        want = np.empty_like(seg)
+        want[..., perm2] = orc.rope_1d(seg[..., perm2], pos2[:, sp], 1e4)
+        assert np.allclose(y2[..., sp * q:(sp + 1) * q], want, rtol=0, atol=1e-13)
+    xq = np.concatenate([x.reshape(t, -1), x.reshape(t, -1)[:, :d]], 1)       # Q: 2 heads, K: 1, V: 1
+    a, b = orc.qkv_rope(xq, pos, 1e4, 2, 1, d, rotate_half=True)
+    assert np.allclose(a, orc.rope_1d(x[:, :2, :], pos, 1e4, rotate_half=True), rtol=0, atol=0)
+    assert np.allclose(b, orc.rope_1d(x[:, 2:3, :], pos, 1e4, rotate_half=True), rtol=0, atol=0)
+
+
+ROPE_PINS = [pin_rope_identity_and_norm, pin_rope_complex, pin_rope_relative, pin_rope_2d_halves, pin_qkv_split, pin_rope_rotate_half]
 
 
 # ============================================== fused QKV projection + RoPE

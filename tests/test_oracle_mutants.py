@@ -43,11 +43,15 @@ MUTANTS = [
     ("attention", "m = lg.max(axis=1)                                   # pass 1: row max",
      "m = lg.max(axis=1) * 0.5", "row max halved"),
     ("rope", "-2.0 * i / span", "-1.0 * i / span", "frequency exponent -i/d"),
-    ("rope", "out[..., 0::2] = x0 * c - x1 * s", "out[..., 0::2] = x0 * c + x1 * s", "rotation sign flipped"),
-    ("rope", "x0 = x[..., 0::2]\n    x1 = x[..., 1::2]", "x0 = x[..., : d_r // 2]\n    x1 = x[..., d_r // 2:]",
-     "rotate-half pairing"),
-    ("rope", "_rotate_span(x[..., : d // 2], positions[:, 0], theta)",
-     "_rotate_span(x[..., : d // 2], positions[:, 1], theta)", "2D first half turned by the column"),
+    ("rope", "out[first] = x0 * c - x1 * s", "out[first] = x0 * c + x1 * s", "rotation sign flipped"),
+    ("rope", "(np.s_[..., 0::2], np.s_[..., 1::2])", "(np.s_[..., :d_r // 2], np.s_[..., d_r // 2:])",
+     "rotate-half pairing for the adjacent form"),
+    ("rope", "(np.s_[..., :d_r // 2], np.s_[..., d_r // 2:]) if rotate_half", "(np.s_[..., 0::2], np.s_[..., 1::2]) if rotate_half",
+     "adjacent pairing for the rotate-half form"),
+    ("rope", "return rot(q, positions, theta, rotate_half), rot(k, positions, theta, rotate_half)",
+     "return rot(q, positions, theta, rotate_half), rot(k, positions, theta)", "flag not passed on to K"),
+    ("rope", "_rotate_span(x[..., : d // 2], positions[:, 0], theta, rotate_half)",
+     "_rotate_span(x[..., : d // 2], positions[:, 1], theta, rotate_half)", "2D first half turned by the column"),
     ("rope", "k = x[:, hq * d:(hq + hkv) * d]", "k = x[:, (hq + hkv) * d:(hq + 2 * hkv) * d]",
      "K read from the V columns"),
     ("sparse", "sel = idx[r][idx[r] >= 0]", "sel = idx[r]", "padding entries not skipped"),
@@ -76,8 +80,8 @@ MUTANTS = [
     ("qkv_proj", "y = x @ w\n    if bias", "y = x @ w[::-1]\n    if bias", "weight rows reversed (input features misaligned)"),
     ("qkv_proj", "v = y[:, (hq + hkv) * d:].reshape(t, hkv, d)", "v = y[:, hq * d:(hq + hkv) * d].reshape(t, hkv, d)",
      "V taken from the K columns"),
-    ("qkv_proj", "q, k = qkv_rope(y, positions, theta, hq, hkv, d)\n    return q, k, v",
-     "q, k = qkv_rope(y, positions, theta, hq, hkv, d)\n    return k, q, v", "Q and K swapped"),
+    ("qkv_proj", "q, k = qkv_rope(y, positions, theta, hq, hkv, d, rotate_half)\n    return q, k, v",
+     "q, k = qkv_rope(y, positions, theta, hq, hkv, d, rotate_half)\n    return k, q, v", "Q and K swapped"),
     ("qkv_proj", "return y[:, :hq * d].reshape(t, hq, d), y[:, hq * d:(hq + hkv) * d].reshape(t, hkv, d), v",
      "return y[:, :hq * d].reshape(t, hq, d), y[:, (hq + hkv) * d:].reshape(t, hkv, d), v",
      "unrotated K taken from the V columns"),
