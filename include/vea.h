@@ -183,13 +183,16 @@ int vea_attn_fwd_workspace_size(int dtype, int batch, int total_q, int total_k, 
  *   head_dim    even (pos_dims 1) or a multiple of 4 (pos_dims 2), and a
  *               multiple of 8; at most 256.
  *   theta       finite, > 0.
+ *   rotate_half 0: the pairs above; 1: rotate-half pairing, pair i of a span
+ *               of width d_r joins features i and i + d_r/2 (same angles);
+ *               head_dim a multiple of 32.
  *   q, k        bf16 outputs [num_tokens, Hq, head_dim] and
  *               [num_tokens, Hkv, head_dim], contiguous; must not overlap x_qkv.
  */
 int vea_qkv_rope(const void* x_qkv, int64_t x_tok_stride,
                  const int32_t* positions, int pos_dims,
                  int num_tokens, int num_heads_q, int num_heads_kv, int head_dim, float theta,
-                 void* q, void* k, void* stream);
+                 int rotate_half, void* q, void* k, void* stream);
 
 /*
  * vea_sparse_mqa_fwd — multi-query attention of each query row over its own
@@ -365,6 +368,10 @@ int vea_rope_cos_sin(const int32_t* positions, int pos_dims, int num_tokens, int
  *   cos_sin     the table of vea_rope_cos_sin for these tokens and head_dim,
  *               or NULL: no rotation (a plain projection and split).
  *   hidden      a multiple of 32.  head_dim: a multiple of 32, <= 256.
+ *   rotate_half_span  0: adjacent pairs (2i, 2i + 1).  head_dim (1D tables)
+ *               or head_dim / 2 (2D tables): rotate-half pairs (i, i + span/2)
+ *               within each span, table entry e of pair i as vea_qkv_rope
+ *               numbers it; head_dim 64 or 128.
  *   q, k, v     bf16 outputs [num_tokens, Hq, head_dim], [num_tokens, Hkv,
  *               head_dim] (both) contiguous; they must not overlap the inputs.
  * All pointers 16-byte aligned, strides multiples of 8 elements
@@ -373,7 +380,7 @@ int vea_rope_cos_sin(const int32_t* positions, int pos_dims, int num_tokens, int
  */
 int vea_qkv_proj_rope(const void* x, int64_t x_tok_stride, const void* w, int64_t w_row_stride, const void* bias,
                       const float* cos_sin, int num_tokens, int hidden, int num_heads_q, int num_heads_kv,
-                      int head_dim, void* q, void* k, void* v, void* stream);
+                      int head_dim, int rotate_half_span, void* q, void* k, void* v, void* stream);
 
 /*
  * vea_attn_probs_piece — debug export (not on the timed path) of the

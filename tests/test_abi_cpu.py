@@ -110,14 +110,16 @@ def test_attn_fwd_workspace_size_validation(lib, args, status):
 
 
 def _rope(lib, **kw):
-    a = dict(x=FAKE, xs=3 * 4 * 64, pos=FAKE, pd=2, t=5, hq=4, hkv=4, d=64, theta=1e4, q=FAKE, k=FAKE)
+    a = dict(x=FAKE, xs=3 * 4 * 64, pos=FAKE, pd=2, t=5, hq=4, hkv=4, d=64, theta=1e4, rh=0, q=FAKE, k=FAKE)
     a.update(kw)
     return lib.vea_qkv_rope(a["x"], a["xs"], a["pos"], a["pd"], a["t"], a["hq"], a["hkv"], a["d"], a["theta"],
-                            a["q"], a["k"], None)
+                            a["rh"], a["q"], a["k"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(pd=3), VEA_EINVAL),
+    (dict(rh=2), VEA_EINVAL),
+    (dict(rh=1, d=48, xs=3 * 4 * 48), VEA_EUNSUPPORTED),      # rotate-half: whole chunks per half span
     (dict(theta=0.0), VEA_EINVAL),
     (dict(theta=-1.0), VEA_EINVAL),
     (dict(theta=float("nan")), VEA_EINVAL),
@@ -239,15 +241,17 @@ def test_topk_validation(lib, kw, status):
 
 
 def _proj(lib, **kw):
-    a = dict(x=FAKE, xs=1024, w=FAKE, ws=3072, b=None, cs=None, t=100, hid=1024, hq=16, hkv=16, d=64,
+    a = dict(x=FAKE, xs=1024, w=FAKE, ws=3072, b=None, cs=None, t=100, hid=1024, hq=16, hkv=16, d=64, rh=0,
              q=FAKE, k=FAKE, v=FAKE)
     a.update(kw)
     return lib.vea_qkv_proj_rope(a["x"], a["xs"], a["w"], a["ws"], a["b"], a["cs"], a["t"], a["hid"], a["hq"],
-                                 a["hkv"], a["d"], a["q"], a["k"], a["v"], None)
+                                 a["hkv"], a["d"], a["rh"], a["q"], a["k"], a["v"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(hid=1000, xs=1000), VEA_EUNSUPPORTED),   # hidden not a multiple of 32
+    (dict(rh=48), VEA_EINVAL),                     # rotate-half span neither d nor d/2
+    (dict(rh=96, d=96, ws=96 * 48), VEA_EUNSUPPORTED),   # rotate-half needs d 64 or 128
     (dict(d=48, ws=2304), VEA_EUNSUPPORTED),       # head_dim not a multiple of 32
     (dict(d=288, ws=288 * 48), VEA_EUNSUPPORTED),
     (dict(xs=512), VEA_ESHAPE),                    # x stride shorter than hidden

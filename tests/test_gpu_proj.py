@@ -154,3 +154,38 @@ def test_projection_then_attention_matches_the_oracle_pipeline(torch):
     o_ref, l_ref = oracle.attention(q, k, v, np.array([0, t]), np.array([0, t]), False, scale)
     assert_bf16_close(_f64(out), o_ref, "out")
     assert_bf16_close(lse.cpu().numpy().astype(np.float64), l_ref, "lse")
+
+
+@pytest.mark.parametrize("d,grid", [(64, None), (128, None), (64, (13, 17)), (128, (13, 17))])
+def test_rotate_half_pairing(torch, d, grid):
+    """Rotate-half pairs (i, i + span/2), span d (1D) or d/2 (2D): the fused
+    projection (with bias) and qkv_rope on its unrotated output, both against
+    the oracle."""
+    import vision_encoder_attention_amd as vea
+    t = 221 if grid is None else grid[0] * grid[1]
+    case = W.qkv_proj(tokens=t, hidden=96, hq=4, hkv=2, d=d, grid=grid, bias=True, seed=730 + d)
+    span = d if grid is None else d // 2
+    log("rotate-half d=%d span=%d" % (d, span))
+    st = R.stage_proj(case)
+    R.run_rope_table(st)
+    vea.qkv_proj_rope(st.x, st.w, st.bias, st.cs, st.q, st.k, st.v, rotate_half_span=span)
+    torch.cuda.synchronize()
+    x = W.bf16_bits_to_f64(case.x)
+    b = W.bf16_bits_to_f64(case.bias)
+    th = float(np.float32(case.theta))
+    q, k, v = oracle.qkv_proj_rope(x, W.bf16_bits_to_f64(case.w), b, case.positions, th, case.hq, case.hkv, d,
+                                   rotate_half=True)
+    _assert_ulp(_f64(st.q), q, "q")
+    _assert_ulp(_f64(st.k), k, "k")
+    _assert_ulp(_f64(st.v), v, "v")
+    # qkv_rope on the (bf16) unrotated projection output, rotate-half
+    plain = R.stage_proj(case, rotate=False)
+    R.run_proj(plain)
+    y = torch.cat([plain.q.reshape(t, -1), plain.k.reshape(t, -1), plain.v.reshape(t, -1)], 1).contiguous()
+    qr = torch.empty_like(plain.q)
+    kr = torch.empty_like(plain.k)
+    vea.qkv_rope(y, st.positions, case.theta, qr, kr, rotate_half=True)
+    torch.cuda.synchronize()
+    q2, k2 = oracle.qkv_rope(_f64(y), case.positions, th, case.hq, case.hkv, d, rotate_half=True)
+    assert_bf16_close(_f64(qr), q2, "qkv_rope q")
+    assert_bf16_close(_f64(kr), k2, "qkv_rope k")

@@ -56,7 +56,7 @@ def load_library():
         lib.vea_attn_fwd_paged.restype = i32
         lib.vea_attn_fwd_workspace_size.argtypes = [i32] * 11 + [ctypes.POINTER(ctypes.c_size_t)]
         lib.vea_attn_fwd_workspace_size.restype = i32
-        lib.vea_qkv_rope.argtypes = [vp, i64, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp]
+        lib.vea_qkv_rope.argtypes = [vp, i64, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp]
         lib.vea_qkv_rope.restype = i32
         lib.vea_sparse_mqa_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp,
                                            ctypes.c_size_t, vp]
@@ -75,7 +75,7 @@ def load_library():
         lib.vea_attn_fwd_fp8.restype = i32
         lib.vea_rope_cos_sin.argtypes = [vp, i32, i32, i32, f32, vp, vp]
         lib.vea_rope_cos_sin.restype = i32
-        lib.vea_qkv_proj_rope.argtypes = [vp, i64, vp, i64, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
+        lib.vea_qkv_proj_rope.argtypes = [vp, i64, vp, i64, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]
         lib.vea_qkv_proj_rope.restype = i32
         lib.vea_attn_probs_piece.argtypes = [i32, vp, i64, vp, i64, vp, i64, i32, i32, i32, i32, i32, i32,
                                              i32, i32, i32, i32, i32, f32, vp, i64, vp]
@@ -247,7 +247,7 @@ def attn_fwd_paged(q, k_cache, v_cache, block_table, page_size, cu_seqlens_q, cu
     return out, lse
 
 
-def qkv_rope(x_qkv, positions, theta, q, k):
+def qkv_rope(x_qkv, positions, theta, q, k, rotate_half=False):
     """Split the fused [T, (Hq+2Hkv) d] projection output into rotated q [T, Hq, d]
     and k [T, Hkv, d] (see vea_qkv_rope); V stays in x_qkv."""
     lib = load_library()
@@ -260,7 +260,8 @@ def qkv_rope(x_qkv, positions, theta, q, k):
         raise ValueError("q and k outputs must be contiguous")
     _int32_dev(positions, "positions")
     st = lib.vea_qkv_rope(_ptr(x_qkv), x_qkv.stride(0), _ptr(positions), positions.dim(), x_qkv.shape[0],
-                          q.shape[1], k.shape[1], q.shape[2], float(theta), _ptr(q), _ptr(k), _stream(x_qkv))
+                          q.shape[1], k.shape[1], q.shape[2], float(theta), int(bool(rotate_half)), _ptr(q), _ptr(k),
+                          _stream(x_qkv))
     _check(st)
     return q, k
 
@@ -334,7 +335,7 @@ def rope_cos_sin(positions, head_dim, theta, out=None):
     return out
 
 
-def qkv_proj_rope(x, w, bias, cos_sin, q, k, v):
+def qkv_proj_rope(x, w, bias, cos_sin, q, k, v, rotate_half_span=0):
     """q, k, v = split(x @ w (+ bias)) with Q and K rotated by the table
     cos_sin (None: not rotated); see vea_qkv_proj_rope.  x [T, hidden] and
     w [hidden, (Hq + 2 Hkv) d] bf16 with contiguous rows; q [T, Hq, d],
@@ -353,7 +354,8 @@ def qkv_proj_rope(x, w, bias, cos_sin, q, k, v):
     if cos_sin is not None and (cos_sin.dtype != torch.float32 or not cos_sin.is_contiguous()):
         raise ValueError("cos_sin must be a contiguous float32 table")
     st = lib.vea_qkv_proj_rope(_ptr(x), x.stride(0), _ptr(w), w.stride(0), _ptr(bias), _ptr(cos_sin), x.shape[0],
-                               x.shape[1], q.shape[1], k.shape[1], q.shape[2], _ptr(q), _ptr(k), _ptr(v), _stream(x))
+                               x.shape[1], q.shape[1], k.shape[1], q.shape[2], int(rotate_half_span), _ptr(q), _ptr(k),
+                               _ptr(v), _stream(x))
     _check(st)
     return q, k, v
 

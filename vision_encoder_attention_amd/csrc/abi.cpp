@@ -321,11 +321,14 @@ int vea_quantize_fp8(const void* x, int64_t x_tok_stride, int num_tokens, int nu
 }
 
 int vea_qkv_rope(const void* x_qkv, int64_t x_tok_stride, const int32_t* positions, int pos_dims, int num_tokens,
-                 int num_heads_q, int num_heads_kv, int head_dim, float theta, void* q, void* k, void* stream) {
+                 int num_heads_q, int num_heads_kv, int head_dim, float theta, int rotate_half, void* q, void* k,
+                 void* stream) {
   if (num_tokens < 0 || num_heads_q <= 0 || num_heads_kv <= 0 || head_dim <= 0) return VEA_ESHAPE;
   if (pos_dims != 1 && pos_dims != 2) return VEA_EINVAL;
   if (!isfinite(theta) || !(theta > 0.f)) return VEA_EINVAL;
   if (head_dim % 8 != 0 || head_dim > 256 || (pos_dims == 2 && head_dim % 4 != 0)) return VEA_EUNSUPPORTED;
+  if (rotate_half != 0 && rotate_half != 1) return VEA_EINVAL;
+  if (rotate_half && head_dim % 32 != 0) return VEA_EUNSUPPORTED;   // whole 16-byte chunks per half span
   if (num_tokens == 0) return VEA_OK;
   if (!x_qkv || !positions || !q || !k) return VEA_EINVAL;
   if (x_tok_stride < (int64_t)(num_heads_q + 2 * num_heads_kv) * head_dim) return VEA_ESHAPE;
@@ -334,7 +337,7 @@ int vea_qkv_rope(const void* x_qkv, int64_t x_tok_stride, const int32_t* positio
   RopeParams p;
   p.x = (const uint16_t*)x_qkv; p.pos = positions; p.q = (uint16_t*)q; p.k = (uint16_t*)k;
   p.x_stride = x_tok_stride; p.tokens = num_tokens; p.hq = num_heads_q; p.hkv = num_heads_kv;
-  p.d = head_dim; p.pos_dims = pos_dims; p.theta = (double)theta;
+  p.d = head_dim; p.pos_dims = pos_dims; p.theta = (double)theta; p.rot_half = rotate_half;
   return finish(hip_status(launch_qkv_rope(p, s)), s);
 }
 
@@ -498,11 +501,14 @@ int vea_rope_cos_sin(const int32_t* positions, int pos_dims, int num_tokens, int
 
 int vea_qkv_proj_rope(const void* x, int64_t x_tok_stride, const void* w, int64_t w_row_stride, const void* bias,
                       const float* cos_sin, int num_tokens, int hidden, int num_heads_q, int num_heads_kv,
-                      int head_dim, void* q, void* k, void* v, void* stream) {
+                      int head_dim, int rotate_half_span, void* q, void* k, void* v, void* stream) {
   if (num_tokens < 0 || hidden <= 0 || num_heads_q <= 0 || num_heads_kv <= 0 || head_dim <= 0) return VEA_ESHAPE;
   const int64_t n = (int64_t)(num_heads_q + 2 * (int64_t)num_heads_kv) * head_dim;
   if (x_tok_stride < hidden || w_row_stride < n) return VEA_ESHAPE;
   if (hidden % kProjStepK != 0 || head_dim % 32 != 0 || head_dim > 256) return VEA_EUNSUPPORTED;
+  if (rotate_half_span != 0 && rotate_half_span != head_dim && rotate_half_span != head_dim / 2) return VEA_EINVAL;
+  // rotate-half partners are found within a wave's 128 features
+  if (rotate_half_span != 0 && head_dim != 64 && head_dim != 128) return VEA_EUNSUPPORTED;
   // Buffer ranges and per-lane offsets are 32-bit.
   if (n > 0x7fffffff / 2 || (int64_t)num_tokens * x_tok_stride * 2 > 0x7fffffff ||
       (int64_t)kProjTileT * x_tok_stride * 2 > 0x7fffffff || (int64_t)hidden * w_row_stride * 2 > 0x7fffffff)
@@ -520,7 +526,7 @@ int vea_qkv_proj_rope(const void* x, int64_t x_tok_stride, const void* w, int64_
   p.q = (uint16_t*)q; p.k = (uint16_t*)k; p.v = (uint16_t*)v;
   p.x_stride = x_tok_stride; p.w_stride = w_row_stride;
   p.tokens = num_tokens; p.hidden = hidden; p.hq = num_heads_q; p.hkv = num_heads_kv; p.d = head_dim;
-  p.n_feat = (int)n; p.ftiles = (int)ftiles;
+  p.n_feat = (int)n; p.ftiles = (int)ftiles; p.rot_span = rotate_half_span;
   return finish(hip_status(launch_qkv_proj(p, s)), s);
 }
 

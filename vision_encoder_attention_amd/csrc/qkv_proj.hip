@@ -258,6 +258,7 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_proj_kernel(ProjParams p, con
     b.dd0 = b.f0 % p.d;                                   // inside the head (multiple of 32)
     return b;
   };
+  const bool rh = p.rot_span != 0 && cs_tab != nullptr;   // rotate-half pairing (pre-pass below)
   // Operands of one block: (cos, sin) of pair entries e, e + 1 of each run a
   // (e = (dd0 + 8a + 4 g2) / 2) and the bias of the run's 4 features.
   struct Ops {
@@ -265,7 +266,7 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_proj_kernel(ProjParams p, con
     u32x2 bb[4];
   };
   auto load_ops = [&](const Blk& b, Ops& o) {
-    if (!b.live) return;
+    if (!b.live || rh) return;
     const int tc = b.t < p.tokens ? b.t : p.tokens - 1;
     if (b.rot) {
 #pragma unroll
@@ -277,19 +278,81 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_proj_kernel(ProjParams p, con
       for (int a = 0; a < 4; ++a) o.bb[a] = *(const u32x2*)(bias + b.base + b.f0 + 8 * a + 4 * g2);
     }
   };
+  // Rotate-half pairs (f, f + span/2): a head lies inside the wave's 128
+  // features (d 64 or 128), so the partner of a first element sits in this
+  // lane, span/2 / 32 blocks on at the same register (span/2 >= 32) or two
+  // runs on in the same block (span/2 = 16).  In that mode this pass adds the
+  // bias and rotates in the accumulators, and the blocks below only store.
+  if (rh) {
+    const int span = p.rot_span, hs = span >> 1;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const Blk b0 = blk(4 * tb);
+      const int tc = b0.t < p.tokens ? b0.t : p.tokens - 1;
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb) {
+        const Blk b = blk(4 * tb + fb);
+        if (!b.live || bias == nullptr) continue;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const u32x2 bb = *(const u32x2*)(bias + b.base + b.f0 + 8 * a + 4 * g2);
+          acc[fb][tb][4 * a] += bf16_lo(bb[0]);
+          acc[fb][tb][4 * a + 1] += bf16_hi(bb[0]);
+          acc[fb][tb][4 * a + 2] += bf16_lo(bb[1]);
+          acc[fb][tb][4 * a + 3] += bf16_hi(bb[1]);
+        }
+      }
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb) {
+        const Blk b = blk(4 * tb + fb);
+        if (!b.live || !b.rot) continue;
+        auto turn = [&](floatx16& A, int ia, floatx16& B, int ib, int e) {
+          const float2 cv = *(const float2*)(cs_tab + ((int64_t)tc * half + e) * 2);
+          const float x0 = A[ia], x1 = B[ib];
+          A[ia] = x0 * cv.x - x1 * cv.y;
+          B[ib] = x0 * cv.y + x1 * cv.x;
+        };
+        if (hs >= 32) {
+          if (b.dd0 % span >= hs) continue;               // a block of second elements
+          // partner block fb + hs / 32 (< 4: the head is in the wave), chosen
+          // by a compile-time index so that the accumulators stay in registers
+          const int e0 = (b.dd0 / span) * hs + b.dd0 % span + 4 * g2;
+          if (hs == 32) {
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                turn(acc[fb][tb], 4 * a + q, acc[fb < 3 ? fb + 1 : 3][tb], 4 * a + q, e0 + 8 * a + q);
+          } else {
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                turn(acc[fb][tb], 4 * a + q, acc[fb < 2 ? fb + 2 : 3][tb], 4 * a + q, e0 + 8 * a + q);
+          }
+        } else {                                          // span 32: partners two runs on
+          const int e0 = (b.dd0 / span) * hs + 4 * g2;
+#pragma unroll
+          for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) turn(acc[fb][tb], 4 * a + q, acc[fb][tb], 4 * (a + 2) + q, e0 + 8 * a + q);
+        }
+      }
+    }
+  }
   auto finish = [&](const Blk& b, const Ops& o, const floatx16& c) {
     if (!b.live) return;
     uint32_t pk[4][2];                                    // bf16 of run a: 4 features 8a + 4 g2 + (0..3)
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       float y0 = c[4 * a], y1 = c[4 * a + 1], y2 = c[4 * a + 2], y3 = c[4 * a + 3];
-      if (bias != nullptr) {
+      if (bias != nullptr && !rh) {
         y0 += bf16_lo(o.bb[a][0]);
         y1 += bf16_hi(o.bb[a][0]);
         y2 += bf16_lo(o.bb[a][1]);
         y3 += bf16_hi(o.bb[a][1]);
       }
-      if (b.rot) {
+      if (b.rot && !rh) {
         const floatx4 cs = o.cs[a];
         const float r0 = y0 * cs[0] - y1 * cs[1], r1 = y0 * cs[1] + y1 * cs[0];
         const float r2 = y2 * cs[2] - y3 * cs[3], r3 = y2 * cs[3] + y3 * cs[2];

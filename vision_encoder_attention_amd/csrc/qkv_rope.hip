@@ -75,6 +75,42 @@ __global__ __launch_bounds__(256) void qkv_rope_kernel(RopeParams p, int tpw) {
   __syncthreads();
 
   const int cph = p.d >> 3;                                  // 16-byte chunks per head
+  if (p.rot_half) {
+    // Rotate-half pairing: pair i of a span joins features i and i + span/2.
+    // A thread owns chunk j of a span's first half and its partner chunk in
+    // the second half (8 pairs).  1D: one span per head (table entries 0 ..
+    // d/2); 2D: two spans of d/2 (entries of the second from d/4 on).
+    const int pph = p.d >> 4;                                // chunk pairs per head
+    const int spc = p.pos_dims == 1 ? pph : (p.d >> 5);      // chunk pairs per span
+    const int npairs = (p.hq + p.hkv) * pph;
+    for (int idx = threadIdx.x; idx < nt * npairs; idx += blockDim.x) {
+      const int tk = idx / npairs, ci = idx - tk * npairs;
+      const int t = t0 + tk;
+      const int head = ci / pph;
+      const int cp = ci - head * pph;
+      const int sp = cp / spc, l = cp - sp * spc;
+      const int c0 = sp * 2 * spc + l, c1 = c0 + spc;         // chunks of the first elements and partners
+      const int ebase = sp * 8 * spc + 8 * l;                 // table entry of the chunk's first pair
+      const uint16_t* src = p.x + (int64_t)t * p.x_stride + (int64_t)head * p.d;
+      const u32x4 v0 = *(const u32x4*)(src + 8 * c0);
+      const u32x4 v1 = *(const u32x4*)(src + 8 * c1);
+      u32x4 o0, o1;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int e = ebase + 2 * w;
+        const float a0 = bf16lo(v0[w]), a1 = bf16hi(v0[w]);
+        const float b0 = bf16lo(v1[w]), b1 = bf16hi(v1[w]);
+        const float ca = cs[tk][e], sa = sn[tk][e], cb = cs[tk][e + 1], sb = sn[tk][e + 1];
+        o0[w] = pack2(fmaf(a0, ca, -(b0 * sa)), fmaf(a1, cb, -(b1 * sb)));
+        o1[w] = pack2(fmaf(a0, sa, b0 * ca), fmaf(a1, sb, b1 * cb));
+      }
+      uint16_t* dst = head < p.hq ? p.q + ((int64_t)t * p.hq + head) * p.d
+                                  : p.k + ((int64_t)t * p.hkv + (head - p.hq)) * p.d;
+      *(u32x4*)(dst + 8 * c0) = o0;
+      *(u32x4*)(dst + 8 * c1) = o1;
+    }
+    return;
+  }
   const int nchunks = (p.hq + p.hkv) * cph;                  // per token
   for (int idx = threadIdx.x; idx < nt * nchunks; idx += blockDim.x) {
     const int tk = idx / nchunks, ci = idx - tk * nchunks;

@@ -64,6 +64,7 @@ struct RopeParams {
   uint16_t* k;
   int64_t x_stride;
   int tokens, hq, hkv, d, pos_dims;
+  int rot_half;              // 1: pairs (i, i + span/2) instead of (2i, 2i + 1)
   double theta;
 };
 
@@ -155,6 +156,7 @@ struct ProjParams {
   int tokens, hidden, hq, hkv, d;
   int n_feat;                // (hq + 2 hkv) d
   int ftiles;                // ceil(n_feat / kProjTileF)
+  int rot_span;              // 0: adjacent pairs; d or d/2: rotate-half pairs within spans of that width
 };
 constexpr int kProjTileF = 256;   // features per workgroup tile
 constexpr int kProjTileT = 256;   // tokens per workgroup tile
