@@ -382,13 +382,28 @@ def bench_proj(torch, steps, warmup):
 
 
 def source_digest(paths) -> str:
-    """sha256 over the given source files (identifies the kernel build a
-    committed counter summary belongs to)."""
+    """sha256 over the sources a kernel is built from (identifies the kernel
+    build a committed counter summary belongs to).  "file#Name" stands for
+    the part of a shared header that kernel uses: the text of its parameter
+    struct Name plus the header's typedef and constexpr lines, so that
+    additions for other kernels do not invalidate the summary."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for pth in paths:
+        name = None
+        if "#" in pth:
+            pth, name = pth.split("#", 1)
         with open(os.path.join(ROOT, pth), "rb") as f:
-            h.update(f.read())
+            data = f.read()
+        if name is not None:
+            text = data.decode()
+            m = re.search(r"^struct %s \{.*?^\};" % re.escape(name), text, re.S | re.M)
+            if m is None:
+                raise ValueError("struct %s not found in %s" % (name, pth))
+            keep = [ln for ln in text.splitlines() if ln.startswith(("typedef", "constexpr"))]
+            data = (m.group(0) + "\n" + "\n".join(keep)).encode()
+        h.update(data)
     return h.hexdigest()[:16]
 
 
