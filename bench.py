@@ -175,6 +175,32 @@ def bench_other(torch, steps, warmup, only=None):
         res.update(bench_proj(torch, steps, warmup))
     if only in (None, "fp8"):
         res.update(bench_fp8(torch, steps, warmup))
+    if only in (None, "decode"):
+        res.update(bench_decode(torch, steps, warmup))
+    return res
+
+
+def bench_decode(torch, steps, warmup):
+    """Decode over paged caches: 64 sequences of one query token each over
+    512..8192 cached keys (GQA 32/8, d 128, 64-row pages) through
+    attn_fwd_paged.  Decode reads the whole cache once per step, so the
+    figure is the K/V read rate against HBM peak."""
+    import numpy as np
+    from vision_encoder_attention_amd import runner as R
+    from vision_encoder_attention_amd import workloads as W
+    rng = np.random.default_rng(70)
+    lk = [int(x) for x in rng.integers(512, 8193, 64)]
+    case = W.random_dense([1] * 64, lk, 32, 8, 128, True, "bf16", seed=71)
+    st = R.stage_dense(case)
+    ms, ms_min = bench_dense_paged(torch, st, steps, warmup)
+    kv_bytes = float(sum(lk)) * 8 * 128 * 2 * 2
+    name = "decode_b64_kv%d_h32-8_d128_paged64" % sum(lk)
+    res = {name: {"attn_fwd_ms": round(ms, 4), "attn_fwd_min_ms": round(ms_min, 4), "kv_bytes": kv_bytes,
+                  "kv_gbs": round(kv_bytes / ms / 1e6, 1), "kv_frac_hbm": round(kv_bytes / ms / 1e6 / PEAK_HBM_GBS, 4),
+                  "note": "the prefill kernel on one-row tiles (one query per sequence and head); a decode kernel "
+                          "would put a KV group's query heads in one tile and split the key range"}}
+    del st
+    torch.cuda.empty_cache()
     return res
 
 
@@ -461,7 +487,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy (reference for HBM byte counters)")
-    ap.add_argument("--only", choices=["varlen_gqa", "long_causal", "sparse_mqa", "indexer", "qkv_proj", "fp8"],
+    ap.add_argument("--only", choices=["varlen_gqa", "long_causal", "sparse_mqa", "indexer", "qkv_proj", "fp8", "decode"],
                     help="only run one of the other workloads (for profiling one kernel family)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

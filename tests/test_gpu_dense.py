@@ -387,3 +387,23 @@ def test_paged_kv_full_size_is_bitwise_unpaged(torch, name, ps):
     kc, vc, bt = _page_caches(torch, st.k, st.v, case.cu_seqlens_k, ps, extra_pages=11, seed=650)
     out, lse = _run_paged(torch, st, kc, vc, bt, ps)
     assert torch.equal(out, st.out) and torch.equal(lse, st.lse)
+
+
+def test_paged_decode_batch(torch):
+    """Decode shape over a paged cache: 24 sequences of one query token each
+    over 200..3000 cached keys (GQA 32/8, d 128, 64-row pages, causal =
+    bottom-right, so each token sees its whole cache): against the oracle's
+    paged view, and bitwise equal to the packed layout."""
+    rng = np.random.default_rng(660)
+    lk = [int(x) for x in rng.integers(200, 3001, 24)]
+    case = W.random_dense([1] * 24, lk, 32, 8, 128, True, "bf16", seed=661)
+    st = R.stage_dense(case)
+    R.run_attn(st)
+    kc, vc, bt = _page_caches(torch, st.k, st.v, case.cu_seqlens_k, 64, extra_pages=5, seed=662)
+    out, lse = _run_paged(torch, st, kc, vc, bt, 64)
+    assert torch.equal(out, st.out) and torch.equal(lse, st.lse)
+    o_ref, l_ref = oracle.attention_paged(W.bf16_bits_to_f64(case.q), W.bf16_bits_to_f64(R.tensor_to_bits(kc)),
+                                          W.bf16_bits_to_f64(R.tensor_to_bits(vc)), bt, 64, case.cu_seqlens_q,
+                                          case.cu_seqlens_k, True, float(np.float32(case.scale)))
+    assert_bf16_close(_f64(out, "bf16"), o_ref, "decode out")
+    assert_bf16_close(lse.cpu().numpy().astype(np.float64), l_ref, "decode lse")
