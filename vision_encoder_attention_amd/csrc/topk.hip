@@ -69,8 +69,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
     v[e] = i < len ? ((uint64_t)order_code(row[i]) << 32) | (uint32_t)~(uint32_t)(s + i) : 0ull;
   }
   int lo = 0;
+  // Fully unrolled: every window, stride and skip below is a compile-time
+  // constant; only the direction bit of a merge block comes from tid.
+#pragma unroll
   for (int sb = 1; sb <= LOG; ++sb) {                   // merge width w = 2^sb
     const int w = 1 << sb;
+#pragma unroll
     for (int hi = sb - 1; hi >= 0; hi -= 4) {           // strides 2^hi .. 2^max(hi-3, 0)
       const int nlo = max(hi - 3, 0);
       if (nlo != lo) {
@@ -92,7 +96,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
           const int e2 = e | (1 << m);
           const bool desc = (idx(lo, e) & w) == 0;
           const uint64_t a = v[e], c = v[e2];
-          const bool sw = desc ? (a < c) : (a > c);
+          const bool sw = (a < c) == desc;                // keys are distinct: a > c is !(a < c)
           v[e] = sw ? c : a;
           v[e2] = sw ? a : c;
         }
