@@ -182,33 +182,52 @@ def bench_other(torch, steps, warmup, only=None):
 
 def bench_decode(torch, steps, warmup):
     """Decode over paged caches: 64 sequences of one query token each over
-    512..8192 cached keys (GQA 32/8, d 128, 64-row pages) through
-    attn_fwd_paged.  Decode reads the whole cache once per step, so the
-    figure is the K/V read rate against HBM peak."""
+    512..8192 cached keys (GQA 32/8, d 128, 64-row pages in shuffled places)
+    through attn_decode (a key/value head's 4 query heads in one workgroup,
+    each cache cut into key ranges that are merged after), beside the
+    prefill kernel on the same caches (attn_fwd_paged, one query row per
+    128-row tile).  Decode reads the whole cache once per step, so the figure
+    is the K/V read rate against HBM peak."""
     import numpy as np
+    import vision_encoder_attention_amd as vea
     from vision_encoder_attention_amd import runner as R
     from vision_encoder_attention_amd import workloads as W
     rng = np.random.default_rng(70)
     lk = [int(x) for x in rng.integers(512, 8193, 64)]
     case = W.random_dense([1] * 64, lk, 32, 8, 128, True, "bf16", seed=71)
     st = R.stage_dense(case)
-    ms, ms_min = bench_dense_paged(torch, st, steps, warmup)
+    prefill_ms, _ = bench_dense_paged(torch, st, steps, warmup)
+    kc, vc, btd = paged_copy(torch, st, 64)
+    out = torch.empty_like(st.q)
+    lse = torch.empty((32, 64), dtype=torch.float32, device="cuda")
+    nbytes = vea.attn_decode_workspace_size(64, max(lk), 32, 8, 128)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+
+    def run():
+        vea.attn_decode(st.q, kc, vc, st.cu_k, c_scale, out, lse, block_table=btd, page_size=64,
+                        max_seqlen_k=max(lk), workspace=ws if nbytes else None)
+
+    c_scale = case.scale
+    warm_up(torch, run, max(1, warmup))
+    tm = Timer(torch)
+    for _ in range(steps):
+        tm.run("decode", run)
+    torch.cuda.synchronize()
+    ms, ms_min = tm.ms("decode")
     kv_bytes = float(sum(lk)) * 8 * 128 * 2 * 2
     name = "decode_b64_kv%d_h32-8_d128_paged64" % sum(lk)
-    res = {name: {"attn_fwd_ms": round(ms, 4), "attn_fwd_min_ms": round(ms_min, 4), "kv_bytes": kv_bytes,
+    res = {name: {"attn_decode_ms": round(ms, 4), "attn_decode_min_ms": round(ms_min, 4), "kv_bytes": kv_bytes,
                   "kv_gbs": round(kv_bytes / ms / 1e6, 1), "kv_frac_hbm": round(kv_bytes / ms / 1e6 / PEAK_HBM_GBS, 4),
-                  "note": "the prefill kernel on one-row tiles (one query per sequence and head); a decode kernel "
-                          "would put a KV group's query heads in one tile and split the key range"}}
-    del st
+                  "workspace_bytes": nbytes, "prefill_kernel_ms": round(prefill_ms, 4)}}
+    del st, kc, vc, ws
     torch.cuda.empty_cache()
     return res
 
 
-def bench_dense_paged(torch, st, steps, warmup, ps=64):
-    """attn_fwd over the staged case's K/V copied into caches of shuffled
-    64-row pages (one block-table row per sequence)."""
+def paged_copy(torch, st, ps):
+    """The staged case's K/V copied into caches of shuffled ps-row pages (one
+    block-table row per sequence)."""
     import numpy as np
-    import vision_encoder_attention_amd as vea
     c = st.case
     lens = np.diff(np.asarray(c.cu_seqlens_k, np.int64))
     pages = [-(-int(n) // ps) for n in lens]
@@ -227,7 +246,15 @@ def bench_dense_paged(torch, st, steps, warmup, ps=64):
     vc = torch.zeros(shape, dtype=st.v.dtype, device="cuda")
     kc[idx] = st.k
     vc[idx] = st.v
-    btd = torch.from_numpy(bt).cuda()
+    return kc, vc, torch.from_numpy(bt).cuda()
+
+
+def bench_dense_paged(torch, st, steps, warmup, ps=64):
+    """attn_fwd over the staged case's K/V copied into caches of shuffled
+    64-row pages (one block-table row per sequence)."""
+    import vision_encoder_attention_amd as vea
+    c = st.case
+    kc, vc, btd = paged_copy(torch, st, ps)
 
     def run():
         vea.attn_fwd_paged(st.q, kc, vc, btd, ps, st.cu_q, st.cu_k, c.causal, c.scale, st.out, st.lse,

@@ -163,6 +163,57 @@ int vea_attn_fwd_workspace_size(int dtype, int batch, int total_q, int total_k, 
                                 int causal, int piece_rows, size_t* bytes);
 
 /*
+ * vea_attn_decode — bf16 attention of one new query token per sequence over
+ * that sequence's cached keys and values (the decode step: every cached key
+ * is visible), packed or paged.
+ * Sources: the scaled dot-product attention and its lse as vea_attn_fwd; a
+ * paged KV cache of fixed-size pages [SGLang] section 2.2; KV rows fetched
+ * through a page table [V32] section 实验方法和结果; the blockwise merge of
+ * partial results over key ranges [V32] eq. (1)(2).
+ *
+ *   q             bf16 [batch, num_heads_q, head_dim], sequence stride
+ *                 q_seq_stride elements (>= num_heads_q * head_dim).
+ *   k, v          block_table NULL: bf16 [total_k, num_heads_kv, head_dim]
+ *                 packed by cu_seqlens_k.  Otherwise caches as in
+ *                 vea_attn_fwd_paged (page_size a power of two 64 .. 65536,
+ *                 block_table [batch, max_pages_per_seq], num_pages pages).
+ *   cu_seqlens_k  device int32 [batch + 1]: sequence b has keys
+ *                 [cu[b], cu[b+1]) (positions 0 .. len - 1 in the cache).
+ *                 A sequence with no keys gets zeros and lse -inf.
+ *   total_k       packed: rows of k/v (= cu[batch]); paged: the sum of the key
+ *                 lengths.  max_seqlen_k bounds every key length.
+ *   num_heads_q / num_heads_kv   a divisor; query head h reads key/value head
+ *                 h / (num_heads_q / num_heads_kv); that ratio <= 128.
+ *   head_dim      64 or 128.
+ *   out           bf16 [batch, num_heads_q, head_dim], stride out_seq_stride.
+ *   lse           nullable; float [num_heads_q, batch], natural log.
+ *   workspace     nullable; with at least vea_attn_decode_workspace_size bytes
+ *                 each (sequence, key/value head) is cut into up to 8 key
+ *                 ranges whose partial results are merged in range order (the
+ *                 result does not depend on the timing of the ranges; it may
+ *                 differ in the last bits from a call without workspace).
+ * One workgroup handles all query heads of one key/value head of one sequence,
+ * so every cached key is read once per (sequence, key/value head).
+ * Errors as vea_attn_fwd; VEA_EUNSUPPORTED for head_dim or a head ratio out of
+ * range.  Nothing is written on error.  Asynchronous on stream.
+ */
+int vea_attn_decode(const void* q, int64_t q_seq_stride,
+                    const void* k, int64_t k_tok_stride,
+                    const void* v, int64_t v_tok_stride,
+                    const int32_t* block_table, int max_pages_per_seq, int page_size, int num_pages,
+                    const int32_t* cu_seqlens_k, int batch, int total_k, int max_seqlen_k,
+                    int num_heads_q, int num_heads_kv, int head_dim, float scale,
+                    void* out, int64_t out_seq_stride, float* lse,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * vea_attn_decode_workspace_size — bytes of workspace vea_attn_decode uses for
+ * these sizes on the current HIP device (0: it splits nothing).
+ */
+int vea_attn_decode_workspace_size(int batch, int max_seqlen_k, int num_heads_q, int num_heads_kv,
+                                   int head_dim, size_t* bytes);
+
+/*
  * vea_qkv_rope — split a fused QKV projection output and apply rotary position
  * embedding to its Q and K heads (V is left in place for vea_attn_fwd to read
  * through a strided pointer).

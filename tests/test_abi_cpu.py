@@ -32,7 +32,7 @@ def lib():
 def test_header_declares_the_operations():
     names = _declared()
     for n in ("vea_attn_fwd", "vea_attn_fwd_workspace_size", "vea_qkv_rope", "vea_sparse_mqa_fwd",
-              "vea_sparse_mqa_workspace_size", "vea_topk_indices", "vea_sparse_mqa_paged_fwd", "vea_attn_fwd_paged",
+              "vea_sparse_mqa_workspace_size", "vea_topk_indices", "vea_sparse_mqa_paged_fwd", "vea_attn_fwd_paged", "vea_attn_decode", "vea_attn_decode_workspace_size",
               "vea_attn_probs_piece", "vea_status_str", "vea_rope_cos_sin", "vea_qkv_proj_rope",
               "vea_quantize_fp8", "vea_attn_fwd_fp8"):
         assert n in names
@@ -196,6 +196,37 @@ def _attn_paged(lib, **kw):
 ])
 def test_attn_paged_validation(lib, kw, status):
     assert _attn_paged(lib, **kw) == status
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, qs=512, k=FAKE, ks=128, v=FAKE, vs=128, bt=None, mp=0, ps=0, npg=0, cuk=FAKE, batch=2, tk=100,
+             mk=60, hq=8, hkv=2, d=64, scale=0.125, out=FAKE, os=512, lse=None)
+    a.update(kw)
+    return lib.vea_attn_decode(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["bt"], a["mp"], a["ps"], a["npg"],
+                               a["cuk"], a["batch"], a["tk"], a["mk"], a["hq"], a["hkv"], a["d"], a["scale"],
+                               a["out"], a["os"], a["lse"], None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), VEA_EUNSUPPORTED),
+    (dict(hq=258, hkv=1), VEA_EUNSUPPORTED),  # a key/value head's query heads exceed one 128-row tile
+    (dict(hq=6, hkv=4), VEA_ESHAPE),          # not a divisor
+    (dict(mk=101), VEA_ESHAPE),               # packed: max_seqlen_k > total_k
+    (dict(bt=FAKE, ps=32, mp=4, npg=10), VEA_ESHAPE),
+    (dict(bt=FAKE, ps=64, mp=0, npg=10), VEA_ESHAPE),
+    (dict(qs=256), VEA_ESHAPE),               # sequence stride shorter than Hq * d
+    (dict(q=None), VEA_EINVAL),
+    (dict(out=FAKE + 2), VEA_EINVAL),
+    (dict(scale=float("nan")), VEA_EINVAL),
+    (dict(batch=0), VEA_OK),
+])
+def test_attn_decode_validation(lib, kw, status):
+    assert _decode(lib, **kw) == status
+    n = ctypes.c_size_t(7)
+    if status == VEA_EUNSUPPORTED:
+        assert lib.vea_attn_decode_workspace_size(2, 60, kw.get("hq", 8), kw.get("hkv", 2), kw.get("d", 64),
+                                                  ctypes.byref(n)) == status
+        assert n.value == 0
 
 
 def _paged(lib, **kw):

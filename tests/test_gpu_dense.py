@@ -407,3 +407,48 @@ def test_paged_decode_batch(torch):
                                           case.cu_seqlens_k, True, float(np.float32(case.scale)))
     assert_bf16_close(_f64(out, "bf16"), o_ref, "decode out")
     assert_bf16_close(lse.cpu().numpy().astype(np.float64), l_ref, "decode lse")
+
+
+@pytest.mark.parametrize("hq,hkv,d,paged", [(32, 8, 128, True), (16, 16, 64, False), (64, 1, 64, False),
+                                            (40, 4, 128, False), (128, 2, 64, True)])
+def test_attn_decode_against_the_oracle(torch, hq, hkv, d, paged):
+    """vea_attn_decode (one query token per sequence, a key/value head's query
+    heads as the rows of one workgroup): sequences with no, one, a ragged
+    number of and several thousand cached keys; packed and over shuffled
+    64-row pages; without workspace and with the key-range split.  Each
+    against the oracle, and bitwise repeatable."""
+    import vision_encoder_attention_amd as vea
+    rng = np.random.default_rng(670 + hq + d)
+    lk = [0, 1, 63, 65, 4100] + [int(x) for x in rng.integers(100, 3000, 11)]
+    b = len(lk)
+    case = W.random_dense([1] * b, lk, hq, hkv, d, False, "bf16", seed=671 + hkv)
+    scale = float(np.float32(case.scale))
+    log("decode h=%d/%d d=%d paged=%s batch=%d keys=%d" % (hq, hkv, d, paged, b, sum(lk)))
+    q = R.bits_to_tensor(case.q, "cuda")
+    k = R.bits_to_tensor(case.k, "cuda")
+    v = R.bits_to_tensor(case.v, "cuda")
+    cuk = torch.from_numpy(np.asarray(case.cu_seqlens_k, np.int32)).cuda()
+    kw = {}
+    if paged:
+        kc, vc, bt = _page_caches(torch, k, v, case.cu_seqlens_k, 64, extra_pages=3, seed=672)
+        k, v = kc, vc
+        kw = dict(block_table=torch.from_numpy(bt).cuda(), page_size=64)
+        o_ref, l_ref = oracle.attention_paged(W.bf16_bits_to_f64(case.q), W.bf16_bits_to_f64(R.tensor_to_bits(kc)),
+                                              W.bf16_bits_to_f64(R.tensor_to_bits(vc)), bt, 64, case.cu_seqlens_q,
+                                              case.cu_seqlens_k, False, scale)
+    else:
+        o_ref, l_ref = oracle.attention(W.bf16_bits_to_f64(case.q), W.bf16_bits_to_f64(case.k),
+                                        W.bf16_bits_to_f64(case.v), case.cu_seqlens_q, case.cu_seqlens_k, False, scale)
+    ws = vea.attn_decode_workspace_size(b, max(lk), hq, hkv, d)
+    log("  workspace %d bytes" % ws)
+    runs = []
+    for workspace in (None, "auto", "auto"):
+        out = torch.full_like(q, float("nan"))
+        lse = torch.full((hq, b), float("nan"), dtype=torch.float32, device="cuda")
+        vea.attn_decode(q, k, v, cuk, case.scale, out, lse, workspace=workspace, **kw)
+        torch.cuda.synchronize()
+        runs.append((out, lse))
+        assert_bf16_close(_f64(out, "bf16"), o_ref, "decode out ws=%s" % workspace)
+        assert_bf16_close(lse.cpu().numpy().astype(np.float64), l_ref, "decode lse ws=%s" % workspace)
+    assert torch.equal(runs[1][0], runs[2][0]) and torch.equal(runs[1][1], runs[2][1])
+    assert torch.all(runs[1][0][0] == 0) and torch.all(torch.isinf(runs[1][1][:, 0]))

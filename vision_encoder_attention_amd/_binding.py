@@ -54,6 +54,11 @@ def load_library():
                                            i32, i32, i32, i32, i32, i32, f32, i32, vp, i64, vp, vp,
                                            ctypes.c_size_t, vp]
         lib.vea_attn_fwd_paged.restype = i32
+        lib.vea_attn_decode.argtypes = [vp, i64, vp, i64, vp, i64, vp, i32, i32, i32, vp, i32, i32, i32, i32, i32,
+                                        i32, f32, vp, i64, vp, vp, ctypes.c_size_t, vp]
+        lib.vea_attn_decode.restype = i32
+        lib.vea_attn_decode_workspace_size.argtypes = [i32] * 5 + [ctypes.POINTER(ctypes.c_size_t)]
+        lib.vea_attn_decode_workspace_size.restype = i32
         lib.vea_attn_fwd_workspace_size.argtypes = [i32] * 11 + [ctypes.POINTER(ctypes.c_size_t)]
         lib.vea_attn_fwd_workspace_size.restype = i32
         lib.vea_qkv_rope.argtypes = [vp, i64, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp]
@@ -243,6 +248,61 @@ def attn_fwd_paged(q, k_cache, v_cache, block_table, page_size, cu_seqlens_q, cu
                                     int(max_seqlen_q), int(max_seqlen_k), q.shape[1], k_cache.shape[1], q.shape[2],
                                     1 if causal else 0, float(scale), int(piece_rows), _ptr(out), os_, _ptr(lse),
                                     _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(q))
+    _check(st)
+    return out, lse
+
+
+def attn_decode_workspace_size(batch, max_seqlen_k, heads_q, heads_kv, head_dim) -> int:
+    """Workspace bytes vea_attn_decode uses for these sizes on the current
+    device (0: no split)."""
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    _check(lib.vea_attn_decode_workspace_size(int(batch), int(max_seqlen_k), int(heads_q), int(heads_kv),
+                                              int(head_dim), ctypes.byref(n)))
+    return n.value
+
+
+def attn_decode(q, k, v, cu_seqlens_k, scale, out, lse=None, *, block_table=None, page_size=0, max_seqlen_k=None,
+                workspace="auto"):
+    """One query token per sequence over its cached keys (see vea_attn_decode):
+    q / out [batch, Hq, d] bf16; k / v packed [total_k, Hkv, d] by
+    cu_seqlens_k, or, with block_table int32 [batch, max_pages_per_seq],
+    caches [num_pages * page_size, Hkv, d]; lse float32 [Hq, batch]."""
+    lib = load_library()
+    torch = _torch()
+    qs, ks, vs, os_ = (_token_major(q, "q"), _token_major(k, "k"), _token_major(v, "v"), _token_major(out, "out"))
+    _int32_dev(cu_seqlens_k, "cu_seqlens_k")
+    if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype or out.dtype != q.dtype:
+        raise TypeError("q, k, v and out must be bfloat16")
+    batch = cu_seqlens_k.numel() - 1
+    if q.shape[0] != batch or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q and out need one row per sequence")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (q.shape[1], batch)):
+        raise ValueError("lse must be contiguous float32 [Hq, batch]")
+    if max_seqlen_k is None:
+        max_seqlen_k = (cu_seqlens_k[1:] - cu_seqlens_k[:-1]).max().item() if batch > 0 else 0
+    total_k = int(cu_seqlens_k[-1].item()) if batch > 0 else 0
+    if block_table is not None:
+        _int32_dev(block_table, "block_table")
+        if block_table.dim() != 2 or not block_table.is_contiguous() or block_table.shape[0] != batch:
+            raise ValueError("block_table must be contiguous int32 [batch, max_pages_per_seq]")
+        page_size = int(page_size)
+        if page_size < 1 or k.shape[0] % page_size or v.shape[0] != k.shape[0]:
+            raise ValueError("cache rows must be a multiple of page_size and equal for k and v")
+        mp, n_pages = block_table.shape[1], k.shape[0] // page_size
+    else:
+        page_size, mp, n_pages = 0, 0, 0
+    with torch.cuda.device(q.device):
+        if isinstance(workspace, str):
+            if workspace != "auto":
+                raise ValueError('workspace must be "auto", None or a uint8 GPU tensor')
+            nbytes = attn_decode_workspace_size(batch, max_seqlen_k, q.shape[1], k.shape[1], q.shape[2])
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
+        st = lib.vea_attn_decode(_ptr(q), qs, _ptr(k), ks, _ptr(v), vs, _ptr(block_table), mp, page_size, n_pages,
+                                 _ptr(cu_seqlens_k), batch, total_k, int(max_seqlen_k), q.shape[1], k.shape[1],
+                                 q.shape[2], float(scale), _ptr(out), os_, _ptr(lse), _ptr(workspace),
+                                 0 if workspace is None else workspace.numel(), _stream(q))
     _check(st)
     return out, lse
 

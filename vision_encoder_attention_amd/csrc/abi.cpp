@@ -113,6 +113,7 @@ int dense_layout(int batch, int max_seqlen_q, int num_heads_q, int piece_rows, D
   p.page_shift = 0;
   p.max_pages = 0;
   p.q_scale = p.k_scale = p.v_scale = nullptr;
+  p.dec_group = 0;
   return VEA_OK;
 }
 
@@ -260,6 +261,121 @@ int vea_attn_fwd_paged(const void* q, int64_t q_tok_stride, const void* k_cache,
                    max_pages_per_seq, page_size, num_pages, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k,
                    max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim, causal, scale, piece_rows, out,
                    out_tok_stride, lse, workspace, workspace_bytes, stream);
+}
+
+namespace {
+
+// Decode split: every (sequence, key/value head) unit is cut into key ranges
+// so that about four rounds of workgroups fill the device (at most 8 ranges,
+// at most one per key tile of the longest cache): the ranges of long caches
+// are then short enough to even out unequal cache lengths.
+int decode_split(int units, int max_seqlen_k, int head_dim, int* nsplit) {
+  *nsplit = 1;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return VEA_EHIP;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return VEA_EHIP;
+  const int slots = cus * dense_bf16_blocks_per_cu(head_dim);
+  if (slots > 0 && units > 0 && units < 4 * slots) *nsplit = std::min(8, (4 * slots + units - 1) / units);
+  *nsplit = std::max(1, std::min(*nsplit, (max_seqlen_k + 63) / 64));
+  return VEA_OK;
+}
+
+int decode_shape_status(int batch, int total_k, int max_seqlen_k, int num_heads_q, int num_heads_kv, int head_dim) {
+  if (batch < 0 || total_k < 0 || max_seqlen_k < 0) return VEA_ESHAPE;
+  if (num_heads_q <= 0 || num_heads_kv <= 0 || num_heads_q % num_heads_kv != 0) return VEA_ESHAPE;
+  if (head_dim != 64 && head_dim != 128) return VEA_EUNSUPPORTED;
+  if (num_heads_q / num_heads_kv > kDenseBM) return VEA_EUNSUPPORTED;   // a group's heads fill one tile
+  if ((int64_t)batch * num_heads_kv * 8 * 8 > 0x7fffffff) return VEA_EUNSUPPORTED;
+  return VEA_OK;
+}
+
+}  // namespace
+
+int vea_attn_decode_workspace_size(int batch, int max_seqlen_k, int num_heads_q, int num_heads_kv, int head_dim,
+                                   size_t* bytes) {
+  if (bytes == nullptr) return VEA_EINVAL;
+  *bytes = 0;
+  int st = decode_shape_status(batch, max_seqlen_k, max_seqlen_k, num_heads_q, num_heads_kv, head_dim);
+  if (st != VEA_OK) return st;
+  int nsplit = 1;
+  st = decode_split(batch * num_heads_kv, max_seqlen_k, head_dim, &nsplit);
+  if (st != VEA_OK) return st;
+  if (nsplit > 1) *bytes = (size_t)batch * num_heads_kv * nsplit * dense_chunk_bytes(head_dim);
+  return VEA_OK;
+}
+
+int vea_attn_decode(const void* q, int64_t q_seq_stride, const void* k, int64_t k_tok_stride, const void* v,
+                    int64_t v_tok_stride, const int32_t* block_table, int max_pages_per_seq, int page_size,
+                    int num_pages, const int32_t* cu_seqlens_k, int batch, int total_k, int max_seqlen_k,
+                    int num_heads_q, int num_heads_kv, int head_dim, float scale, void* out, int64_t out_seq_stride,
+                    float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = decode_shape_status(batch, total_k, max_seqlen_k, num_heads_q, num_heads_kv, head_dim);
+  if (st != VEA_OK) return st;
+  if (!isfinite(scale)) return VEA_EINVAL;
+  int shift = 0;
+  if (block_table != nullptr) {
+    if (page_size < 64 || page_size > (1 << 16) || (page_size & (page_size - 1)) || num_pages < 0) return VEA_ESHAPE;
+    while ((1 << shift) < page_size) ++shift;
+    if (max_pages_per_seq < (max_seqlen_k + page_size - 1) / page_size) return VEA_ESHAPE;
+  } else if (max_seqlen_k > total_k) {
+    return VEA_ESHAPE;
+  }
+  if (batch == 0) return VEA_OK;
+  if (!q || !out || !cu_seqlens_k) return VEA_EINVAL;
+  const bool has_keys = block_table != nullptr ? num_pages > 0 : total_k > 0;
+  if (has_keys && (!k || !v)) return VEA_EINVAL;
+  const int64_t qrow = (int64_t)num_heads_q * head_dim, krow = (int64_t)num_heads_kv * head_dim;
+  if (q_seq_stride < qrow || out_seq_stride < qrow || k_tok_stride < krow || v_tok_stride < krow) return VEA_ESHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return VEA_EINVAL;
+  if ((q_seq_stride * 2) % 16 || (k_tok_stride * 2) % 16 || (v_tok_stride * 2) % 16 || (out_seq_stride * 2) % 16)
+    return VEA_EINVAL;
+  if (workspace != nullptr && !aligned16(workspace)) return VEA_EWORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  if (check_enabled()) {
+    std::vector<int32_t> cu;
+    st = fetch_ints(cu_seqlens_k, (size_t)batch + 1, s, cu);
+    if (st != VEA_OK) return st;
+    if (cu[0] != 0) return VEA_ERANGE;
+    for (int b = 0; b < batch; ++b)
+      if (cu[b + 1] < cu[b] || cu[b + 1] - cu[b] > max_seqlen_k) return VEA_ERANGE;
+    if (block_table == nullptr && cu[batch] != total_k) return VEA_ERANGE;
+    if (block_table != nullptr) {
+      std::vector<int32_t> bt;
+      st = fetch_ints(block_table, (size_t)batch * max_pages_per_seq, s, bt);
+      if (st != VEA_OK) return st;
+      for (int b = 0; b < batch; ++b)
+        for (int pg = 0; pg < (cu[b + 1] - cu[b] + page_size - 1) / page_size; ++pg) {
+          const int32_t x = bt[(size_t)b * max_pages_per_seq + pg];
+          if (x < 0 || x >= num_pages) return VEA_ERANGE;
+        }
+    }
+  }
+  DenseParams p;
+  p.q = q; p.k = k; p.v = v; p.out = out; p.lse = lse;
+  p.cu_q = cu_seqlens_k; p.cu_k = cu_seqlens_k;
+  p.q_stride = q_seq_stride; p.k_stride = k_tok_stride; p.v_stride = v_tok_stride; p.o_stride = out_seq_stride;
+  p.batch = batch; p.total_q = batch; p.total_k = total_k;
+  p.hq = num_heads_kv; p.hkv = num_heads_kv; p.group = 1;     // units are (sequence, key/value head)
+  st = dense_layout(batch, num_heads_q / num_heads_kv, num_heads_kv, 0, p);
+  if (st != VEA_OK) return st;
+  p.dec_group = num_heads_q / num_heads_kv;
+  p.xcd_map = 0;
+  p.scale = scale;
+  p.block_table = block_table;
+  p.page_shift = shift;
+  p.max_pages = max_pages_per_seq;
+  if (workspace != nullptr) {
+    int nsplit = 1;
+    st = decode_split(p.units, max_seqlen_k, head_dim, &nsplit);
+    if (st != VEA_OK) return st;
+    if (nsplit > 1) {
+      if (workspace_bytes < (size_t)p.units * nsplit * dense_chunk_bytes(head_dim)) return VEA_EWORKSPACE;
+      p.full_units = 0;
+      p.nsplit = nsplit;
+      p.ws = (float*)workspace;
+    }
+  }
+  return finish(hip_status(launch_attn_fwd_bf16(p, head_dim, false, s)), s);
 }
 
 int vea_attn_fwd_fp8(const void* q, int64_t q_tok_stride, const void* k, int64_t k_tok_stride, const void* v,

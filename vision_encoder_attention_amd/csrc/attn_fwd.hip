@@ -129,6 +129,22 @@ __device__ __forceinline__ bool tile_range(const DenseParams& p, int b, int t, i
   return true;
 }
 
+// Decode units (one query token per sequence): unit (sequence b, key/value
+// head h) has as rows the dec_group query heads of that key/value head, which
+// all read the same K/V; the keys are the sequence's cache, all visible.
+__device__ __forceinline__ void decode_range(const DenseParams& p, int b, TileRange& r) {
+  const int ks = clampi(p.cu_k[b], 0, p.total_k);
+  const int ke = clampi(p.cu_k[b + 1], ks, p.total_k);
+  r.qs = b;
+  r.ks = ks;
+  r.len_q = p.dec_group;
+  r.len_k = ke - ks;
+  r.row0 = 0;
+  r.row_end = p.dec_group;
+  r.kend = r.len_k;
+  r.kfull = r.len_k;
+}
+
 // =============================================================== bf16 path
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
@@ -183,7 +199,7 @@ struct Cfg {
   }
 };
 
-template <int D, bool CAUSAL, bool PAGED>
+template <int D, bool CAUSAL, bool PAGED, bool DECODE = false>
 __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(DenseParams p) {
   using C = Cfg<D>;
   // Two K stages and two V stages in distinct arrays: the compiler can then see
@@ -205,7 +221,11 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
   int b, h, t;
   decode_unit(p, id, b, h, t);
   TileRange tr;
-  if (!tile_range(p, b, t, C::BM, CAUSAL, tr)) return;   // uniform over the workgroup
+  if constexpr (DECODE) {
+    decode_range(p, b, tr);
+  } else {
+    if (!tile_range(p, b, t, C::BM, CAUSAL, tr)) return;   // uniform over the workgroup
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -221,8 +241,11 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
   // ---- Q fragment (B operand of S^T = K Q^T): Q[qi][16 ks + 8 g2 .. +7]
   u32x4 qf[D / 16];
   {
-    const uint16_t* src = (const uint16_t*)p.q + (int64_t)(tr.qs + (qvalid ? qi : tr.row0)) * p.q_stride +
-                          (int64_t)h * D + 8 * g2;
+    // decode: row qi of unit (b, h) is query head h * dec_group + qi of token b
+    const uint16_t* src = DECODE ? (const uint16_t*)p.q + (int64_t)b * p.q_stride +
+                                       (int64_t)(h * p.dec_group + (qvalid ? qi : 0)) * D + 8 * g2
+                                 : (const uint16_t*)p.q + (int64_t)(tr.qs + (qvalid ? qi : tr.row0)) * p.q_stride +
+                                       (int64_t)h * D + 8 * g2;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       const u32x4 v = *(const u32x4*)(src + 16 * ks);
@@ -522,6 +545,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
     // (fp32), reference max m (log2 domain) and sum l
     float* w = p.ws + (size_t)(blockIdx.x - p.full_units) * (C::BM * (D + 2));
     const int rl = wave * 32 + l32;                     // row within the tile
+    if (DECODE && !qvalid) return;                      // decode: only the few real rows are merged
 #pragma unroll
     for (int nb = 0; nb < D / 32; ++nb)
 #pragma unroll
@@ -536,7 +560,8 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
   }
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qvalid) {
-    uint16_t* dst = (uint16_t*)p.out + (int64_t)(tr.qs + qi) * p.o_stride + (int64_t)h * D + 4 * g2;
+    uint16_t* dst = DECODE ? (uint16_t*)p.out + (int64_t)b * p.o_stride + (int64_t)(h * p.dec_group + qi) * D + 4 * g2
+                           : (uint16_t*)p.out + (int64_t)(tr.qs + qi) * p.o_stride + (int64_t)h * D + 4 * g2;
 #pragma unroll
     for (int nb = 0; nb < D / 32; ++nb)
 #pragma unroll
@@ -546,8 +571,8 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
                                 pack_bf16x2(ov[4 * r4 + 2] * inv, ov[4 * r4 + 3] * inv)};
         *(u32x2*)(dst + 32 * nb + 8 * r4) = w;
       }
-    if (p.lse != nullptr && g2 == 0)
-      p.lse[(int64_t)h * p.total_q + tr.qs + qi] = l_tot > 0.f ? (m_used + log2f(l_tot)) * kLn2 : -INFINITY;
+    const int64_t li = DECODE ? (int64_t)(h * p.dec_group + qi) * p.total_q + b : (int64_t)h * p.total_q + tr.qs + qi;
+    if (p.lse != nullptr && g2 == 0) p.lse[li] = l_tot > 0.f ? (m_used + log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
@@ -897,7 +922,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(DenseParams p) {
   int b, h, t;
   decode_unit(p, p.full_units + tu, b, h, t);
   TileRange tr;
-  if (!tile_range(p, b, t, kDenseBM, false, tr)) return;
+  if (p.dec_group > 0) decode_range(p, b, tr);
+  else if (!tile_range(p, b, t, kDenseBM, false, tr)) return;
   constexpr int SL = D / 16;                            // 16-column slices per row
   const int item = blockIdx.y * 256 + threadIdx.x;
   const int rl = item / SL, sc = item - rl * SL;        // row within the tile, slice
@@ -939,11 +965,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(DenseParams p) {
   u32x4 w[2];
 #pragma unroll
   for (int j = 0; j < 8; ++j) w[j >> 2][j & 3] = pack_bf16x2(acc[2 * j] * inv, acc[2 * j + 1] * inv);
-  uint16_t* dst = (uint16_t*)p.out + (int64_t)(tr.qs + qi) * p.o_stride + (int64_t)h * D + 16 * sc;
+  const bool dec = p.dec_group > 0;
+  uint16_t* dst = dec ? (uint16_t*)p.out + (int64_t)b * p.o_stride + (int64_t)(h * p.dec_group + qi) * D + 16 * sc
+                      : (uint16_t*)p.out + (int64_t)(tr.qs + qi) * p.o_stride + (int64_t)h * D + 16 * sc;
   *(u32x4*)dst = w[0];
   *(u32x4*)(dst + 8) = w[1];
-  if (sc == 0 && p.lse != nullptr)
-    p.lse[(int64_t)h * p.total_q + tr.qs + qi] = l > 0.f ? (mmax + log2f(l)) * kLn2 : -INFINITY;
+  const int64_t lsi = dec ? (int64_t)(h * p.dec_group + qi) * p.total_q + b : (int64_t)h * p.total_q + tr.qs + qi;
+  if (sc == 0 && p.lse != nullptr) p.lse[lsi] = l > 0.f ? (mmax + log2f(l)) * kLn2 : -INFINITY;
 }
 
 template <int D>
@@ -1158,6 +1186,11 @@ int dense_bf16_blocks_per_cu(int head_dim) {
 
 template <int D>
 void launch_dense(const DenseParams& p, bool causal, bool paged, dim3 grid, dim3 block, hipStream_t s) {
+  if (p.dec_group > 0) {                                // decode units (never causal)
+    if (paged) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, true, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, false, true>), grid, block, 0, s, p);
+    return;
+  }
   if (paged) {
     if (causal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, true>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, true>), grid, block, 0, s, p);

@@ -55,6 +55,10 @@ struct DenseParams {
   const float* q_scale;
   const float* k_scale;
   const float* v_scale;
+  // Decode units (> 0): unit (b, h) covers query heads h * dec_group ..
+  // + dec_group - 1 of token b (q, out [batch, ...] with stride q/o_stride,
+  // lse [Hq, batch]); hq then counts key/value heads and group is 1.
+  int dec_group;
 };
 
 struct RopeParams {
