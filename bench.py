@@ -192,9 +192,8 @@ def bench_decode(torch, steps, warmup):
     import vision_encoder_attention_amd as vea
     from vision_encoder_attention_amd import runner as R
     from vision_encoder_attention_amd import workloads as W
-    rng = np.random.default_rng(70)
-    lk = [int(x) for x in rng.integers(512, 8193, 64)]
-    case = W.random_dense([1] * 64, lk, 32, 8, 128, True, "bf16", seed=71)
+    case = W.decode()
+    lk = [int(x) for x in np.diff(np.asarray(case.cu_seqlens_k, np.int64))]
     st = R.stage_dense(case)
     prefill_ms, _ = bench_dense_paged(torch, st, steps, warmup)
     kc, vc, btd = paged_copy(torch, st, 64)
@@ -215,7 +214,7 @@ def bench_decode(torch, steps, warmup):
     torch.cuda.synchronize()
     ms, ms_min = tm.ms("decode")
     kv_bytes = float(sum(lk)) * 8 * 128 * 2 * 2
-    name = "decode_b64_kv%d_h32-8_d128_paged64" % sum(lk)
+    name = case.name + "_paged64"
     res = {name: {"attn_decode_ms": round(ms, 4), "attn_decode_min_ms": round(ms_min, 4), "kv_bytes": kv_bytes,
                   "kv_gbs": round(kv_bytes / ms / 1e6, 1), "kv_frac_hbm": round(kv_bytes / ms / 1e6 / PEAK_HBM_GBS, 4),
                   "workspace_bytes": nbytes, "prefill_kernel_ms": round(prefill_ms, 4)}}

@@ -452,3 +452,37 @@ def test_attn_decode_against_the_oracle(torch, hq, hkv, d, paged):
         assert_bf16_close(lse.cpu().numpy().astype(np.float64), l_ref, "decode lse ws=%s" % workspace)
     assert torch.equal(runs[1][0], runs[2][0]) and torch.equal(runs[1][1], runs[2][1])
     assert torch.all(runs[1][0][0] == 0) and torch.all(torch.isinf(runs[1][1][:, 0]))
+
+
+def test_attn_decode_full_size_sampled_sequences(torch):
+    """The decode workload as the benchmark runs it (64 sequences, 512..8192
+    cached keys, GQA 32/8, d 128, shuffled 64-row pages, with the key-range
+    split): sampled sequences (shortest, longest, random) against the oracle
+    on those sequences alone, and bitwise equal to the packed layout."""
+    import vision_encoder_attention_amd as vea
+    case = W.decode()
+    st = R.stage_dense(case)
+    lk = np.diff(np.asarray(case.cu_seqlens_k, np.int64))
+    log("decode full size: %s" % case.name)
+    kc, vc, bt = _page_caches(torch, st.k, st.v, case.cu_seqlens_k, 64, extra_pages=8, seed=680)
+    out = torch.empty_like(st.q)
+    lse = torch.empty((case.num_heads_q, len(lk)), dtype=torch.float32, device="cuda")
+    vea.attn_decode(st.q, kc, vc, st.cu_k, case.scale, out, lse, block_table=torch.from_numpy(bt).cuda(),
+                    page_size=64)
+    out2 = torch.empty_like(out)
+    lse2 = torch.empty_like(lse)
+    vea.attn_decode(st.q, st.k, st.v, st.cu_k, case.scale, out2, lse2)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    rng = np.random.default_rng(681)
+    seqs = np.unique(np.concatenate([[int(np.argmin(lk)), int(np.argmax(lk))], rng.integers(0, len(lk), 4)]))
+    cu = np.asarray(case.cu_seqlens_k, np.int64)
+    got_o = _f64(out, "bf16")
+    got_l = lse.cpu().numpy().astype(np.float64)
+    for b in seqs:
+        k = W.bf16_bits_to_f64(case.k[cu[b]:cu[b + 1]])
+        v = W.bf16_bits_to_f64(case.v[cu[b]:cu[b + 1]])
+        q = W.bf16_bits_to_f64(case.q[b:b + 1])
+        o_ref, l_ref = oracle.attention(q, k, v, [0, 1], [0, int(lk[b])], False, float(np.float32(case.scale)))
+        assert_bf16_close(got_o[b:b + 1], o_ref, "decode seq %d (%d keys) out" % (b, lk[b]))
+        assert_bf16_close(got_l[:, b:b + 1], l_ref, "decode seq %d lse" % b)

@@ -251,6 +251,18 @@ def random_dense(lengths_q, lengths_k, hq: int, hkv: int, d: int, causal: bool, 
 
 # --------------------------------------------------------------- sparse case
 
+def decode(batch: int = 64, lo: int = 512, hi: int = 8192, hq: int = 32, hkv: int = 8, d: int = 128,
+           seed: int = 70) -> DenseCase:
+    """Decode step: one new query token per sequence over cached keys of
+    lengths drawn uniformly in [lo, hi] (GQA 32/8, d 128 as the varlen
+    batch); causal with one query row = every cached key visible."""
+    rng = np.random.default_rng(seed)
+    lk = [int(x) for x in rng.integers(lo, hi + 1, batch)]
+    c = random_dense([1] * batch, lk, hq, hkv, d, True, "bf16", seed=seed + 1)
+    c.name = "decode_b%d_kv%d_h%d-%d_d%d" % (batch, sum(lk), hq, hkv, d)
+    return c
+
+
 def sparse_mqa(rows: int = 323, heads: int = 128, n_kv: int = 2590, d_qk: int = 576, d_v: int = 512,
                k: int = 2048, seed: int = 5, valid_offset: Optional[int] = None) -> SparseCase:
     """Top-k sparse MQA over a shared latent KV.
