@@ -237,6 +237,12 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
   // ---- this lane's query row (local index in the sequence)
   const int qi = tr.row0 + wave * 32 + l32;
   const bool qvalid = qi < tr.row_end;
+  // A wave whose 32 rows are all past the tile's end (the short last tile of
+  // a piece) still issues its share of the K/V DMA and meets every barrier,
+  // but skips the MFMA and softmax work.  Only where the branch costs no
+  // extra spills: elsewhere (d 128, causal, decode) it measured no faster.
+  constexpr bool SKIP_DEAD = !CAUSAL && D == 64 && !DECODE;
+  const bool live = !SKIP_DEAD || tr.row0 + __builtin_amdgcn_readfirstlane(wave) * 32 < tr.row_end;
 
   // ---- Q fragment (B operand of S^T = K Q^T): Q[qi][16 ks + 8 g2 .. +7]
   u32x4 qf[D / 16];
@@ -487,19 +493,28 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
       }
     }
     // QK^T of tile kt under the softmax of tile kt-1, then P V of tile kt-1
-    if constexpr (HAS_S) qk(k_rd, sn0, sn1);
-    u32x4 pb[4];
-    float t = softmax_p(sp0, sp1, m_use, pb);
-    if (__any(t > 8192.f || m_used == -INFINITY)) {
-      asm volatile("; rare: recompute the logits, move the reference max, recompute P" ::);
-      floatx16 r0, r1;
-      qk_global(kt - 1, r0, r1);
-      if (kt - 1 >= n_full) mask(kt - 1, r0, r1);
-      m_use = softmax_ref(r0, r1);
-      t = softmax_p(r0, r1, m_use, pb);
+    if constexpr (HAS_S) {
+      if (live) {
+        qk(k_rd, sn0, sn1);
+      } else {
+        sn0 = (floatx16){};
+        sn1 = (floatx16){};
+      }
     }
-    l_run += t;
-    pv(pb, v_rd);
+    if (live) {
+      u32x4 pb[4];
+      float t = softmax_p(sp0, sp1, m_use, pb);
+      if (__any(t > 8192.f || m_used == -INFINITY)) {
+        asm volatile("; rare: recompute the logits, move the reference max, recompute P" ::);
+        floatx16 r0, r1;
+        qk_global(kt - 1, r0, r1);
+        if (kt - 1 >= n_full) mask(kt - 1, r0, r1);
+        m_use = softmax_ref(r0, r1);
+        t = softmax_p(r0, r1, m_use, pb);
+      }
+      l_run += t;
+      pv(pb, v_rd);
+    }
     if constexpr (HAS_S) {
       if (kt >= n_full) {
         asm volatile("; masked tile" ::);
