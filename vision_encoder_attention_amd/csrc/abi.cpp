@@ -114,6 +114,7 @@ int dense_layout(int batch, int max_seqlen_q, int num_heads_q, int piece_rows, D
   p.max_pages = 0;
   p.q_scale = p.k_scale = p.v_scale = nullptr;
   p.dec_group = 0;
+  p.ws_rows = kDenseBM;
   return VEA_OK;
 }
 
@@ -280,6 +281,12 @@ int decode_split(int units, int max_seqlen_k, int head_dim, int* nsplit) {
   return VEA_OK;
 }
 
+// Bytes of one decode split chunk: the group's rows (rounded up to 4, which
+// keeps every chunk 16-byte aligned) x (d + 2) floats.
+size_t decode_chunk_bytes(int group, int head_dim) {
+  return (size_t)((group + 3) & ~3) * (head_dim + 2) * sizeof(float);
+}
+
 int decode_shape_status(int batch, int total_k, int max_seqlen_k, int num_heads_q, int num_heads_kv, int head_dim) {
   if (batch < 0 || total_k < 0 || max_seqlen_k < 0) return VEA_ESHAPE;
   if (num_heads_q <= 0 || num_heads_kv <= 0 || num_heads_q % num_heads_kv != 0) return VEA_ESHAPE;
@@ -300,7 +307,7 @@ int vea_attn_decode_workspace_size(int batch, int max_seqlen_k, int num_heads_q,
   int nsplit = 1;
   st = decode_split(batch * num_heads_kv, max_seqlen_k, head_dim, &nsplit);
   if (st != VEA_OK) return st;
-  if (nsplit > 1) *bytes = (size_t)batch * num_heads_kv * nsplit * dense_chunk_bytes(head_dim);
+  if (nsplit > 1) *bytes = (size_t)batch * num_heads_kv * nsplit * decode_chunk_bytes(num_heads_q / num_heads_kv, head_dim);
   return VEA_OK;
 }
 
@@ -359,6 +366,7 @@ int vea_attn_decode(const void* q, int64_t q_seq_stride, const void* k, int64_t 
   st = dense_layout(batch, num_heads_q / num_heads_kv, num_heads_kv, 0, p);
   if (st != VEA_OK) return st;
   p.dec_group = num_heads_q / num_heads_kv;
+  p.ws_rows = (p.dec_group + 3) & ~3;
   p.xcd_map = 0;
   p.scale = scale;
   p.block_table = block_table;
@@ -369,7 +377,8 @@ int vea_attn_decode(const void* q, int64_t q_seq_stride, const void* k, int64_t 
     st = decode_split(p.units, max_seqlen_k, head_dim, &nsplit);
     if (st != VEA_OK) return st;
     if (nsplit > 1) {
-      if (workspace_bytes < (size_t)p.units * nsplit * dense_chunk_bytes(head_dim)) return VEA_EWORKSPACE;
+      if (workspace_bytes < (size_t)p.units * nsplit * decode_chunk_bytes(p.dec_group, head_dim))
+        return VEA_EWORKSPACE;
       p.full_units = 0;
       p.nsplit = nsplit;
       p.ws = (float*)workspace;

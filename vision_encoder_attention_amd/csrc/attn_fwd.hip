@@ -558,7 +558,8 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
   if (split) {
     // partial result of this key range, per tile row: unnormalized O
     // (fp32), reference max m (log2 domain) and sum l
-    float* w = p.ws + (size_t)(blockIdx.x - p.full_units) * (C::BM * (D + 2));
+    const int wr = DECODE ? p.ws_rows : C::BM;          // rows per chunk
+    float* w = p.ws + (size_t)(blockIdx.x - p.full_units) * (wr * (D + 2));
     const int rl = wave * 32 + l32;                     // row within the tile
     if (DECODE && !qvalid) return;                      // decode: only the few real rows are merged
 #pragma unroll
@@ -568,8 +569,8 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
         *(floatx4*)(w + rl * D + 32 * nb + 8 * r4 + 4 * g2) =
             (floatx4){o[nb][4 * r4], o[nb][4 * r4 + 1], o[nb][4 * r4 + 2], o[nb][4 * r4 + 3]};
     if (g2 == 0) {
-      w[C::BM * D + rl] = m_used;
-      w[C::BM * D + C::BM + rl] = l_tot;
+      w[wr * D + rl] = m_used;
+      w[wr * D + wr + rl] = l_tot;
     }
     return;
   }
@@ -944,7 +945,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(DenseParams p) {
   const int rl = item / SL, sc = item - rl * SL;        // row within the tile, slice
   const int qi = tr.row0 + rl;
   if (rl >= kDenseBM || qi >= tr.row_end) return;
-  constexpr size_t CF = (size_t)kDenseBM * (D + 2);     // floats per chunk
+  const int wr = p.dec_group > 0 ? p.ws_rows : kDenseBM;  // rows per chunk
+  const size_t CF = (size_t)wr * (D + 2);               // floats per chunk
   const float* base = p.ws + (size_t)tu * NS * CF;
   // every chunk's m, l and 16 values loaded up front (one memory latency)
   float mi[NS], li[NS];
@@ -952,8 +954,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(DenseParams p) {
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
     const float* c = base + i * CF;
-    mi[i] = c[kDenseBM * D + rl];
-    li[i] = c[kDenseBM * D + kDenseBM + rl];
+    mi[i] = c[wr * D + rl];
+    li[i] = c[wr * D + wr + rl];
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) vi[i][q4] = ((const floatx4*)(c + rl * D + 16 * sc))[q4];
   }

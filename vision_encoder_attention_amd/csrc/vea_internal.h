@@ -59,6 +59,9 @@ struct DenseParams {
   // + dec_group - 1 of token b (q, out [batch, ...] with stride q/o_stride,
   // lse [Hq, batch]); hq then counts key/value heads and group is 1.
   int dec_group;
+  // Rows per split chunk in ws: kDenseBM, or for decode units dec_group
+  // rounded up to a multiple of 4 (only those rows are ever written).
+  int ws_rows;
 };
 
 struct RopeParams {
