@@ -204,7 +204,7 @@ def bench_decode(torch, steps, warmup):
 
     def run():
         vea.attn_decode(st.q, kc, vc, st.cu_k, c_scale, out, lse, block_table=btd, page_size=64,
-                        max_seqlen_k=max(lk), workspace=ws if nbytes else None)
+                        max_seqlen_k=max(lk), total_k=sum(lk), workspace=ws if nbytes else None)
 
     c_scale = case.scale
     warm_up(torch, run, max(1, warmup))
@@ -258,7 +258,7 @@ def bench_dense_paged(torch, st, steps, warmup, ps=64):
     def run():
         vea.attn_fwd_paged(st.q, kc, vc, btd, ps, st.cu_q, st.cu_k, c.causal, c.scale, st.out, st.lse,
                            piece_rows=c.piece_rows, max_seqlen_q=st.max_q, max_seqlen_k=st.max_k,
-                           workspace=st.ws)
+                           total_k=int(c.cu_seqlens_k[-1]), workspace=st.ws)
 
     warm_up(torch, run, max(1, warmup))
     tm = Timer(torch)

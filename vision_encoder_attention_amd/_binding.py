@@ -204,11 +204,13 @@ def attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, causal, scale, out, lse=None, 
 
 
 def attn_fwd_paged(q, k_cache, v_cache, block_table, page_size, cu_seqlens_q, cu_seqlens_k, causal, scale, out,
-                   lse=None, *, piece_rows=0, max_seqlen_q=None, max_seqlen_k=None, workspace="auto"):
+                   lse=None, *, piece_rows=0, max_seqlen_q=None, max_seqlen_k=None, total_k=None,
+                   workspace="auto"):
     """attn_fwd (bf16) over paged K/V caches (see vea_attn_fwd_paged):
     k_cache / v_cache [num_pages * page_size, Hkv, d] (token strides free),
     block_table int32 [batch, max_pages_per_seq]; cu_seqlens_k gives the key
-    lengths."""
+    lengths.  max_seqlen_* and total_k (the sum of the key lengths) default
+    to values read from cu_seqlens with a host copy (synchronising)."""
     lib = load_library()
     torch = _torch()
     qs, ks, vs, os_ = (_token_major(q, "q"), _token_major(k_cache, "k_cache"), _token_major(v_cache, "v_cache"),
@@ -234,7 +236,8 @@ def attn_fwd_paged(q, k_cache, v_cache, block_table, page_size, cu_seqlens_q, cu
         lk = (cu_seqlens_k[1:] - cu_seqlens_k[:-1]).max().item() if batch > 0 else 0
         max_seqlen_q = lq if max_seqlen_q is None else max_seqlen_q
         max_seqlen_k = lk if max_seqlen_k is None else max_seqlen_k
-    total_k = int(cu_seqlens_k[-1].item()) if batch > 0 else 0
+    if total_k is None:
+        total_k = int(cu_seqlens_k[-1].item()) if batch > 0 else 0
     with torch.cuda.device(q.device):
         if isinstance(workspace, str):
             if workspace != "auto":
@@ -263,11 +266,13 @@ def attn_decode_workspace_size(batch, max_seqlen_k, heads_q, heads_kv, head_dim)
 
 
 def attn_decode(q, k, v, cu_seqlens_k, scale, out, lse=None, *, block_table=None, page_size=0, max_seqlen_k=None,
-                workspace="auto"):
+                total_k=None, workspace="auto"):
     """One query token per sequence over its cached keys (see vea_attn_decode):
     q / out [batch, Hq, d] bf16; k / v packed [total_k, Hkv, d] by
     cu_seqlens_k, or, with block_table int32 [batch, max_pages_per_seq],
-    caches [num_pages * page_size, Hkv, d]; lse float32 [Hq, batch]."""
+    caches [num_pages * page_size, Hkv, d]; lse float32 [Hq, batch].
+    max_seqlen_k and total_k (the sum of the key lengths) default to values
+    read from cu_seqlens_k with a host copy (synchronising)."""
     lib = load_library()
     torch = _torch()
     qs, ks, vs, os_ = (_token_major(q, "q"), _token_major(k, "k"), _token_major(v, "v"), _token_major(out, "out"))
@@ -282,7 +287,8 @@ def attn_decode(q, k, v, cu_seqlens_k, scale, out, lse=None, *, block_table=None
         raise ValueError("lse must be contiguous float32 [Hq, batch]")
     if max_seqlen_k is None:
         max_seqlen_k = (cu_seqlens_k[1:] - cu_seqlens_k[:-1]).max().item() if batch > 0 else 0
-    total_k = int(cu_seqlens_k[-1].item()) if batch > 0 else 0
+    if total_k is None:
+        total_k = int(cu_seqlens_k[-1].item()) if batch > 0 else 0
     if block_table is not None:
         _int32_dev(block_table, "block_table")
         if block_table.dim() != 2 or not block_table.is_contiguous() or block_table.shape[0] != batch:
