@@ -181,7 +181,10 @@ int vea_attn_fwd_workspace_size(int dtype, int batch, int total_q, int total_k, 
  *                 [cu[b], cu[b+1]) (positions 0 .. len - 1 in the cache).
  *                 A sequence with no keys gets zeros and lse -inf.
  *   total_k       packed: rows of k/v (= cu[batch]); paged: the sum of the key
- *                 lengths.  max_seqlen_k bounds every key length.
+ *                 lengths (= cu[batch]).  Key offsets are clamped to total_k,
+ *                 so a total_k above the rows k/v hold reads past them: it
+ *                 is a contract violation (VEA_ERANGE under VEA_CHECK when
+ *                 cu[batch] != total_k).  max_seqlen_k bounds every key length.
  *   num_heads_q / num_heads_kv   a divisor; query head h reads key/value head
  *                 h / (num_heads_q / num_heads_kv); that ratio <= 128.
  *   head_dim      64 or 128.

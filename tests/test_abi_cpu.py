@@ -229,6 +229,22 @@ def test_attn_decode_validation(lib, kw, status):
         assert n.value == 0
 
 
+def test_decode_binding_packed_total_k():
+    """Packed K/V: the binding passes k's row count as total_k and rejects any
+    other value, and k/v of unequal lengths (the kernel bounds its key rows by
+    total_k, so a larger value would read past the buffers)."""
+    from vision_encoder_attention_amd._binding import packed_total_k
+    assert packed_total_k(100, 100) == 100
+    assert packed_total_k(100, 100, 100) == 100
+    assert packed_total_k(0, 0, None) == 0
+    with pytest.raises(ValueError):
+        packed_total_k(100, 100, 101)
+    with pytest.raises(ValueError):
+        packed_total_k(100, 100, 99)
+    with pytest.raises(ValueError):
+        packed_total_k(100, 99)
+
+
 def _paged(lib, **kw):
     a = dict(q=FAKE, kv=FAKE, pt=FAKE, ps=64, npg=41, idx=FAKE, r=3, h=128, nkv=2590, dqk=576, dv=512, k=64,
              scale=0.04, out=FAKE, lse=None)

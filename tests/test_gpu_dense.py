@@ -474,6 +474,20 @@ def test_attn_decode_full_size_sampled_sequences(torch):
     vea.attn_decode(st.q, st.k, st.v, st.cu_k, case.scale, out2, lse2)
     torch.cuda.synchronize()
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    # the sizes passed explicitly (no read-back of cu_seqlens_k), as the
+    # benchmark calls it: same bits; a packed total_k other than k's rows is
+    # rejected before any launch
+    out3 = torch.empty_like(out)
+    lse3 = torch.empty_like(lse)
+    vea.attn_decode(st.q, kc, vc, st.cu_k, case.scale, out3, lse3, block_table=torch.from_numpy(bt).cuda(),
+                    page_size=64, max_seqlen_k=int(lk.max()), total_k=int(lk.sum()))
+    vea.attn_decode(st.q, st.k, st.v, st.cu_k, case.scale, out2, lse2, max_seqlen_k=int(lk.max()),
+                    total_k=st.k.shape[0])
+    torch.cuda.synchronize()
+    assert torch.equal(out, out3) and torch.equal(lse, lse3)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    with pytest.raises(ValueError):
+        vea.attn_decode(st.q, st.k, st.v, st.cu_k, case.scale, out2, lse2, total_k=st.k.shape[0] + 64)
     rng = np.random.default_rng(681)
     seqs = np.unique(np.concatenate([[int(np.argmin(lk)), int(np.argmax(lk))], rng.integers(0, len(lk), 4)]))
     cu = np.asarray(case.cu_seqlens_k, np.int64)

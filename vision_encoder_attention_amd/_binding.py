@@ -255,6 +255,16 @@ def attn_fwd_paged(q, k_cache, v_cache, block_table, page_size, cu_seqlens_q, cu
     return out, lse
 
 
+def packed_total_k(k_rows: int, v_rows: int, total_k=None) -> int:
+    """total_k of a packed K/V pair: the kernel bounds every key row by it, so
+    it must be the number of rows k and v really hold."""
+    if v_rows != k_rows:
+        raise ValueError("packed k and v need the same number of rows (%d, %d)" % (k_rows, v_rows))
+    if total_k is not None and int(total_k) != k_rows:
+        raise ValueError("packed K/V: total_k (%d) must equal k.shape[0] (%d)" % (int(total_k), k_rows))
+    return int(k_rows)
+
+
 def attn_decode_workspace_size(batch, max_seqlen_k, heads_q, heads_kv, head_dim) -> int:
     """Workspace bytes vea_attn_decode uses for these sizes on the current
     device (0: no split)."""
@@ -271,8 +281,11 @@ def attn_decode(q, k, v, cu_seqlens_k, scale, out, lse=None, *, block_table=None
     q / out [batch, Hq, d] bf16; k / v packed [total_k, Hkv, d] by
     cu_seqlens_k, or, with block_table int32 [batch, max_pages_per_seq],
     caches [num_pages * page_size, Hkv, d]; lse float32 [Hq, batch].
-    max_seqlen_k and total_k (the sum of the key lengths) default to values
-    read from cu_seqlens_k with a host copy (synchronising)."""
+    max_seqlen_k defaults to the longest key length, read from cu_seqlens_k
+    with a host copy (synchronising).  total_k: for packed K/V it is
+    k.shape[0] (any other value is rejected); for paged caches it must be the
+    sum of the key lengths (cu_seqlens_k[-1]), read back from the device when
+    omitted."""
     lib = load_library()
     torch = _torch()
     qs, ks, vs, os_ = (_token_major(q, "q"), _token_major(k, "k"), _token_major(v, "v"), _token_major(out, "out"))
@@ -287,7 +300,9 @@ def attn_decode(q, k, v, cu_seqlens_k, scale, out, lse=None, *, block_table=None
         raise ValueError("lse must be contiguous float32 [Hq, batch]")
     if max_seqlen_k is None:
         max_seqlen_k = (cu_seqlens_k[1:] - cu_seqlens_k[:-1]).max().item() if batch > 0 else 0
-    if total_k is None:
+    if block_table is None:
+        total_k = packed_total_k(k.shape[0], v.shape[0], total_k)
+    elif total_k is None:
         total_k = int(cu_seqlens_k[-1].item()) if batch > 0 else 0
     if block_table is not None:
         _int32_dev(block_table, "block_table")

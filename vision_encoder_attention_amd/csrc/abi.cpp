@@ -345,7 +345,7 @@ int vea_attn_decode(const void* q, int64_t q_seq_stride, const void* k, int64_t 
     if (cu[0] != 0) return VEA_ERANGE;
     for (int b = 0; b < batch; ++b)
       if (cu[b + 1] < cu[b] || cu[b + 1] - cu[b] > max_seqlen_k) return VEA_ERANGE;
-    if (block_table == nullptr && cu[batch] != total_k) return VEA_ERANGE;
+    if (cu[batch] != total_k) return VEA_ERANGE;     // packed: the rows of k/v; paged: the key total
     if (block_table != nullptr) {
       std::vector<int32_t> bt;
       st = fetch_ints(block_table, (size_t)batch * max_pages_per_seq, s, bt);
