@@ -25,11 +25,17 @@ Sources:
   进一步探索, eq. (1)(2).
 
 The computation is organised per (sequence, head, block of query rows) only to
-bound memory; every row is evaluated by the definition above on its own.
+bound memory and to let independent units run on several host threads
+(``workers``); every row is evaluated by the definition above on its own.  A
+block of a causal sequence forms its logits only over the keys some row of
+the block may see (keys past the block's last allowed key are masked for every
+row, so leaving them out changes no value).
 """
 from __future__ import annotations
 
 import numpy as np
+
+from oracle.pool import run_units
 
 __all__ = ["attention", "attn_probs", "allowed_key_count", "kv_head", "attention_paged"]
 
@@ -79,7 +85,7 @@ def _rows_of_seq(rows_global: np.ndarray, cq: np.ndarray, b: int) -> np.ndarray:
 
 
 def attention(q, k, v, cu_seqlens_q, cu_seqlens_k, causal: bool, scale: float,
-              rows=None, heads=None, row_block: int = 512):
+              rows=None, heads=None, row_block: int = 512, workers: int = 1):
     """Plain float64 attention over a packed variable-length batch.
 
     Args:
@@ -92,7 +98,9 @@ def attention(q, k, v, cu_seqlens_q, cu_seqlens_k, causal: bool, scale: float,
       rows: optional 1-D array of global query rows to evaluate (others are
          left as NaN in ``out`` and ``lse``); None = all rows.
       heads: optional list of query heads to evaluate; None = all.
-      row_block: rows evaluated together (memory bound only).
+      row_block: rows evaluated together (memory bound only; long key ranges
+         use smaller blocks so one block's logits stay near 2^24 values).
+      workers: host threads evaluating (sequence, head, row block) units.
 
     Returns:
       out [total_q, Hq, d_v] float64, lse [Hq, total_q] float64 (natural log).
@@ -113,30 +121,37 @@ def attention(q, k, v, cu_seqlens_q, cu_seqlens_k, causal: bool, scale: float,
     out = np.full((total_q, hq, dv), fill, dtype=np.float64)
     lse = np.full((hq, total_q), fill, dtype=np.float64)
 
+    units = []
     for b in range(len(cq) - 1):
+        len_k = int(ck[b + 1] - ck[b])
+        sel = _rows_of_seq(all_rows, cq, b)
+        blk = max(16, min(row_block, (1 << 24) // max(len_k, 1)))
+        for h in head_list:
+            for s in range(0, sel.size, blk):
+                units.append((b, h, sel[s:s + blk]))
+
+    def unit(u):
+        b, h, r = u
         q0, k0 = int(cq[b]), int(ck[b])
         len_q, len_k = int(cq[b + 1] - cq[b]), int(ck[b + 1] - ck[b])
-        sel = _rows_of_seq(all_rows, cq, b)
-        if sel.size == 0:
-            continue
-        for h in head_list:
-            g = kv_head(h, hq, hkv)
-            kk = k[k0:k0 + len_k, g, :]          # [L_k, d]
-            vv = v[k0:k0 + len_k, g, :]          # [L_k, d_v]
-            for s in range(0, sel.size, row_block):
-                r = sel[s:s + row_block]
-                il = r - q0                          # local row indices
-                logits = scale * (q[r, h, :] @ kk.T)  # [n, L_k]
-                n_allowed = allowed_key_count(il, len_q, len_k, causal)
-                mask = np.arange(len_k)[None, :] < n_allowed[:, None]
-                o_blk = np.zeros((r.size, dv))
-                lse_blk = np.full(r.size, -np.inf)
-                has = n_allowed > 0
-                if has.any():
-                    e, m, l_sum = masked_softmax_stats(logits[has], mask[has])
-                    o_blk[has], lse_blk[has] = finish_rows(e, m, l_sum, vv)
-                out[r, h, :] = o_blk
-                lse[h, r] = lse_blk
+        g = kv_head(h, hq, hkv)
+        il = r - q0                                  # local row indices
+        n_allowed = allowed_key_count(il, len_q, len_k, causal)
+        nk = int(n_allowed.max()) if n_allowed.size else 0   # keys some row of the block sees
+        kk = k[k0:k0 + nk, g, :]                     # [nk, d]
+        vv = v[k0:k0 + nk, g, :]                     # [nk, d_v]
+        o_blk = np.zeros((r.size, dv))
+        lse_blk = np.full(r.size, -np.inf)
+        has = n_allowed > 0
+        if has.any():
+            logits = scale * (q[r[has], h, :] @ kk.T)        # [n, nk]
+            mask = np.arange(nk)[None, :] < n_allowed[has][:, None]
+            e, m, l_sum = masked_softmax_stats(logits, mask)
+            o_blk[has], lse_blk[has] = finish_rows(e, m, l_sum, vv)
+        out[r, h, :] = o_blk
+        lse[h, r] = lse_blk
+
+    run_units(unit, units, workers)
     return out, lse
 
 

@@ -21,14 +21,16 @@ from __future__ import annotations
 import numpy as np
 
 from oracle.paging import paged_rows
+from oracle.pool import run_units
 
 __all__ = ["sparse_mqa", "sparse_mqa_paged"]
 
 
-def sparse_mqa(q, kv_latent, topk_idx, d_v: int, scale: float, rows=None):
+def sparse_mqa(q, kv_latent, topk_idx, d_v: int, scale: float, rows=None, workers: int = 1):
     """q [R, H, d_qk], kv_latent [n_kv, d_qk], topk_idx int [R, k].
 
     rows: optional subset of query rows to evaluate (others NaN).
+    workers: host threads evaluating query rows (each row is independent).
     Returns out [R, H, d_v] float64 and lse [H, R] float64.
     """
     q = np.asarray(q, dtype=np.float64)
@@ -43,12 +45,13 @@ def sparse_mqa(q, kv_latent, topk_idx, d_v: int, scale: float, rows=None):
     fill = 0.0 if rows is None else np.nan
     out = np.full((n_rows, heads, d_v), fill)
     lse = np.full((heads, n_rows), fill)
-    for r in row_list:
+
+    def row(r):
         sel = idx[r][idx[r] >= 0]
         if sel.size == 0:
             out[r] = 0.0
             lse[:, r] = -np.inf
-            continue
+            return
         kr = kv[sel]                                  # gathered rows [n, d_qk]
         logits = float(scale) * (q[r] @ kr.T)         # [H, n]
         m = logits.max(axis=1)
@@ -56,6 +59,8 @@ def sparse_mqa(q, kv_latent, topk_idx, d_v: int, scale: float, rows=None):
         l_sum = e.sum(axis=1)
         out[r] = (e @ kr[:, :d_v]) / l_sum[:, None]
         lse[:, r] = m + np.log(l_sum)
+
+    run_units(row, row_list, workers)
     return out, lse
 
 

@@ -7,12 +7,18 @@ import sys
 
 import numpy as np
 
+from oracle.pool import host_cores
+
 # Tolerances (stated per output tensor):
 #   fp32 path: normwise max relative error  max|g - r| / max|r|  <= 1e-5
 #   bf16 path: max |g - r| <= 2e-2  and  cosine(g, r) >= 0.999
 F32_NORMWISE = 1e-5
 BF16_MAX_ABS = 2e-2
 BF16_MIN_COS = 0.999
+
+# Host threads for the oracle on full-size workloads (the GPU host's CPU share
+# is 16 cores).
+ORACLE_WORKERS = max(1, min(16, host_cores()))
 
 
 def log(msg):

@@ -152,6 +152,31 @@ def pin_brute_force(orc):
             assert np.allclose(l1[fin], l2[fin], rtol=0, atol=1e-14)
 
 
+def pin_blocks_and_workers(orc):
+    """Row blocks of 1..3 rows (each causal block bounds its own key range)
+    evaluated on several threads give the pure-Python result, and the same
+    bits as one block per sequence on one thread."""
+    lq, lk, hq, hkv = [7, 0, 5, 9], [9, 2, 5, 6], 4, 2
+    rng = _rng(230)
+    d, dv = 4, 3
+    q = rng.standard_normal((sum(lq), hq, d))
+    k = rng.standard_normal((sum(lk), hkv, d))
+    v = rng.standard_normal((sum(lk), hkv, dv))
+    for causal in (False, True):
+        o2, l2 = _brute(q, k, v, lq, lk, causal, 0.45)
+        fin = np.isfinite(l2)
+        ref = None
+        for blk, workers in ((1, 3), (2, 2), (3, 4), (512, 1)):
+            o1, l1 = orc.attention(q, k, v, _cu(lq), _cu(lk), causal, 0.45, row_block=blk, workers=workers)
+            assert np.allclose(o1, o2, rtol=0, atol=1e-14)
+            assert np.array_equal(fin, np.isfinite(l1))
+            assert np.allclose(l1[fin], l2[fin], rtol=0, atol=1e-14)
+            if blk == 1:
+                ref = (o1, l1)
+        o3, l3 = orc.attention(q, k, v, _cu(lq), _cu(lk), causal, 0.45, row_block=1, workers=1)
+        assert np.array_equal(o3, ref[0]) and np.array_equal(l3, ref[1])
+
+
 def pin_torch_sdpa(orc):
     """torch CPU float64 scaled_dot_product_attention with an explicit boolean
     mask (an independent implementation of the same definition), GQA via
@@ -328,7 +353,7 @@ def pin_attention_paged_roundtrip(orc):
     assert np.array_equal(o, want_o) and np.array_equal(l, want_l)
 
 
-DENSE_PINS = [pin_attention_paged_roundtrip, pin_zero_query_mean, pin_one_hot_select, pin_brute_force, pin_torch_sdpa, pin_online_merge,
+DENSE_PINS = [pin_blocks_and_workers, pin_attention_paged_roundtrip, pin_zero_query_mean, pin_one_hot_select, pin_brute_force, pin_torch_sdpa, pin_online_merge,
               pin_single_key_and_causal_edges, pin_packing_and_gqa, pin_probs, pin_row_subset]
 
 
@@ -705,6 +730,9 @@ def pin_sparse_permutation(orc):
     o1, l1 = orc.sparse_mqa(q, kv, idx, 8, 0.3)
     o2, l2 = orc.sparse_mqa(q, kv, W.permute_rows(idx.astype(np.int32), 9), 8, 0.3)
     assert np.allclose(o1, o2, rtol=0, atol=1e-14) and np.allclose(l1, l2, rtol=0, atol=1e-14)
+    # rows on several threads: the same bits
+    o3, l3 = orc.sparse_mqa(q, kv, idx, 8, 0.3, workers=3)
+    assert np.array_equal(o1, o3) and np.array_equal(l1, l3)
 
 
 def pin_sparse_brute(orc):

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.gpu_util import assert_bf16_close, assert_f32_close, log, metrics
+from tests.gpu_util import ORACLE_WORKERS, assert_bf16_close, assert_f32_close, log, metrics
 from vision_encoder_attention_amd import runner as R
 from vision_encoder_attention_amd import workloads as W
 
@@ -63,7 +63,7 @@ def _check_case(torch, case, piece_rows=None, rows=None):
         assert_bf16_close(_f64(st.k, "bf16"), k_ref, "rope k")
     q, k, v = _inputs64(case, st)
     o_ref, l_ref = oracle.attention(q, k, v, case.cu_seqlens_q, case.cu_seqlens_k, case.causal,
-                                    float(np.float32(case.scale)), rows=rows)
+                                    float(np.float32(case.scale)), rows=rows, workers=ORACLE_WORKERS)
     sel = slice(None) if rows is None else np.asarray(rows)
     check = assert_f32_close if case.dtype == "f32" else assert_bf16_close
     check(out[sel], o_ref[sel], "out")
@@ -72,7 +72,7 @@ def _check_case(torch, case, piece_rows=None, rows=None):
         # end to end from the fused projection, unrounded q/k (reported and gated alike)
         v64 = W.bf16_bits_to_f64(case.v_from_x())
         o_e2e, l_e2e = oracle.attention(q_ref, k_ref, v64, case.cu_seqlens_q, case.cu_seqlens_k, case.causal,
-                                        float(np.float32(case.scale)), rows=rows)
+                                        float(np.float32(case.scale)), rows=rows, workers=ORACLE_WORKERS)
         assert_bf16_close(out[sel], o_e2e[sel], "out (end to end)")
         assert_bf16_close(lse[:, sel], l_e2e[:, sel], "lse (end to end)")
     return st
@@ -225,38 +225,114 @@ def test_probability_piece_export(torch):
             assert np.abs(pg - p_ref).max() < 1e-4
 
 
-# ------------------------------------------- full-size workloads, sampled
+# ------------------------------------ full-size workloads, whole tensors
 
-def _sample_rows(case, per_seq=12, seed=7):
-    rng = np.random.default_rng(seed)
-    rows = []
-    cq = case.cu_seqlens_q
-    for b in range(case.batch):
-        lo, hi = int(cq[b]), int(cq[b + 1])
-        if hi <= lo:
-            continue
-        pick = set([lo, hi - 1, min(lo + 127, hi - 1), min(lo + 128, hi - 1)])
-        if case.piece_rows:
-            for p in range(lo + case.piece_rows, hi, case.piece_rows):
-                pick.update([p - 1, p])
-        pick.update(rng.integers(lo, hi, size=per_seq).tolist())
-        rows.extend(sorted(pick))
-    return np.array(sorted(set(rows)), dtype=np.int64)
+@pytest.fixture(scope="module")
+def full_run(torch):
+    """One GPU pass of a full-size workload in the benchmark's launch
+    configuration (qkv_rope, then attn_fwd with the workspace the call asks
+    for), kept on the host as float64, plus a second pass compared bitwise.
+    Shared by the tests below so that each oracle slice is its own test."""
+    cache = {}
+
+    def get(name):
+        if name not in cache:
+            case = W.full_case(name)
+            log("full-size GPU run: %s" % case.name)
+            st = R.stage_dense(case)
+            R.run_dense(st)
+            torch.cuda.synchronize()
+            o0, l0 = st.out.clone(), st.lse.clone()
+            R.run_dense(st)
+            torch.cuda.synchronize()
+            run = dict(case=case, repeat_bitwise=bool(torch.equal(st.out, o0) and torch.equal(st.lse, l0)),
+                       finite=bool(torch.isfinite(st.out.float()).all()),
+                       out=_f64(st.out, "bf16"), lse=st.lse.cpu().numpy().astype(np.float64),
+                       q=_f64(st.q, "bf16") if case.x_qkv is not None else None,
+                       k=_f64(st.k, "bf16") if case.x_qkv is not None else None,
+                       split=st.ws is not None, ref={})
+            del st, o0, l0
+            torch.cuda.empty_cache()
+            cache[name] = run
+        return cache[name]
+    return get
 
 
-@pytest.mark.parametrize("name", ["vision", "varlen_gqa", "long_causal"])
-def test_full_size_sampled(torch, name):
-    """Full-size workloads in the benchmark's launch configuration, checked
-    on sampled rows (piece boundaries, tile boundaries, first/last rows and
-    random rows) for every head, plus run-to-run bitwise equality."""
-    case = W.full_case(name)
-    rows = _sample_rows(case, per_seq=24 if case.batch == 1 else 6)
-    st = _check_case(torch, case, rows=rows)
-    o0, l0 = st.out.clone(), st.lse.clone()
-    R.run_dense(st)
-    torch.cuda.synchronize()
-    assert torch.equal(st.out, o0) and torch.equal(st.lse, l0)
-    assert bool(torch.isfinite(st.out.float()).all())
+def _attn_inputs(run):
+    """q, k, v as attn_fwd saw them (GPU-produced q and k for fused cases)."""
+    case = run["case"]
+    if case.x_qkv is not None:
+        return run["q"], run["k"], W.bf16_bits_to_f64(case.v_from_x())
+    return tuple(W.bf16_bits_to_f64(a) for a in (case.q, case.k, case.v))
+
+
+def _rope_and_attention(run, end_to_end=False, heads=None):
+    """Gate rope q / k (whole), and out / lse of ``heads`` (all: the whole
+    tensors) against the oracle run on the kernel's own q / k, or end to end
+    from x_qkv (unrounded q / k)."""
+    case = run["case"]
+    assert run["repeat_bitwise"] and run["finite"]
+    if case.x_qkv is not None and not end_to_end:
+        q_ref, k_ref = oracle.qkv_rope(W.bf16_bits_to_f64(case.x_qkv), case.positions, case.theta,
+                                       case.num_heads_q, case.num_heads_kv, case.head_dim)
+        assert_bf16_close(run["q"], q_ref, "rope q (whole)")
+        assert_bf16_close(run["k"], k_ref, "rope k (whole)")
+    if end_to_end:
+        q, k = oracle.qkv_rope(W.bf16_bits_to_f64(case.x_qkv), case.positions, case.theta,
+                               case.num_heads_q, case.num_heads_kv, case.head_dim)
+        v = W.bf16_bits_to_f64(case.v_from_x())
+    else:
+        q, k, v = _attn_inputs(run)
+    hs = list(range(case.num_heads_q)) if heads is None else list(heads)
+    o_ref, l_ref = oracle.attention(q, k, v, case.cu_seqlens_q, case.cu_seqlens_k, case.causal,
+                                    float(np.float32(case.scale)), heads=None if heads is None else hs,
+                                    workers=ORACLE_WORKERS)
+    tag = " (end to end)" if end_to_end else ""
+    part = "" if heads is None else " heads %d-%d" % (hs[0], hs[-1])
+    assert_bf16_close(run["out"][:, hs], o_ref[:, hs], "out%s%s" % (part, tag))
+    assert_bf16_close(run["lse"][hs], l_ref[hs], "lse%s%s" % (part, tag))
+    return o_ref, l_ref
+
+
+@pytest.mark.parametrize("name", ["vision", "varlen_gqa"])
+def test_full_size_whole_tensors(full_run, name):
+    """Full-size vision image and varlen GQA batch: every element of rope q,
+    rope k, out and lse against the oracle (attention on the kernel's own q
+    and k), run-to-run bitwise equality."""
+    _rope_and_attention(full_run(name))
+
+
+@pytest.mark.parametrize("name", ["vision", "varlen_gqa"])
+def test_full_size_whole_tensors_end_to_end(full_run, name):
+    """The same outputs against the oracle chain from the fused projection
+    output (q and k rotated in float64, never rounded)."""
+    _rope_and_attention(full_run(name), end_to_end=True)
+
+
+LONG_PARTS = 4
+
+
+@pytest.mark.parametrize("part", range(LONG_PARTS))
+def test_full_size_long_causal_whole(full_run, part):
+    """The 32768-token causal prefill (q x 4: peaked rows), every element of
+    out and lse: the oracle runs over a quarter of the heads per test (each
+    about a quarter minute on 16 host cores); the last part gates the whole
+    tensors from the four slices."""
+    run = full_run("long_causal")
+    hq = run["case"].num_heads_q
+    per = hq // LONG_PARTS
+    heads = range(part * per, (part + 1) * per)
+    o_ref, l_ref = _rope_and_attention(run, heads=heads)
+    run["ref"][part] = (list(heads), o_ref[:, list(heads)], l_ref[list(heads)])
+    if part == LONG_PARTS - 1:
+        assert sorted(run["ref"]) == list(range(LONG_PARTS)), "earlier parts did not run"
+        o_all = np.empty_like(run["out"])
+        l_all = np.empty_like(run["lse"])
+        for hs, o_p, l_p in run["ref"].values():
+            o_all[:, hs] = o_p
+            l_all[hs] = l_p
+        assert_bf16_close(run["out"], o_all, "out (whole tensor)")
+        assert_bf16_close(run["lse"], l_all, "lse (whole tensor)")
 
 
 # ------------------------- split of the last round of workgroups (workspace)

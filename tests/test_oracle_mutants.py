@@ -32,12 +32,14 @@ MUTANTS = [
      "return (e @ vv) / l_sum[:, None], np.log(l_sum)", "lse drops the row max"),
     ("attention", "return (e @ vv) / l_sum[:, None], m + np.log(l_sum)",
      "return (e @ vv), m + np.log(l_sum)", "output not normalised"),
-    ("attention", "logits = scale * (q[r, h, :] @ kk.T)", "logits = scale * scale * (q[r, h, :] @ kk.T)",
+    ("attention", "logits = scale * (q[r[has], h, :] @ kk.T)", "logits = scale * scale * (q[r[has], h, :] @ kk.T)",
      "scale applied twice"),
-    ("attention", "kk = k[k0:k0 + len_k, g, :]", "kk = k[q0:q0 + len_k, g, :]",
+    ("attention", "kk = k[k0:k0 + nk, g, :]", "kk = k[q0:q0 + nk, g, :]",
      "keys addressed with the query prefix offset"),
-    ("attention", "vv = v[k0:k0 + len_k, g, :]", "vv = v[k0:k0 + len_k, h % v.shape[1], :]",
+    ("attention", "vv = v[k0:k0 + nk, g, :]", "vv = v[k0:k0 + nk, h % v.shape[1], :]",
      "values from the wrong head"),
+    ("attention", "nk = int(n_allowed.max()) if n_allowed.size else 0",
+     "nk = int(n_allowed.min()) if n_allowed.size else 0", "a causal block's keys cut to its first row's"),
     ("attention", "e = np.where(mask, np.exp(lg - m[:, None]), 0.0)",
      "e = np.exp(np.where(mask, logits, 0.0) - m[:, None])", "masked keys given logit 0 instead of excluded"),
     ("attention", "m = lg.max(axis=1)                                   # pass 1: row max",
