@@ -8,10 +8,14 @@ tensors already resident in device memory.  Prints ONE JSON line on stdout;
 details go to stderr.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
+    python bench.py --only WORKLOAD      (one workload, its JSON on stderr)
 
-The other workloads (varlen causal GQA prefill, 32K causal prefill, top-k
-sparse MQA) are timed too and reported under "workloads" in the same line.
-Kernel times come from HIP events recorded on the stream the kernels run on.
+The other workloads (the fp32 single-head case, the varlen causal GQA
+prefill, the 32K causal prefill, top-k sparse MQA, and the next-step kernels)
+are timed too and reported under "workloads" in the same line, each with a
+roofline object.  Kernel times come from HIP events recorded on the stream the
+kernels run on (torch's current stream); mean, median and min over the timed
+launches are reported.
 """
 from __future__ import annotations
 
@@ -27,6 +31,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 MFMA (twice the bf16 rate)
+PEAK_FP32_TFLOPS = 157.3       # MI355X dense fp32 (matrix and vector)
+EVICT_BYTES = 1 << 30          # a 1 GiB fill evicts L2 (4 MB per XCD) and the 256 MB MALL
 
 
 def err(*a):
@@ -93,7 +99,8 @@ def warm_up(torch, fn, steps):
 
 
 class Timer:
-    """Per-launch HIP event pairs on torch's current stream."""
+    """Per-launch HIP event pairs on torch's current stream (the stream the
+    binding launches the kernels on)."""
 
     def __init__(self, torch):
         self.torch = torch
@@ -107,12 +114,91 @@ class Timer:
         e1.record()
         self.pairs.setdefault(name, []).append((e0, e1))
 
+    def times(self, name):
+        return [a.elapsed_time(b) for a, b in self.pairs[name]]
+
     def ms(self, name):
-        v = [a.elapsed_time(b) for a, b in self.pairs[name]]
+        v = self.times(name)
         return sum(v) / len(v), min(v)
+
+    def stats(self, name):
+        """mean, median and min in ms."""
+        import statistics
+        v = self.times(name)
+        return {"mean": sum(v) / len(v), "median": statistics.median(v), "min": min(v)}
+
+
+def roofline(bound, kernel, achieved, peak, unit, traffic_profile=None, algorithmic_bytes=None, **extra):
+    """The roofline object of one kernel launch: achieved against the
+    published peak, and the counter-measured HBM bytes per launch from a
+    committed summary (null when absent or stale)."""
+    r = {"bound": bound, "kernel": kernel, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4),
+         "traffic": committed_traffic(traffic_profile) if traffic_profile else None}
+    if algorithmic_bytes is not None:
+        r["algorithmic_bytes"] = algorithmic_bytes
+    r.update(extra)
+    return r
+
+
+def rope_cold(torch, st, steps):
+    """qkv_rope with L2 and MALL evicted before every launch (a 1 GiB fill,
+    untimed): its inputs then come from HBM, as they would straight after
+    the projection of a batch larger than the caches."""
+    from vision_encoder_attention_amd import runner as R
+    scratch = torch.empty(EVICT_BYTES, dtype=torch.uint8, device="cuda")
+    tm = Timer(torch)
+    for _ in range(steps):
+        scratch.fill_(1)
+        tm.run("rope", lambda: R.run_rope(st))
+    torch.cuda.synchronize()
+    del scratch
+    return tm.stats("rope")
+
+
+def _r(x, n=4):
+    return round(x, n)
+
+
+def dense_entry(torch, wname, case, st, tm, steps, with_rope):
+    """Workload entry of a dense bf16 case: attn_fwd times and roofline, and
+    qkv_rope warm (inputs resident in L2 / MALL from the step before) and
+    cold (L2 and MALL evicted before each launch)."""
+    fl = dense_flops(case)
+    a = tm.stats("attn_fwd")
+    tflops = fl / a["mean"] / 1e9
+    d, causal = case.head_dim, case.causal
+    kname = "attn_fwd_bf16_kernel<%d,%s,false,false>" % (d, "true" if causal else "false")
+    split = st.ws is not None
+    if split:
+        kname += " + attn_merge_kernel<%d>" % d
+    prof = "attn_fwd_bf16_d%d%s_%s_counters.txt" % (d, "_causal" if causal else "", wname)
+    ent = {"attn_fwd_ms": _r(a["mean"]), "attn_fwd_median_ms": _r(a["median"]), "attn_fwd_min_ms": _r(a["min"]),
+           "attn_tflops": round(tflops, 2), "attn_frac_bf16_peak": _r(tflops / PEAK_BF16_TFLOPS),
+           "flops": fl, "tokens": case.total_q, "causal": causal,
+           "heads": [case.num_heads_q, case.num_heads_kv], "head_dim": d, "piece_rows": case.piece_rows,
+           "last_round_split": split,
+           "roofline": roofline("mfma", kname, tflops, PEAK_BF16_TFLOPS, "TFLOP/s", prof,
+                                4 * case.total_q * case.num_heads_q * d * 2)}
+    if with_rope:
+        rb = rope_bytes(case)
+        r = tm.stats("qkv_rope")
+        c = rope_cold(torch, st, steps)
+        rprof = "qkv_rope_%s_counters.txt" % wname
+        ent.update({"qkv_rope_ms": _r(r["mean"], 5), "qkv_rope_median_ms": _r(r["median"], 5),
+                    "qkv_rope_min_ms": _r(r["min"], 5),
+                    "qkv_rope_warm_gbs": round(rb / r["mean"] / 1e6, 1),
+                    "qkv_rope_cold_ms": _r(c["mean"], 5), "qkv_rope_cold_median_ms": _r(c["median"], 5),
+                    "qkv_rope_cold_min_ms": _r(c["min"], 5),
+                    "qkv_rope_bytes": rb,
+                    "qkv_rope_roofline": roofline("hbm", "qkv_rope_kernel (L2 and MALL evicted before each launch)",
+                                                  rb / c["mean"] / 1e6, PEAK_HBM_GBS, "GB/s", rprof, rb)})
+    return ent
 
 
 def bench_vision(torch, args):
+    """The headline step: qkv_rope then attn_fwd over the vision image, K
+    steps after the warm-up; per-kernel events and per-step events."""
     from vision_encoder_attention_amd import runner as R
     from vision_encoder_attention_amd import workloads as W
     case = W.vision()
@@ -122,60 +208,95 @@ def bench_vision(torch, args):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
         tm.run("qkv_rope", lambda: R.run_rope(st))
         tm.run("attn_fwd", lambda: R.run_attn(st))
+        e1.record()
+        tm.pairs.setdefault("step", []).append((e0, e1))
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    return case, tm, wall_ms
+    ent = dense_entry(torch, "vision", case, st, tm, max(5, min(args.steps, 20)), with_rope=True)
+    del st
+    torch.cuda.empty_cache()
+    return case, tm, wall_ms, ent
 
 
-def bench_other(torch, steps, warmup, only=None):
-    """The remaining workloads: one timed kernel family each, after `warmup`
-    untimed passes of the same work (the clock ramps up over the first
-    launches)."""
+def bench_single_head(torch, steps, warmup):
+    """The fp32 single-head case (N = 256, d 64, 4 pieces of 64): a
+    latency-bound launch of 16 workgroups; TFLOP/s against the fp32 peak as
+    context."""
+    from vision_encoder_attention_amd import runner as R
+    from vision_encoder_attention_amd import workloads as W
+    case = W.single_head_f32()
+    st = R.stage_dense(case)
+    warm_up(torch, lambda: R.run_attn(st), max(1, warmup))
+    tm = Timer(torch)
+    for _ in range(steps):
+        tm.run("attn_fwd", lambda: R.run_attn(st))
+    torch.cuda.synchronize()
+    fl = dense_flops(case)
+    a = tm.stats("attn_fwd")
+    tf = fl / a["mean"] / 1e9
+    return {case.name: {"attn_fwd_us": round(a["mean"] * 1e3, 2), "attn_fwd_median_us": round(a["median"] * 1e3, 2),
+                        "attn_fwd_min_us": round(a["min"] * 1e3, 2), "attn_tflops": round(tf, 4),
+                        "flops": fl, "piece_rows": case.piece_rows,
+                        "roofline": roofline("mfma", "attn_fwd_f32_kernel<64,false>", tf, PEAK_FP32_TFLOPS, "TFLOP/s",
+                                             note="latency-bound: 8 workgroups of 128 rows for 1.7e7 flops")}}
+
+
+def bench_dense(torch, name, steps, warmup):
+    """varlen_gqa or long_causal: qkv_rope (varlen) and attn_fwd, each launch
+    timed; the varlen batch also over 64-row pages."""
     from vision_encoder_attention_amd import runner as R
     from vision_encoder_attention_amd import workloads as W
     res = {}
-    for name in ("varlen_gqa", "long_causal"):
-        if only is not None and name != only:
-            continue
-        case = W.full_case(name)
-        st = R.stage_dense(case)
-        warm_up(torch, lambda: R.run_dense(st), max(1, warmup))
-        tm = Timer(torch)
-        for _ in range(steps):
-            if case.x_qkv is not None:
-                tm.run("qkv_rope", lambda: R.run_rope(st))
-            tm.run("attn_fwd", lambda: R.run_attn(st))
-        torch.cuda.synchronize()
-        fl = dense_flops(case)
-        a_ms, a_min = tm.ms("attn_fwd")
-        ent = {"attn_fwd_ms": round(a_ms, 4), "attn_fwd_min_ms": round(a_min, 4),
-               "attn_tflops": round(fl / a_ms / 1e9, 2), "attn_frac_bf16_peak": round(fl / a_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
-               "flops": fl, "tokens": case.total_q, "causal": case.causal,
-               "heads": [case.num_heads_q, case.num_heads_kv], "head_dim": case.head_dim}
+    case = W.full_case(name)
+    st = R.stage_dense(case)
+    warm_up(torch, lambda: R.run_dense(st), max(1, warmup))
+    tm = Timer(torch)
+    for _ in range(steps):
         if case.x_qkv is not None:
-            r_ms, _ = tm.ms("qkv_rope")
-            rb = rope_bytes(case)
-            ent.update({"qkv_rope_ms": round(r_ms, 4), "qkv_rope_gbs": round(rb / r_ms / 1e6, 1),
-                        "qkv_rope_frac_hbm": round(rb / r_ms / 1e6 / PEAK_HBM_GBS, 4)})
-        res[case.name] = ent
-        if name == "varlen_gqa":
-            p_ms, p_min = bench_dense_paged(torch, st, steps, warmup)
-            res[case.name + "_paged64"] = {"attn_fwd_ms": round(p_ms, 4), "attn_fwd_min_ms": round(p_min, 4),
-                                           "attn_frac_bf16_peak": round(fl / p_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
-                                           "page_size": 64}
-        del st
-        torch.cuda.empty_cache()
-    if only in (None, "sparse_mqa"):
+            tm.run("qkv_rope", lambda: R.run_rope(st))
+        tm.run("attn_fwd", lambda: R.run_attn(st))
+    torch.cuda.synchronize()
+    res[case.name] = dense_entry(torch, name, case, st, tm, steps, with_rope=case.x_qkv is not None)
+    if name == "varlen_gqa":
+        fl = dense_flops(case)
+        p = bench_dense_paged(torch, st, steps, warmup)
+        res[case.name + "_paged64"] = {"attn_fwd_ms": _r(p["mean"]), "attn_fwd_median_ms": _r(p["median"]),
+                                       "attn_fwd_min_ms": _r(p["min"]),
+                                       "attn_frac_bf16_peak": _r(fl / p["mean"] / 1e9 / PEAK_BF16_TFLOPS),
+                                       "page_size": 64}
+    del st
+    torch.cuda.empty_cache()
+    return res
+
+
+WORKLOADS = ("single_head_f32", "vision", "varlen_gqa", "long_causal", "sparse_mqa", "indexer", "qkv_proj", "fp8",
+             "decode")
+
+
+def bench_other(torch, steps, warmup, only=None):
+    """The workloads other than the headline step, each after its own warm-up
+    (the clock ramps up over the first launches)."""
+    res = {}
+    want = (lambda n: only is None or n == only)
+    if want("single_head_f32"):
+        res.update(bench_single_head(torch, steps, warmup))
+    for name in ("varlen_gqa", "long_causal"):
+        if want(name):
+            res.update(bench_dense(torch, name, steps, warmup))
+    if want("sparse_mqa"):
         res.update(bench_sparse(torch, steps, warmup))
-    if only in (None, "indexer"):
+    if want("indexer"):
         res.update(bench_indexer(torch, steps, warmup))
-    if only in (None, "qkv_proj"):
+    if want("qkv_proj"):
         res.update(bench_proj(torch, steps, warmup))
-    if only in (None, "fp8"):
+    if want("fp8"):
         res.update(bench_fp8(torch, steps, warmup))
-    if only in (None, "decode"):
+    if want("decode"):
         res.update(bench_decode(torch, steps, warmup))
     return res
 
@@ -195,7 +316,7 @@ def bench_decode(torch, steps, warmup):
     case = W.decode()
     lk = [int(x) for x in np.diff(np.asarray(case.cu_seqlens_k, np.int64))]
     st = R.stage_dense(case)
-    prefill_ms, _ = bench_dense_paged(torch, st, steps, warmup)
+    prefill_ms = bench_dense_paged(torch, st, steps, warmup)["mean"]
     kc, vc, btd = paged_copy(torch, st, 64)
     out = torch.empty_like(st.q)
     lse = torch.empty((32, 64), dtype=torch.float32, device="cuda")
@@ -212,12 +333,16 @@ def bench_decode(torch, steps, warmup):
     for _ in range(steps):
         tm.run("decode", run)
     torch.cuda.synchronize()
-    ms, ms_min = tm.ms("decode")
+    t = tm.stats("decode")
     kv_bytes = float(sum(lk)) * 8 * 128 * 2 * 2
     name = case.name + "_paged64"
-    res = {name: {"attn_decode_ms": round(ms, 4), "attn_decode_min_ms": round(ms_min, 4), "kv_bytes": kv_bytes,
-                  "kv_gbs": round(kv_bytes / ms / 1e6, 1), "kv_frac_hbm": round(kv_bytes / ms / 1e6 / PEAK_HBM_GBS, 4),
-                  "workspace_bytes": nbytes, "prefill_kernel_ms": round(prefill_ms, 4)}}
+    res = {name: {"attn_decode_ms": _r(t["mean"]), "attn_decode_median_ms": _r(t["median"]),
+                  "attn_decode_min_ms": _r(t["min"]), "kv_bytes": kv_bytes,
+                  "kv_gbs": round(kv_bytes / t["mean"] / 1e6, 1),
+                  "kv_frac_hbm": _r(kv_bytes / t["mean"] / 1e6 / PEAK_HBM_GBS),
+                  "workspace_bytes": nbytes, "prefill_kernel_ms": _r(prefill_ms),
+                  "roofline": roofline("hbm", "attn_fwd_bf16_kernel<128,false,true,true> + attn_merge_kernel<128>",
+                                       kv_bytes / t["mean"] / 1e6, PEAK_HBM_GBS, "GB/s", None, kv_bytes)}}
     del st, kc, vc, ws
     torch.cuda.empty_cache()
     return res
@@ -265,7 +390,7 @@ def bench_dense_paged(torch, st, steps, warmup, ps=64):
     for _ in range(steps):
         tm.run("paged", run)
     torch.cuda.synchronize()
-    return tm.ms("paged")
+    return tm.stats("paged")
 
 
 def bench_sparse(torch, steps, warmup):
@@ -280,7 +405,7 @@ def bench_sparse(torch, steps, warmup):
     res = {}
     case = W.full_case("sparse_mqa")
     st = R.stage_sparse(case)
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    scratch = torch.empty(EVICT_BYTES, dtype=torch.uint8, device="cuda")
     by, fl = sparse_bytes(case), sparse_flops(case)
 
     def timed(name, fn):
@@ -293,7 +418,7 @@ def bench_sparse(torch, steps, warmup):
             scratch.fill_(1)
             tm.run(name, fn)
         torch.cuda.synchronize()
-        return tm.ms(name)
+        return tm.stats(name)
 
     ps = 64
     rng = np.random.default_rng(64)
@@ -304,17 +429,23 @@ def bench_sparse(torch, steps, warmup):
     cache[table[j // ps] * ps + j % ps] = case.kv_latent
     kvc = R.bits_to_tensor(cache, "cuda")
     pt = torch.from_numpy(table).cuda()
-    p_ms, p_min = timed("paged", lambda: vea.sparse_mqa_paged_fwd(st.q, kvc, pt, ps, case.kv_latent.shape[0], st.idx,
-                                                                  case.k, case.scale, st.out, st.lse,
-                                                                  workspace=st.ws))
-    s_ms, s_min = timed("sparse", lambda: R.run_sparse(st))
-    res[case.name] = {"sparse_mqa_ms": round(s_ms, 4), "sparse_mqa_min_ms": round(s_min, 4),
-                      "gbs": round(by / s_ms / 1e6, 1), "frac_hbm": round(by / s_ms / 1e6 / PEAK_HBM_GBS, 4),
-                      "tflops": round(fl / s_ms / 1e9, 2), "bytes": by, "flops": fl,
-                      "hbm_traffic_counter_bytes": committed_traffic("sparse_mqa_hbm_counters.txt")}
-    res[case.name + "_paged64"] = {"sparse_mqa_ms": round(p_ms, 4), "sparse_mqa_min_ms": round(p_min, 4),
-                                   "gbs": round(by / p_ms / 1e6, 1), "frac_hbm": round(by / p_ms / 1e6 / PEAK_HBM_GBS, 4),
-                                   "page_size": ps}
+    p = timed("paged", lambda: vea.sparse_mqa_paged_fwd(st.q, kvc, pt, ps, case.kv_latent.shape[0], st.idx,
+                                                         case.k, case.scale, st.out, st.lse, workspace=st.ws))
+    t = timed("sparse", lambda: R.run_sparse(st))
+    gbs = by / t["mean"] / 1e6
+    res[case.name] = {"sparse_mqa_ms": _r(t["mean"]), "sparse_mqa_median_ms": _r(t["median"]),
+                      "sparse_mqa_min_ms": _r(t["min"]), "gbs": round(gbs, 1),
+                      "frac_hbm": _r(gbs / PEAK_HBM_GBS), "tflops": round(fl / t["mean"] / 1e9, 2),
+                      "frac_bf16_peak": _r(fl / t["mean"] / 1e9 / PEAK_BF16_TFLOPS), "bytes": by, "flops": fl,
+                      "roofline": roofline("hbm", "sparse_mqa_kernel<576,512,2048> + sparse_merge_kernel", gbs,
+                                           PEAK_HBM_GBS, "GB/s", "sparse_mqa_counters.txt", by,
+                                           mfma_frac=_r(fl / t["mean"] / 1e9 / PEAK_BF16_TFLOPS))}
+    tr = res[case.name]["roofline"]["traffic"]
+    if tr:
+        res[case.name]["hbm_counter_gbs"] = round(tr / t["mean"] / 1e6, 1)
+    res[case.name + "_paged64"] = {"sparse_mqa_ms": _r(p["mean"]), "sparse_mqa_median_ms": _r(p["median"]),
+                                   "sparse_mqa_min_ms": _r(p["min"]), "gbs": round(by / p["mean"] / 1e6, 1),
+                                   "frac_hbm": _r(by / p["mean"] / 1e6 / PEAK_HBM_GBS), "page_size": ps}
     del scratch, st, kvc
     torch.cuda.empty_cache()
     return res
@@ -334,10 +465,11 @@ def bench_indexer(torch, steps, warmup):
     for _ in range(steps):
         tm.run("topk", lambda: vea.topk_indices(x, ic.k, out, None, lens))
     torch.cuda.synchronize()
-    t_ms, t_min = tm.ms("topk")
+    t = tm.stats("topk")
     by = indexer_bytes(ic)
-    res[ic.name] = {"topk_ms": round(t_ms, 4), "topk_min_ms": round(t_min, 4), "gbs": round(by / t_ms / 1e6, 1),
-                    "frac_hbm": round(by / t_ms / 1e6 / PEAK_HBM_GBS, 4), "bytes": by,
+    res[ic.name] = {"topk_ms": _r(t["mean"]), "topk_median_ms": _r(t["median"]), "topk_min_ms": _r(t["min"]),
+                    "gbs": round(by / t["mean"] / 1e6, 1), "frac_hbm": _r(by / t["mean"] / 1e6 / PEAK_HBM_GBS),
+                    "bytes": by,
                     "note": "one workgroup per row sorts the row's keys in LDS; latency-bound, not HBM-bound"}
     return res
 
@@ -378,14 +510,17 @@ def bench_fp8(torch, steps, warmup):
             tm.run("bf16", lambda: R.run_attn(st))
         torch.cuda.synchronize()
         fl = dense_flops(case)
-        f_ms, f_min = tm.ms("fp8")
+        f = tm.stats("fp8")
         b_ms, _ = tm.ms("bf16")
         qn_ms, _ = tm.ms("quant")
-        res[case.name + "_fp8"] = {"attn_fwd_fp8_ms": round(f_ms, 4), "attn_fwd_fp8_min_ms": round(f_min, 4),
-                                   "tflops": round(fl / f_ms / 1e9, 2),
-                                   "frac_fp8_peak": round(fl / f_ms / 1e9 / PEAK_FP8_TFLOPS, 4),
-                                   "bf16_attn_fwd_ms": round(b_ms, 4), "quantize_qkv_ms": round(qn_ms, 4),
-                                   "flops": fl}
+        tf = fl / f["mean"] / 1e9
+        res[case.name + "_fp8"] = {"attn_fwd_fp8_ms": _r(f["mean"]), "attn_fwd_fp8_median_ms": _r(f["median"]),
+                                   "attn_fwd_fp8_min_ms": _r(f["min"]), "tflops": round(tf, 2),
+                                   "frac_fp8_peak": _r(tf / PEAK_FP8_TFLOPS),
+                                   "bf16_attn_fwd_ms": _r(b_ms), "quantize_qkv_ms": _r(qn_ms), "flops": fl,
+                                   "roofline": roofline("mfma", "attn_fwd_fp8_kernel<%d,%s>" % (
+                                       case.head_dim, "true" if case.causal else "false"), tf, PEAK_FP8_TFLOPS,
+                                       "TFLOP/s")}
         del st, q, k, v, q8, k8, v8, out, lse
         torch.cuda.empty_cache()
     return res
@@ -421,42 +556,18 @@ def bench_proj(torch, steps, warmup):
             tm.run("unfused", unfused)
         torch.cuda.synchronize()
         fl = 2.0 * t * hid * n
-        p_ms, p_min = tm.ms("proj")
+        pr = tm.stats("proj")
         u_ms, _ = tm.ms("unfused")
         tb_ms, _ = tm.ms("table")
-        res[case.name] = {"qkv_proj_rope_ms": round(p_ms, 4), "qkv_proj_rope_min_ms": round(p_min, 4),
-                          "tflops": round(fl / p_ms / 1e9, 2), "frac_bf16_peak": round(fl / p_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
-                          "flops": fl, "rope_table_ms": round(tb_ms, 4),
-                          "unfused_matmul_plus_qkv_rope_ms": round(u_ms, 4)}
+        tf = fl / pr["mean"] / 1e9
+        res[case.name] = {"qkv_proj_rope_ms": _r(pr["mean"]), "qkv_proj_rope_median_ms": _r(pr["median"]),
+                          "qkv_proj_rope_min_ms": _r(pr["min"]), "tflops": round(tf, 2),
+                          "frac_bf16_peak": _r(tf / PEAK_BF16_TFLOPS), "flops": fl, "rope_table_ms": _r(tb_ms),
+                          "unfused_matmul_plus_qkv_rope_ms": _r(u_ms),
+                          "roofline": roofline("mfma", "qkv_proj_kernel", tf, PEAK_BF16_TFLOPS, "TFLOP/s")}
         del st, y, qr, kr
         torch.cuda.empty_cache()
     return res
-
-
-def source_digest(paths) -> str:
-    """sha256 over the sources a kernel is built from (identifies the kernel
-    build a committed counter summary belongs to).  "file#Name" stands for
-    the part of a shared header that kernel uses: the text of its parameter
-    struct Name plus the header's typedef and constexpr lines, so that
-    additions for other kernels do not invalidate the summary."""
-    import hashlib
-    import re
-    h = hashlib.sha256()
-    for pth in paths:
-        name = None
-        if "#" in pth:
-            pth, name = pth.split("#", 1)
-        with open(os.path.join(ROOT, pth), "rb") as f:
-            data = f.read()
-        if name is not None:
-            text = data.decode()
-            m = re.search(r"^struct %s \{.*?^\};" % re.escape(name), text, re.S | re.M)
-            if m is None:
-                raise ValueError("struct %s not found in %s" % (name, pth))
-            keep = [ln for ln in text.splitlines() if ln.startswith(("typedef", "constexpr"))]
-            data = (m.group(0) + "\n" + "\n".join(keep)).encode()
-        h.update(data)
-    return h.hexdigest()[:16]
 
 
 def committed_traffic(profile: str):
@@ -472,36 +583,116 @@ def committed_traffic(profile: str):
         for line in f:
             if line.startswith("RESULT "):
                 rec = json.loads(line[len("RESULT "):])
+    from vision_encoder_attention_amd.profsum import source_digest
     if not rec or rec.get("source_digest") != source_digest(rec["sources"]):
         return None
     return rec["hbm_bytes_per_launch"]
 
 
-def cpu_baseline():
-    """The float64 oracle timed on the same workload: RoPE of all 8547 tokens
-    and attention of all 16 heads over all rows (about 10 s of host work)."""
+def host_info(workers):
+    """The host facts reported with the oracle timings."""
+    import platform
+    import numpy as np
+    model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                blas = "%s %s (%s)" % (i.get("internal_api"), i.get("version"), i.get("architecture"))
+                break
+    except Exception:
+        pass
+    from oracle.pool import host_cores
+    return {"cores_visible": host_cores(), "oracle_threads": workers, "cpu_model": model,
+            "numpy": np.__version__, "blas": blas}
+
+
+def cpu_oracle(workers):
+    """The float64 oracle timed on the host cores, per workload, on the same
+    seeded inputs the GPU ran: whole workloads where they take seconds, a
+    fraction of the heads (1/8) for the varlen batch and the 32K prefill, so
+    the whole run stays within about 10-30 s of host time.  Independent
+    (sequence, head, row block) units run on ``workers`` threads, BLAS on one
+    thread per worker.  Returns (headline baseline object, per-workload
+    timings)."""
     import numpy as np
     import oracle
     from vision_encoder_attention_amd import workloads as W
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        cores = 1
-    case = W.vision()
-    heads = list(range(case.num_heads_q))
+    per = {}
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    # fp32 single head: the whole case, repeated for a stable figure
+    c = W.single_head_f32()
+    n_rep = 20
+    dt = timed(lambda: [oracle.attention(c.q, c.k, c.v, c.cu_seqlens_q, c.cu_seqlens_k, False,
+                                         float(np.float32(c.scale))) for _ in range(n_rep)]) / n_rep
+    per[c.name] = {"oracle_ms": round(dt * 1e3, 3), "sample": "whole case", "gflops": round(dense_flops(c) / dt / 1e9, 2)}
+
+    # vision: the whole step (RoPE of every token, attention of every head)
+    c = W.vision()
+    x64, v64 = W.bf16_bits_to_f64(c.x_qkv), W.bf16_bits_to_f64(c.v_from_x())
+    box = {}
+
+    def vision_step():
+        q, k = oracle.qkv_rope(x64, c.positions, c.theta, c.num_heads_q, c.num_heads_kv, c.head_dim)
+        box["t_rope"] = time.perf_counter()
+        oracle.attention(q, k, v64, c.cu_seqlens_q, c.cu_seqlens_k, False, float(np.float32(c.scale)),
+                         workers=workers)
     t0 = time.perf_counter()
-    q, k = oracle.qkv_rope(W.bf16_bits_to_f64(case.x_qkv), case.positions, case.theta, case.num_heads_q,
-                           case.num_heads_kv, case.head_dim)
-    oracle.attention(q, k, W.bf16_bits_to_f64(case.v_from_x()), case.cu_seqlens_q, case.cu_seqlens_k, False,
-                     float(np.float32(case.scale)), heads=heads)
-    dt = time.perf_counter() - t0
-    fl = dense_flops(case) * len(heads) / case.num_heads_q
-    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": "float64 oracle on the whole vision step: qkv_rope of all 8547 tokens + attention of all "
-                      "16 heads x 8547 rows (%.3g attention flops in %.1f s; numpy matmul on %d BLAS threads, "
-                      "elementwise ops on 1)"
-                      % (fl, dt, cores)}
+    vision_s = timed(vision_step)
+    rope_s = box["t_rope"] - t0
+    vfl = dense_flops(c)
+    per[c.name] = {"oracle_s": round(vision_s, 3), "qkv_rope_s": round(rope_s, 3), "sample": "whole step",
+                   "gflops": round(vfl / (vision_s - rope_s) / 1e9, 2)}
+    headline = {"value": round(vfl / vision_s / 1e12, 6), "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+                "sample": "float64 oracle on the whole vision step: qkv_rope of all 8547 tokens + attention of all "
+                          "16 heads x 8547 rows (%.4g attention flops in %.2f s on %d host threads)"
+                          % (vfl, vision_s, workers)}
+    del x64, v64
+
+    # varlen GQA: RoPE of every token, attention of key/value head 0's query heads
+    c = W.varlen_gqa()
+    x64, v64 = W.bf16_bits_to_f64(c.x_qkv), W.bf16_bits_to_f64(c.v_from_x())
+    heads = list(range(c.num_heads_q // c.num_heads_kv))
+    q, k = oracle.qkv_rope(x64, c.positions, c.theta, c.num_heads_q, c.num_heads_kv, c.head_dim)
+    dt = timed(lambda: oracle.attention(q, k, v64, c.cu_seqlens_q, c.cu_seqlens_k, True, float(np.float32(c.scale)),
+                                        heads=heads, workers=workers))
+    frac = len(heads) / c.num_heads_q
+    per[c.name] = {"oracle_sample_s": round(dt, 3), "sample": "attention of query heads 0-%d (1/%d of the flops)"
+                   % (len(heads) - 1, round(1 / frac)), "oracle_est_full_s": round(dt / frac, 2),
+                   "gflops": round(dense_flops(c) * frac / dt / 1e9, 2)}
+    del x64, v64, q, k
+
+    # 32K causal: two of the 16 heads
+    c = W.long_causal()
+    q, k, v = (W.bf16_bits_to_f64(a[:, :2]) for a in (c.q, c.k, c.v))
+    dt = timed(lambda: oracle.attention(q, k, v, c.cu_seqlens_q, c.cu_seqlens_k, True, float(np.float32(c.scale)),
+                                        workers=workers))
+    frac = 2 / c.num_heads_q
+    per[c.name] = {"oracle_sample_s": round(dt, 3), "sample": "attention of heads 0-1 (1/8 of the flops)",
+                   "oracle_est_full_s": round(dt / frac, 2), "gflops": round(dense_flops(c) * frac / dt / 1e9, 2)}
+    del q, k, v
+
+    # sparse MQA: the whole workload
+    c = W.sparse_mqa()
+    q, kv = W.bf16_bits_to_f64(c.q), W.bf16_bits_to_f64(c.kv_latent)
+    dt = timed(lambda: oracle.sparse_mqa(q, kv, c.topk_idx, c.d_v, float(np.float32(c.scale)), workers=workers))
+    per[c.name] = {"oracle_s": round(dt, 3), "sample": "whole workload",
+                   "gbs": round(sparse_bytes(c) / dt / 1e9, 3), "gflops": round(sparse_flops(c) / dt / 1e9, 2)}
+    return headline, per
 
 
 def main():
@@ -513,14 +704,21 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy (reference for HBM byte counters)")
-    ap.add_argument("--only", choices=["varlen_gqa", "long_causal", "sparse_mqa", "indexer", "qkv_proj", "fp8", "decode"],
-                    help="only run one of the other workloads (for profiling one kernel family)")
+    ap.add_argument("--only", choices=WORKLOADS,
+                    help="only run one workload (for profiling one kernel family); its JSON goes to stderr")
+    ap.add_argument("--oracle-only", action="store_true", help="only time the CPU oracle (no GPU needed)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         err("bench.py measures one GPU: this library's path runs on a single MI355X "
             "(every workload here fits one GPU; multi-GPU sharding is described in DESIGN.md, not run). "
             "Use --gpus 1.")
         sys.exit(2)
+    from oracle.pool import host_cores
+    workers = max(1, min(16, host_cores()))
+    if args.oracle_only:
+        head, per = cpu_oracle(workers)
+        err(json.dumps({"cpu_baseline": head, "per_workload": per, "host": host_info(workers)}))
+        return
 
     import torch
     import vision_encoder_attention_amd as vea
@@ -532,10 +730,6 @@ def main():
     props = torch.cuda.get_device_properties(0)
     err("device: %s, %d CUs" % (props.name, props.multi_processor_count))
 
-    if args.only:
-        res = bench_other(torch, max(3, min(args.steps, 20)), args.warmup, only=args.only)
-        err(json.dumps(res))
-        return
     if args.calibrate_copy:
         n = 512 << 20
         a = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -545,15 +739,20 @@ def main():
         torch.cuda.synchronize()
         err("copied %d bytes 3 times (expect FETCH_SIZE and WRITE_SIZE of %d KiB per copy)" % (n, n >> 10))
         return
+    if args.only == "vision":
+        case, tm, wall_ms, ent = bench_vision(torch, args)
+        err(json.dumps({case.name: ent}))
+        return
+    if args.only:
+        res = bench_other(torch, max(3, min(args.steps, 20)), args.warmup, only=args.only)
+        err(json.dumps(res))
+        return
 
-    case, tm, wall_ms = bench_vision(torch, args)
+    case, tm, wall_ms, vis = bench_vision(torch, args)
     fl = dense_flops(case)
-    a_ms, a_min = tm.ms("attn_fwd")
-    r_ms, r_min = tm.ms("qkv_rope")
-    rb = rope_bytes(case)
-    achieved = fl / a_ms / 1e9
-    err("vision: step %.4f ms (wall), attn_fwd %.4f ms avg (%.1f TFLOP/s), qkv_rope %.4f ms (%.0f GB/s)"
-        % (wall_ms, a_ms, achieved, r_ms, rb / r_ms / 1e6))
+    step = tm.stats("step")
+    err("vision: step %.4f ms (wall), attn_fwd %.4f ms avg (%.1f TFLOP/s), qkv_rope %.4f ms warm, %.4f ms cold"
+        % (wall_ms, vis["attn_fwd_ms"], vis["attn_tflops"], vis["qkv_rope_ms"], vis["qkv_rope_cold_ms"]))
 
     line = {
         "metric": "attention fwd TFLOP/s (qkv_rope + piecewise attn_fwd step), % of bf16 MFMA peak",
@@ -562,7 +761,10 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup_done,
+        "warmup_requested": args.warmup,
         "ms_per_step": round(wall_ms, 5),
+        "ms_per_step_median": round(step["median"], 5),
+        "ms_per_step_min": round(step["min"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -571,22 +773,20 @@ def main():
         "config": {"workload": "vision_encoder_8547tok_111x77grid_h16_d64_qb1462_2dRoPE",
                    "tokens": case.total_q, "heads": case.num_heads_q, "head_dim": case.head_dim,
                    "piece_rows": case.piece_rows, "causal": False, "flops_per_step": fl},
-        "kernels": {"attn_fwd_ms": round(a_ms, 5), "attn_fwd_min_ms": round(a_min, 5),
-                    "qkv_rope_ms": round(r_ms, 5), "qkv_rope_gbs": round(rb / r_ms / 1e6, 1),
-                    "qkv_rope_frac_hbm": round(rb / r_ms / 1e6 / PEAK_HBM_GBS, 4)},
-        "roofline": {"bound": "mfma", "kernel": "attn_fwd_bf16_kernel<64,false,false>", "achieved": round(achieved, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": committed_traffic("attn_fwd_vision_hbm_counters.txt"),
-                     "traffic_unit": "bytes per launch (HBM, counter-measured)",
-                     "algorithmic_bytes": 4 * case.total_q * case.num_heads_q * case.head_dim * 2},
+        "kernels": {k: v for k, v in vis.items() if k.startswith(("attn_fwd", "qkv_rope")) and k != "qkv_rope_roofline"},
+        "roofline": vis["roofline"],
+        "rooflines": {"qkv_rope": vis["qkv_rope_roofline"]},
     }
     if not args.no_extra:
         line["workloads"] = bench_other(torch, max(5, min(args.steps, 20)), args.warmup)
         for k, v in line["workloads"].items():
             err("%s: %s" % (k, v))
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline()
-        err("cpu_baseline: %s" % line["cpu_baseline"])
+        head, per = cpu_oracle(workers)
+        head["per_workload"] = per
+        head["host"] = host_info(workers)
+        line["cpu_baseline"] = head
+        err("cpu_baseline: %s" % json.dumps(head))
     print(json.dumps(line), flush=True)
 
 

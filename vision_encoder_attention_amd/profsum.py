@@ -1,0 +1,183 @@
+"""Summaries of rocprofv3 output for the kernels of this library.
+
+Two reports, each printed as text (the files under ``profiles/`` are these
+reports, with the commands that produced the raw data):
+
+* ``trace``: per-kernel call counts and durations from a
+  ``rocprofv3 --kernel-trace --stats --output-format csv`` run, plus the
+  average over each kernel's last N dispatches.  ``bench.py`` runs its timed
+  launches after its warm-up ones, so the last N dispatches of a kernel are
+  the timed window that the benchmark's HIP events cover.
+* ``counters``: HBM bytes of one launch from a ``FETCH_SIZE`` run and a
+  ``WRITE_SIZE`` run (KiB per dispatch), each scaled by what the same counter
+  reads for a device-to-device copy of known size (``bench.py
+  --calibrate-copy``), next to the launch's algorithmic bytes; optionally the
+  MFMA counters of a third run.  The last line (``RESULT {...}``) is read
+  back by ``bench.py``, which reports the traffic only while the kernel's
+  sources still hash to the digest recorded there.
+
+    python -m vision_encoder_attention_amd.profsum trace DIR [--last N] [--match TEXT ...]
+    python -m vision_encoder_attention_amd.profsum counters --kernel TEXT --fetch DIR --write DIR
+        --copy-fetch DIR --copy-write DIR --algorithmic-bytes B --sources FILE ... [--mfma DIR]
+        [--last N]
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+COPY_BYTES = 512 << 20          # size of bench.py --calibrate-copy
+
+
+def _one(dir_, suffix):
+    files = sorted(glob.glob(os.path.join(dir_, "**", "*" + suffix), recursive=True))
+    if not files:
+        raise SystemExit("no *%s under %s" % (suffix, dir_))
+    return files[0]
+
+
+def _rows(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def source_digest(paths) -> str:
+    """sha256 over the sources a kernel is built from.  "file#Name" stands for
+    the part of a shared header the kernel uses: the text of its parameter
+    struct Name plus the header's typedef and constexpr lines, so additions
+    for other kernels do not invalidate a summary."""
+    h = hashlib.sha256()
+    for pth in paths:
+        name = None
+        if "#" in pth:
+            pth, name = pth.split("#", 1)
+        with open(os.path.join(ROOT, pth), "rb") as f:
+            data = f.read()
+        if name is not None:
+            text = data.decode()
+            m = re.search(r"^struct %s \{.*?^\};" % re.escape(name), text, re.S | re.M)
+            if m is None:
+                raise ValueError("struct %s not found in %s" % (name, pth))
+            keep = [ln for ln in text.splitlines() if ln.startswith(("typedef", "constexpr"))]
+            data = (m.group(0) + "\n" + "\n".join(keep)).encode()
+        h.update(data)
+    return h.hexdigest()[:16]
+
+
+def trace_report(dir_, last=20, match=None):
+    rows = _rows(_one(dir_, "_kernel_trace.csv"))
+    per = {}
+    for r in rows:
+        per.setdefault(r["Kernel_Name"], []).append(
+            (int(r["Dispatch_Id"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    out = ["%-96s %6s %10s %10s %10s %10s %10s" % ("kernel", "calls", "avg_us", "min_us", "max_us",
+                                                    "last%d_avg" % last, "last%d_med" % last)]
+    order = sorted(per.items(), key=lambda kv: -sum(d for _, d in kv[1]))
+    for name, ds in order:
+        if match and not any(m in name for m in match):
+            continue
+        ds.sort()
+        dur = [d for _, d in ds]
+        tail = dur[-last:]
+        out.append("%-96s %6d %10.2f %10.2f %10.2f %10.2f %10.2f" % (
+            name[:96], len(dur), sum(dur) / len(dur), min(dur), max(dur), sum(tail) / len(tail),
+            statistics.median(tail)))
+    return "\n".join(out)
+
+
+def _counter(dir_, counter, kernel):
+    vals = []
+    for r in _rows(_one(dir_, "_counter_collection.csv")):
+        if r["Counter_Name"] == counter and kernel in r["Kernel_Name"]:
+            vals.append((int(r["Dispatch_Id"]), float(r["Counter_Value"]), r["Kernel_Name"]))
+    vals.sort()
+    return vals
+
+
+def counters_report(kernel, fetch, write, copy_fetch, copy_write, algorithmic_bytes, sources, mfma=None, last=0):
+    out = []
+    f = _counter(fetch, "FETCH_SIZE", kernel)
+    w = _counter(write, "WRITE_SIZE", kernel)
+    if not f or not w:
+        raise SystemExit("kernel %r not found in the counter runs" % kernel)
+    full_name = f[0][2]
+    cf = [v for _, v, _ in _counter(copy_fetch, "FETCH_SIZE", "copyBuffer")]
+    cw = [v for _, v, _ in _counter(copy_write, "WRITE_SIZE", "copyBuffer")]
+    fs = (COPY_BYTES >> 10) / statistics.median(cf)
+    ws = (COPY_BYTES >> 10) / statistics.median(cw)
+    fv = [v for _, v, _ in f][-last:] if last else [v for _, v, _ in f]
+    wv = [v for _, v, _ in w][-last:] if last else [v for _, v, _ in w]
+    rd = statistics.mean(fv) * 1024 * fs
+    wr = statistics.mean(wv) * 1024 * ws
+    out.append("kernel: %s" % full_name)
+    out.append("  FETCH_SIZE per dispatch (KiB): mean %.0f, min %.0f, max %.0f over %d dispatches"
+               % (statistics.mean(fv), min(fv), max(fv), len(fv)))
+    out.append("  WRITE_SIZE per dispatch (KiB): mean %.0f, min %.0f, max %.0f over %d dispatches"
+               % (statistics.mean(wv), min(wv), max(wv), len(wv)))
+    out.append("copy calibration (__amd_rocclr_copyBuffer, %d KiB read + %d KiB written):"
+               % (COPY_BYTES >> 10, COPY_BYTES >> 10))
+    out.append("  FETCH_SIZE %s -> scale %.4f" % ([round(x) for x in cf], fs))
+    out.append("  WRITE_SIZE %s -> scale %.4f" % ([round(x) for x in cw], ws))
+    out.append("")
+    out.append("HBM bytes per launch: read %.4g + written %.4g = %.4g" % (rd, wr, rd + wr))
+    out.append("algorithmic bytes per launch: %.4g  (ratio %.3f)" % (algorithmic_bytes, (rd + wr) / algorithmic_bytes))
+    rec = {"kernel": full_name, "hbm_bytes_per_launch": int(round(rd + wr)), "read_bytes": int(round(rd)),
+           "write_bytes": int(round(wr)), "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+           "algorithmic_bytes": int(algorithmic_bytes), "sources": list(sources),
+           "source_digest": source_digest(sources)}
+    if mfma:
+        rows = [r for r in _rows(_one(mfma, "_counter_collection.csv")) if kernel in r["Kernel_Name"]]
+        names = sorted(set(r["Counter_Name"] for r in rows))
+        means = {}
+        for n in names:
+            vs = [(int(r["Dispatch_Id"]), float(r["Counter_Value"])) for r in rows if r["Counter_Name"] == n]
+            vs.sort()
+            vv = [v for _, v in vs][-last:] if last else [v for _, v in vs]
+            means[n] = statistics.mean(vv)
+        out.append("")
+        out.append("counter means per dispatch: " + ", ".join("%s %.6g" % (n, means[n]) for n in names))
+        for n in names:
+            if n.startswith("SQ_INSTS_VALU_MFMA_MOPS_"):
+                out.append("  %s x 512 = %.4g MFMA flops per launch" % (n, means[n] * 512))
+                rec["mfma_flops_per_launch"] = means[n] * 512
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in means and "GRBM_GUI_ACTIVE" in means:
+            rec["mfma_busy_cycles"] = means["SQ_VALU_MFMA_BUSY_CYCLES"]
+            rec["gui_active_cycles"] = means["GRBM_GUI_ACTIVE"]
+    out.append("")
+    out.append("RESULT " + json.dumps(rec))
+    return "\n".join(out)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("dir")
+    t.add_argument("--last", type=int, default=20)
+    t.add_argument("--match", nargs="*")
+    c = sub.add_parser("counters")
+    c.add_argument("--kernel", required=True)
+    for n in ("fetch", "write", "copy-fetch", "copy-write"):
+        c.add_argument("--" + n, required=True)
+    c.add_argument("--mfma")
+    c.add_argument("--algorithmic-bytes", type=float, required=True)
+    c.add_argument("--sources", nargs="+", required=True)
+    c.add_argument("--last", type=int, default=0)
+    a = ap.parse_args(argv)
+    if a.cmd == "trace":
+        print(trace_report(a.dir, a.last, a.match))
+    else:
+        print(counters_report(a.kernel, a.fetch, a.write, a.copy_fetch, a.copy_write, a.algorithmic_bytes, a.sources,
+                              a.mfma, a.last))
+
+
+if __name__ == "__main__":
+    sys.exit(main())
