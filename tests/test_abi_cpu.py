@@ -419,3 +419,27 @@ def test_product_path_never_touches_the_oracle():
                 src = open(os.path.join(base, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", src, flags=re.M), f
                 assert "oracle/" not in src and "import oracle" not in src, f
+
+
+def test_roctx_ranges_do_not_change_validation():
+    """VEA_ROCTX=1 wraps every entry point in a roctx range (the library opens
+    the roctx library on first use): calls still validate and return as
+    before, in a fresh process where the variable is set from the start."""
+    code = r"""
+import ctypes, sys
+sys.path.insert(0, %r)
+from vision_encoder_attention_amd import _binding
+lib = _binding.load_library()
+a = [1, 0x10000, 128, 0x10000, 128, 0x10000, 128, 0x10000, 0x10000, 0, 0, 0, 0, 0, 8, 2, 64, 0, 0.125, 0,
+     0x10000, 128, None, None, 0, None]
+assert lib.vea_attn_fwd(*a) == 0                      # batch 0: nothing to compute
+a[9] = 1; a[10] = 10; a[11] = 10; a[12] = 10; a[13] = 10; a[16] = 96
+assert lib.vea_attn_fwd(*a) == -4                     # head_dim 96: unsupported
+import os
+if os.path.exists("/opt/rocm/lib/librocprofiler-sdk-roctx.so.1"):
+    assert "rocprofiler-sdk-roctx" in open("/proc/self/maps").read(), "roctx library not opened"
+print("ok")
+""" % ROOT
+    env = dict(os.environ, VEA_ROCTX="1")
+    res = subprocess.run([os.sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=120)
+    assert res.returncode == 0 and res.stdout.strip().endswith("ok"), res.stderr

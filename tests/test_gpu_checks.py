@@ -5,6 +5,8 @@
   calls under VEA_CHECK give bitwise the same results as without it.
 * Two independent calls on two streams give bitwise the results of running
   them one after the other (no shared state, one writer per output).
+* Workgroups taking their units in another order (VEA_DEBUG_WG_ORDER) give
+  bitwise the same results.
 """
 import os
 
@@ -104,3 +106,77 @@ def test_two_streams_match_sequential_results(torch):
     got = (sa.out, sa.lse, sb.out, sb.lse, sp.out, sp.lse)
     for g, r in zip(got, ref):
         assert torch.equal(g, r)
+
+
+def _order_cases(torch):
+    """Launches that cover every kernel family and launch shape the order
+    check touches: a pieced image with the split of the last round (its tile
+    count just above one round of workgroups: 3 per CU for d 64), a causal
+    GQA varlen batch with empty sequences, the fp32 path, decode units with
+    key-range splits, FP8 attention and sparse MQA with its split."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles = (cus * 3) // 16 + 4
+    return dict(
+        vision=W.vision(grid_rows=tiles, grid_cols=128, heads=16, d=64, piece_rows=128 * ((tiles + 1) // 2),
+                        seed=720),
+        varlen=W.varlen_gqa(lengths=[130, 0, 257, 1, 700], hq=8, hkv=2, d=128, seed=721),
+        f32=W.single_head_f32(n=300, piece_rows=70, seed=722),
+        sparse=W.sparse_mqa(rows=300, heads=128, n_kv=900, k=512, seed=723),
+    )
+
+
+def _run_all(torch, staged):
+    import vision_encoder_attention_amd as vea
+    outs = []
+    for name, st in staged.items():
+        if name == "sparse":
+            R.run_sparse(st)
+            outs += [st.out.clone(), st.lse.clone()]
+        elif name == "decode":
+            q, k, v, cuk, out, lse = st
+            vea.attn_decode(q, k, v, cuk, 0.088, out, lse)
+            outs += [out.clone(), lse.clone()]
+        elif name == "fp8":
+            (q8, qs), (k8, ks), (v8, vs), cu, out, lse = st
+            vea.attn_fwd_fp8(q8, qs, k8, ks, v8, vs, cu, cu, True, 0.09, out, lse, max_seqlen_q=600, max_seqlen_k=600)
+            outs += [out.clone(), lse.clone()]
+        else:
+            R.run_dense(st)
+            outs += [st.out.clone(), st.lse.clone()]
+    torch.cuda.synchronize()
+    return outs
+
+
+@pytest.mark.parametrize("order", ["reverse", "stride"])
+def test_workgroup_order_does_not_change_results(torch, order):
+    """Race smoke: the grid's workgroups take their units in reversed or
+    strided order (VEA_DEBUG_WG_ORDER) and every output stays bitwise equal.
+    Each unit owns its outputs (and its split chunk's workspace slot), so the
+    order in which units run, and which ones are resident together, can change
+    nothing."""
+    import vision_encoder_attention_amd as vea
+    cases = _order_cases(torch)
+    staged = {n: (R.stage_sparse(c) if n == "sparse" else R.stage_dense(c)) for n, c in cases.items()}
+    assert staged["vision"].ws is not None and staged["sparse"].ws is not None
+    dec = W.random_dense([1] * 40, [int(x) for x in range(50, 4050, 100)], 32, 8, 128, True, "bf16", seed=724)
+    dq, dk, dv = (R.bits_to_tensor(a, "cuda") for a in (dec.q, dec.k, dec.v))
+    staged["decode"] = (dq, dk, dv, torch.from_numpy(dec.cu_seqlens_k.astype("int32")).cuda(),
+                        torch.empty_like(dq), torch.empty((32, 40), dtype=torch.float32, device="cuda"))
+    f8 = W.random_dense([600, 77], [600, 77], 8, 4, 64, True, "bf16", seed=725)
+    fq, fk, fv = (R.bits_to_tensor(a, "cuda") for a in (f8.q, f8.k, f8.v))
+    staged["fp8"] = (vea.quantize_fp8(fq, 0), vea.quantize_fp8(fk, 1), vea.quantize_fp8(fv, 2),
+                     torch.from_numpy(f8.cu_seqlens_q.astype("int32")).cuda(), torch.empty_like(fq),
+                     torch.empty((8, 677), dtype=torch.float32, device="cuda"))
+    ref = _run_all(torch, staged)
+    old = os.environ.get("VEA_DEBUG_WG_ORDER")
+    os.environ["VEA_DEBUG_WG_ORDER"] = order
+    try:
+        got = _run_all(torch, staged)
+    finally:
+        if old is None:
+            os.environ.pop("VEA_DEBUG_WG_ORDER", None)
+        else:
+            os.environ["VEA_DEBUG_WG_ORDER"] = old
+    assert len(got) == len(ref) == 12
+    for i, (g, r) in enumerate(zip(got, ref)):
+        assert torch.equal(g, r), "output %d differs under %s order" % (i, order)

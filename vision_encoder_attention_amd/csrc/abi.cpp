@@ -10,11 +10,13 @@
 #include "../../include/vea.h"
 #include "vea_internal.h"
 
+#include <dlfcn.h>
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 using namespace vea;
@@ -29,6 +31,47 @@ bool check_enabled() {
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? VEA_OK : VEA_EHIP; }
+
+// VEA_ROCTX=1: every entry point is a named roctx range, so that a
+// rocprofv3 --marker-trace timeline shows the library calls around their
+// kernels.  The roctx library is opened on first use; without it (or without
+// the variable) the ranges cost one load of a flag.
+struct RoctxApi {
+  int (*push)(const char*) = nullptr;
+  int (*pop)() = nullptr;
+};
+
+const RoctxApi& roctx_api() {
+  static RoctxApi api;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    const char* e = getenv("VEA_ROCTX");
+    if (e == nullptr || e[0] == '\0' || strcmp(e, "0") == 0) return;
+    void* h = dlopen("librocprofiler-sdk-roctx.so.1", RTLD_NOW | RTLD_LOCAL);
+    if (h == nullptr) h = dlopen("/opt/rocm/lib/librocprofiler-sdk-roctx.so.1", RTLD_NOW | RTLD_LOCAL);
+    if (h == nullptr) return;
+    auto push = reinterpret_cast<int (*)(const char*)>(dlsym(h, "roctxRangePushA"));
+    auto pop = reinterpret_cast<int (*)()>(dlsym(h, "roctxRangePop"));
+    if (push != nullptr && pop != nullptr) {
+      api.push = push;
+      api.pop = pop;
+    }
+  });
+  return api;
+}
+
+class Range {
+ public:
+  explicit Range(const char* name) : api_(roctx_api()) {
+    if (api_.push != nullptr) api_.push(name);
+  }
+  ~Range() {
+    if (api_.pop != nullptr) api_.pop();
+  }
+
+ private:
+  const RoctxApi& api_;
+};
 
 // VEA_CHECK: copy a device int32 array to the host after draining the stream.
 int fetch_ints(const int32_t* dev, size_t n, hipStream_t s, std::vector<int32_t>& host) {
@@ -51,6 +94,15 @@ int check_cu(const int32_t* cu, int batch, int total, int max_len, hipStream_t s
   return VEA_OK;
 }
 
+int gcd_int(int a, int b) {
+  while (b != 0) {
+    const int t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+
 int finish(int st, hipStream_t s) {
   if (st != VEA_OK) return st;
   if (check_enabled()) {
@@ -60,6 +112,24 @@ int finish(int st, hipStream_t s) {
 }
 
 }  // namespace
+
+namespace vea {
+
+int wg_order_perm(int grid) {
+  const char* e = getenv("VEA_DEBUG_WG_ORDER");
+  if (e == nullptr || grid < 2) return 0;
+  if (strcmp(e, "reverse") == 0) return 1;
+  if (strcmp(e, "stride") == 0) {
+    if (grid < 4) return 1;
+    // a multiplier near 0.618 grid, coprime to grid (a bijection of the slots)
+    int a = std::max(2, (int)(grid * 0.618));
+    while (gcd_int(a, grid) != 1) a = a + 1 < grid ? a + 1 : 2;
+    return a;
+  }
+  return 0;
+}
+
+}  // namespace vea
 
 extern "C" {
 
@@ -115,6 +185,8 @@ int dense_layout(int batch, int max_seqlen_q, int num_heads_q, int piece_rows, D
   p.q_scale = p.k_scale = p.v_scale = nullptr;
   p.dec_group = 0;
   p.ws_rows = kDenseBM;
+  p.grid = 0;
+  p.wg_perm = 0;
   return VEA_OK;
 }
 
@@ -246,6 +318,7 @@ int vea_attn_fwd(int dtype, const void* q, int64_t q_tok_stride, const void* k, 
                  int batch, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int num_heads_q,
                  int num_heads_kv, int head_dim, int causal, float scale, int piece_rows, void* out,
                  int64_t out_tok_stride, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  Range range("vea_attn_fwd");
   return dense_fwd(dtype, q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, nullptr, 0, 0, 0, cu_seqlens_q,
                    cu_seqlens_k, batch, total_q, total_k, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv,
                    head_dim, causal, scale, piece_rows, out, out_tok_stride, lse, workspace, workspace_bytes, stream);
@@ -257,6 +330,7 @@ int vea_attn_fwd_paged(const void* q, int64_t q_tok_stride, const void* k_cache,
                        int batch, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int num_heads_q,
                        int num_heads_kv, int head_dim, int causal, float scale, int piece_rows, void* out,
                        int64_t out_tok_stride, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  Range range("vea_attn_fwd_paged");
   if (block_table == nullptr && batch > 0 && total_q > 0) return VEA_EINVAL;
   return dense_fwd(VEA_BF16, q, q_tok_stride, k_cache, k_tok_stride, v_cache, v_tok_stride, block_table,
                    max_pages_per_seq, page_size, num_pages, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k,
@@ -316,6 +390,7 @@ int vea_attn_decode(const void* q, int64_t q_seq_stride, const void* k, int64_t 
                     int num_pages, const int32_t* cu_seqlens_k, int batch, int total_k, int max_seqlen_k,
                     int num_heads_q, int num_heads_kv, int head_dim, float scale, void* out, int64_t out_seq_stride,
                     float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  Range range("vea_attn_decode");
   int st = decode_shape_status(batch, total_k, max_seqlen_k, num_heads_q, num_heads_kv, head_dim);
   if (st != VEA_OK) return st;
   if (!isfinite(scale)) return VEA_EINVAL;
@@ -392,6 +467,7 @@ int vea_attn_fwd_fp8(const void* q, int64_t q_tok_stride, const void* k, int64_t
                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch, int total_q, int total_k,
                      int max_seqlen_q, int max_seqlen_k, int num_heads_q, int num_heads_kv, int head_dim, int causal,
                      float scale, int piece_rows, void* out, int64_t out_tok_stride, float* lse, void* stream) {
+  Range range("vea_attn_fwd_fp8");
   // same shape rules as the bf16 path
   int st = dense_shape_status(VEA_BF16, batch, total_q, total_k, max_seqlen_q, max_seqlen_k, num_heads_q,
                               num_heads_kv, head_dim, causal, piece_rows);
@@ -430,6 +506,7 @@ int vea_attn_fwd_fp8(const void* q, int64_t q_tok_stride, const void* k, int64_t
 
 int vea_quantize_fp8(const void* x, int64_t x_tok_stride, int num_tokens, int num_heads, int head_dim,
                      int granularity, void* out, float* scales, void* stream) {
+  Range range("vea_quantize_fp8");
   if (num_tokens < 0 || num_heads <= 0) return VEA_ESHAPE;
   if (granularity < 0 || granularity > 2) return VEA_EINVAL;
   if (head_dim != 64 && head_dim != 128) return VEA_EUNSUPPORTED;
@@ -448,6 +525,7 @@ int vea_quantize_fp8(const void* x, int64_t x_tok_stride, int num_tokens, int nu
 int vea_qkv_rope(const void* x_qkv, int64_t x_tok_stride, const int32_t* positions, int pos_dims, int num_tokens,
                  int num_heads_q, int num_heads_kv, int head_dim, float theta, int rotate_half, void* q, void* k,
                  void* stream) {
+  Range range("vea_qkv_rope");
   if (num_tokens < 0 || num_heads_q <= 0 || num_heads_kv <= 0 || head_dim <= 0) return VEA_ESHAPE;
   if (pos_dims != 1 && pos_dims != 2) return VEA_EINVAL;
   if (!isfinite(theta) || !(theta > 0.f)) return VEA_EINVAL;
@@ -534,6 +612,8 @@ int sparse_fwd(const void* q, const void* kv, const int32_t* page_table, int pag
   p.page_table = page_table;
   p.page_shift = shift;
   p.n_phys = (int)n_phys;
+  p.grid = 0;
+  p.wg_perm = 0;
   if (workspace != nullptr) {
     int cus = 0;
     st = current_cus(&cus);
@@ -568,6 +648,7 @@ int sparse_fwd(const void* q, const void* kv, const int32_t* page_table, int pag
 int vea_sparse_mqa_fwd(const void* q, const void* kv_latent, const int32_t* topk_idx, int num_rows, int num_heads,
                        int n_kv, int d_qk, int d_v, int k, float scale, void* out, float* lse, void* workspace,
                        size_t workspace_bytes, void* stream) {
+  Range range("vea_sparse_mqa_fwd");
   return sparse_fwd(q, kv_latent, nullptr, 0, 0, topk_idx, num_rows, num_heads, n_kv, d_qk, d_v, k, scale, out, lse,
                     workspace, workspace_bytes, stream);
 }
@@ -576,6 +657,7 @@ int vea_sparse_mqa_paged_fwd(const void* q, const void* kv_cache, const int32_t*
                              int num_pages, const int32_t* topk_idx, int num_rows, int num_heads, int n_kv, int d_qk,
                              int d_v, int k, float scale, void* out, float* lse, void* workspace,
                              size_t workspace_bytes, void* stream) {
+  Range range("vea_sparse_mqa_paged_fwd");
   if (page_table == nullptr && num_rows > 0) return VEA_EINVAL;
   return sparse_fwd(q, kv_cache, page_table, page_size, num_pages, topk_idx, num_rows, num_heads, n_kv, d_qk, d_v, k,
                     scale, out, lse, workspace, workspace_bytes, stream);
@@ -583,6 +665,7 @@ int vea_sparse_mqa_paged_fwd(const void* q, const void* kv_cache, const int32_t*
 
 int vea_topk_indices(const float* logits, int64_t row_stride, const int32_t* row_starts, const int32_t* row_lens,
                      int num_rows, int n, int k, int32_t* out, void* stream) {
+  Range range("vea_topk_indices");
   if (num_rows < 0 || n < 1 || k < 1) return VEA_ESHAPE;
   if (row_stride < n) return VEA_ESHAPE;
   if (n > kTopkMaxN) return VEA_EUNSUPPORTED;
@@ -610,6 +693,7 @@ int vea_topk_indices(const float* logits, int64_t row_stride, const int32_t* row
 
 int vea_rope_cos_sin(const int32_t* positions, int pos_dims, int num_tokens, int head_dim, float theta,
                      float* cos_sin, void* stream) {
+  Range range("vea_rope_cos_sin");
   if (num_tokens < 0 || head_dim <= 0) return VEA_ESHAPE;
   if (pos_dims != 1 && pos_dims != 2) return VEA_EINVAL;
   if (!isfinite(theta) || !(theta > 0.f)) return VEA_EINVAL;
@@ -627,6 +711,7 @@ int vea_rope_cos_sin(const int32_t* positions, int pos_dims, int num_tokens, int
 int vea_qkv_proj_rope(const void* x, int64_t x_tok_stride, const void* w, int64_t w_row_stride, const void* bias,
                       const float* cos_sin, int num_tokens, int hidden, int num_heads_q, int num_heads_kv,
                       int head_dim, int rotate_half_span, void* q, void* k, void* v, void* stream) {
+  Range range("vea_qkv_proj_rope");
   if (num_tokens < 0 || hidden <= 0 || num_heads_q <= 0 || num_heads_kv <= 0 || head_dim <= 0) return VEA_ESHAPE;
   const int64_t n = (int64_t)(num_heads_q + 2 * (int64_t)num_heads_kv) * head_dim;
   if (x_tok_stride < hidden || w_row_stride < n) return VEA_ESHAPE;
@@ -659,6 +744,7 @@ int vea_attn_probs_piece(int dtype, const void* q, int64_t q_tok_stride, const v
                          const float* lse, int64_t lse_row_stride, int head, int num_heads_q, int num_heads_kv,
                          int head_dim, int seq_begin_q, int len_q, int seq_begin_k, int len_k, int q0, int rows,
                          int causal, float scale, float* p_out, int64_t p_row_stride, void* stream) {
+  Range range("vea_attn_probs_piece");
   if (dtype != VEA_BF16 && dtype != VEA_F32) return VEA_EDTYPE;
   if (num_heads_q <= 0 || num_heads_kv <= 0 || num_heads_q % num_heads_kv) return VEA_ESHAPE;
   if (head < 0 || head >= num_heads_q || head_dim <= 0) return VEA_ESHAPE;

@@ -210,7 +210,8 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
   __shared__ __attribute__((aligned(1024))) unsigned char vst1[C::TILE];
 
   // unit, and for a split unit of the last round, its key-range chunk
-  int id = blockIdx.x, chunk = 0;
+  const int slot = wg_slot(blockIdx.x, p.grid, p.wg_perm);
+  int id = slot, chunk = 0;
   const bool split = id >= p.full_units;
   if (split) {
     const int u2 = id - p.full_units;
@@ -559,7 +560,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
     // partial result of this key range, per tile row: unnormalized O
     // (fp32), reference max m (log2 domain) and sum l
     const int wr = DECODE ? p.ws_rows : C::BM;          // rows per chunk
-    float* w = p.ws + (size_t)(blockIdx.x - p.full_units) * (wr * (D + 2));
+    float* w = p.ws + (size_t)(slot - p.full_units) * (wr * (D + 2));
     const int rl = wave * 32 + l32;                     // row within the tile
     if (DECODE && !qvalid) return;                      // decode: only the few real rows are merged
 #pragma unroll
@@ -662,7 +663,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_fp8_kernel(De
   __shared__ __attribute__((aligned(1024))) unsigned char vst1[C::TILE];
 
   int b, h, t;
-  decode_unit(p, blockIdx.x, b, h, t);
+  decode_unit(p, wg_slot(blockIdx.x, p.grid, p.wg_perm), b, h, t);
   TileRange tr;
   if (!tile_range(p, b, t, C::BM, CAUSAL, tr)) return;   // uniform over the workgroup
 
@@ -1027,7 +1028,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_f32_kernel(DenseParams p) {
   __shared__ __attribute__((aligned(16))) float vsm[C::BN * C::ROW];
 
   int b, h, t;
-  decode_unit(p, blockIdx.x, b, h, t);
+  decode_unit(p, wg_slot(blockIdx.x, p.grid, p.wg_perm), b, h, t);
   TileRange tr;
   if (!tile_range(p, b, t, C::BM, CAUSAL, tr)) return;
 
@@ -1217,9 +1218,12 @@ void launch_dense(const DenseParams& p, bool causal, bool paged, dim3 grid, dim3
   }
 }
 
-hipError_t launch_attn_fwd_fp8(const DenseParams& p, int head_dim, bool causal, hipStream_t s) {
-  if (p.nsplit != 1 || p.full_units != p.units || p.block_table != nullptr) return hipErrorInvalidValue;
-  const dim3 grid(p.units), block(256);
+hipError_t launch_attn_fwd_fp8(const DenseParams& p0, int head_dim, bool causal, hipStream_t s) {
+  if (p0.nsplit != 1 || p0.full_units != p0.units || p0.block_table != nullptr) return hipErrorInvalidValue;
+  const dim3 grid(p0.units), block(256);
+  DenseParams p = p0;
+  p.grid = p0.units;
+  p.wg_perm = wg_order_perm(p.grid);
   if (head_dim == 64) {
     if (causal) hipLaunchKernelGGL((attn_fwd_fp8_kernel<64, true>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((attn_fwd_fp8_kernel<64, false>), grid, block, 0, s, p);
@@ -1232,11 +1236,15 @@ hipError_t launch_attn_fwd_fp8(const DenseParams& p, int head_dim, bool causal, 
   return hipGetLastError();
 }
 
-hipError_t launch_attn_fwd_bf16(const DenseParams& p, int head_dim, bool causal, hipStream_t s) {
-  const bool split = p.nsplit > 1;
-  if (split ? (causal || p.ws == nullptr || p.full_units < 0 || p.full_units >= p.units) : p.full_units != p.units)
+hipError_t launch_attn_fwd_bf16(const DenseParams& p0, int head_dim, bool causal, hipStream_t s) {
+  const bool split = p0.nsplit > 1;
+  if (split ? (causal || p0.ws == nullptr || p0.full_units < 0 || p0.full_units >= p0.units)
+            : p0.full_units != p0.units)
     return hipErrorInvalidValue;
-  const dim3 grid(p.full_units + (p.units - p.full_units) * p.nsplit), block(256);
+  const dim3 grid(p0.full_units + (p0.units - p0.full_units) * p0.nsplit), block(256);
+  DenseParams p = p0;
+  p.grid = (int)grid.x;
+  p.wg_perm = wg_order_perm(p.grid);
   const bool paged = p.block_table != nullptr;
   if (head_dim == 64) {
     launch_dense<64>(p, causal, paged, grid, block, s);
@@ -1255,8 +1263,11 @@ hipError_t launch_attn_fwd_bf16(const DenseParams& p, int head_dim, bool causal,
   return hipGetLastError();
 }
 
-hipError_t launch_attn_fwd_f32(const DenseParams& p, int head_dim, bool causal, hipStream_t s) {
-  const dim3 grid(p.units), block(256);
+hipError_t launch_attn_fwd_f32(const DenseParams& p0, int head_dim, bool causal, hipStream_t s) {
+  const dim3 grid(p0.units), block(256);
+  DenseParams p = p0;
+  p.grid = p0.units;
+  p.wg_perm = wg_order_perm(p.grid);
   if (head_dim != 64) return hipErrorInvalidValue;
   if (causal) hipLaunchKernelGGL((attn_fwd_f32_kernel<64, true>), grid, block, 0, s, p);
   else hipLaunchKernelGGL((attn_fwd_f32_kernel<64, false>), grid, block, 0, s, p);

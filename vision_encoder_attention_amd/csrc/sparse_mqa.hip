@@ -191,7 +191,8 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
   __shared__ int wsum[C::WAVES];
 
   // workgroup unit (row, head block) and, for a split unit, its chunk
-  int unit = blockIdx.x, chunk = 0;
+  const int slot = wg_slot(blockIdx.x, p.grid, p.wg_perm);
+  int unit = slot, chunk = 0;
   const bool split = unit >= p.full_units;
   if (split) {
     const int u2 = unit - p.full_units;
@@ -644,7 +645,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
     // partial result of this key range: unnormalized O^T in fp32 (a row is
     // two 1 KB halves, staged one half at a time), reference max m (log2
     // domain) and sum l, per head of the workgroup
-    float* w = p.ws + (size_t)(blockIdx.x - p.full_units) * (C::HEADS * (DV + 2));
+    float* w = p.ws + (size_t)(slot - p.full_units) * (C::HEADS * (DV + 2));
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
@@ -787,15 +788,18 @@ SparseSplit sparse_split_plan(int units, int k, int cus) {
 
 size_t sparse_chunk_bytes(int d_v) { return (size_t)kSparseHeadsPerWG * (d_v + 2) * sizeof(float); }
 
-hipError_t launch_sparse_mqa(const SparseParams& p, int d_qk, int d_v, hipStream_t s) {
+hipError_t launch_sparse_mqa(const SparseParams& p0, int d_qk, int d_v, hipStream_t s) {
   if (d_qk != 576 || d_v != 512) return hipErrorInvalidValue;
-  if (p.k > 4096) return hipErrorInvalidValue;
-  if (p.rows == 0) return hipSuccess;
-  const int units = p.rows * p.head_blocks;
-  if (p.nsplit > 1 ? (p.ws == nullptr || p.full_units < 0 || p.full_units >= units) : p.full_units != units)
+  if (p0.k > 4096) return hipErrorInvalidValue;
+  if (p0.rows == 0) return hipSuccess;
+  const int units = p0.rows * p0.head_blocks;
+  if (p0.nsplit > 1 ? (p0.ws == nullptr || p0.full_units < 0 || p0.full_units >= units) : p0.full_units != units)
     return hipErrorInvalidValue;
-  const int tail = units - p.full_units;
-  const dim3 grid(p.full_units + tail * p.nsplit), block(256);
+  const int tail = units - p0.full_units;
+  const dim3 grid(p0.full_units + tail * p0.nsplit), block(256);
+  SparseParams p = p0;
+  p.grid = (int)grid.x;
+  p.wg_perm = wg_order_perm(p.grid);
   if (p.k <= 2048) hipLaunchKernelGGL((sparse_mqa_kernel<576, 512, 2048>), grid, block, 0, s, p);
   else hipLaunchKernelGGL((sparse_mqa_kernel<576, 512, 4096>), grid, block, 0, s, p);
   if (tail > 0 && p.nsplit > 1) {

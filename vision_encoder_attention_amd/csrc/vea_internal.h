@@ -62,6 +62,10 @@ struct DenseParams {
   // Rows per split chunk in ws: kDenseBM, or for decode units dec_group
   // rounded up to a multiple of 4 (only those rows are ever written).
   int ws_rows;
+  // Order check (VEA_DEBUG_WG_ORDER): workgroup i of the grid of `grid`
+  // workgroups takes grid slot wg_slot(i, grid, wg_perm); 0 is the identity.
+  int grid;
+  int wg_perm;
 };
 
 struct RopeParams {
@@ -74,6 +78,20 @@ struct RopeParams {
   int rot_half;              // 1: pairs (i, i + span/2) instead of (2i, 2i + 1)
   double theta;
 };
+
+// Grid slot of workgroup i under an order-check permutation of the grid:
+// perm 0 the identity, 1 the reverse order, otherwise i * perm mod grid (perm
+// coprime to grid, so a bijection).  Results must not depend on it: every
+// slot is one independent unit with its own output.
+__host__ __device__ inline int wg_slot(int i, int grid, int perm) {
+  if (perm == 0) return i;
+  if (perm == 1) return grid - 1 - i;
+  return (int)(((int64_t)i * perm) % grid);
+}
+
+// The permutation VEA_DEBUG_WG_ORDER asks for ("reverse" or "stride"; unset
+// or anything else: 0) for a grid of `grid` workgroups.
+int wg_order_perm(int grid);
 
 struct SparseParams {
   const uint16_t* q;
@@ -96,6 +114,9 @@ struct SparseParams {
   const int32_t* page_table; // nullable: kv holds the logical rows
   int page_shift;
   int n_phys;                // rows of kv (the buffer bound); n_kv when not paged
+  // Order check (VEA_DEBUG_WG_ORDER), as in DenseParams.
+  int grid;
+  int wg_perm;
 };
 
 // Split plan of the dense bf16 kernel for one non-causal sequence: `units`
