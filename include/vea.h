@@ -48,7 +48,8 @@ typedef enum vea_status {
   VEA_EUNSUPPORTED = -4, /* valid request outside the compiled kernel set (e.g. head_dim) */
   VEA_ERANGE = -5,       /* VEA_CHECK only: bad cu_seqlens or top-k index found on the host */
   VEA_EWORKSPACE = -6,   /* caller workspace smaller than the call needs, or misaligned */
-  VEA_EHIP = -7          /* the HIP runtime reported an error (launch or VEA_CHECK sync) */
+  VEA_EHIP = -7,         /* the HIP runtime reported an error (launch or VEA_CHECK sync) */
+  VEA_ESCRATCH = -8      /* vea_attn_fwd_noalloc: the call needs more than the static scratch */
 } vea_status;
 
 typedef enum vea_dtype { VEA_F32 = 0, VEA_BF16 = 1 } vea_dtype;
@@ -152,6 +153,41 @@ int vea_attn_fwd_paged(const void* q, int64_t q_tok_stride,
                        int causal, float scale, int piece_rows,
                        void* out, int64_t out_tok_stride, float* lse,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * vea_attn_fwd_noalloc — vea_attn_fwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation and the same kernels, with the
+ * split of the last round of workgroups using a static scratch array inside
+ * the library instead of a caller workspace.  Nothing is allocated by the
+ * call (no hipMalloc, hipFree or allocating library routine); the caller
+ * passes inputs and outputs as for vea_attn_fwd.
+ *
+ *   Arguments    as vea_attn_fwd, without workspace / workspace_bytes.
+ *   Scratch      VEA_ATTN_NOALLOC_SCRATCH_BYTES (36 MiB) of device memory per
+ *                GPU the library runs on, held until the process ends.  It
+ *                holds partial results of split rows; nothing in it needs to
+ *                start at zero.  A call whose split needs more than that
+ *                (vea_attn_fwd_workspace_size reports more; not reachable on
+ *                a 256-CU MI355X, where every shape needs at most 34.1 MB)
+ *                returns VEA_ESCRATCH and launches nothing.
+ *   Result       bitwise that of vea_attn_fwd with a workspace of
+ *                vea_attn_fwd_workspace_size bytes (the same split plan).
+ *   Concurrency  every call on one GPU shares that GPU's scratch and leaves
+ *                its last contents there: calls that overlap on one GPU
+ *                (different streams, or several host threads) race and must
+ *                be ordered by the caller, e.g. on one stream.
+ */
+#define VEA_ATTN_NOALLOC_SCRATCH_BYTES ((size_t)36 << 20)
+int vea_attn_fwd_noalloc(int dtype,
+                         const void* q, int64_t q_tok_stride,
+                         const void* k, int64_t k_tok_stride,
+                         const void* v, int64_t v_tok_stride,
+                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                         int batch, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                         int num_heads_q, int num_heads_kv, int head_dim,
+                         int causal, float scale, int piece_rows,
+                         void* out, int64_t out_tok_stride, float* lse, void* stream);
 
 /*
  * vea_attn_fwd_workspace_size — bytes of workspace vea_attn_fwd uses for these

@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for st in (0, -1, -2, -3, -4, -5, -6, -7):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert lib.vea_status_str(st).decode().startswith("VEA_")
     assert lib.vea_version().decode().startswith("vea ")
 

@@ -16,10 +16,10 @@ in ``include/vea.h``); this package is a thin binding over it:
 
 ``workloads`` holds the seeded synthetic inputs; ``build`` compiles the library.
 """
-from ._binding import (VeaError, attn_decode, attn_decode_workspace_size, attn_fwd, attn_fwd_paged, attn_fwd_workspace_size, attn_probs_piece, lib_path, load_library,  # noqa: F401
+from ._binding import (VeaError, attn_decode, attn_decode_workspace_size, attn_fwd, attn_fwd_noalloc, attn_fwd_paged, attn_fwd_workspace_size, attn_probs_piece, lib_path, load_library,  # noqa: F401
                        attn_fwd_fp8, quantize_fp8, qkv_proj_rope, qkv_rope, rope_cos_sin, sparse_mqa_fwd, sparse_mqa_paged_fwd,
                        sparse_mqa_workspace_size, status_str, topk_indices)
 
-__all__ = ["attn_decode", "attn_decode_workspace_size", "attn_fwd", "attn_fwd_paged", "attn_fwd_workspace_size", "qkv_rope", "sparse_mqa_fwd", "sparse_mqa_workspace_size", "attn_probs_piece",
+__all__ = ["attn_decode", "attn_decode_workspace_size", "attn_fwd", "attn_fwd_noalloc", "attn_fwd_paged", "attn_fwd_workspace_size", "qkv_rope", "sparse_mqa_fwd", "sparse_mqa_workspace_size", "attn_probs_piece",
            "sparse_mqa_paged_fwd", "topk_indices", "qkv_proj_rope", "rope_cos_sin", "quantize_fp8", "attn_fwd_fp8", "VeaError", "load_library",
            "lib_path", "status_str"]

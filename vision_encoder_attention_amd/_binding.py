@@ -50,6 +50,9 @@ def load_library():
         lib.vea_attn_fwd.argtypes = [i32, vp, i64, vp, i64, vp, i64, vp, vp, i32, i32, i32, i32, i32,
                                      i32, i32, i32, i32, f32, i32, vp, i64, vp, vp, ctypes.c_size_t, vp]
         lib.vea_attn_fwd.restype = i32
+        lib.vea_attn_fwd_noalloc.argtypes = [i32, vp, i64, vp, i64, vp, i64, vp, vp, i32, i32, i32, i32, i32,
+                                             i32, i32, i32, i32, f32, i32, vp, i64, vp, vp]
+        lib.vea_attn_fwd_noalloc.restype = i32
         lib.vea_attn_fwd_paged.argtypes = [vp, i64, vp, i64, vp, i64, vp, i32, i32, i32, vp, vp, i32, i32, i32,
                                            i32, i32, i32, i32, i32, i32, f32, i32, vp, i64, vp, vp,
                                            ctypes.c_size_t, vp]
@@ -199,6 +202,36 @@ def attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, causal, scale, out, lse=None, 
                               k.shape[1], q.shape[2], 1 if causal else 0, float(scale), int(piece_rows),
                               _ptr(out), os_, _ptr(lse), _ptr(workspace),
                               0 if workspace is None else workspace.numel(), _stream(q))
+    _check(st)
+    return out, lse
+
+
+def attn_fwd_noalloc(q, k, v, cu_seqlens_q, cu_seqlens_k, causal, scale, out, lse=None, *, piece_rows=0,
+                     max_seqlen_q, max_seqlen_k):
+    """attn_fwd for callers that cannot allocate (see vea_attn_fwd_noalloc):
+    the split of the last round uses the library's static scratch, so the
+    call allocates nothing; max_seqlen_q / max_seqlen_k are required (no
+    read-back of cu_seqlens).  Calls that overlap on one GPU race on that
+    scratch."""
+    lib = load_library()
+    qs, ks, vs, os_ = (_token_major(q, "q"), _token_major(k, "k"), _token_major(v, "v"),
+                       _token_major(out, "out"))
+    _int32_dev(cu_seqlens_q, "cu_seqlens_q")
+    _int32_dev(cu_seqlens_k, "cu_seqlens_k")
+    dt = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype or out.dtype != q.dtype:
+        raise TypeError("q, k, v and out must share a dtype")
+    if lse is not None:
+        torch = _torch()
+        if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (q.shape[1], q.shape[0]):
+            raise ValueError("lse must be contiguous float32 [Hq, total_q]")
+    torch = _torch()
+    with torch.cuda.device(q.device):
+        st = lib.vea_attn_fwd_noalloc(dt, _ptr(q), qs, _ptr(k), ks, _ptr(v), vs, _ptr(cu_seqlens_q),
+                                      _ptr(cu_seqlens_k), cu_seqlens_q.numel() - 1, q.shape[0], k.shape[0],
+                                      int(max_seqlen_q), int(max_seqlen_k), q.shape[1], k.shape[1], q.shape[2],
+                                      1 if causal else 0, float(scale), int(piece_rows), _ptr(out), os_, _ptr(lse),
+                                      _stream(q))
     _check(st)
     return out, lse
 

@@ -143,6 +143,8 @@ const char* vea_status_str(int status) {
     case VEA_ERANGE: return "VEA_ERANGE: index data out of range (VEA_CHECK)";
     case VEA_EWORKSPACE: return "VEA_EWORKSPACE: workspace too small";
     case VEA_EHIP: return "VEA_EHIP: HIP runtime error";
+    case VEA_ESCRATCH:
+      return "VEA_ESCRATCH: the call needs more scratch than vea_attn_fwd_noalloc's static array (36 MiB)";
     default: return "unknown vea status";
   }
 }
@@ -322,6 +324,25 @@ int vea_attn_fwd(int dtype, const void* q, int64_t q_tok_stride, const void* k, 
   return dense_fwd(dtype, q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, nullptr, 0, 0, 0, cu_seqlens_q,
                    cu_seqlens_k, batch, total_q, total_k, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv,
                    head_dim, causal, scale, piece_rows, out, out_tok_stride, lse, workspace, workspace_bytes, stream);
+}
+
+int vea_attn_fwd_noalloc(int dtype, const void* q, int64_t q_tok_stride, const void* k, int64_t k_tok_stride,
+                         const void* v, int64_t v_tok_stride, const int32_t* cu_seqlens_q,
+                         const int32_t* cu_seqlens_k, int batch, int total_q, int total_k, int max_seqlen_q,
+                         int max_seqlen_k, int num_heads_q, int num_heads_kv, int head_dim, int causal, float scale,
+                         int piece_rows, void* out, int64_t out_tok_stride, float* lse, void* stream) {
+  Range range("vea_attn_fwd_noalloc");
+  // the split plan of vea_attn_fwd for these sizes, served from the static scratch
+  size_t need = 0;
+  int st = vea_attn_fwd_workspace_size(dtype, batch, total_q, total_k, max_seqlen_q, max_seqlen_k, num_heads_q,
+                                       num_heads_kv, head_dim, causal, piece_rows, &need);
+  if (st != VEA_OK) return st;
+  if (need > VEA_ATTN_NOALLOC_SCRATCH_BYTES) return VEA_ESCRATCH;
+  void* ws = nullptr;
+  if (need > 0 && attn_noalloc_scratch(&ws) != hipSuccess) return VEA_EHIP;
+  return dense_fwd(dtype, q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, nullptr, 0, 0, 0, cu_seqlens_q,
+                   cu_seqlens_k, batch, total_q, total_k, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv,
+                   head_dim, causal, scale, piece_rows, out, out_tok_stride, lse, ws, need, stream);
 }
 
 int vea_attn_fwd_paged(const void* q, int64_t q_tok_stride, const void* k_cache, int64_t k_tok_stride,

@@ -45,7 +45,11 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
+#include <vector>
+
+#include "../../include/vea.h"
 
 namespace vea {
 namespace {
@@ -1169,7 +1173,32 @@ __global__ __launch_bounds__(256) void attn_probs_kernel(ProbsParams p) {
   *dst = expf(p.scale * dot - l);
 }
 
+// Scratch of vea_attn_fwd_noalloc: the split chunks of the last round of
+// workgroups (at most one chunk per resident workgroup).  Host code never
+// passes the array's name to a kernel: its device address on the current
+// device comes from attn_noalloc_scratch below.
+__device__ __align__(256) unsigned char scratch[VEA_ATTN_NOALLOC_SCRATCH_BYTES];
+
 }  // namespace
+
+hipError_t attn_noalloc_scratch(void** ptr) {
+  *ptr = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::vector<void*> addr;                       // per device, resolved once
+  std::lock_guard<std::mutex> lock(mu);
+  if ((size_t)dev >= addr.size()) addr.resize(dev + 1, nullptr);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // with device `dev` current
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 DenseSplit dense_split_plan(int units, int empty, int slots, int key_tiles) {
   // Units go out in grid order, `slots` at a time; the first `empty` have no

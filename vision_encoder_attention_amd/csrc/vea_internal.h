@@ -89,6 +89,11 @@ __host__ __device__ inline int wg_slot(int i, int grid, int perm) {
   return (int)(((int64_t)i * perm) % grid);
 }
 
+// Device address of the calling device's static scratch of
+// vea_attn_fwd_noalloc (VEA_ATTN_NOALLOC_SCRATCH_BYTES), resolved once per
+// device; hipSuccess or the runtime's error.
+hipError_t attn_noalloc_scratch(void** ptr);
+
 // The permutation VEA_DEBUG_WG_ORDER asks for ("reverse" or "stride"; unset
 // or anything else: 0) for a grid of `grid` workgroups.
 int wg_order_perm(int grid);
