@@ -53,6 +53,15 @@ def dense_flops(case) -> float:
     return 4.0 * case.head_dim * case.num_heads_q * pairs
 
 
+def attn_bytes(case) -> float:
+    """Algorithmic HBM bytes of one attn_fwd launch: q and out (Hq heads), k
+    and v (Hkv heads) once each, and lse (fp32)."""
+    e = 2 if case.dtype == "bf16" else 4
+    d = case.head_dim
+    return float(case.total_q * 2 * case.num_heads_q * d * e + case.total_k * 2 * case.num_heads_kv * d * e
+                 + case.total_q * case.num_heads_q * 4)
+
+
 def rope_bytes(case) -> float:
     """Algorithmic HBM bytes of qkv_rope: read Q and K columns, write q and k, read positions."""
     t = case.total_q
@@ -178,8 +187,7 @@ def dense_entry(torch, wname, case, st, tm, steps, with_rope):
            "flops": fl, "tokens": case.total_q, "causal": causal,
            "heads": [case.num_heads_q, case.num_heads_kv], "head_dim": d, "piece_rows": case.piece_rows,
            "last_round_split": split,
-           "roofline": roofline("mfma", kname, tflops, PEAK_BF16_TFLOPS, "TFLOP/s", prof,
-                                4 * case.total_q * case.num_heads_q * d * 2)}
+           "roofline": roofline("mfma", kname, tflops, PEAK_BF16_TFLOPS, "TFLOP/s", prof, attn_bytes(case))}
     if with_rope:
         rb = rope_bytes(case)
         r = tm.stats("qkv_rope")

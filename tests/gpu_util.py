@@ -58,3 +58,16 @@ def assert_f32_close(got, ref, name):
     assert m["finite_match"], "%s: -inf/NaN positions differ" % name
     assert m["normwise"] <= F32_NORMWISE, "%s: normwise rel %.3g > %.1g" % (name, m["normwise"], F32_NORMWISE)
     return m
+
+
+def first_split_tiles(head_dim, heads=16):
+    """Smallest number of 128-row query tiles per head of one non-causal bf16
+    image (one piece) for which attn_fwd splits the last round of workgroups
+    on this device (the round size depends on the CU count and the kernel's
+    occupancy, so tests ask the library instead of assuming it)."""
+    import vision_encoder_attention_amd as vea
+    for t in range(1, 4096):
+        n = 128 * t
+        if vea.attn_fwd_workspace_size(1, 1, n, n, n, n, heads, heads, head_dim, False, 0) > 0:
+            return t
+    raise RuntimeError("no split found")

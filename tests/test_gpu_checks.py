@@ -111,11 +111,11 @@ def test_two_streams_match_sequential_results(torch):
 def _order_cases(torch):
     """Launches that cover every kernel family and launch shape the order
     check touches: a pieced image with the split of the last round (its tile
-    count just above one round of workgroups: 3 per CU for d 64), a causal
+    count just above one round of resident workgroups), a causal
     GQA varlen batch with empty sequences, the fp32 path, decode units with
     key-range splits, FP8 attention and sparse MQA with its split."""
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    tiles = (cus * 3) // 16 + 4
+    from tests.gpu_util import first_split_tiles
+    tiles = first_split_tiles(64) + 4
     return dict(
         vision=W.vision(grid_rows=tiles, grid_cols=128, heads=16, d=64, piece_rows=128 * ((tiles + 1) // 2),
                         seed=720),

@@ -38,8 +38,8 @@ def _both(torch, case):
 
 def test_noalloc_equals_the_workspace_entry_point(torch):
     import vision_encoder_attention_amd as vea
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    tiles = (cus * 3) // 16 + 4
+    from tests.gpu_util import first_split_tiles
+    tiles = first_split_tiles(64) + 4
     cases = [W.vision(),                                             # the benchmarked image: 23.8 MB of split chunks
              W.vision(grid_rows=tiles, grid_cols=128, heads=16, d=64, piece_rows=128 * ((tiles + 1) // 2), seed=730),
              W.random_dense([5000], [5000], 16, 16, 128, False, "bf16", seed=731),   # d 128: the largest split

@@ -597,6 +597,509 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
   }
 }
 
+// ======================================== bf16, head_dim 64, one packed sequence
+// The image case (non-causal, packed K/V, no decode units).  At head_dim 64 a
+// 64-key step holds 16 MFMAs per 32 query rows but the same softmax work per
+// logit as at 128, so the kernel is bound by instruction issue rather than by
+// the matrix cores.  Here a workgroup is 2 waves x 64 query rows (the 128-row
+// tile of the other kernels, so the launch layout, the split of the last
+// round and its merge are shared), and each wave holds two independent 32-row
+// blocks:
+//   * every K and V^T operand read from LDS feeds two MFMAs (one per block),
+//     half the LDS traffic per flop of a 32-row wave;
+//   * the two blocks' logit -> softmax -> P V chains are independent, so one
+//     block's exponentials issue while the other's MFMAs run;
+//   * a 2-wave workgroup meets its barrier with less skew than a 4-wave one.
+// K and V of one step are staged together (double-buffered, one barrier per
+// step); the max-free softmax with its rare path is the other kernel's.
+constexpr int kD64Threads = 128;
+
+template <bool PAGED>
+__global__ __launch_bounds__(kD64Threads, 2) void attn_fwd_d64_kernel(DenseParams p) {
+  constexpr int D = 64, BN = 64, CPR = D / 8;
+  constexpr int TILE = BN * D * 2;                       // 8 KB: one K (or V) tile
+  constexpr int LOADS = TILE / (kD64Threads * 16);       // 16-byte DMA loads per lane per tile
+  static_assert(LOADS == 4, "tile split");
+  using C = Cfg<D>;                                      // swizzle of the 16-byte chunks
+  __shared__ __attribute__((aligned(1024))) unsigned char kst0[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char kst1[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char vst0[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char vst1[TILE];
+
+  const int slot = wg_slot(blockIdx.x, p.grid, p.wg_perm);
+  int id = slot, chunk = 0;
+  const bool split = id >= p.full_units;
+  if (split) {
+    const int u2 = id - p.full_units;
+    const int tu = u2 / p.nsplit;
+    chunk = u2 - tu * p.nsplit;
+    id = p.full_units + tu;
+  }
+  int b, h, t;
+  decode_unit(p, id, b, h, t);
+  TileRange tr;
+  if (!tile_range(p, b, t, kDenseBM, false, tr)) return;   // uniform over the workgroup
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int g2 = lane >> 5;
+  const int kvh = h / p.group;
+  const int rw0 = tr.row0 + wave * 64;                   // first row of this wave
+  // A wave whose 64 rows all lie past the tile's end (the short last tile of
+  // a piece) issues its DMA share and meets every barrier, nothing else.
+  const bool live = rw0 < tr.row_end;
+
+  // ---- Q fragments of the two blocks: Q[row][16 ks + 8 g2 .. +7]
+  u32x4 qf[2][D / 16];
+  bool qvalid[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int qi = rw0 + 32 * r + l32;
+    qvalid[r] = qi < tr.row_end;
+    const uint16_t* src = (const uint16_t*)p.q + (int64_t)(tr.qs + (qvalid[r] ? qi : tr.row0)) * p.q_stride +
+                          (int64_t)h * D + 8 * g2;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const u32x4 v = *(const u32x4*)(src + 16 * ks);
+      qf[r][ks] = qvalid[r] ? v : (u32x4){0u, 0u, 0u, 0u};
+    }
+  }
+  float c = fabsf(p.scale) * kLog2e;
+  if (p.scale < 0.f) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) qf[r][ks] ^= (u32x4){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+  }
+  c = fmaxf(c, FLT_MIN);
+
+  const int n_all = (tr.kend + BN - 1) / BN;
+  int kt0 = 0, n_tiles = n_all;
+  if (split) {
+    kt0 = (n_all * chunk) / p.nsplit;
+    n_tiles = (n_all * (chunk + 1)) / p.nsplit - kt0;
+  }
+  const int n_full = tr.kend / BN - kt0;                 // (local) tiles without the key tail
+
+  // ---- DMA of K/V tiles into LDS (see the other kernel; 2 waves here)
+  const int64_t ksb = p.k_stride * 2, vsb = p.v_stride * 2;
+  int voff_k[LOADS], voff_v[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int sl = (wave * LOADS + i) * 64 + lane;
+    const int r = sl / CPR, ch = (sl % CPR) ^ C::swz(r);
+    voff_k[i] = (int)(r * ksb) + 16 * ch;
+    voff_v[i] = (int)(r * vsb) + 16 * ch;
+  }
+  // Key row j of this sequence: row tr.ks + j of the packed K/V, or for a
+  // paged cache row j's page from the sequence's block-table row (a 64-key
+  // tile never spans two pages).
+  const unsigned char* kbase =
+      (const unsigned char*)p.k + ((PAGED ? 0 : (int64_t)tr.ks * p.k_stride) + (int64_t)kvh * D) * 2;
+  const unsigned char* vbase =
+      (const unsigned char*)p.v + ((PAGED ? 0 : (int64_t)tr.ks * p.v_stride) + (int64_t)kvh * D) * 2;
+  auto phys_row = [&](int j) __attribute__((always_inline)) -> int64_t {
+    if constexpr (!PAGED) return j;
+    const int64_t page = p.block_table[(int64_t)b * p.max_pages + (j >> p.page_shift)];
+    return (page << p.page_shift) | (j & ((1 << p.page_shift) - 1));
+  };
+  auto issue = [&](int kt, const unsigned char* base, int64_t sb, const int* voff, unsigned char* stage) __attribute__((always_inline)) {
+    const int j0 = (kt0 + kt) * BN;
+    const int rows = min(tr.kend - j0, BN);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(base + phys_row(j0) * sb), (short)0, (int)(rows * sb), 0x00020000);
+    unsigned char* dst = stage + wave * LOADS * 1024;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16,
+                                               (unsigned)voff[i], 0, 0, 0);
+  };
+
+  // ---- per-lane LDS read offsets (the other kernel's)
+  const int sw = C::swz(l32);
+  int koff[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = l32 * D * 2 + 16 * ((2 * ks + g2) ^ sw);
+  const int i16 = lane & 15, G16 = lane >> 4, nhalf = G16 & 1;
+  const int vr0 = 4 * g2 + (i16 >> 2);
+  int voff0[D / 32], voff1[D / 32];
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb) {
+    const int ch = 4 * nb + 2 * nhalf + ((i16 & 3) >> 1);
+    voff0[nb] = vr0 * D * 2 + 16 * (ch ^ C::swz(vr0)) + 8 * (i16 & 1);
+    voff1[nb] = (vr0 + 8) * D * 2 + 16 * (ch ^ C::swz(vr0 + 8)) + 8 * (i16 & 1);
+  }
+
+  floatx16 o[2][D / 32];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) o[r][nb] = (floatx16){};
+  float m_used[2] = {-INFINITY, -INFINITY};   // reference max (times c, log2 domain)
+  float m_use[2] = {0.f, 0.f};                // m_used, or 0 while a row has none
+  float l_run[2] = {0.f, 0.f};                // lane-partial sums of P
+
+  auto mask = [&](int kt, floatx16& s0, floatx16& s1) __attribute__((always_inline)) {
+    const int j0 = (kt0 + kt) * BN + 4 * g2;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = j0 + 8 * (r >> 2) + (r & 3);
+      if (j >= tr.len_k) s0[r] = -INFINITY;
+      if (j + 32 >= tr.len_k) s1[r] = -INFINITY;
+    }
+  };
+  // P = 2^(s c - m), packed bf16 for the P V product; returns the lane's fp32 sum
+  auto softmax_p = [&](const floatx16& s0, const floatx16& s1, float mu, u32x4* pb) __attribute__((always_inline)) -> float {
+    float tq[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const floatx16& sv = kb == 0 ? s0 : s1;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        uint32_t w[4];
+        float pr[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float e0 = fast_exp2(fmaf(sv[8 * hf + 2 * q], c, -mu));
+          const float e1 = fast_exp2(fmaf(sv[8 * hf + 2 * q + 1], c, -mu));
+          pr[q] = e0 + e1;
+          w[q] = pack_bf16x2(e0, e1);
+        }
+        tq[2 * kb + hf] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+        pb[2 * kb + hf] = (u32x4){w[0], w[1], w[2], w[3]};
+      }
+    }
+    return (tq[0] + tq[1]) + (tq[2] + tq[3]);
+  };
+  // Rare part of block r: the tile's row max moves the reference where it
+  // exceeds it by more than 8 (log2 units), with O and l rescaled.
+  auto move_ref = [&](int r, const floatx16& s0, const floatx16& s1) __attribute__((always_inline)) {
+    float mx = vmax(s0[0], s1[0]);
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = vmax(vmax(mx, s0[i]), s1[i]);
+    mx = lane_swap_max(mx);
+    const float mx_sc = (mx == -INFINITY) ? -INFINITY : mx * c;
+    const bool upd = mx_sc > m_used[r] + 8.0f;
+    const float m_new = upd ? mx_sc : m_used[r];
+    const float alpha = upd ? fast_exp2(m_used[r] - m_new) : 1.0f;
+    m_used[r] = m_new;
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) o[r][nb] *= alpha;
+    l_run[r] *= alpha;
+    m_use[r] = (m_new == -INFINITY) ? 0.f : m_new;
+  };
+  // S^T of block r for tile kt from K in global memory: the same operands in
+  // the same order as the LDS path (rows past the key bound clamp to the last
+  // one; they are masked).
+  auto qk_global = [&](int r, int kt, floatx16& s0, floatx16& s1) __attribute__((always_inline)) {
+    const int j0 = (kt0 + kt) * BN;
+    const unsigned char* pa = kbase + phys_row(min(j0 + l32, tr.kend - 1)) * ksb + 16 * g2;
+    const unsigned char* pb2 = kbase + phys_row(min(j0 + 32 + l32, tr.kend - 1)) * ksb + 16 * g2;
+    s0 = (floatx16){};
+    s1 = (floatx16){};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const u32x4 a0 = *(const u32x4*)(pa + 32 * ks);
+      const u32x4 a1 = *(const u32x4*)(pb2 + 32 * ks);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), as_bf16x8(qf[r][ks]), s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), as_bf16x8(qf[r][ks]), s1, 0, 0, 0);
+    }
+  };
+  // Careful key step (the fallback, practically never taken): one block at a
+  // time, with the rare-path check before its P V, so a tile whose P would
+  // grow past 2^8 moves the reference first.  MASK: the step holds the key
+  // tail (only the last step of a range).
+  auto step_careful = [&](int kt, const unsigned char* ks_, const unsigned char* vs_, auto mask_tag)
+      __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      floatx16 s0 = (floatx16){}, s1 = (floatx16){};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const u32x4 a0 = *(const u32x4*)(ks_ + koff[ks]);
+        const u32x4 a1 = *(const u32x4*)(ks_ + 32 * D * 2 + koff[ks]);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), as_bf16x8(qf[r][ks]), s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), as_bf16x8(qf[r][ks]), s1, 0, 0, 0);
+      }
+      if constexpr (MASK) mask(kt, s0, s1);
+      u32x4 pb[4];
+      float t = softmax_p(s0, s1, m_use[r], pb);
+      if (__any(t > 8192.f || m_used[r] == -INFINITY)) {
+        asm volatile("; rare: recompute the logits, move the reference max, recompute P" ::);
+        floatx16 r0, r1;
+        qk_global(r, kt, r0, r1);
+        if constexpr (MASK) mask(kt, r0, r1);
+        move_ref(r, r0, r1);
+        t = softmax_p(r0, r1, m_use[r], pb);
+      }
+      l_run[r] += t;
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) {
+          const u32x2 lo = lds_read_tr(vs_ + st * 16 * D * 2 + voff0[nb]);
+          const u32x2 hi = lds_read_tr(vs_ + st * 16 * D * 2 + voff1[nb]);
+          const u32x4 vop = (u32x4){lo[0], lo[1], hi[0], hi[1]};
+          o[r][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vop), as_bf16x8(pb[st]), o[r][nb], 0, 0, 0);
+        }
+    }
+  };
+
+  bool bad = false;
+  // P of one 32-key half (accumulator s) with reference mu: two packed
+  // operands (k-steps 2h, 2h + 1) and the lane's fp32 sum.
+  auto half_p = [&](const floatx16& sv, float mu, u32x4* pb) __attribute__((always_inline)) -> float {
+    float tq[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      uint32_t w[4];
+      float pr[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float e0 = fast_exp2(fmaf(sv[8 * hf + 2 * q], c, -mu));
+        const float e1 = fast_exp2(fmaf(sv[8 * hf + 2 * q + 1], c, -mu));
+        pr[q] = e0 + e1;
+        w[q] = pack_bf16x2(e0, e1);
+      }
+      tq[hf] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      pb[hf] = (u32x4){w[0], w[1], w[2], w[3]};
+    }
+    return tq[0] + tq[1];
+  };
+  auto set_ref = [&](int r, const floatx16& s0, const floatx16& s1) __attribute__((always_inline)) {
+    float mx = vmax(s0[0], s1[0]);
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = vmax(vmax(mx, s0[i]), s1[i]);
+    mx = lane_swap_max(mx);
+    m_used[r] = (mx == -INFINITY) ? -INFINITY : mx * c;
+    m_use[r] = (m_used[r] == -INFINITY) ? 0.f : m_used[r];
+  };
+  // Fast key step: no branch.  The first step of a range sets each row's
+  // reference from its own maximum (FIRST); later steps use it unchanged,
+  // however large P grows, and only record (in `bad`, per lane) a tile whose
+  // lane sum is not below 2^100 (so some P may have overflowed).  A workgroup
+  // with any such tile recomputes its range with the careful step.  With the
+  // reference at the first tile's maximum a P can exceed 1 only where a later
+  // logit exceeds every logit of the first tile; fp32 and bf16 keep their
+  // relative precision up to 2^127, so such P change no result unless they
+  // overflow.  The tile is processed in two 32-key halves, each in the order
+  // S_A, S_B (with A's softmax), P_A V (with B's softmax), P_B V, so that one
+  // block's exponentials issue under the other block's MFMAs while only a
+  // half tile of logits, P and operands is live.
+  auto step_fast = [&](int kt, const unsigned char* ks_, const unsigned char* vs_, auto mask_tag, auto first_tag)
+      __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr bool FIRST = decltype(first_tag)::value;
+    if constexpr (FIRST) {
+      // once per range, one block at a time: the reference is the block's
+      // row maximum over the whole first tile
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        floatx16 s0 = (floatx16){}, s1 = (floatx16){};
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const u32x4 a0 = *(const u32x4*)(ks_ + koff[ks]);
+          const u32x4 a1 = *(const u32x4*)(ks_ + 32 * D * 2 + koff[ks]);
+          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), as_bf16x8(qf[r][ks]), s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), as_bf16x8(qf[r][ks]), s1, 0, 0, 0);
+        }
+        if constexpr (MASK) mask(kt, s0, s1);
+        set_ref(r, s0, s1);
+        u32x4 pb[4];
+        const float t = softmax_p(s0, s1, m_use[r], pb);
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+          for (int nb = 0; nb < D / 32; ++nb) {
+            const u32x2 lo = lds_read_tr(vs_ + st * 16 * D * 2 + voff0[nb]);
+            const u32x2 hi = lds_read_tr(vs_ + st * 16 * D * 2 + voff1[nb]);
+            const u32x4 vop = (u32x4){lo[0], lo[1], hi[0], hi[1]};
+            o[r][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vop), as_bf16x8(pb[st]), o[r][nb], 0, 0, 0);
+          }
+        bad = bad || !(t < 0x1p100f);
+        l_run[r] += t;
+      }
+      return;
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      // keys 32 hh .. 32 hh + 31 of the tile: K rows, V^T k-steps 2 hh, 2 hh + 1
+      u32x4 kop[D / 16];
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) kop[ks] = *(const u32x4*)(ks_ + hh * 32 * D * 2 + koff[ks]);
+      floatx16 sa = (floatx16){}, sb = (floatx16){};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop[ks]), as_bf16x8(qf[0][ks]), sa, 0, 0, 0);
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+        sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop[ks]), as_bf16x8(qf[1][ks]), sb, 0, 0, 0);
+      if constexpr (MASK) {
+        const int j0 = (kt0 + kt) * BN + 32 * hh + 4 * g2;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool out_of_range = j0 + 8 * (r >> 2) + (r & 3) >= tr.len_k;
+          if (out_of_range) {
+            sa[r] = -INFINITY;
+            sb[r] = -INFINITY;
+          }
+        }
+      }
+      u32x4 pa[2], pb[2];
+      const float ta = half_p(sa, m_use[0], pa);
+      // S_A, then S_B's MFMAs one at a time between slices of A's softmax
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      }
+      u32x4 vop[2][D / 32];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) {
+          const int st = 2 * hh + s2;
+          const u32x2 lo = lds_read_tr(vs_ + st * 16 * D * 2 + voff0[nb]);
+          const u32x2 hi = lds_read_tr(vs_ + st * 16 * D * 2 + voff1[nb]);
+          vop[s2][nb] = (u32x4){lo[0], lo[1], hi[0], hi[1]};
+        }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb)
+          o[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vop[s2][nb]), as_bf16x8(pa[s2]), o[0][nb], 0, 0, 0);
+      const float tb = half_p(sb, m_use[1], pb);
+      // P_A V, then P_B V with B's softmax interleaved into the first
+#pragma unroll
+      for (int i = 0; i < 2 * (D / 32); ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb)
+          o[1][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vop[s2][nb]), as_bf16x8(pb[s2]), o[1][nb], 0, 0, 0);
+      bad = bad || !(ta < 0x1p100f) || !(tb < 0x1p100f);   // NaN counts as bad
+      l_run[0] += ta;
+      l_run[1] += tb;
+    }
+  };
+
+  // ---- key loop: stage kt % 2 holds K(kt) and V(kt); the DMA of tile kt+1
+  // is issued right after the barrier that retires tile kt-1's stage.  Steps
+  // before n_full hold no key tail.
+  auto iter = [&](int kt, auto odd_tag, auto mask_tag, auto first_tag, auto careful_tag)
+      __attribute__((always_inline)) {
+    constexpr bool ODD = decltype(odd_tag)::value;
+    unsigned char* k_rd = ODD ? kst1 : kst0;
+    unsigned char* v_rd = ODD ? vst1 : vst0;
+    unsigned char* k_wr = ODD ? kst0 : kst1;
+    unsigned char* v_wr = ODD ? vst0 : vst1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // this lane's DMA of tile kt landed
+    __syncthreads();                                     // everyone's; tile kt-1's stage is free
+    if (kt + 1 < n_tiles) {
+      issue(kt + 1, kbase, ksb, voff_k, k_wr);
+      issue(kt + 1, vbase, vsb, voff_v, v_wr);
+    }
+    if (live) {
+      if constexpr (decltype(careful_tag)::value) step_careful(kt, k_rd, v_rd, mask_tag);
+      else step_fast(kt, k_rd, v_rd, mask_tag, first_tag);
+      if (kt + 1 == n_tiles) {
+        // After the range's last MFMAs the compiler may reuse their A/B
+        // operand registers right away (register copies where the loop's
+        // paths join).  A write that lands before an MFMA still waiting in
+        // the matrix pipe has read its operands corrupts that product; the
+        // pipe's depth depends on the other wave's MFMAs, so the result
+        // would depend on timing.  32 wait states let the pipe drain first.
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  const int n_plain = min(n_tiles, max(n_full, 0));
+  auto run = [&](auto careful_tag) __attribute__((always_inline)) {
+    constexpr bool CAREFUL = decltype(careful_tag)::value;
+    using F = std::false_type;
+    using T = std::true_type;
+    using FIRST = std::integral_constant<bool, !CAREFUL>;
+    issue(0, kbase, ksb, voff_k, kst0);
+    issue(0, vbase, vsb, voff_v, vst0);
+    if (n_plain > 0) iter(0, F{}, F{}, FIRST{}, careful_tag);
+    else iter(0, F{}, T{}, FIRST{}, careful_tag);         // the only step holds the key tail
+    int kt = 1;
+    for (; kt + 1 < n_plain; kt += 2) {
+      iter(kt, T{}, F{}, F{}, careful_tag);
+      iter(kt + 1, F{}, F{}, F{}, careful_tag);
+    }
+    if (kt < n_plain) {                                  // one more plain step (odd), then the tail (even)
+      iter(kt, T{}, F{}, F{}, careful_tag);
+      if (kt + 1 < n_tiles) iter(kt + 1, F{}, T{}, F{}, careful_tag);
+    } else if (kt < n_tiles) {                           // the tail step (odd)
+      iter(kt, T{}, T{}, F{}, careful_tag);
+    }
+  };
+  if (n_tiles > 0) {
+    run(std::false_type{});
+    // the decision is the workgroup's: the careful pass stages tiles with
+    // barriers that both waves must meet
+    if (__syncthreads_or(bad ? 1 : 0)) {
+      asm volatile("; rare: recompute the range with per-step reference moves" ::);
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) o[r][nb] = (floatx16){};
+        m_used[r] = -INFINITY;
+        m_use[r] = 0.f;
+        l_run[r] = 0.f;
+      }
+      run(std::true_type{});
+    }
+  }
+
+  // ---- epilogue
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const float l_tot = lane_swap_add(l_run[r]);
+    const int rl = wave * 64 + 32 * r + l32;             // row within the tile
+    if (split) {
+      float* w = p.ws + (size_t)(slot - p.full_units) * (kDenseBM * (D + 2));
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *(floatx4*)(w + rl * D + 32 * nb + 8 * r4 + 4 * g2) =
+              (floatx4){o[r][nb][4 * r4], o[r][nb][4 * r4 + 1], o[r][nb][4 * r4 + 2], o[r][nb][4 * r4 + 3]};
+      if (g2 == 0) {
+        w[kDenseBM * D + rl] = m_used[r];
+        w[kDenseBM * D + kDenseBM + rl] = l_tot;
+      }
+      continue;
+    }
+    if (!qvalid[r]) continue;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const int qi = rw0 + 32 * r + l32;
+    uint16_t* dst = (uint16_t*)p.out + (int64_t)(tr.qs + qi) * p.o_stride + (int64_t)h * D + 4 * g2;
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const floatx16& ov = o[r][nb];
+        const u32x2 w = (u32x2){pack_bf16x2(ov[4 * r4 + 0] * inv, ov[4 * r4 + 1] * inv),
+                                pack_bf16x2(ov[4 * r4 + 2] * inv, ov[4 * r4 + 3] * inv)};
+        *(u32x2*)(dst + 32 * nb + 8 * r4) = w;
+      }
+    if (p.lse != nullptr && g2 == 0)
+      p.lse[(int64_t)h * p.total_q + tr.qs + qi] = l_tot > 0.f ? (m_used[r] + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
 // =============================================================== fp8 path
 // Attention on OCP FP8 E4M3 inputs (v_mfma_scale_f32_32x32x64_f8f6f4, unit
 // scales).  FP8 is allowed for the matrix products, the softmax statistics
@@ -1224,8 +1727,8 @@ size_t dense_chunk_bytes(int head_dim) { return (size_t)kDenseBM * (head_dim + 2
 int dense_bf16_blocks_per_cu(int head_dim) {
   int n = 0;
   hipError_t e = hipErrorInvalidValue;
-  if (head_dim == 64)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_bf16_kernel<64, false, false>, 256, 0);
+  if (head_dim == 64)   // the packed image kernel (the one the split plan serves)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_d64_kernel<false>, kD64Threads, 0);
   else if (head_dim == 128)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_bf16_kernel<128, false, false>, 256, 0);
   return e == hipSuccess ? n : 0;
@@ -1238,12 +1741,16 @@ void launch_dense(const DenseParams& p, bool causal, bool paged, dim3 grid, dim3
     else hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, false, true>), grid, block, 0, s, p);
     return;
   }
-  if (paged) {
+  if (!causal && D == 64) {                             // one kernel for both layouts: paged = packed bitwise
+    if (paged) hipLaunchKernelGGL(attn_fwd_d64_kernel<true>, grid, dim3(kD64Threads), 0, s, p);
+    else hipLaunchKernelGGL(attn_fwd_d64_kernel<false>, grid, dim3(kD64Threads), 0, s, p);
+  } else if (paged) {
     if (causal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, true>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, true>), grid, block, 0, s, p);
+  } else if (causal) {
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, false>), grid, block, 0, s, p);
   } else {
-    if (causal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, false>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, false>), grid, block, 0, s, p);
   }
 }
 

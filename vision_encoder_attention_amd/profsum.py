@@ -19,7 +19,7 @@ reports, with the commands that produced the raw data):
     python -m vision_encoder_attention_amd.profsum trace DIR [--last N] [--match TEXT ...]
     python -m vision_encoder_attention_amd.profsum counters --kernel TEXT --fetch DIR --write DIR
         --copy-fetch DIR --copy-write DIR --algorithmic-bytes B --sources FILE ... [--mfma DIR]
-        [--last N]
+        [--extra DIR ...] [--last N]
 """
 from __future__ import annotations
 
@@ -102,7 +102,8 @@ def _counter(dir_, counter, kernel):
     return vals
 
 
-def counters_report(kernel, fetch, write, copy_fetch, copy_write, algorithmic_bytes, sources, mfma=None, last=0):
+def counters_report(kernel, fetch, write, copy_fetch, copy_write, algorithmic_bytes, sources, mfma=None, last=0,
+                    extra=None, xcds=8, simds=1024):
     out = []
     f = _counter(fetch, "FETCH_SIZE", kernel)
     w = _counter(write, "WRITE_SIZE", kernel)
@@ -133,24 +134,41 @@ def counters_report(kernel, fetch, write, copy_fetch, copy_write, algorithmic_by
            "write_bytes": int(round(wr)), "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
            "algorithmic_bytes": int(algorithmic_bytes), "sources": list(sources),
            "source_digest": source_digest(sources)}
-    if mfma:
-        rows = [r for r in _rows(_one(mfma, "_counter_collection.csv")) if kernel in r["Kernel_Name"]]
-        names = sorted(set(r["Counter_Name"] for r in rows))
-        means = {}
-        for n in names:
+    means = {}
+    for run in ([mfma] if mfma else []) + list(extra or []):
+        rows = [r for r in _rows(_one(run, "_counter_collection.csv")) if kernel in r["Kernel_Name"]]
+        for n in sorted(set(r["Counter_Name"] for r in rows)):
             vs = [(int(r["Dispatch_Id"]), float(r["Counter_Value"])) for r in rows if r["Counter_Name"] == n]
             vs.sort()
             vv = [v for _, v in vs][-last:] if last else [v for _, v in vs]
             means[n] = statistics.mean(vv)
+    if means:
         out.append("")
-        out.append("counter means per dispatch: " + ", ".join("%s %.6g" % (n, means[n]) for n in names))
-        for n in names:
+        out.append("counter means per dispatch (summed over the device's XCDs / SEs / SIMDs):")
+        for n in sorted(means):
+            out.append("  %-32s %.6g" % (n, means[n]))
+        gui = means.get("GRBM_GUI_ACTIVE")
+        cyc = gui / xcds if gui else None           # kernel cycles (GUI_ACTIVE is summed over the XCDs)
+        for n in means:
             if n.startswith("SQ_INSTS_VALU_MFMA_MOPS_"):
                 out.append("  %s x 512 = %.4g MFMA flops per launch" % (n, means[n] * 512))
                 rec["mfma_flops_per_launch"] = means[n] * 512
-        if "SQ_VALU_MFMA_BUSY_CYCLES" in means and "GRBM_GUI_ACTIVE" in means:
-            rec["mfma_busy_cycles"] = means["SQ_VALU_MFMA_BUSY_CYCLES"]
-            rec["gui_active_cycles"] = means["GRBM_GUI_ACTIVE"]
+        if cyc:
+            out.append("  kernel cycles (GRBM_GUI_ACTIVE / %d XCDs): %.6g" % (xcds, cyc))
+            rec["kernel_cycles"] = cyc
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in means:
+                f = means["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * simds)
+                out.append("  MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (cycles x %d SIMDs) = %.3f" % (simds, f))
+                rec["mfma_busy_frac"] = round(f, 4)
+            if "SQ_ACTIVE_INST_VALU" in means and "SQ_WAVE_CYCLES" in means:
+                out.append("  VALU-active share of wave cycles: SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES = %.3f"
+                           % (means["SQ_ACTIVE_INST_VALU"] / means["SQ_WAVE_CYCLES"]))
+            if "SQ_INSTS_VALU" in means:
+                out.append("  VALU instructions per SIMD-cycle: SQ_INSTS_VALU / (cycles x %d SIMDs) = %.3f"
+                           % (simds, means["SQ_INSTS_VALU"] / (cyc * simds)))
+            if "SQ_VALU_MFMA_COEXEC_CYCLES" in means:
+                out.append("  MFMA co-execution: SQ_VALU_MFMA_COEXEC_CYCLES / (cycles x %d SIMDs) = %.3f"
+                           % (simds, means["SQ_VALU_MFMA_COEXEC_CYCLES"] / (cyc * simds)))
     out.append("")
     out.append("RESULT " + json.dumps(rec))
     return "\n".join(out)
@@ -168,6 +186,9 @@ def main(argv=None):
     for n in ("fetch", "write", "copy-fetch", "copy-write"):
         c.add_argument("--" + n, required=True)
     c.add_argument("--mfma")
+    c.add_argument("--extra", nargs="*", help="further counter runs whose means are listed")
+    c.add_argument("--xcds", type=int, default=8)
+    c.add_argument("--simds", type=int, default=1024)
     c.add_argument("--algorithmic-bytes", type=float, required=True)
     c.add_argument("--sources", nargs="+", required=True)
     c.add_argument("--last", type=int, default=0)
@@ -176,7 +197,7 @@ def main(argv=None):
         print(trace_report(a.dir, a.last, a.match))
     else:
         print(counters_report(a.kernel, a.fetch, a.write, a.copy_fetch, a.copy_write, a.algorithmic_bytes, a.sources,
-                              a.mfma, a.last))
+                              a.mfma, a.last, a.extra, a.xcds, a.simds))
 
 
 if __name__ == "__main__":
