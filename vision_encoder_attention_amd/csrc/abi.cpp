@@ -169,9 +169,10 @@ int dense_shape_status(int dtype, int batch, int total_q, int total_k, int max_s
 }
 
 // Launch shape: (sequence, piece, tile, head) units.
-int dense_layout(int batch, int max_seqlen_q, int num_heads_q, int piece_rows, DenseParams& p) {
+int dense_layout(int batch, int max_seqlen_q, int num_heads_q, int piece_rows, int bm, DenseParams& p) {
   p.qb = (piece_rows > 0 && piece_rows < max_seqlen_q) ? piece_rows : max_seqlen_q;
-  p.tiles_per_piece = (p.qb + kDenseBM - 1) / kDenseBM;
+  p.bm = bm;
+  p.tiles_per_piece = (p.qb + bm - 1) / bm;
   const int64_t pieces = ((int64_t)max_seqlen_q + p.qb - 1) / p.qb;
   const int64_t tps = pieces * p.tiles_per_piece;
   const int64_t units = (int64_t)batch * tps * num_heads_q;
@@ -186,7 +187,7 @@ int dense_layout(int batch, int max_seqlen_q, int num_heads_q, int piece_rows, D
   p.max_pages = 0;
   p.q_scale = p.k_scale = p.v_scale = nullptr;
   p.dec_group = 0;
-  p.ws_rows = kDenseBM;
+  p.ws_rows = bm;
   p.grid = 0;
   p.wg_perm = 0;
   return VEA_OK;
@@ -204,7 +205,7 @@ int dense_split(int dtype, int batch, int total_q, int total_k, int num_heads_q,
   const int per_cu = dense_bf16_blocks_per_cu(head_dim);
   int64_t real_tiles = 0;                               // tiles with rows, per head
   for (int64_t r0 = 0; r0 < total_q; r0 += p.qb)
-    real_tiles += (std::min<int64_t>(p.qb, total_q - r0) + kDenseBM - 1) / kDenseBM;
+    real_tiles += (std::min<int64_t>(p.qb, total_q - r0) + p.bm - 1) / p.bm;
   const int empty = p.units - (int)(real_tiles * num_heads_q);
   plan = dense_split_plan(p.units, std::max(empty, 0), cus * per_cu, (total_k + 63) / 64);
   return VEA_OK;
@@ -222,12 +223,12 @@ int vea_attn_fwd_workspace_size(int dtype, int batch, int total_q, int total_k, 
   if (st != VEA_OK) return st;
   if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return VEA_OK;
   DenseParams p;
-  st = dense_layout(batch, max_seqlen_q, num_heads_q, piece_rows, p);
+  st = dense_layout(batch, max_seqlen_q, num_heads_q, piece_rows, dense_tile_rows(dtype == VEA_BF16, head_dim, causal), p);
   if (st != VEA_OK) return st;
   DenseSplit plan;
   st = dense_split(dtype, batch, total_q, total_k, num_heads_q, head_dim, causal, p, plan);
   if (st != VEA_OK) return st;
-  *bytes = (size_t)plan.chunks * dense_chunk_bytes(head_dim);
+  *bytes = (size_t)plan.chunks * dense_chunk_bytes(p.bm, head_dim);
   return VEA_OK;
 }
 
@@ -289,7 +290,8 @@ int dense_fwd(int dtype, const void* q, int64_t q_tok_stride, const void* k, int
   p.q_stride = q_tok_stride; p.k_stride = k_tok_stride; p.v_stride = v_tok_stride; p.o_stride = out_tok_stride;
   p.batch = batch; p.total_q = total_q; p.total_k = total_k;
   p.hq = num_heads_q; p.hkv = num_heads_kv; p.group = num_heads_q / num_heads_kv;
-  st = dense_layout(batch, max_seqlen_q, num_heads_q, piece_rows, p);
+  st = dense_layout(batch, max_seqlen_q, num_heads_q, piece_rows, dense_tile_rows(dtype == VEA_BF16, head_dim, causal),
+                    p);
   if (st != VEA_OK) return st;
   p.xcd_map = (num_heads_kv % 8 == 0) ? 1 : 0;
   p.scale = scale;
@@ -301,7 +303,7 @@ int dense_fwd(int dtype, const void* q, int64_t q_tok_stride, const void* k, int
     st = dense_split(dtype, batch, total_q, total_k, num_heads_q, head_dim, causal, p, plan);
     if (st != VEA_OK) return st;
     if (plan.nsplit > 1) {
-      if (workspace_bytes < (size_t)plan.chunks * dense_chunk_bytes(head_dim)) return VEA_EWORKSPACE;
+      if (workspace_bytes < (size_t)plan.chunks * dense_chunk_bytes(p.bm, head_dim)) return VEA_EWORKSPACE;
       p.full_units = plan.full_units;
       p.nsplit = plan.nsplit;
       p.ws = (float*)workspace;
@@ -459,7 +461,7 @@ int vea_attn_decode(const void* q, int64_t q_seq_stride, const void* k, int64_t 
   p.q_stride = q_seq_stride; p.k_stride = k_tok_stride; p.v_stride = v_tok_stride; p.o_stride = out_seq_stride;
   p.batch = batch; p.total_q = batch; p.total_k = total_k;
   p.hq = num_heads_kv; p.hkv = num_heads_kv; p.group = 1;     // units are (sequence, key/value head)
-  st = dense_layout(batch, num_heads_q / num_heads_kv, num_heads_kv, 0, p);
+  st = dense_layout(batch, num_heads_q / num_heads_kv, num_heads_kv, 0, kDenseBM, p);
   if (st != VEA_OK) return st;
   p.dec_group = num_heads_q / num_heads_kv;
   p.ws_rows = (p.dec_group + 3) & ~3;
@@ -517,7 +519,7 @@ int vea_attn_fwd_fp8(const void* q, int64_t q_tok_stride, const void* k, int64_t
   p.q_stride = q_tok_stride; p.k_stride = k_tok_stride; p.v_stride = v_tok_stride; p.o_stride = out_tok_stride;
   p.batch = batch; p.total_q = total_q; p.total_k = total_k;
   p.hq = num_heads_q; p.hkv = num_heads_kv; p.group = num_heads_q / num_heads_kv;
-  st = dense_layout(batch, max_seqlen_q, num_heads_q, piece_rows, p);
+  st = dense_layout(batch, max_seqlen_q, num_heads_q, piece_rows, kDenseBM, p);
   if (st != VEA_OK) return st;
   p.xcd_map = (num_heads_kv % 8 == 0) ? 1 : 0;
   p.scale = scale;

@@ -598,28 +598,27 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
 }
 
 // ======================================== bf16, head_dim 64, one packed sequence
-// The image case (non-causal, packed K/V, no decode units).  At head_dim 64 a
-// 64-key step holds 16 MFMAs per 32 query rows but the same softmax work per
-// logit as at 128, so the kernel is bound by instruction issue rather than by
-// the matrix cores.  Here a workgroup is 2 waves x 64 query rows (the 128-row
-// tile of the other kernels, so the launch layout, the split of the last
-// round and its merge are shared), and each wave holds two independent 32-row
+// The image case (non-causal, packed or paged K/V, no decode units).  At
+// head_dim 64 a 64-key step holds 16 MFMAs per 32 query rows but the same
+// softmax work per logit as at 128, so the kernel is bound by instruction
+// issue and by the K/V staging rather than by the matrix cores.  Here a
+// workgroup is 4 waves x 64 query rows (a 256-row tile: half the K/V DMA per
+// flop of a 128-row tile), and each wave holds two independent 32-row
 // blocks:
 //   * every K and V^T operand read from LDS feeds two MFMAs (one per block),
 //     half the LDS traffic per flop of a 32-row wave;
 //   * the two blocks' logit -> softmax -> P V chains are independent, so one
-//     block's exponentials issue while the other's MFMAs run;
-//   * a 2-wave workgroup meets its barrier with less skew than a 4-wave one.
+//     block's exponentials issue while the other's MFMAs run.
 // K and V of one step are staged together (double-buffered, one barrier per
 // step); the max-free softmax with its rare path is the other kernel's.
-constexpr int kD64Threads = 128;
+constexpr int kD64Threads = 256;                         // 4 waves x 64 rows = kD64BM
 
 template <bool PAGED>
 __global__ __launch_bounds__(kD64Threads, 2) void attn_fwd_d64_kernel(DenseParams p) {
   constexpr int D = 64, BN = 64, CPR = D / 8;
   constexpr int TILE = BN * D * 2;                       // 8 KB: one K (or V) tile
   constexpr int LOADS = TILE / (kD64Threads * 16);       // 16-byte DMA loads per lane per tile
-  static_assert(LOADS == 4, "tile split");
+  static_assert(LOADS == 2 && kD64Threads / 64 * 64 == kD64BM, "tile split");
   using C = Cfg<D>;                                      // swizzle of the 16-byte chunks
   __shared__ __attribute__((aligned(1024))) unsigned char kst0[TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char kst1[TILE];
@@ -638,7 +637,7 @@ __global__ __launch_bounds__(kD64Threads, 2) void attn_fwd_d64_kernel(DenseParam
   int b, h, t;
   decode_unit(p, id, b, h, t);
   TileRange tr;
-  if (!tile_range(p, b, t, kDenseBM, false, tr)) return;   // uniform over the workgroup
+  if (!tile_range(p, b, t, kD64BM, false, tr)) return;     // uniform over the workgroup
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -683,7 +682,7 @@ __global__ __launch_bounds__(kD64Threads, 2) void attn_fwd_d64_kernel(DenseParam
   }
   const int n_full = tr.kend / BN - kt0;                 // (local) tiles without the key tail
 
-  // ---- DMA of K/V tiles into LDS (see the other kernel; 2 waves here)
+  // ---- DMA of K/V tiles into LDS (see the other kernel)
   const int64_t ksb = p.k_stride * 2, vsb = p.v_stride * 2;
   int voff_k[LOADS], voff_v[LOADS];
 #pragma unroll
@@ -1069,7 +1068,7 @@ __global__ __launch_bounds__(kD64Threads, 2) void attn_fwd_d64_kernel(DenseParam
     const float l_tot = lane_swap_add(l_run[r]);
     const int rl = wave * 64 + 32 * r + l32;             // row within the tile
     if (split) {
-      float* w = p.ws + (size_t)(slot - p.full_units) * (kDenseBM * (D + 2));
+      float* w = p.ws + (size_t)(slot - p.full_units) * (kD64BM * (D + 2));
 #pragma unroll
       for (int nb = 0; nb < D / 32; ++nb)
 #pragma unroll
@@ -1077,8 +1076,8 @@ __global__ __launch_bounds__(kD64Threads, 2) void attn_fwd_d64_kernel(DenseParam
           *(floatx4*)(w + rl * D + 32 * nb + 8 * r4 + 4 * g2) =
               (floatx4){o[r][nb][4 * r4], o[r][nb][4 * r4 + 1], o[r][nb][4 * r4 + 2], o[r][nb][4 * r4 + 3]};
       if (g2 == 0) {
-        w[kDenseBM * D + rl] = m_used[r];
-        w[kDenseBM * D + kDenseBM + rl] = l_tot;
+        w[kD64BM * D + rl] = m_used[r];
+        w[kD64BM * D + kD64BM + rl] = l_tot;
       }
       continue;
     }
@@ -1447,13 +1446,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(DenseParams p) {
   decode_unit(p, p.full_units + tu, b, h, t);
   TileRange tr;
   if (p.dec_group > 0) decode_range(p, b, tr);
-  else if (!tile_range(p, b, t, kDenseBM, false, tr)) return;
+  else if (!tile_range(p, b, t, p.bm, false, tr)) return;
   constexpr int SL = D / 16;                            // 16-column slices per row
   const int item = blockIdx.y * 256 + threadIdx.x;
   const int rl = item / SL, sc = item - rl * SL;        // row within the tile, slice
   const int qi = tr.row0 + rl;
-  if (rl >= kDenseBM || qi >= tr.row_end) return;
-  const int wr = p.dec_group > 0 ? p.ws_rows : kDenseBM;  // rows per chunk
+  const int wr = p.ws_rows;                             // rows per chunk
+  if (rl >= wr || qi >= tr.row_end) return;
   const size_t CF = (size_t)wr * (D + 2);               // floats per chunk
   const float* base = p.ws + (size_t)tu * NS * CF;
   // every chunk's m, l and 16 values loaded up front (one memory latency)
@@ -1722,7 +1721,7 @@ DenseSplit dense_split_plan(int units, int empty, int slots, int key_tiles) {
   return s;
 }
 
-size_t dense_chunk_bytes(int head_dim) { return (size_t)kDenseBM * (head_dim + 2) * sizeof(float); }
+size_t dense_chunk_bytes(int bm, int head_dim) { return (size_t)bm * (head_dim + 2) * sizeof(float); }
 
 int dense_bf16_blocks_per_cu(int head_dim) {
   int n = 0;
@@ -1736,6 +1735,7 @@ int dense_bf16_blocks_per_cu(int head_dim) {
 
 template <int D>
 void launch_dense(const DenseParams& p, bool causal, bool paged, dim3 grid, dim3 block, hipStream_t s) {
+  // p.bm was chosen by dense_tile_rows for the same (dtype, head_dim, causal)
   if (p.dec_group > 0) {                                // decode units (never causal)
     if (paged) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, true, true>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, false, true>), grid, block, 0, s, p);
@@ -1755,7 +1755,8 @@ void launch_dense(const DenseParams& p, bool causal, bool paged, dim3 grid, dim3
 }
 
 hipError_t launch_attn_fwd_fp8(const DenseParams& p0, int head_dim, bool causal, hipStream_t s) {
-  if (p0.nsplit != 1 || p0.full_units != p0.units || p0.block_table != nullptr) return hipErrorInvalidValue;
+  if (p0.nsplit != 1 || p0.full_units != p0.units || p0.block_table != nullptr || p0.bm != kDenseBM)
+    return hipErrorInvalidValue;
   const dim3 grid(p0.units), block(256);
   DenseParams p = p0;
   p.grid = p0.units;
@@ -1773,6 +1774,8 @@ hipError_t launch_attn_fwd_fp8(const DenseParams& p0, int head_dim, bool causal,
 }
 
 hipError_t launch_attn_fwd_bf16(const DenseParams& p0, int head_dim, bool causal, hipStream_t s) {
+  const int want_bm = p0.dec_group > 0 ? kDenseBM : dense_tile_rows(1, head_dim, causal);
+  if (p0.bm != want_bm) return hipErrorInvalidValue;
   const bool split = p0.nsplit > 1;
   if (split ? (causal || p0.ws == nullptr || p0.full_units < 0 || p0.full_units >= p0.units)
             : p0.full_units != p0.units)
@@ -1792,7 +1795,7 @@ hipError_t launch_attn_fwd_bf16(const DenseParams& p0, int head_dim, bool causal
   if (split) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 mgrid(p.units - p.full_units, kDenseBM * head_dim / 16 / 256);
+    const dim3 mgrid(p.units - p.full_units, p.bm * head_dim / 16 / 256);
     const hipError_t me = head_dim == 64 ? launch_merge<64>(p, mgrid, s) : launch_merge<128>(p, mgrid, s);
     if (me != hipSuccess) return me;
   }
@@ -1800,6 +1803,7 @@ hipError_t launch_attn_fwd_bf16(const DenseParams& p0, int head_dim, bool causal
 }
 
 hipError_t launch_attn_fwd_f32(const DenseParams& p0, int head_dim, bool causal, hipStream_t s) {
+  if (p0.bm != kDenseBM) return hipErrorInvalidValue;
   const dim3 grid(p0.units), block(256);
   DenseParams p = p0;
   p.grid = p0.units;

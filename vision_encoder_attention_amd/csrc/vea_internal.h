@@ -31,6 +31,7 @@ struct DenseParams {
   int batch, total_q, total_k;
   int hq, hkv, group;        // group = hq / hkv
   int qb;                    // rows per piece (> 0, already resolved)
+  int bm;                    // query rows per tile (kDenseBM, or kD64BM for the head_dim 64 image kernel)
   int tiles_per_piece, tiles_per_seq;
   int units;                 // batch * tiles_per_seq * hq
   int xcd_map;               // 1: spread kv heads over the 8 XCDs
@@ -131,8 +132,8 @@ struct DenseSplit {
   int full_units, nsplit, chunks;
 };
 DenseSplit dense_split_plan(int units, int empty, int slots, int key_tiles);
-// Bytes of workspace per split chunk: kDenseBM x (d + 2) floats.
-size_t dense_chunk_bytes(int head_dim);
+// Bytes of workspace per split chunk: bm x (d + 2) floats.
+size_t dense_chunk_bytes(int bm, int head_dim);
 // Workgroups of the dense bf16 kernel resident per CU (0 if unknown).
 int dense_bf16_blocks_per_cu(int head_dim);
 
@@ -218,6 +219,12 @@ hipError_t launch_quant_fp8(const QuantParams& p, hipStream_t s);
 // Tile shape of the dense bf16/f32 kernels (query rows per workgroup); the
 // host uses it to size the launch.
 constexpr int kDenseBM = 128;
+// The head_dim 64 non-causal bf16 kernel (packed or paged) covers 256 rows.
+constexpr int kD64BM = 256;
+// Query rows per tile of a bf16/f32 (non-decode) launch of these parameters.
+inline int dense_tile_rows(int dtype_bf16, int head_dim, int causal) {
+  return (dtype_bf16 && head_dim == 64 && !causal) ? kD64BM : kDenseBM;
+}
 constexpr int kSparseHeadsPerWG = 128;
 
 }  // namespace vea
