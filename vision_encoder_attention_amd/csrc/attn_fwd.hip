@@ -923,41 +923,15 @@ __global__ __launch_bounds__(kD64Threads, 2) void attn_fwd_d64_kernel(DenseParam
       }
       return;
     }
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      // keys 32 hh .. 32 hh + 31 of the tile: K rows, V^T k-steps 2 hh, 2 hh + 1
-      u32x4 kop[D / 16];
+    // Two 32-key halves, rotated so that every block's softmax issues under
+    // about eight MFMAs of the other block or of the next half:
+    //   S_A0 | S_B0 + sm A0 | P_A0 V, S_A1 + sm B0 | P_B0 V, S_B1 + sm A1 |
+    //   P_A1 V + sm B1 | P_B1 V
+    auto kread = [&](int hh, u32x4* kop) __attribute__((always_inline)) {
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) kop[ks] = *(const u32x4*)(ks_ + hh * 32 * D * 2 + koff[ks]);
-      floatx16 sa = (floatx16){}, sb = (floatx16){};
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks)
-        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop[ks]), as_bf16x8(qf[0][ks]), sa, 0, 0, 0);
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks)
-        sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop[ks]), as_bf16x8(qf[1][ks]), sb, 0, 0, 0);
-      if constexpr (MASK) {
-        const int j0 = (kt0 + kt) * BN + 32 * hh + 4 * g2;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bool out_of_range = j0 + 8 * (r >> 2) + (r & 3) >= tr.len_k;
-          if (out_of_range) {
-            sa[r] = -INFINITY;
-            sb[r] = -INFINITY;
-          }
-        }
-      }
-      u32x4 pa[2], pb[2];
-      const float ta = half_p(sa, m_use[0], pa);
-      // S_A, then S_B's MFMAs one at a time between slices of A's softmax
-#pragma unroll
-      for (int i = 0; i < D / 16; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-#pragma unroll
-      for (int i = 0; i < D / 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-      }
-      u32x4 vop[2][D / 32];
+    };
+    auto vread = [&](int hh, u32x4 (*vop)[D / 32]) __attribute__((always_inline)) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -967,27 +941,56 @@ __global__ __launch_bounds__(kD64Threads, 2) void attn_fwd_d64_kernel(DenseParam
           const u32x2 hi = lds_read_tr(vs_ + st * 16 * D * 2 + voff1[nb]);
           vop[s2][nb] = (u32x4){lo[0], lo[1], hi[0], hi[1]};
         }
+    };
+    auto qk = [&](int r, const u32x4* kop) __attribute__((always_inline)) -> floatx16 {
+      floatx16 acc = (floatx16){};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop[ks]), as_bf16x8(qf[r][ks]), acc, 0, 0, 0);
+      return acc;
+    };
+    auto pv = [&](int r, u32x4 (*vop)[D / 32], const u32x4* pb) __attribute__((always_inline)) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int nb = 0; nb < D / 32; ++nb)
-          o[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vop[s2][nb]), as_bf16x8(pa[s2]), o[0][nb], 0, 0, 0);
-      const float tb = half_p(sb, m_use[1], pb);
-      // P_A V, then P_B V with B's softmax interleaved into the first
+          o[r][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vop[s2][nb]), as_bf16x8(pb[s2]), o[r][nb], 0,
+                                                             0, 0);
+    };
+    auto mask_half = [&](int hh, floatx16& sa, floatx16& sb) __attribute__((always_inline)) {
+      const int j0 = (kt0 + kt) * BN + 32 * hh + 4 * g2;
 #pragma unroll
-      for (int i = 0; i < 2 * (D / 32); ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      for (int r = 0; r < 16; ++r) {
+        if (j0 + 8 * (r >> 2) + (r & 3) >= tr.len_k) {
+          sa[r] = -INFINITY;
+          sb[r] = -INFINITY;
+        }
       }
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb)
-          o[1][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vop[s2][nb]), as_bf16x8(pb[s2]), o[1][nb], 0, 0, 0);
-      bad = bad || !(ta < 0x1p100f) || !(tb < 0x1p100f);   // NaN counts as bad
-      l_run[0] += ta;
-      l_run[1] += tb;
-    }
+    };
+    u32x4 kop0[D / 16], kop1[D / 16], vop0[2][D / 32], vop1[2][D / 32];
+    u32x4 pa0[2], pb0[2], pa1[2], pb1[2];
+    kread(0, kop0);
+    floatx16 sa0 = qk(0, kop0);
+    floatx16 sb0 = qk(1, kop0);
+    if constexpr (MASK) mask_half(0, sa0, sb0);
+    const float ta0 = half_p(sa0, m_use[0], pa0);
+    vread(0, vop0);
+    kread(1, kop1);
+    pv(0, vop0, pa0);
+    floatx16 sa1 = qk(0, kop1);
+    const float tb0 = half_p(sb0, m_use[1], pb0);
+    pv(1, vop0, pb0);
+    floatx16 sb1 = qk(1, kop1);
+    if constexpr (MASK) mask_half(1, sa1, sb1);
+    const float ta1 = half_p(sa1, m_use[0], pa1);
+    vread(1, vop1);
+    pv(0, vop1, pa1);
+    const float tb1 = half_p(sb1, m_use[1], pb1);
+    pv(1, vop1, pb1);
+    const float ta = ta0 + ta1, tb = tb0 + tb1;
+    bad = bad || !(ta < 0x1p100f) || !(tb < 0x1p100f);   // NaN counts as bad
+    l_run[0] += ta;
+    l_run[1] += tb;
   };
 
   // ---- key loop: stage kt % 2 holds K(kt) and V(kt); the DMA of tile kt+1
