@@ -850,7 +850,7 @@ __global__ __launch_bounds__(kD64Threads, 2) void attn_fwd_d64_kernel(DenseParam
   bool bad = false;
   // P of one 32-key half (accumulator s) with reference mu: two packed
   // operands (k-steps 2h, 2h + 1) and the lane's fp32 sum.
-  auto half_p = [&](const floatx16& sv, float mu, u32x4* pb) __attribute__((always_inline)) -> float {
+  auto half_p = [&](const floatx16& sv, u32x4* pb) __attribute__((always_inline)) -> float {
     float tq[2];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
@@ -858,8 +858,8 @@ __global__ __launch_bounds__(kD64Threads, 2) void attn_fwd_d64_kernel(DenseParam
       float pr[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float e0 = fast_exp2(fmaf(sv[8 * hf + 2 * q], c, -mu));
-        const float e1 = fast_exp2(fmaf(sv[8 * hf + 2 * q + 1], c, -mu));
+        const float e0 = fast_exp2(sv[8 * hf + 2 * q] * c);
+        const float e1 = fast_exp2(sv[8 * hf + 2 * q + 1] * c);
         pr[q] = e0 + e1;
         w[q] = pack_bf16x2(e0, e1);
       }
@@ -868,61 +868,18 @@ __global__ __launch_bounds__(kD64Threads, 2) void attn_fwd_d64_kernel(DenseParam
     }
     return tq[0] + tq[1];
   };
-  auto set_ref = [&](int r, const floatx16& s0, const floatx16& s1) __attribute__((always_inline)) {
-    float mx = vmax(s0[0], s1[0]);
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = vmax(vmax(mx, s0[i]), s1[i]);
-    mx = lane_swap_max(mx);
-    m_used[r] = (mx == -INFINITY) ? -INFINITY : mx * c;
-    m_use[r] = (m_used[r] == -INFINITY) ? 0.f : m_used[r];
-  };
-  // Fast key step: no branch.  The first step of a range sets each row's
-  // reference from its own maximum (FIRST); later steps use it unchanged,
-  // however large P grows, and only record (in `bad`, per lane) a tile whose
-  // lane sum is not below 2^100 (so some P may have overflowed).  A workgroup
-  // with any such tile recomputes its range with the careful step.  With the
-  // reference at the first tile's maximum a P can exceed 1 only where a later
-  // logit exceeds every logit of the first tile; fp32 and bf16 keep their
-  // relative precision up to 2^127, so such P change no result unless they
-  // overflow.  The tile is processed in two 32-key halves, each in the order
-  // S_A, S_B (with A's softmax), P_A V (with B's softmax), P_B V, so that one
-  // block's exponentials issue under the other block's MFMAs while only a
-  // half tile of logits, P and operands is live.
-  auto step_fast = [&](int kt, const unsigned char* ks_, const unsigned char* vs_, auto mask_tag, auto first_tag)
+  // Fast key step: no branch and no per-row reference: P = 2^(s c) (one
+  // multiply before each exponential).  Each tile records (in `bad`, per
+  // lane) a lane sum that is not below 2^100, where some P may have
+  // overflowed, and the range ends by recording a row sum below 2^-100,
+  // where the row's significant P may have left the normal range.  A
+  // workgroup with any such lane recomputes its range with the careful step.
+  // Without either, every P that matters is a normal fp32 / bf16 number, and
+  // these keep their relative precision at any exponent, so the missing
+  // reference changes no result; the lse is log(l) with reference 0.
+  auto step_fast = [&](int kt, const unsigned char* ks_, const unsigned char* vs_, auto mask_tag)
       __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    constexpr bool FIRST = decltype(first_tag)::value;
-    if constexpr (FIRST) {
-      // once per range, one block at a time: the reference is the block's
-      // row maximum over the whole first tile
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        floatx16 s0 = (floatx16){}, s1 = (floatx16){};
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const u32x4 a0 = *(const u32x4*)(ks_ + koff[ks]);
-          const u32x4 a1 = *(const u32x4*)(ks_ + 32 * D * 2 + koff[ks]);
-          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), as_bf16x8(qf[r][ks]), s0, 0, 0, 0);
-          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), as_bf16x8(qf[r][ks]), s1, 0, 0, 0);
-        }
-        if constexpr (MASK) mask(kt, s0, s1);
-        set_ref(r, s0, s1);
-        u32x4 pb[4];
-        const float t = softmax_p(s0, s1, m_use[r], pb);
-#pragma unroll
-        for (int st = 0; st < 4; ++st)
-#pragma unroll
-          for (int nb = 0; nb < D / 32; ++nb) {
-            const u32x2 lo = lds_read_tr(vs_ + st * 16 * D * 2 + voff0[nb]);
-            const u32x2 hi = lds_read_tr(vs_ + st * 16 * D * 2 + voff1[nb]);
-            const u32x4 vop = (u32x4){lo[0], lo[1], hi[0], hi[1]};
-            o[r][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vop), as_bf16x8(pb[st]), o[r][nb], 0, 0, 0);
-          }
-        bad = bad || !(t < 0x1p100f);
-        l_run[r] += t;
-      }
-      return;
-    }
     // Two 32-key halves, rotated so that every block's softmax issues under
     // about eight MFMAs of the other block or of the next half:
     //   S_A0 | S_B0 + sm A0 | P_A0 V, S_A1 + sm B0 | P_B0 V, S_B1 + sm A1 |
@@ -973,19 +930,19 @@ __global__ __launch_bounds__(kD64Threads, 2) void attn_fwd_d64_kernel(DenseParam
     floatx16 sa0 = qk(0, kop0);
     floatx16 sb0 = qk(1, kop0);
     if constexpr (MASK) mask_half(0, sa0, sb0);
-    const float ta0 = half_p(sa0, m_use[0], pa0);
+    const float ta0 = half_p(sa0, pa0);
     vread(0, vop0);
     kread(1, kop1);
     pv(0, vop0, pa0);
     floatx16 sa1 = qk(0, kop1);
-    const float tb0 = half_p(sb0, m_use[1], pb0);
+    const float tb0 = half_p(sb0, pb0);
     pv(1, vop0, pb0);
     floatx16 sb1 = qk(1, kop1);
     if constexpr (MASK) mask_half(1, sa1, sb1);
-    const float ta1 = half_p(sa1, m_use[0], pa1);
+    const float ta1 = half_p(sa1, pa1);
     vread(1, vop1);
     pv(0, vop1, pa1);
-    const float tb1 = half_p(sb1, m_use[1], pb1);
+    const float tb1 = half_p(sb1, pb1);
     pv(1, vop1, pb1);
     const float ta = ta0 + ta1, tb = tb0 + tb1;
     bad = bad || !(ta < 0x1p100f) || !(tb < 0x1p100f);   // NaN counts as bad
@@ -996,8 +953,7 @@ __global__ __launch_bounds__(kD64Threads, 2) void attn_fwd_d64_kernel(DenseParam
   // ---- key loop: stage kt % 2 holds K(kt) and V(kt); the DMA of tile kt+1
   // is issued right after the barrier that retires tile kt-1's stage.  Steps
   // before n_full hold no key tail.
-  auto iter = [&](int kt, auto odd_tag, auto mask_tag, auto first_tag, auto careful_tag)
-      __attribute__((always_inline)) {
+  auto iter = [&](int kt, auto odd_tag, auto mask_tag, auto careful_tag) __attribute__((always_inline)) {
     constexpr bool ODD = decltype(odd_tag)::value;
     unsigned char* k_rd = ODD ? kst1 : kst0;
     unsigned char* v_rd = ODD ? vst1 : vst0;
@@ -1011,7 +967,7 @@ __global__ __launch_bounds__(kD64Threads, 2) void attn_fwd_d64_kernel(DenseParam
     }
     if (live) {
       if constexpr (decltype(careful_tag)::value) step_careful(kt, k_rd, v_rd, mask_tag);
-      else step_fast(kt, k_rd, v_rd, mask_tag, first_tag);
+      else step_fast(kt, k_rd, v_rd, mask_tag);
       if (kt + 1 == n_tiles) {
         // After the range's last MFMAs the compiler may reuse their A/B
         // operand registers right away (register copies where the loop's
@@ -1027,30 +983,33 @@ __global__ __launch_bounds__(kD64Threads, 2) void attn_fwd_d64_kernel(DenseParam
   };
   const int n_plain = min(n_tiles, max(n_full, 0));
   auto run = [&](auto careful_tag) __attribute__((always_inline)) {
-    constexpr bool CAREFUL = decltype(careful_tag)::value;
     using F = std::false_type;
     using T = std::true_type;
-    using FIRST = std::integral_constant<bool, !CAREFUL>;
     issue(0, kbase, ksb, voff_k, kst0);
     issue(0, vbase, vsb, voff_v, vst0);
-    if (n_plain > 0) iter(0, F{}, F{}, FIRST{}, careful_tag);
-    else iter(0, F{}, T{}, FIRST{}, careful_tag);         // the only step holds the key tail
+    if (n_plain > 0) iter(0, F{}, F{}, careful_tag);
+    else iter(0, F{}, T{}, careful_tag);                 // the only step holds the key tail
     int kt = 1;
     for (; kt + 1 < n_plain; kt += 2) {
-      iter(kt, T{}, F{}, F{}, careful_tag);
-      iter(kt + 1, F{}, F{}, F{}, careful_tag);
+      iter(kt, T{}, F{}, careful_tag);
+      iter(kt + 1, F{}, F{}, careful_tag);
     }
     if (kt < n_plain) {                                  // one more plain step (odd), then the tail (even)
-      iter(kt, T{}, F{}, F{}, careful_tag);
-      if (kt + 1 < n_tiles) iter(kt + 1, F{}, T{}, F{}, careful_tag);
+      iter(kt, T{}, F{}, careful_tag);
+      if (kt + 1 < n_tiles) iter(kt + 1, F{}, T{}, careful_tag);
     } else if (kt < n_tiles) {                           // the tail step (odd)
-      iter(kt, T{}, T{}, F{}, careful_tag);
+      iter(kt, T{}, T{}, careful_tag);
     }
   };
   if (n_tiles > 0) {
     run(std::false_type{});
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {                        // reference 0 on the fast path
+      m_used[r] = 0.f;
+      if (live) bad = bad || !(lane_swap_add(l_run[r]) >= 0x1p-100f);   // a wave with no rows has no sums
+    }
     // the decision is the workgroup's: the careful pass stages tiles with
-    // barriers that both waves must meet
+    // barriers that every wave must meet
     if (__syncthreads_or(bad ? 1 : 0)) {
       asm volatile("; rare: recompute the range with per-step reference moves" ::);
 #pragma unroll
