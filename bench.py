@@ -177,7 +177,10 @@ def dense_entry(torch, wname, case, st, tm, steps, with_rope):
     a = tm.stats("attn_fwd")
     tflops = fl / a["mean"] / 1e9
     d, causal = case.head_dim, case.causal
-    kname = "attn_fwd_bf16_kernel<%d,%s,false,false>" % (d, "true" if causal else "false")
+    if d == 64 and not causal:
+        kname = "attn_fwd_d64_kernel<false>"
+    else:
+        kname = "attn_fwd_bf16_kernel<%d,%s,false,false>" % (d, "true" if causal else "false")
     split = st.ws is not None
     if split:
         kname += " + attn_merge_kernel<%d>" % d

@@ -115,6 +115,54 @@ def test_edge_cases(torch, i):
     _check_case(torch, case)
 
 
+def _extreme_logit_case(seed, n, heads, mode):
+    """Non-causal head_dim 64 images whose logits leave the range of a fixed
+    exponent reference: 'over' has rows with q x 64 (2^(s c) would overflow
+    fp32), 'under' has every key nearly opposite to every query (all logits
+    near -700 in log2 units), 'mixed' scales only the first 100 rows of the
+    first head (one workgroup of 256 rows where some rows need the careful
+    path and the rest do not)."""
+    rng = np.random.default_rng(seed)
+    q = W.randn_bf16_bits(rng, (n, heads, 64))
+    k = W.randn_bf16_bits(rng, (n, heads, 64))
+    v = W.randn_bf16_bits(rng, (n, heads, 64))
+    if mode in ("over", "mixed"):
+        big = W.randn_bf16_bits(rng, (n, heads, 64), mul=64.0)
+        if mode == "over":
+            q = big
+        else:
+            q[:100, 0] = big[:100, 0]
+    if mode == "under":
+        q = np.full((n, heads, 64), 0x4100, np.uint16)                     # 8.0
+        k = W.f32_to_bf16_bits(-8.0 + rng.standard_normal((n, heads, 64), dtype=np.float32))
+    cu = np.array([0, n], np.int32)
+    return W.DenseCase("extreme_%s" % mode, "bf16", heads, heads, 64, False, 0.125, 300, cu, cu.copy(), q, k, v)
+
+
+@pytest.mark.parametrize("mode", ["over", "under", "mixed"])
+def test_image_kernel_fallback_paths(torch, mode):
+    """The head_dim 64 image kernel's fast path uses no per-row reference and
+    hands a workgroup to the careful per-step path when a P overflowed or a
+    row's sum underflowed: both extremes (and a workgroup where only some
+    rows need it) against the oracle, with the key-range split (96 units
+    fill less than one round, so every unit splits; bitwise repeatable) and
+    without it."""
+    case = _extreme_logit_case(750 + len(mode), 1337, 16, mode)
+    st = _check_case(torch, case)
+    o0, l0 = st.out.clone(), st.lse.clone()
+    R.run_attn(st)
+    torch.cuda.synchronize()
+    assert torch.equal(st.out, o0) and torch.equal(st.lse, l0)
+    whole = R.stage_dense(case, split=False)
+    R.run_attn(whole)
+    torch.cuda.synchronize()
+    q, k, v = _inputs64(case, whole)
+    o_ref, l_ref = oracle.attention(q, k, v, case.cu_seqlens_q, case.cu_seqlens_k, False,
+                                    float(np.float32(case.scale)), workers=ORACLE_WORKERS)
+    assert_bf16_close(_f64(whole.out, "bf16"), o_ref, "out (no split)")
+    assert_bf16_close(whole.lse.cpu().numpy().astype(np.float64), l_ref, "lse (no split)")
+
+
 # --------------------------------------------- invariances and determinism
 
 def test_piece_rows_do_not_change_results(torch):
