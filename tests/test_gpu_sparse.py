@@ -127,6 +127,18 @@ def test_large_cache_uses_the_sorting_network(torch):
     assert torch.equal(perm.out, st.out) and torch.equal(perm.lse, st.lse)
 
 
+@pytest.mark.parametrize("n_kv,k", [(10000, 1024), (20000, 3000)])
+def test_counts_in_the_stage_ring(torch, n_kv, k):
+    """Counting-sort counts too many for their own LDS array (more than 4088
+    cache rows up to 2048 indices, 18424 up to 4096) are kept in the stage
+    ring, so Q is loaded after the sort rather than under it: same results,
+    bitwise invariant to index order."""
+    case = W.sparse_mqa(rows=3, heads=128, n_kv=n_kv, k=k, seed=31 + k)
+    st = _check(torch, case, name="n_kv %d k %d" % (n_kv, k))
+    perm = _run(torch, case, W.permute_rows(case.topk_idx, 109))
+    assert torch.equal(perm.out, st.out) and torch.equal(perm.lse, st.lse)
+
+
 def test_more_than_2048_indices(torch):
     """k in (2048, 4096] uses the three-stage variant of the kernel."""
     case = W.sparse_mqa(rows=2, heads=128, n_kv=3500, k=3000, seed=19)

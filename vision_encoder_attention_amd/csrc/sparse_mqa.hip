@@ -149,7 +149,13 @@ struct SCfg {
   static_assert(DQK % 32 == 0 && DV % 64 == 0 && DV <= DQK, "latent dims");
   static_assert(HEADS == kSparseHeadsPerWG, "host launch shape");
   static_assert(NT == 16, "the accumulator waits name 16 O^T tiles");
-  static_assert(NSTAGE * TILE + MAXK * 4 + WAVES * 4 <= 160 * 1024, "LDS budget");
+  // 32-bit words of LDS left for the counting sort's counts (two per word)
+  static constexpr int CNTW = (160 * 1024 - NSTAGE * TILE - MAXK * 4 - WAVES * 4) / 4;
+  static_assert(CNTW > 0, "LDS budget");
+  // Q through the ring needs a stage per wave (one stage = one wave's Q
+  // rows); the three-stage variant loads Q straight into registers.
+  static constexpr bool QDMA = NSTAGE >= WAVES;
+  static_assert(TILE == HPW * ROWB, "a wave's Q rows fill one stage");
   // Chunk swizzle.  Rows r and r + 1 sit 32 banks apart (1152-byte rows), so
   // the swizzle works on the row pair x = (r / 2) % 8 and permutes the low 3
   // bits of a chunk index (it stays inside aligned groups of 8 chunks; rows r
@@ -189,6 +195,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[C::NSTAGE * C::TILE];
   __shared__ int sidx[MAXK];
   __shared__ int wsum[C::WAVES];
+  __shared__ uint32_t cntbuf[C::CNTW];
 
   // workgroup unit (row, head block) and, for a split unit, its chunk
   const int slot = wg_slot(blockIdx.x, p.grid, p.wg_perm);
@@ -208,31 +215,56 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
   const int l32 = lane & 31;
   const int g2 = lane >> 5;                             // which half of the wave
 
-  // ---- loads issued up front, so their latency runs under the sort: this
-  // thread's share of the row's indices (entries tid + THREADS j; entries
-  // past k are excluded where they are used), then the Q^T fragment (B
-  // operand of S^T = K Q^T): head l32 of this wave, dims 16 ks + 8 g2 .. +7.
-  // Addresses are clamped so every load is unconditional (the compiler can
-  // then wait for the index loads alone), and the sort's barriers wait for
-  // LDS only.
+  // ---- this thread's share of the row's indices (entries tid + THREADS j;
+  // entries past k are excluded where they are used), loaded first so their
+  // latency overlaps the count buffer's clearing.
   const int32_t* irow = p.idx + (int64_t)row * p.k;
   constexpr int IPT = MAXK / C::THREADS;
   int xi[IPT];
 #pragma unroll
   for (int j = 0; j < IPT; ++j) xi[j] = irow[min(tid + C::THREADS * j, p.k - 1)];
-  asm volatile("" ::: "memory");                        // index loads first
   const int head0 = hb * C::HEADS + wave * C::HPW;      // wave-uniform
   const bool active = head0 < p.heads;                  // wave has at least one head
-  const int head = head0 + l32;
-  const bool hvalid = head < p.heads;
   u32x4 qf[C::KSTEPS];
-  {
-    const uint16_t* src = p.q + ((int64_t)row * p.heads + (hvalid ? head : 0)) * DQK + 8 * g2;
+  if constexpr (!C::QDMA) {
+    // Q^T fragments straight from global memory (head l32 of this wave, dims
+    // 16 ks + 8 g2 .. +7), issued after the index loads so the sort waits
+    // for those alone; heads past the count load head 0 and are zeroed later.
+    const int hq = head0 + l32 < p.heads ? head0 + l32 : 0;
+    const uint16_t* src = p.q + ((int64_t)row * p.heads + hq) * DQK + 8 * g2;
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks) qf[ks] = *(const u32x4*)(src + 16 * ks);
   }
   auto lds_barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
   const float c = fmaxf(fabsf(p.scale) * kLog2e, FLT_MIN);   // scale 0: logits ~0, masked ones stay -inf
+
+  // ---- Q of this wave's 32 heads by DMA into stage `wave` of the ring,
+  // which is idle until the key loop: 36 fully coalesced 1 KB blocks (the
+  // heads of a row are consecutive), laid out like a K tile (head r in
+  // place of latent row r, same chunk swizzle), so the Q^T fragments (B
+  // operand of S^T = K Q^T: head l32, dims 16 ks + 8 g2 .. +7) are read
+  // back exactly like K operands.  Loading them straight into registers
+  // would make every load instruction touch 32 rows.  Heads past the count
+  // read zeros.  Issued once the sort no longer needs the ring (the
+  // counting sort keeps its counts there when they do not fit cntbuf).
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)ring;
+  const uint64_t q_addr = (uint64_t)(uintptr_t)(p.q + (int64_t)row * p.heads * DQK);
+  const i32x4 q_rsrc = (i32x4){(int)(uint32_t)q_addr, (int)(uint32_t)(q_addr >> 32) & 0xFFFF, p.heads * C::ROWB,
+                               0x00020000};
+  auto q_dma = [&] {
+    if constexpr (!C::QDMA) return;
+    const uint32_t dst = ring_lds + (uint32_t)(wave * C::TILE);
+#pragma unroll
+    for (int bk = 0; bk < C::BLOCKS; ++bk) {
+      const int sl = bk * 64 + lane;
+      const int r = sl / C::CPR;
+      const int ph = sl - r * C::CPR;
+      const int col = 16 * ((ph & ~7) | ((ph & 7) ^ C::swz(r)));
+      const uint32_t off = __umul24((uint32_t)(head0 + r), (uint32_t)C::ROWB) + (uint32_t)col;
+      dma16(q_rsrc, dst + (uint32_t)(bk * 1024), head0 + r < p.heads ? off : 0xFFFFFFF0u);
+    }
+  };
+  bool q_issued = false;
 
   // ---- canonical order: the row's valid indices in ascending order (with
   // their multiplicity) in sidx[0, nvalid).
@@ -243,7 +275,8 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
     // incremented by LDS atomics (the counts do not depend on their order),
     // then one block-wide exclusive scan over runs of consecutive rows and a
     // scatter of each row's index count times.
-    uint32_t* cnt = (uint32_t*)ring;
+    const bool own = p.n_kv <= 2 * C::CNTW;             // counts in cntbuf: the ring is free for Q
+    uint32_t* cnt = own ? cntbuf : (uint32_t*)ring;
     const int nw = (p.n_kv + 1) >> 1;
     for (int i = tid; i < nw; i += C::THREADS) cnt[i] = 0u;
     lds_barrier();
@@ -254,6 +287,10 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
         atomicAdd(&cnt[x >> 1], 1u << (16 * (x & 1)));
     }
     lds_barrier();
+    if (own) {                                          // the index loads are in: Q's DMAs run under the scan
+      q_dma();
+      q_issued = true;
+    }
     auto count = [&](int v) -> int { return (int)((cnt[v >> 1] >> (16 * (v & 1))) & 0xFFFFu); };
     const int per = (p.n_kv + C::THREADS - 1) / C::THREADS;
     const int v0 = min(tid * per, p.n_kv), v1 = min(v0 + per, p.n_kv);
@@ -289,6 +326,8 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
       if (i < n2) sidx[i] = (i < p.k && x >= 0 && x < p.n_kv) ? x : INT_MAX;
     }
     lds_barrier();
+    q_dma();                                            // the network works in sidx only
+    q_issued = true;
     for (int size = 2; size <= n2; size <<= 1) {
       for (int stride = size >> 1; stride > 0; stride >>= 1) {
         for (int t = tid; t < (n2 >> 1); t += C::THREADS) {
@@ -313,6 +352,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
   // chunk's share of a split unit.  The key loop sees the list from entry
   // t0 BN on (srow) and the valid count from there (nloc).
   nvalid = __builtin_amdgcn_readfirstlane(nvalid);
+  if (!q_issued) q_dma();                               // counts were in the ring
   if (p.page_table != nullptr) {
     // Paged cache: translate the sorted logical positions to physical rows
     // in place.  The order stays that of the logical positions, so the
@@ -341,7 +381,6 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
   const uint64_t kv_addr = (uint64_t)(uintptr_t)p.kv;
   const i32x4 kv_rsrc = (i32x4){(int)(uint32_t)kv_addr, (int)(uint32_t)(kv_addr >> 32) & 0xFFFF,
                                 (int)((int64_t)p.n_phys * C::ROWB), 0x00020000};
-  const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)ring;
   // Slot (row, byte column) of each of this lane's DMA blocks, packed
   // row << 16 | column; the same for every tile.
   int g_rc[C::BPW];
@@ -352,20 +391,34 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
     const int ph = sl - r * C::CPR;
     g_rc[bi] = (r << 16) | (16 * ((ph & ~7) | ((ph & 7) ^ C::swz(r))));
   }
-  auto gather = [&](int kt) {
+  // A gather is issued for every step, also for tiles past this range's
+  // n_tiles (those DMAs read zeros into a stage no step reads again), so
+  // that the key loop has no branch around it and the count of DMAs in
+  // flight at each wait is fixed.  The index reads (gather_idx) and the DMAs
+  // (gather_dma, one per block) are separate so that the step can spread
+  // them between its MFMAs.
+  // g_rc is read through an opaque copy at each use, so that its row and
+  // column parts are recomputed there rather than kept live as 18 values.
+  auto gather_idx = [&](int kt, int bi) -> int {
+    int g = g_rc[bi];
+    asm volatile("" : "+v"(g));
+    return srow[min(kt * C::BN + (g >> 16), slim)];
+  };
+  auto gather_dma = [&](int kt, int x, int bi) {
     const uint32_t dst = ring_lds + (uint32_t)((kt % C::NSTAGE) * C::TILE);
-    int x[C::BPW];                                      // all index reads first: one LDS wait
+    const int lim = kt < n_tiles ? nloc - kt * C::BN : 0;   // rows of the tile that exist
+    int g = g_rc[bi];
+    asm volatile("" : "+v"(g));
+    const uint32_t off = __umul24((uint32_t)x, (uint32_t)C::ROWB) + (uint32_t)(g & 0xFFFF);
+    dma16(kv_rsrc, __builtin_amdgcn_readfirstlane(dst + (uint32_t)((bi * C::WAVES + wave) * 1024)),
+          (g >> 16) < lim ? off : 0xFFFFFFF0u);         // past the range or the valid count: zeros
+  };
+  auto gather = [&](int kt) {
+    int x[C::BPW];
 #pragma unroll
-    for (int bi = 0; bi < C::BPW; ++bi) x[bi] = srow[min(kt * C::BN + (g_rc[bi] >> 16), slim)];
+    for (int bi = 0; bi < C::BPW; ++bi) x[bi] = gather_idx(kt, bi);
 #pragma unroll
-    for (int bi = 0; bi < C::BPW; ++bi) asm volatile("" : "+v"(x[bi]));   // keep the reads unconditional
-#pragma unroll
-    for (int bi = 0; bi < C::BPW; ++bi) {
-      const int j = kt * C::BN + (g_rc[bi] >> 16);
-      const uint32_t off = __umul24((uint32_t)x[bi], (uint32_t)C::ROWB) + (uint32_t)(g_rc[bi] & 0xFFFF);
-      dma16(kv_rsrc, __builtin_amdgcn_readfirstlane(dst + (uint32_t)((bi * C::WAVES + wave) * 1024)),
-            j < nloc ? off : 0xFFFFFFF0u);                // past the end: zeros
-    }
+    for (int bi = 0; bi < C::BPW; ++bi) gather_dma(kt, x[bi], bi);
   };
 
 
@@ -476,6 +529,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
     } else if constexpr (P == 12) {
       sf.w[7] = pack_bf16x2(sf.e[14], sf.e[15]);
       l_run += sf.e[14] + sf.e[15];
+      asm volatile("" : "+v"(l_run));                   // summed here, not after the step
     }
   };
   auto rescale_o = [&](const Soft& sf) {
@@ -493,22 +547,33 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
   };
   // QK: the QK^T slots of the tile in kst into s, then (PV) the P V slots of
   // the previous tile (pb, V from vst) with the softmax of s under them.
-  // Returns the packed P of s in pb.
-  // `issue` runs between the first operand reads and the first MFMA (the
-  // next tile's DMA issue hides their latency).
-  auto step_mma = [&](int kt, const unsigned char* kst, const unsigned char* vst, floatx16& s, u32x4* pb, Soft& sf,
-                      auto pv_tag, auto&& issue) {
+  // Returns the packed P of s in pb.  The gather of tile kg is spread over
+  // the step's MFMA slots, one DMA every GSP slots from slot GS on (every
+  // slot's worth of DMAs at once would queue behind each other in the
+  // texture unit and stall the issuing wave); the index read of each block
+  // goes out GS slots before its DMA, so it has returned with the operand
+  // reads issued before it.
+  constexpr int GS = PD;
+  constexpr int GSP_QK = (NQK - GS) / C::BPW;               // step 0: QK^T slots only
+  constexpr int GSP_PV = (NQK + NPV - GS) / C::BPW;
+  static_assert(GSP_QK >= 1 && GS + (C::BPW - 1) * GSP_QK < NQK, "the gather fits under the QK^T slots");
+  auto step_mma = [&](int kt, int kg, const unsigned char* kst, const unsigned char* vst, floatx16& s, u32x4* pb,
+                      Soft& sf, auto pv_tag) {
     constexpr bool PV = decltype(pv_tag)::value;
     constexpr int LAST = PV ? NQK + NPV : NQK;
+    constexpr int GSP = PV ? GSP_PV : GSP_QK;
     u32x4 opr[PD];
     floatx16 s1;
+    int xg[C::BPW];
     static_for<0, PD>([&](auto i) { opr[i.value] = load_op(kst, vst, i); });
-    issue();
     __builtin_amdgcn_sched_barrier(0);
     static_for<0, LAST>([&](auto slot_tag) {
       constexpr int SL = decltype(slot_tag)::value;
       const u32x4 a = opr[SL % PD];
       if constexpr (SL + PD < LAST) opr[SL % PD] = load_op(kst, vst, std::integral_constant<int, SL + PD>{});
+      if constexpr (SL % GSP == 0 && SL / GSP < C::BPW) xg[SL / GSP] = gather_idx(kg, SL / GSP);
+      if constexpr (SL >= GS && (SL - GS) % GSP == 0 && (SL - GS) / GSP < C::BPW)
+        gather_dma(kg, xg[(SL - GS) / GSP], (SL - GS) / GSP);
       if constexpr (SL < NQK) {
         // two accumulators (even / odd k-steps): back-to-back MFMAs never
         // wait on each other's result
@@ -542,6 +607,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
     valu_to_xdl(pb[0], pb[1]);
   };
   // Last P V (no QK^T slots).
+  static_assert(NQK % PD == 0, "last_pv's operand ring starts where step_mma's left off");
   auto last_pv = [&](const unsigned char* vst, const u32x4* pb) {
     u32x4 opr[PD];
     static_for<0, PD>([&](auto i) { opr[i.value] = load_op(vst, vst, std::integral_constant<int, NQK + i.value>{}); });
@@ -555,34 +621,47 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
     });
   };
 
-  // Wait until this lane's DMA of tile t has landed (the DMAs of later tiles
-  // may stay in flight; vector memory loads complete in issue order), then
-  // for every wave's.  The barrier also retires the reads of the stage the
-  // next DMA refills.
-  auto wait_tile = [&](int t) {
-    if (C::DIST == 2 && t + 1 < n_tiles) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::BPW) : "memory");
+  // Wait until this lane's DMA of tile t has landed (with DIST 2 the DMAs
+  // of tile t + 1, real or past the range, stay in flight; vector memory
+  // loads complete in issue order), then for every wave's.  The barrier also
+  // retires the reads of the stage the next DMA refills.
+  auto wait_tile = [&](int) {
+    if constexpr (C::DIST == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::BPW) : "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
   auto stage_ptr = [&](int t) -> const unsigned char* { return ring + (t % C::NSTAGE) * C::TILE; };
 
-  // first tiles in flight before the wait for Q
+  // Q^T fragments from this wave's stage once its own DMAs have landed
+  // (nothing else is in flight on the vector memory counter now); every
+  // wave is done reading before the first tiles overwrite the stages.
+  if constexpr (C::QDMA) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const unsigned char* qst = ring + wave * C::TILE;
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) qf[ks] = *(const u32x4*)(qst + kb[ks & 3] + 128 * (ks >> 2));
+    lds_barrier();
+  }
   if (n_tiles > 0) {
     gather(0);
-    if (C::DIST == 2 && 1 < n_tiles) gather(1);
+    if constexpr (C::DIST == 2) gather(1);
   }
-  // Q of heads past the count is zero; a negative scale negates Q (exact
-  // sign-bit flip) so the exponent scale is positive.
+  // Q of heads past the count is zero (the DMA reads zeros for them); a
+  // negative scale negates Q (exact sign-bit flip) so the exponent scale is
+  // positive.
+  if constexpr (!C::QDMA) {
 #pragma unroll
-  for (int ks = 0; ks < C::KSTEPS; ++ks)
-    if (!hvalid) qf[ks] = (u32x4){0u, 0u, 0u, 0u};
+    for (int ks = 0; ks < C::KSTEPS; ++ks)
+      if (head0 + l32 >= p.heads) qf[ks] = (u32x4){0u, 0u, 0u, 0u};
+  }
   if (p.scale < 0.f) {
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks) qf[ks] ^= (u32x4){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
   }
-  // Retire the Q loads here: otherwise the compiler waits for them (vmcnt(0),
-  // which would also drain the in-flight tile DMAs) at their first use inside
-  // the key loop, on every iteration.
+  // Retire the Q reads or loads here: otherwise the compiler waits for them
+  // (lgkmcnt(0) or vmcnt(0), which would also drain the operand reads or the
+  // tile DMAs in flight) at their first use inside the key loop, on every
+  // iteration.
 #pragma unroll
   for (int ks = 0; ks < C::KSTEPS; ++ks) asm volatile("" : "+v"(qf[ks]));
 
@@ -590,31 +669,34 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
     u32x4 pb[2];                                        // packed P of the previous tile
     // step 0: QK^T and softmax of tile 0
     wait_tile(0);
-    auto issue0 = [&] { if (C::DIST < n_tiles) gather(C::DIST); };
     if (active) {
       floatx16 s;
       Soft sf;
-      step_mma(0, stage_ptr(0), stage_ptr(0), s, pb, sf, std::false_type{}, issue0);
+      step_mma(0, C::DIST, stage_ptr(0), stage_ptr(0), s, pb, sf, std::false_type{});
       pack_p(sf, pb);
     } else {
-      issue0();
+      gather(C::DIST);
     }
     // steps 1 .. n_tiles-1: QK^T and softmax of tile t under P V of tile t-1
     for (int t = 1; t < n_tiles; ++t) {
       wait_tile(t);
-      auto issue = [&] { if (t + C::DIST < n_tiles) gather(t + C::DIST); };
       if (active) {
         floatx16 s;
         Soft sf;
-        step_mma(t, stage_ptr(t), stage_ptr(t - 1), s, pb, sf, std::true_type{}, issue);
-        rescale_o(sf);
+        step_mma(t, t + C::DIST, stage_ptr(t), stage_ptr(t - 1), s, pb, sf, std::true_type{});
+        // P packed before the rare rescale branch: with its uses after the
+        // branch the compiler sinks the exponentials past it, out from under
+        // the MFMAs of the step
         pack_p(sf, pb);
+        rescale_o(sf);
       } else {
-        issue();
+        gather(t + C::DIST);
       }
     }
     // last step: P V of tile n_tiles-1
     if (active) last_pv(stage_ptr(n_tiles - 1), pb);
+    // the DMAs past the range may still be writing their (unread) stages
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
   // ---- epilogue: O / l (bf16 RNE), lse = ln 2 * (m + log2 l)
