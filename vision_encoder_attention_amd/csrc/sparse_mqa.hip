@@ -149,8 +149,11 @@ struct SCfg {
   static_assert(DQK % 32 == 0 && DV % 64 == 0 && DV <= DQK, "latent dims");
   static_assert(HEADS == kSparseHeadsPerWG, "host launch shape");
   static_assert(NT == 16, "the accumulator waits name 16 O^T tiles");
+  // Sorted index list: MAXK entries plus DIST tiles of padding, read (never
+  // used) by the DMAs of the steps past the last tile.
+  static constexpr int SIDX = MAXK + DIST * BN;
   // 32-bit words of LDS left for the counting sort's counts (two per word)
-  static constexpr int CNTW = (160 * 1024 - NSTAGE * TILE - MAXK * 4 - WAVES * 4) / 4;
+  static constexpr int CNTW = (160 * 1024 - NSTAGE * TILE - SIDX * 4 - WAVES * 4) / 4;
   static_assert(CNTW > 0, "LDS budget");
   // Q through the ring needs a stage per wave (one stage = one wave's Q
   // rows); the three-stage variant loads Q straight into registers.
@@ -193,7 +196,7 @@ template <int DQK, int DV, int MAXK>
 __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
   using C = SCfg<DQK, DV, MAXK>;
   __shared__ __attribute__((aligned(1024))) unsigned char ring[C::NSTAGE * C::TILE];
-  __shared__ int sidx[MAXK];
+  __shared__ int sidx[C::SIDX];
   __shared__ int wsum[C::WAVES];
   __shared__ uint32_t cntbuf[C::CNTW];
 
@@ -365,6 +368,10 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
     lds_barrier();
   }
   const int n_all = (nvalid + C::BN - 1) / C::BN;
+  // The rest of the last tile holds n_phys: its DMA offset is past the
+  // buffer's record bound, so those rows read as zeros.
+  for (int i = nvalid + tid; i < n_all * C::BN; i += C::THREADS) sidx[i] = p.n_phys;
+  lds_barrier();
   int t0 = 0, n_tiles = n_all;
   if (split) {
     t0 = (n_all * chunk) / p.nsplit;
@@ -372,15 +379,15 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
   }
   const int nloc = nvalid - t0 * C::BN;
   const int* srow = sidx + t0 * C::BN;
-  const int slim = MAXK - 1 - t0 * C::BN;               // last entry of sidx, from srow
 
 
   // ---- gather by DMA: 1 KB block bk of a tile is filled by wave bk % WAVES;
   // slot sl of the tile holds row sl / CPR, physical chunk sl % CPR =
   // logical chunk ^ swz(row).
   const uint64_t kv_addr = (uint64_t)(uintptr_t)p.kv;
-  const i32x4 kv_rsrc = (i32x4){(int)(uint32_t)kv_addr, (int)(uint32_t)(kv_addr >> 32) & 0xFFFF,
-                                (int)((int64_t)p.n_phys * C::ROWB), 0x00020000};
+  const int kv_records = (int)((int64_t)p.n_phys * C::ROWB);
+  const i32x4 kv_rsrc = (i32x4){(int)(uint32_t)kv_addr, (int)(uint32_t)(kv_addr >> 32) & 0xFFFF, kv_records,
+                                0x00020000};
   // Slot (row, byte column) of each of this lane's DMA blocks, packed
   // row << 16 | column; the same for every tile.
   int g_rc[C::BPW];
@@ -392,9 +399,10 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
     g_rc[bi] = (r << 16) | (16 * ((ph & ~7) | ((ph & 7) ^ C::swz(r))));
   }
   // A gather is issued for every step, also for tiles past this range's
-  // n_tiles (those DMAs read zeros into a stage no step reads again), so
-  // that the key loop has no branch around it and the count of DMAs in
-  // flight at each wait is fixed.  The index reads (gather_idx) and the DMAs
+  // n_tiles (those DMAs get a record bound of 0, so they read zeros into a
+  // stage no step reads again), so that the key loop has no branch around
+  // it and the count of DMAs in flight at each wait is fixed.  Their index
+  // reads stay inside sidx: (t0 + n_tiles + DIST) BN <= SIDX.  The index reads (gather_idx) and the DMAs
   // (gather_dma, one per block) are separate so that the step can spread
   // them between its MFMAs.
   // g_rc is read through an opaque copy at each use, so that its row and
@@ -402,16 +410,16 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
   auto gather_idx = [&](int kt, int bi) -> int {
     int g = g_rc[bi];
     asm volatile("" : "+v"(g));
-    return srow[min(kt * C::BN + (g >> 16), slim)];
+    return srow[kt * C::BN + (g >> 16)];
   };
   auto gather_dma = [&](int kt, int x, int bi) {
     const uint32_t dst = ring_lds + (uint32_t)((kt % C::NSTAGE) * C::TILE);
-    const int lim = kt < n_tiles ? nloc - kt * C::BN : 0;   // rows of the tile that exist
+    i32x4 rs = kv_rsrc;
+    rs[2] = __builtin_amdgcn_readfirstlane(kt < n_tiles ? kv_records : 0);
     int g = g_rc[bi];
     asm volatile("" : "+v"(g));
-    const uint32_t off = __umul24((uint32_t)x, (uint32_t)C::ROWB) + (uint32_t)(g & 0xFFFF);
-    dma16(kv_rsrc, __builtin_amdgcn_readfirstlane(dst + (uint32_t)((bi * C::WAVES + wave) * 1024)),
-          (g >> 16) < lim ? off : 0xFFFFFFF0u);         // past the range or the valid count: zeros
+    dma16(rs, __builtin_amdgcn_readfirstlane(dst + (uint32_t)((bi * C::WAVES + wave) * 1024)),
+          __umul24((uint32_t)x, (uint32_t)C::ROWB) + (uint32_t)(g & 0xFFFF));
   };
   auto gather = [&](int kt) {
     int x[C::BPW];
