@@ -401,12 +401,12 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
   // A gather is issued for every step, also for tiles past this range's
   // n_tiles (those DMAs get a record bound of 0, so they read zeros into a
   // stage no step reads again), so that the key loop has no branch around
-  // it and the count of DMAs in flight at each wait is fixed.  Their index
-  // reads stay inside sidx: (t0 + n_tiles + DIST) BN <= SIDX.  The index reads (gather_idx) and the DMAs
-  // (gather_dma, one per block) are separate so that the step can spread
-  // them between its MFMAs.
-  // g_rc is read through an opaque copy at each use, so that its row and
-  // column parts are recomputed there rather than kept live as 18 values.
+  // it and the count of DMAs in flight at each wait is fixed; their index
+  // reads stay inside sidx, (t0 + n_tiles + DIST) BN <= SIDX.  The index
+  // reads (gather_idx) and the DMAs (gather_dma, one per block) are separate
+  // so that the step can spread them between its MFMAs.  g_rc is read
+  // through an opaque copy at each use, so that its row and column parts are
+  // recomputed there rather than kept live as 18 values.
   auto gather_idx = [&](int kt, int bi) -> int {
     int g = g_rc[bi];
     asm volatile("" : "+v"(g));
