@@ -294,11 +294,23 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
       q_dma();
       q_issued = true;
     }
-    auto count = [&](int v) -> int { return (int)((cnt[v >> 1] >> (16 * (v & 1))) & 0xFFFFu); };
-    const int per = (p.n_kv + C::THREADS - 1) / C::THREADS;
+    // Each thread owns a run of `per` consecutive rows (even, so the run
+    // starts on a count word), read RPT rows (RPT / 2 independent words) at
+    // a time; the high half of the last word past n_kv was cleared above.
+    constexpr int RPT = 16;
+    const int per = ((p.n_kv + C::THREADS - 1) / C::THREADS + 1) & ~1;
     const int v0 = min(tid * per, p.n_kv), v1 = min(v0 + per, p.n_kv);
+    auto words = [&](int vb, uint32_t (&w)[RPT / 2]) {
+#pragma unroll
+      for (int j = 0; j < RPT / 2; ++j) w[j] = vb + 2 * j < v1 ? cnt[(vb >> 1) + j] : 0u;
+    };
     int tot = 0;
-    for (int v = v0; v < v1; ++v) tot += count(v);
+    for (int vb = v0; vb < v1; vb += RPT) {
+      uint32_t w[RPT / 2];
+      words(vb, w);
+#pragma unroll
+      for (int j = 0; j < RPT / 2; ++j) tot += (int)((w[j] & 0xFFFFu) + (w[j] >> 16));
+    }
     int incl = tot;                                     // inclusive scan over the wave
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -314,8 +326,17 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
       if (w < wave) base += wsum[w];
       nvalid += wsum[w];
     }
-    for (int v = v0; v < v1; ++v)
-      for (int c = count(v); c > 0; --c) sidx[base++] = v;
+    for (int vb = v0; vb < v1; vb += RPT) {
+      uint32_t w[RPT / 2];
+      words(vb, w);
+#pragma unroll
+      for (int j = 0; j < 2 * (RPT / 2); ++j) {         // row vb + j appears count times
+        const int c = (int)((w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+        if (c == 1) sidx[base] = vb + j;                // the usual case: distinct indices
+        else for (int r = 0; r < c; ++r) sidx[base + r] = vb + j;
+        base += c;
+      }
+    }
     lds_barrier();
   } else {
     // Bitonic sorting network in LDS; padding and out-of-range entries become
