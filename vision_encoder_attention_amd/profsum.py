@@ -19,7 +19,11 @@ reports, with the commands that produced the raw data):
     python -m vision_encoder_attention_amd.profsum trace DIR [--last N] [--match TEXT ...]
     python -m vision_encoder_attention_amd.profsum counters --kernel TEXT --fetch DIR --write DIR
         --copy-fetch DIR --copy-write DIR --algorithmic-bytes B --sources FILE ... [--mfma DIR]
-        [--extra DIR ...] [--last N]
+        [--extra DIR ...] [--also TEXT ...] [--last N]
+
+``--also`` names kernels launched with the main one in the same call (a
+merge kernel after a split); their bytes per dispatch are added to the
+launch's traffic.  The MFMA and extra counters are the main kernel's.
 """
 from __future__ import annotations
 
@@ -103,13 +107,22 @@ def _counter(dir_, counter, kernel):
 
 
 def counters_report(kernel, fetch, write, copy_fetch, copy_write, algorithmic_bytes, sources, mfma=None, last=0,
-                    extra=None, xcds=8, simds=1024):
+                    extra=None, xcds=8, simds=1024, also=None):
     out = []
     f = _counter(fetch, "FETCH_SIZE", kernel)
     w = _counter(write, "WRITE_SIZE", kernel)
     if not f or not w:
         raise SystemExit("kernel %r not found in the counter runs" % kernel)
     full_name = f[0][2]
+    more = []                                            # (name, fetch KiB, write KiB) per dispatch of the --also kernels
+    for k in also or []:
+        fa = _counter(fetch, "FETCH_SIZE", k)
+        wa = _counter(write, "WRITE_SIZE", k)
+        if not fa or not wa:
+            raise SystemExit("kernel %r not found in the counter runs" % k)
+        fva = [v for _, v, _ in fa][-last:] if last else [v for _, v, _ in fa]
+        wva = [v for _, v, _ in wa][-last:] if last else [v for _, v, _ in wa]
+        more.append((fa[0][2], statistics.mean(fva), statistics.mean(wva), len(fva)))
     cf = [v for _, v, _ in _counter(copy_fetch, "FETCH_SIZE", "copyBuffer")]
     cw = [v for _, v, _ in _counter(copy_write, "WRITE_SIZE", "copyBuffer")]
     fs = (COPY_BYTES >> 10) / statistics.median(cf)
@@ -123,6 +136,13 @@ def counters_report(kernel, fetch, write, copy_fetch, copy_write, algorithmic_by
                % (statistics.mean(fv), min(fv), max(fv), len(fv)))
     out.append("  WRITE_SIZE per dispatch (KiB): mean %.0f, min %.0f, max %.0f over %d dispatches"
                % (statistics.mean(wv), min(wv), max(wv), len(wv)))
+    for name, fm, wm, n in more:
+        out.append("launched with it: %s" % name)
+        out.append("  FETCH_SIZE per dispatch (KiB): mean %.0f over %d dispatches" % (fm, n))
+        out.append("  WRITE_SIZE per dispatch (KiB): mean %.0f over %d dispatches" % (wm, n))
+        rd += fm * 1024 * fs
+        wr += wm * 1024 * ws
+        full_name += " + " + name
     out.append("copy calibration (__amd_rocclr_copyBuffer, %d KiB read + %d KiB written):"
                % (COPY_BYTES >> 10, COPY_BYTES >> 10))
     out.append("  FETCH_SIZE %s -> scale %.4f" % ([round(x) for x in cf], fs))
@@ -192,12 +212,13 @@ def main(argv=None):
     c.add_argument("--algorithmic-bytes", type=float, required=True)
     c.add_argument("--sources", nargs="+", required=True)
     c.add_argument("--last", type=int, default=0)
+    c.add_argument("--also", nargs="*", help="kernels launched with the main one whose bytes count with it")
     a = ap.parse_args(argv)
     if a.cmd == "trace":
         print(trace_report(a.dir, a.last, a.match))
     else:
         print(counters_report(a.kernel, a.fetch, a.write, a.copy_fetch, a.copy_write, a.algorithmic_bytes, a.sources,
-                              a.mfma, a.last, a.extra, a.xcds, a.simds))
+                              a.mfma, a.last, a.extra, a.xcds, a.simds, a.also))
 
 
 if __name__ == "__main__":
