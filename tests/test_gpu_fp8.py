@@ -199,3 +199,49 @@ def test_fp8_full_size_vision_sampled_rows(torch):
     o, l = _run(torch, cu, q8, qs, k8, ks, v8, vs, False, 0.125, piece_rows=1462)
     rows = np.unique(np.concatenate([[0, 127, 1461, 1462, t - 1], rng.integers(0, t, 12)]))
     _bound_and_check(cu, q8, qs, k8, ks, v8, vs, False, 0.125, o, l, rows=rows)
+
+
+def test_fp8_mfma_accumulation_measured_through_lse(torch):
+    """The accumulation property the logit bound above rests on, measured
+    through the public entry point: with one key the lse is the logit itself,
+    so a head whose 64 products are one large product 2^(2a) and 63 products
+    of 1 shows what the FP8 MFMA's sum drops.  From 2^14 on, exactly the 7
+    small products that share the large one's group of 8 vanish; below that
+    the sum loses fewer; equal products are summed exactly; and every case
+    stays inside e_s of the module docstring."""
+    d = 64
+    cases = [(a, p) for a in range(9) for p in (0, 37)] + [(None, None)]   # (log2 of the large factor, its position)
+    h = len(cases)
+    one = 0x38                                          # E4M3 1.0
+    q8 = np.full((1, h, d), one, np.uint8)
+    exact = np.empty(h)
+    for i, (a, p) in enumerate(cases):
+        if a is None:
+            exact[i] = d                                # 64 products of 1
+        else:
+            q8[0, i, p] = (a + 7) << 3                  # E4M3 2^a (bias 7, mantissa 0)
+            exact[i] = 2.0 ** (2 * a) + (d - 1)
+    k8 = q8.copy()                                      # products q_j k_j = q_j^2
+    v8 = np.full((1, h, d), one, np.uint8)
+    qs = np.ones((1, h), np.float32)
+    ks = np.ones(h, np.float32)
+    vs = np.ones((h, d), np.float32)
+    scale = 2.0 ** -10
+    o, l = _run(torch, [0, 1], q8, qs, k8, ks, v8, vs, False, scale)
+    got = l[:, 0] / scale                               # the kernel's sum of products
+    drop = exact - got
+    log("fp8 MFMA sum of one large product 2^(2a) and 63 ones: drop per (a, position) %s" %
+        {c: round(float(x), 3) for c, x in zip(cases, drop)})
+    e_s = (7 * 2.0 ** -13 + (d + 10) * 2.0 ** -24) * exact                   # in product units
+    tol = e_s + (1e-5 * np.abs(exact * scale) + 1e-4) / scale
+    assert np.all(np.abs(drop) <= tol)
+    assert np.all(np.abs(drop - np.round(drop)) < 0.05)  # whole products of 1 are dropped, nothing else
+    drop = np.round(drop)
+    for (a, p), x in zip(cases, drop):
+        if a is None:
+            assert x == 0
+        elif a >= 7:
+            assert x == 7, (a, p, x)
+        else:
+            assert 0 <= x <= 7, (a, p, x)
+    assert np.all(o == 1.0)                             # one key: the output is its value row
