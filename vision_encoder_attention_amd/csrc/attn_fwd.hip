@@ -1470,6 +1470,8 @@ hipError_t launch_merge(const DenseParams& p, dim3 grid, hipStream_t s) {
     case 6: hipLaunchKernelGGL((attn_merge_kernel<D, 6>), grid, dim3(256), 0, s, p); break;
     case 7: hipLaunchKernelGGL((attn_merge_kernel<D, 7>), grid, dim3(256), 0, s, p); break;
     case 8: hipLaunchKernelGGL((attn_merge_kernel<D, 8>), grid, dim3(256), 0, s, p); break;
+    case 9: hipLaunchKernelGGL((attn_merge_kernel<D, 9>), grid, dim3(256), 0, s, p); break;
+    case 10: hipLaunchKernelGGL((attn_merge_kernel<D, 10>), grid, dim3(256), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipSuccess;
@@ -1669,13 +1671,13 @@ DenseSplit dense_split_plan(int units, int empty, int slots, int key_tiles) {
   // rows and end at once.  The last round holds (units - empty) % slots real
   // units and would leave most slots idle for a whole unit's time, so each of
   // them is split into as many key ranges as the idle slots allow (at most
-  // 8, at most one per key tile; a split below 2 is not worth the merge).
+  // 10, at most one per key tile; a split below 2 is not worth the merge).
   DenseSplit s{units, 1, 0};
   const int real = units - empty;
   if (slots <= 0 || real <= slots) return s;
   const int tail = real % slots;
   if (tail == 0) return s;
-  const int nsplit = std::min(std::min(8, slots / tail), key_tiles);
+  const int nsplit = std::min(std::min(10, slots / tail), key_tiles);
   if (nsplit < 2) return s;
   s.full_units = units - tail;
   s.nsplit = nsplit;
