@@ -20,6 +20,7 @@ launches are reported.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -95,7 +96,9 @@ def warm_up(torch, fn, steps):
     wall time.  The GPU's clock ramps up over tens of milliseconds of
     sustained load (the vision step runs ~20% slower over its first ~80
     launches), so a fixed handful of warmup launches would time the ramp.
-    Returns the number of calls made."""
+    Returns the number of calls made.  Python's cyclic garbage collector is
+    off while the GPU is timed (main turns it off); it runs here instead, so
+    no collection pause can fall between an event and the launch it times."""
     n = 0
     t0 = time.perf_counter()
     while n < steps or (time.perf_counter() - t0) * 1e3 < WARM_MS:
@@ -104,6 +107,7 @@ def warm_up(torch, fn, steps):
         if n % 8 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
+    gc.collect()
     return n
 
 
@@ -751,6 +755,7 @@ def main():
         torch.cuda.synchronize()
         err("copied %d bytes 3 times (expect FETCH_SIZE and WRITE_SIZE of %d KiB per copy)" % (n, n >> 10))
         return
+    gc.disable()                                         # collections run in warm_up, not while timing
     if args.only == "vision":
         case, tm, wall_ms, ent = bench_vision(torch, args)
         err(json.dumps({case.name: ent}))
@@ -793,6 +798,7 @@ def main():
         line["workloads"] = bench_other(torch, max(5, min(args.steps, 20)), args.warmup)
         for k, v in line["workloads"].items():
             err("%s: %s" % (k, v))
+    gc.enable()
     if not args.no_cpu_baseline:
         head, per = cpu_oracle(workers)
         head["per_workload"] = per
