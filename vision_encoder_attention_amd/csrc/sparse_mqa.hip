@@ -593,7 +593,6 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
     constexpr int LAST = PV ? NQK + NPV : NQK;
     constexpr int GSP = PV ? GSP_PV : GSP_QK;
     u32x4 opr[PD];
-    floatx16 s1;
     int xg[C::BPW];
     static_for<0, PD>([&](auto i) { opr[i.value] = load_op(kst, vst, i); });
     __builtin_amdgcn_sched_barrier(0);
@@ -605,23 +604,19 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(SparseParams p) {
       if constexpr (SL >= GS && (SL - GS) % GSP == 0 && (SL - GS) / GSP < C::BPW)
         gather_dma(kg, xg[(SL - GS) / GSP], (SL - GS) / GSP);
       if constexpr (SL < NQK) {
-        // two accumulators (even / odd k-steps): back-to-back MFMAs never
-        // wait on each other's result
+        // one accumulator: MFMAs that accumulate into the same registers
+        // issue back to back at the full rate
         if constexpr (SL == 0) mfma_s_first(s, a, qf[0]);
-        else if constexpr (SL == 1) mfma_s_first(s1, a, qf[1]);
-        else if constexpr (SL & 1) mfma_s(s1, a, qf[SL]);
         else mfma_s(s, a, qf[SL]);
         if constexpr (SL == NQK - 1 && !PV) {
-          xdl_drain_v(s1);
-          s += s1;
+          xdl_drain_v(s);
           mask_tail(kt, s);                             // keys past the valid count -> -inf
         }
       } else {
         constexpr int J = SL - NQK, KS = J / C::NT, NTI = J % C::NT;
         mfma_o(o[NTI], a, pb[KS]);
         if constexpr (J == 0) {                         // under the first P V MFMA: finish S^T
-          xdl_drain_v(s1);
-          s += s1;
+          xdl_drain_v(s);
           mask_tail(kt, s);                             // keys past the valid count -> -inf
         }
         // softmax pieces under P V slots 1 .. 13
