@@ -597,7 +597,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
   }
 }
 
-// ======================================== bf16, head_dim 64, one packed sequence
+// ============================================ bf16, head_dim 64, non-causal
 // The image case (non-causal, packed or paged K/V, no decode units).  At
 // head_dim 64 a 64-key step holds 16 MFMAs per 32 query rows but the same
 // softmax work per logit as at 128, so the kernel is bound by instruction
@@ -610,7 +610,10 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_fwd_bf16_kernel(D
 //   * the two blocks' logit -> softmax -> P V chains are independent, so one
 //     block's exponentials issue while the other's MFMAs run.
 // K and V of one step are staged together (double-buffered, one barrier per
-// step); the max-free softmax with its rare path is the other kernel's.
+// step).  The fast path forms P = 2^(s c) with no reference at all and
+// checks that fp32 held (every lane sum of a tile below 2^100, every row sum
+// at least 2^-100); a workgroup where it did not recomputes its key range on
+// the careful path, the other kernel's lazily moved reference.
 constexpr int kD64Threads = 256;                         // 4 waves x 64 rows = kD64BM
 
 template <bool PAGED>

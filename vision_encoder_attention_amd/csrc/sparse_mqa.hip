@@ -24,9 +24,9 @@
 //            zeros through the buffer's record bound), into a ring of stages
 //            filled ahead of use, 16-byte chunks XOR-swizzled within each row;
 //   S^T      = K Q^T, fp32 accumulation;
-//   softmax  fp32 online update with a lazily moved reference max, one step
-//            behind the MFMAs: the exponentials of tile t-1 run under the
-//            QK^T MFMAs of tile t;
+//   softmax  fp32 online update with a lazily moved reference max; the
+//            softmax of tile t runs on the VALU under the P V MFMAs of tile
+//            t-1, so each step is QK^T of tile t, then P V of tile t-1;
 //   O^T     += V^T P^T; the V^T operands come straight from the row-major tile
 //            with ds_read_b64_tr_b16 (each 16-lane group reads a 4-key x
 //            16-column block and receives it transposed).
