@@ -97,8 +97,11 @@ def warm_up(torch, fn, steps):
     sustained load (the vision step runs ~20% slower over its first ~80
     launches), so a fixed handful of warmup launches would time the ramp.
     Returns the number of calls made.  Python's cyclic garbage collector is
-    off while the GPU is timed (main turns it off); it runs here instead, so
-    no collection pause can fall between an event and the launch it times."""
+    off while the GPU is timed (main turns it off); it runs here instead,
+    first, so that no collection pause falls between an event and the launch
+    it times, and none leaves the GPU idle (and its clock falling) between the
+    warm-up and the timed launches."""
+    gc.collect()
     n = 0
     t0 = time.perf_counter()
     while n < steps or (time.perf_counter() - t0) * 1e3 < WARM_MS:
@@ -107,28 +110,57 @@ def warm_up(torch, fn, steps):
         if n % 8 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
-    gc.collect()
     return n
+
+
+_EVENT_POOL = []
+
+
+def reserve_events(torch, n):
+    """Create n event pairs and record each once, untimed.  The HIP event
+    behind a torch event is created at its first record; made inside a timed
+    loop, the first few hundred hold the host back long enough for the GPU to
+    run dry between launches, and the idle time lands inside the timings."""
+    fresh = []
+    while len(_EVENT_POOL) + len(fresh) < n:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        e1.record()
+        fresh.append((e0, e1))
+    torch.cuda.synchronize()
+    _EVENT_POOL.extend(fresh)
 
 
 class Timer:
     """Per-launch HIP event pairs on torch's current stream (the stream the
-    binding launches the kernels on)."""
+    binding launches the kernels on), taken from the pool that
+    reserve_events fills, and returned to it once read."""
 
     def __init__(self, torch):
         self.torch = torch
         self.pairs = {}
+        self.vals = {}
 
     def run(self, name, fn):
-        e0 = self.torch.cuda.Event(enable_timing=True)
-        e1 = self.torch.cuda.Event(enable_timing=True)
+        if _EVENT_POOL:
+            e0, e1 = _EVENT_POOL.pop()
+        else:
+            e0 = self.torch.cuda.Event(enable_timing=True)
+            e1 = self.torch.cuda.Event(enable_timing=True)
         e0.record()
         fn()
         e1.record()
         self.pairs.setdefault(name, []).append((e0, e1))
 
     def times(self, name):
-        return [a.elapsed_time(b) for a, b in self.pairs[name]]
+        """Milliseconds per launch (read once, after the caller's synchronize;
+        the events then go back to the pool)."""
+        if name not in self.vals:
+            pairs = self.pairs.pop(name)
+            self.vals[name] = [a.elapsed_time(b) for a, b in pairs]
+            _EVENT_POOL.extend(pairs)
+        return self.vals[name]
 
     def ms(self, name):
         v = self.times(name)
@@ -212,29 +244,34 @@ def dense_entry(torch, wname, case, st, tm, steps, with_rope):
 
 
 def bench_vision(torch, args):
-    """The headline step: qkv_rope then attn_fwd over the vision image, K
-    steps after the warm-up, with one event pair per step and nothing else
-    inside the step (each event is a command of its own on the stream).  A
-    second pass of K steps times each kernel with its own events, for the
-    rooflines."""
+    """The headline step: qkv_rope then attn_fwd over the vision image.  After
+    the warm-up, K steps run back to back between two synchronizations with
+    nothing else on the stream; their wall time per step is the headline.  A
+    second pass of K steps with one event pair per step gives the median and
+    minimum of single steps, and a third times each kernel with its own
+    events, for the rooflines."""
     from vision_encoder_attention_amd import runner as R
     from vision_encoder_attention_amd import workloads as W
     case = W.vision()
     st = R.stage_dense(case)
     args.warmup_done = warm_up(torch, lambda: R.run_dense(st), args.warmup)
-    steps = Timer(torch)
+    reserve_events(torch, 3 * args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        steps.run("step", lambda: R.run_dense(st))
+        R.run_dense(st)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    steps = Timer(torch)
+    for _ in range(args.steps):
+        steps.run("step", lambda: R.run_dense(st))
+    torch.cuda.synchronize()
     tm = Timer(torch)
     for _ in range(args.steps):
         tm.run("qkv_rope", lambda: R.run_rope(st))
         tm.run("attn_fwd", lambda: R.run_attn(st))
     torch.cuda.synchronize()
-    tm.pairs["step"] = steps.pairs["step"]
+    tm.vals["step"] = steps.times("step")
     ent = dense_entry(torch, "vision", case, st, tm, max(5, min(args.steps, 20)), with_rope=True)
     del st
     torch.cuda.empty_cache()
@@ -758,6 +795,7 @@ def main():
         torch.cuda.synchronize()
         err("copied %d bytes 3 times (expect FETCH_SIZE and WRITE_SIZE of %d KiB per copy)" % (n, n >> 10))
         return
+    reserve_events(torch, 3 * max(args.steps, 20))
     gc.disable()                                         # collections run in warm_up, not while timing
     if args.only == "vision":
         case, tm, wall_ms, ent = bench_vision(torch, args)
