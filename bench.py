@@ -179,7 +179,10 @@ def roofline(bound, kernel, achieved, peak, unit, traffic_profile=None, algorith
     committed summary (null when absent or stale)."""
     r = {"bound": bound, "kernel": kernel, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
          "frac": round(achieved / peak, 4),
-         "traffic": committed_traffic(traffic_profile) if traffic_profile else None}
+         "traffic": None}
+    if traffic_profile:                                  # file name, or (file name, workload label)
+        prof, entry = traffic_profile if isinstance(traffic_profile, tuple) else (traffic_profile, None)
+        r["traffic"] = committed_traffic(prof, entry)
     if algorithmic_bytes is not None:
         r["algorithmic_bytes"] = algorithmic_bytes
     r.update(extra)
@@ -575,7 +578,7 @@ def bench_fp8(torch, steps, warmup):
                                    "bf16_attn_fwd_ms": _r(b_ms), "quantize_qkv_ms": _r(qn_ms), "flops": fl,
                                    "roofline": roofline("mfma", "attn_fwd_fp8_kernel<%d,%s>" % (
                                        case.head_dim, "true" if case.causal else "false"), tf, PEAK_FP8_TFLOPS,
-                                       "TFLOP/s")}
+                                       "TFLOP/s", ("attn_fwd_fp8_hbm_counters.txt", FP8_PROFILE_ENTRY[name]))}
         del st, q, k, v, q8, k8, v8, out, lse
         torch.cuda.empty_cache()
     return res
@@ -589,7 +592,7 @@ def bench_proj(torch, steps, warmup):
     from vision_encoder_attention_amd import runner as R
     from vision_encoder_attention_amd import workloads as W
     res = {}
-    for case in (W.vision_proj(), W.varlen_proj()):
+    for case, label in ((W.vision_proj(), "vision"), (W.varlen_proj(), "varlen")):
         st = R.stage_proj(case)
         R.run_rope_table(st)
         t, hid = case.x.shape
@@ -619,17 +622,25 @@ def bench_proj(torch, steps, warmup):
                           "qkv_proj_rope_min_ms": _r(pr["min"]), "tflops": round(tf, 2),
                           "frac_bf16_peak": _r(tf / PEAK_BF16_TFLOPS), "flops": fl, "rope_table_ms": _r(tb_ms),
                           "unfused_matmul_plus_qkv_rope_ms": _r(u_ms),
-                          "roofline": roofline("mfma", "qkv_proj_kernel", tf, PEAK_BF16_TFLOPS, "TFLOP/s")}
+                          "roofline": roofline("mfma", "qkv_proj_kernel", tf, PEAK_BF16_TFLOPS, "TFLOP/s",
+                                               ("qkv_proj_hbm_counters.txt", "%s %d x %d -> %d" % (label, t, hid, n)))}
         del st, y, qr, kr
         torch.cuda.empty_cache()
     return res
 
 
-def committed_traffic(profile: str):
+# workload labels of the FP8 counter summary, by workload
+FP8_PROFILE_ENTRY = {"vision": "vision 8547 tokens, 16 heads, d 64",
+                     "varlen_gqa": "varlen 32876 tokens, 32/8 heads, d 128, causal",
+                     "long_causal": "32K causal, 16 heads, d 128"}
+
+
+def committed_traffic(profile: str, entry=None):
     """HBM bytes per launch recorded in a committed counter summary under
     profiles/ (FETCH_SIZE and WRITE_SIZE, each scaled by what the same counter
     reads for a plain copy of known size), or None when the kernel source has
-    changed since the counters were taken."""
+    changed since the counters were taken.  A summary that covers several
+    workloads is read at the entry whose workload label is `entry`."""
     path = os.path.join(ROOT, "profiles", profile)
     if not os.path.exists(path):
         return None
@@ -641,7 +652,10 @@ def committed_traffic(profile: str):
     from vision_encoder_attention_amd.profsum import source_digest
     if not rec or rec.get("source_digest") != source_digest(rec["sources"]):
         return None
-    return rec["hbm_bytes_per_launch"]
+    if "entries" in rec:                                 # one summary for several workloads
+        hit = [e for e in rec["entries"] if e.get("workload") == entry]
+        return hit[0]["hbm_bytes_per_launch"] if hit else None
+    return rec.get("hbm_bytes_per_launch")
 
 
 def host_info(workers):
