@@ -7,6 +7,9 @@
   them one after the other (no shared state, one writer per output).
 * Workgroups taking their units in another order (VEA_DEBUG_WG_ORDER) give
   bitwise the same results.
+* The bindings reject mismatched shapes and tensors on another device before
+  anything is launched: the C entry points see only pointers and sizes, so a
+  short buffer would otherwise be read or written past its end.
 """
 import os
 
@@ -180,3 +183,75 @@ def test_workgroup_order_does_not_change_results(torch, order):
     assert len(got) == len(ref) == 12
     for i, (g, r) in enumerate(zip(got, ref)):
         assert torch.equal(g, r), "output %d differs under %s order" % (i, order)
+
+
+def test_bindings_reject_mismatched_shapes_before_launch(torch):
+    """One mismatch per case; every call raises ValueError and its output,
+    filled with a sentinel, is untouched (nothing was launched)."""
+    import vision_encoder_attention_amd as vea
+    dev = "cuda"
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    t, hq, hkv, d = 96, 4, 2, 64
+    q = torch.randn(t, hq, d, device=dev).to(bf)
+    k = torch.randn(t, hkv, d, device=dev).to(bf)
+    v = torch.randn(t, hkv, d, device=dev).to(bf)
+    cu = torch.tensor([0, 40, t], dtype=i32, device=dev)
+    out = torch.full((t, hq, d), 7.0, device=dev).to(bf)
+    lse = torch.full((hq, t), 7.0, device=dev)
+
+    def rejects(fn, watch):
+        before = watch.clone()
+        with pytest.raises(ValueError):
+            fn()
+        torch.cuda.synchronize()
+        assert torch.equal(watch, before)
+
+    rejects(lambda: vea.attn_fwd(q, k, v[:50], cu, cu, False, 0.125, out, lse), out)           # v rows
+    rejects(lambda: vea.attn_fwd(q, k, v[:, :, :32].contiguous(), cu, cu, False, 0.125, out), out)  # v head_dim
+    rejects(lambda: vea.attn_fwd(q, k, v, cu, cu, False, 0.125, out[:50]), out)               # out rows
+    rejects(lambda: vea.attn_fwd(q, k, v, cu, cu[:2], False, 0.125, out), out)                # cu lengths
+    rejects(lambda: vea.attn_fwd(q, k, v, cu, cu, False, 0.125, out, lse.cpu()), out)          # lse on the host
+    rejects(lambda: vea.attn_fwd_noalloc(q, k, v[:50], cu, cu, False, 0.125, out, max_seqlen_q=56,
+                                         max_seqlen_k=56), out)
+    kc = torch.randn(128, hkv, d, device=dev).to(bf)
+    bt = torch.tensor([[0, 1], [0, 1]], dtype=i32, device=dev)
+    rejects(lambda: vea.attn_fwd_paged(q, kc, kc[:, :1].contiguous(), bt, 64, cu, cu, False, 0.125, out,
+                                       max_seqlen_q=56, max_seqlen_k=56, total_k=t), out)      # v_cache heads
+    qd = torch.randn(2, hq, d, device=dev).to(bf)
+    od = torch.full((2, hq, d), 7.0, device=dev).to(bf)
+    rejects(lambda: vea.attn_decode(qd, k[:, :, :32].contiguous(), v[:, :, :32].contiguous(), cu, 0.125, od), od)
+    # rope: outputs shorter than the projection output, positions of the wrong length
+    x = torch.randn(t, (hq + 2 * hkv) * d, device=dev).to(bf)
+    pos = torch.arange(t, dtype=i32, device=dev)
+    qo = torch.full((t, hq, d), 7.0, device=dev).to(bf)
+    ko = torch.full((t, hkv, d), 7.0, device=dev).to(bf)
+    rejects(lambda: vea.qkv_rope(x, pos, 1e4, qo[:50], ko), qo)
+    rejects(lambda: vea.qkv_rope(x, pos[:50], 1e4, qo, ko), qo)
+    # FP8: a q scale of the wrong shape
+    q8 = torch.zeros(t, hq, d, dtype=torch.uint8, device=dev)
+    k8 = torch.zeros(t, hkv, d, dtype=torch.uint8, device=dev)
+    rejects(lambda: vea.attn_fwd_fp8(q8, torch.ones(t, device=dev), k8, torch.ones(hkv, device=dev), k8,
+                                     torch.ones(hkv, d, device=dev), cu, cu, False, 0.125, out), out)
+    # projection: a weight of the wrong height
+    hid = 128
+    xp = torch.randn(t, hid, device=dev).to(bf)
+    wp = torch.randn(hid // 2, (hq + 2 * hkv) * d, device=dev).to(bf)
+    vo = torch.full((t, hkv, d), 7.0, device=dev).to(bf)
+    rejects(lambda: vea.qkv_proj_rope(xp, wp, None, None, qo, ko, vo), qo)
+    # sparse MQA: latent rows narrower than q's d_qk, out with the wrong heads
+    r, h, dqk, dv, kk = 3, 128, 576, 512, 64
+    qs_ = torch.randn(r, h, dqk, device=dev).to(bf)
+    kv = torch.randn(100, dqk, device=dev).to(bf)
+    idx = torch.zeros(r, kk, dtype=i32, device=dev)
+    os_ = torch.full((r, h, dv), 7.0, device=dev).to(bf)
+    rejects(lambda: vea.sparse_mqa_fwd(qs_, kv[:, :512].contiguous(), idx, kk, 0.04, os_), os_)
+    rejects(lambda: vea.sparse_mqa_fwd(qs_, kv, idx, kk, 0.04, os_[:, :64].contiguous()), os_)
+    pt = torch.arange(2, dtype=i32, device=dev)
+    rejects(lambda: vea.sparse_mqa_paged_fwd(qs_, kv[:64, :512].contiguous(), pt, 64, 100, idx, kk, 0.04, os_), os_)
+    # top-k: an output on the host
+    lg = torch.randn(4, 300, device=dev)
+    ot = torch.full((4, 32), 7, dtype=i32, device=dev)
+    rejects(lambda: vea.topk_indices(lg, 32, ot.cpu()), ot)
+    # probability export: a piece past k's rows
+    pb = torch.full((10, t), 7.0, device=dev)
+    rejects(lambda: vea.attn_probs_piece(q, k, lse, 0, 0, t, 0, t + 5, 0, 10, False, 0.125, pb), pb)

@@ -139,6 +139,28 @@ def _token_major(t, name):
     return t.stride(0)
 
 
+def _on_device(dev, *named):
+    """Every given tensor, (name, tensor) pairs, None skipped, lives on dev:
+    the call launches on q's device with raw pointers, so a tensor elsewhere
+    would be read through an address that means nothing there."""
+    for name, t in named:
+        if t is not None and t.device != dev:
+            raise ValueError("%s must be on %s (the device of the call), not %s" % (name, dev, t.device))
+
+
+def _shape(t, want, name):
+    if tuple(t.shape) != tuple(want):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(want), tuple(t.shape)))
+
+
+def _dense_shapes(q, k, v, out, kname="k", vname="v"):
+    """k and v of one shape [rows, Hkv, d] with q's d; out of q's shape."""
+    _shape(v, k.shape, vname)
+    if k.shape[2] != q.shape[2]:
+        raise ValueError("%s must have q's head_dim %d, got %d" % (kname, q.shape[2], k.shape[2]))
+    _shape(out, q.shape, "out")
+
+
 def _int32_dev(t, name):
     torch = _torch()
     if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
@@ -176,6 +198,12 @@ def attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, causal, scale, out, lse=None, 
     dt = _dtype_code(q)
     if k.dtype != q.dtype or v.dtype != q.dtype or out.dtype != q.dtype:
         raise TypeError("q, k, v and out must share a dtype")
+    _dense_shapes(q, k, v, out)
+    if cu_seqlens_k.numel() != cu_seqlens_q.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k need the same number of entries")
+    _on_device(q.device, ("k", k), ("v", v), ("out", out), ("cu_seqlens_q", cu_seqlens_q),
+               ("cu_seqlens_k", cu_seqlens_k), ("lse", lse),
+               ("workspace", None if isinstance(workspace, str) else workspace))
     if lse is not None:
         torch = _torch()
         if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (q.shape[1], q.shape[0]):
@@ -221,6 +249,11 @@ def attn_fwd_noalloc(q, k, v, cu_seqlens_q, cu_seqlens_k, causal, scale, out, ls
     dt = _dtype_code(q)
     if k.dtype != q.dtype or v.dtype != q.dtype or out.dtype != q.dtype:
         raise TypeError("q, k, v and out must share a dtype")
+    _dense_shapes(q, k, v, out)
+    if cu_seqlens_k.numel() != cu_seqlens_q.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k need the same number of entries")
+    _on_device(q.device, ("k", k), ("v", v), ("out", out), ("cu_seqlens_q", cu_seqlens_q),
+               ("cu_seqlens_k", cu_seqlens_k), ("lse", lse))
     if lse is not None:
         torch = _torch()
         if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (q.shape[1], q.shape[0]):
@@ -258,6 +291,12 @@ def attn_fwd_paged(q, k_cache, v_cache, block_table, page_size, cu_seqlens_q, cu
     page_size = int(page_size)
     if page_size < 1 or k_cache.shape[0] % page_size or v_cache.shape[0] != k_cache.shape[0]:
         raise ValueError("cache rows must be a multiple of page_size and equal for k and v")
+    _dense_shapes(q, k_cache, v_cache, out, "k_cache", "v_cache")
+    if cu_seqlens_k.numel() != cu_seqlens_q.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k need the same number of entries")
+    _on_device(q.device, ("k_cache", k_cache), ("v_cache", v_cache), ("out", out), ("block_table", block_table),
+               ("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k), ("lse", lse),
+               ("workspace", None if isinstance(workspace, str) else workspace))
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
                             or tuple(lse.shape) != (q.shape[1], q.shape[0])):
         raise ValueError("lse must be contiguous float32 [Hq, total_q]")
@@ -328,6 +367,9 @@ def attn_decode(q, k, v, cu_seqlens_k, scale, out, lse=None, *, block_table=None
     batch = cu_seqlens_k.numel() - 1
     if q.shape[0] != batch or tuple(out.shape) != tuple(q.shape):
         raise ValueError("q and out need one row per sequence")
+    _dense_shapes(q, k, v, out)
+    _on_device(q.device, ("k", k), ("v", v), ("out", out), ("cu_seqlens_k", cu_seqlens_k), ("lse", lse),
+               ("block_table", block_table), ("workspace", None if isinstance(workspace, str) else workspace))
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
                             or tuple(lse.shape) != (q.shape[1], batch)):
         raise ValueError("lse must be contiguous float32 [Hq, batch]")
@@ -373,6 +415,14 @@ def qkv_rope(x_qkv, positions, theta, q, k, rotate_half=False):
     if not (q.is_contiguous() and k.is_contiguous()):
         raise ValueError("q and k outputs must be contiguous")
     _int32_dev(positions, "positions")
+    t = x_qkv.shape[0]
+    if q.dim() != 3 or k.dim() != 3 or q.shape[0] != t or k.shape[0] != t or k.shape[2] != q.shape[2]:
+        raise ValueError("q [T, Hq, d] and k [T, Hkv, d] must have x_qkv's T tokens and one head_dim")
+    if x_qkv.shape[1] < (q.shape[1] + k.shape[1]) * q.shape[2]:
+        raise ValueError("x_qkv holds fewer columns than the Q and K heads")
+    if positions.shape[0] != t or not (positions.dim() == 1 or (positions.dim() == 2 and positions.shape[1] == 2)):
+        raise ValueError("positions must be int32 [T] or [T, 2]")
+    _on_device(x_qkv.device, ("q", q), ("k", k), ("positions", positions))
     st = lib.vea_qkv_rope(_ptr(x_qkv), x_qkv.stride(0), _ptr(positions), positions.dim(), x_qkv.shape[0],
                           q.shape[1], k.shape[1], q.shape[2], float(theta), int(bool(rotate_half)), _ptr(q), _ptr(k),
                           _stream(x_qkv))
@@ -415,10 +465,21 @@ def attn_fwd_fp8(q, q_scale, k, k_scale, v, v_scale, cu_seqlens_q, cu_seqlens_k,
     for t, n in ((q_scale, "q_scale"), (k_scale, "k_scale"), (v_scale, "v_scale")):
         if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
             raise ValueError("%s must be a contiguous float32 GPU tensor" % n)
-    if out.dtype != torch.bfloat16 or out.stride(2) != 1:
-        raise ValueError("out must be bfloat16 with contiguous head_dim")
+    if out.dtype != torch.bfloat16 or out.dim() != 3 or out.stride(2) != 1 or out.stride(1) != out.shape[2]:
+        raise ValueError("out must be bfloat16 [Tq, Hq, d] with contiguous heads")
     _int32_dev(cu_seqlens_q, "cu_seqlens_q")
     _int32_dev(cu_seqlens_k, "cu_seqlens_k")
+    _dense_shapes(q, k, v, out)
+    _shape(q_scale, q.shape[:2], "q_scale")
+    _shape(k_scale, (k.shape[1],), "k_scale")
+    _shape(v_scale, (v.shape[1], v.shape[2]), "v_scale")
+    if cu_seqlens_k.numel() != cu_seqlens_q.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k need the same number of entries")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (q.shape[1], q.shape[0])):
+        raise ValueError("lse must be contiguous float32 [Hq, Tq]")
+    _on_device(q.device, ("q_scale", q_scale), ("k", k), ("k_scale", k_scale), ("v", v), ("v_scale", v_scale),
+               ("out", out), ("lse", lse), ("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k))
     if max_seqlen_q is None or max_seqlen_k is None:
         cq = cu_seqlens_q.cpu()
         ck = cu_seqlens_k.cpu()
@@ -467,11 +528,35 @@ def qkv_proj_rope(x, w, bias, cos_sin, q, k, v, rotate_half_span=0):
         raise ValueError("bias must be contiguous")
     if cos_sin is not None and (cos_sin.dtype != torch.float32 or not cos_sin.is_contiguous()):
         raise ValueError("cos_sin must be a contiguous float32 table")
+    t, hidden = x.shape
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k and v must be [T, heads, d]")
+    d = q.shape[2]
+    n = (q.shape[1] + 2 * k.shape[1]) * d
+    _shape(q, (t, q.shape[1], d), "q")
+    _shape(k, (t, k.shape[1], d), "k")
+    _shape(v, k.shape, "v")
+    _shape(w, (hidden, n), "w")
+    if bias is not None:
+        _shape(bias, (n,), "bias")
+    if cos_sin is not None:
+        _shape(cos_sin, (t, d // 2, 2), "cos_sin")
+    _on_device(x.device, ("w", w), ("bias", bias), ("cos_sin", cos_sin), ("q", q), ("k", k), ("v", v))
     st = lib.vea_qkv_proj_rope(_ptr(x), x.stride(0), _ptr(w), w.stride(0), _ptr(bias), _ptr(cos_sin), x.shape[0],
                                x.shape[1], q.shape[1], k.shape[1], q.shape[2], int(rotate_half_span), _ptr(q), _ptr(k),
                                _ptr(v), _stream(x))
     _check(st)
     return q, k, v
+
+
+def _sparse_shapes(q, kv, out, kvname):
+    """q [R, H, d_qk], kv [rows, d_qk], out [R, H, d_v]."""
+    if q.dim() != 3 or kv.dim() != 2 or out.dim() != 3:
+        raise ValueError("q and out must be [rows, heads, dim] and %s [rows, d_qk]" % kvname)
+    if kv.shape[1] != q.shape[2]:
+        raise ValueError("%s rows must hold q's d_qk = %d values" % (kvname, q.shape[2]))
+    if out.shape[:2] != q.shape[:2]:
+        raise ValueError("out must have q's rows and heads %s" % (tuple(q.shape[:2]),))
 
 
 def sparse_mqa_workspace_size(rows, heads, d_qk, d_v, k) -> int:
@@ -496,6 +581,9 @@ def sparse_mqa_fwd(q, kv_latent, topk_idx, k, scale, out, lse=None, workspace="a
         if t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
             raise ValueError("%s must be a contiguous bfloat16 GPU tensor" % n)
     _int32_dev(topk_idx, "topk_idx")
+    _sparse_shapes(q, kv_latent, out, "kv_latent")
+    _on_device(q.device, ("kv_latent", kv_latent), ("topk_idx", topk_idx), ("out", out), ("lse", lse),
+               ("workspace", None if isinstance(workspace, str) else workspace))
     if topk_idx.shape != (q.shape[0], k):
         raise ValueError("topk_idx must be [rows, k]")
     if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (q.shape[1], q.shape[0])
@@ -530,6 +618,9 @@ def sparse_mqa_paged_fwd(q, kv_cache, page_table, page_size, n_kv, topk_idx, k, 
             raise ValueError("%s must be a contiguous bfloat16 GPU tensor" % n)
     _int32_dev(topk_idx, "topk_idx")
     _int32_dev(page_table, "page_table")
+    _sparse_shapes(q, kv_cache, out, "kv_cache")
+    _on_device(q.device, ("kv_cache", kv_cache), ("page_table", page_table), ("topk_idx", topk_idx), ("out", out),
+               ("lse", lse), ("workspace", None if isinstance(workspace, str) else workspace))
     page_size = int(page_size)
     if page_size < 1 or kv_cache.shape[0] % page_size:
         raise ValueError("kv_cache rows must be a multiple of page_size")
@@ -570,6 +661,7 @@ def topk_indices(logits, k, out, row_starts=None, row_lens=None):
             _int32_dev(t, nm)
             if t.numel() != logits.shape[0]:
                 raise ValueError("%s must have one entry per row" % nm)
+    _on_device(logits.device, ("out", out), ("row_starts", row_starts), ("row_lens", row_lens))
     st = lib.vea_topk_indices(_ptr(logits), logits.stride(0), _ptr(row_starts), _ptr(row_lens), logits.shape[0],
                               logits.shape[1], int(k), _ptr(out), _stream(logits))
     _check(st)
@@ -583,6 +675,13 @@ def attn_probs_piece(q, k, lse, head, seq_begin_q, len_q, seq_begin_k, len_k, q0
     qs, ks = _token_major(q, "q"), _token_major(k, "k")
     if p_out.stride(1) != 1:
         raise ValueError("p_out rows must be contiguous")
+    if int(seq_begin_q) + int(len_q) > q.shape[0] or int(seq_begin_k) + int(len_k) > k.shape[0]:
+        raise ValueError("the piece's sequence lies past q's or k's rows")
+    if p_out.dim() != 2 or p_out.shape[0] < int(rows) or p_out.shape[1] < int(len_k):
+        raise ValueError("p_out must hold rows x len_k values")
+    if lse.dim() != 2 or lse.shape[0] != q.shape[1] or lse.stride(1) != 1:
+        raise ValueError("lse must be the float32 [Hq, total_q] output of attn_fwd")
+    _on_device(q.device, ("k", k), ("lse", lse), ("p_out", p_out))
     st = lib.vea_attn_probs_piece(_dtype_code(q), _ptr(q), qs, _ptr(k), ks, _ptr(lse), lse.stride(0), int(head),
                                   q.shape[1], k.shape[1], q.shape[2], int(seq_begin_q), int(len_q),
                                   int(seq_begin_k), int(len_k), int(q0), int(rows), 1 if causal else 0,
