@@ -117,20 +117,20 @@ def test_rotation_table_against_the_oracle(torch):
 
 
 @pytest.mark.parametrize("name", ["vision", "varlen"])
-def test_full_size_sampled_rows_and_bitwise_repeat(torch, name):
+def test_full_size_whole_tensors_and_bitwise_repeat(torch, name):
     """The full projections (vision: 8547 x 1024 -> 3072, 2D; varlen: 32876 x
-    4096 -> 6144, GQA, 1D) against the oracle on sampled token rows (tile
-    edges, the last token, random rows), and bitwise equal on a second run."""
+    4096 -> 6144, GQA, 1D): every element of q, k and v within one bf16 ulp
+    of the oracle, and bitwise equal on a second run."""
     case = W.vision_proj() if name == "vision" else W.varlen_proj()
     t = case.x.shape[0]
     log("proj full %s T=%d hidden=%d" % (name, t, case.x.shape[1]))
     st = _run(torch, case)
-    rng = np.random.default_rng(713)
-    rows = np.unique(np.concatenate([[0, 127, 128, 255, t - 129, t - 128, t - 1], rng.integers(0, t, 40)]))
-    q, k, v = _oracle(case, rows=rows)
-    _assert_ulp(_f64(st.q[rows]), q, "q")
-    _assert_ulp(_f64(st.k[rows]), k, "k")
-    _assert_ulp(_f64(st.v[rows]), v, "v")
+    q, k, v = _oracle(case)
+    _assert_ulp(_f64(st.q), q, "q")
+    del q
+    _assert_ulp(_f64(st.k), k, "k")
+    _assert_ulp(_f64(st.v), v, "v")
+    del k, v
     q1, k1, v1 = st.q.clone(), st.k.clone(), st.v.clone()
     R.run_proj(st)
     torch.cuda.synchronize()
