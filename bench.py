@@ -489,7 +489,16 @@ def bench_sparse(torch, steps, warmup):
     pt = torch.from_numpy(table).cuda()
     p = timed("paged", lambda: vea.sparse_mqa_paged_fwd(st.q, kvc, pt, ps, case.kv_latent.shape[0], st.idx,
                                                          case.k, case.scale, st.out, st.lse, workspace=st.ws))
+    # the same index sets with each row independently permuted: the kernel sorts
+    # every row first, so neither the time nor the bits may depend on the order
+    prng = np.random.default_rng(65)
+    perm = torch.from_numpy(np.stack([prng.permutation(row) for row in case.topk_idx]).astype(np.int32)).cuda()
+    out_p, lse_p = torch.empty_like(st.out), torch.empty_like(st.lse)
+    pm = timed("permuted", lambda: vea.sparse_mqa_fwd(st.q, st.kv, perm, case.k, case.scale, out_p, lse_p,
+                                                      workspace=st.ws))
     t = timed("sparse", lambda: R.run_sparse(st))
+    torch.cuda.synchronize()
+    perm_equal = bool(torch.equal(out_p, st.out) and torch.equal(lse_p, st.lse))
     gbs = by / t["mean"] / 1e6
     res[case.name] = {"sparse_mqa_ms": _r(t["mean"]), "sparse_mqa_median_ms": _r(t["median"]),
                       "sparse_mqa_min_ms": _r(t["min"]), "gbs": round(gbs, 1),
@@ -504,7 +513,11 @@ def bench_sparse(torch, steps, warmup):
     res[case.name + "_paged64"] = {"sparse_mqa_ms": _r(p["mean"]), "sparse_mqa_median_ms": _r(p["median"]),
                                    "sparse_mqa_min_ms": _r(p["min"]), "gbs": round(by / p["mean"] / 1e6, 1),
                                    "frac_hbm": _r(by / p["mean"] / 1e6 / PEAK_HBM_GBS), "page_size": ps}
-    del scratch, st, kvc
+    res[case.name + "_rows_permuted"] = {"sparse_mqa_ms": _r(pm["mean"]), "sparse_mqa_median_ms": _r(pm["median"]),
+                                         "sparse_mqa_min_ms": _r(pm["min"]),
+                                         "frac_hbm": _r(by / pm["mean"] / 1e6 / PEAK_HBM_GBS),
+                                         "bitwise_equal_to_unpermuted": perm_equal}
+    del scratch, st, kvc, perm, out_p, lse_p
     torch.cuda.empty_cache()
     return res
 

@@ -189,6 +189,11 @@ def counters_report(kernel, fetch, write, copy_fetch, copy_write, algorithmic_by
             if "SQ_VALU_MFMA_COEXEC_CYCLES" in means:
                 out.append("  MFMA co-execution: SQ_VALU_MFMA_COEXEC_CYCLES / (cycles x %d SIMDs) = %.3f"
                            % (simds, means["SQ_VALU_MFMA_COEXEC_CYCLES"] / (cyc * simds)))
+        if "TCC_HIT_sum" in means and "TCC_MISS_sum" in means:
+            req = means["TCC_HIT_sum"] + means["TCC_MISS_sum"]
+            if req > 0:
+                out.append("  L2 hit rate: TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum) = %.3f" % (means["TCC_HIT_sum"] / req))
+                rec["l2_hit_rate"] = round(means["TCC_HIT_sum"] / req, 4)
     out.append("")
     out.append("RESULT " + json.dumps(rec))
     return "\n".join(out)
